@@ -1,0 +1,221 @@
+"""QLoRA NF4 linear layer for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over libqlora_nf4.so (C ABI in include/qlora_nf4.h).  This
+module only marshals arguments: it checks devices / dtypes / contiguity, passes
+raw device pointers and the current HIP stream, and allocates outputs and
+workspaces with torch.  Every step of the computation runs in the library's
+hand-written HIP kernels; there is no CPU or PyTorch fallback.
+
+Public API (names follow the pages' problem statement):
+    quantize(w, block_size=64, double_quant=False, dq_group=256) -> NF4Weight
+    dequantize(q, dtype=torch.bfloat16) -> Tensor [rows, cols]
+    linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False)
+    linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False)
+    workspace_bytes(op, m, rows, cols, r, dtype) ; levels()
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import QloraError, QloraNf4  # noqa: F401
+
+__all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "workspace_bytes",
+           "levels", "QloraError", "dtype_code"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.float32:
+        return _lib.QLORA_F32
+    if dtype == torch.bfloat16:
+        return _lib.QLORA_BF16
+    if dtype == torch.float16:
+        return _lib.QLORA_F16
+    raise TypeError("unsupported dtype %s (float32, bfloat16 or float16)" % (dtype,))
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need_cuda(name, t, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+@dataclass
+class NF4Weight:
+    """An NF4-quantized frozen weight [rows, cols] held in device memory."""
+    rows: int
+    cols: int
+    block_size: int
+    double_quant: bool
+    dq_group: int
+    codes: "object"                      # uint8 [rows*cols/2]
+    absmax: "object" = None              # float32 [nb]
+    absmax_q: "object" = None            # uint8 [nb]
+    absmax_scale2: "object" = None       # float32 [ng]
+
+    @property
+    def shape(self) -> Tuple[int, int]:
+        return (self.rows, self.cols)
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def size_bytes(self) -> int:
+        n = self.codes.numel()
+        for t in (self.absmax, self.absmax_q, self.absmax_scale2):
+            if t is not None:
+                n += t.numel() * t.element_size()
+        return n
+
+    def descriptor(self) -> QloraNf4:
+        return QloraNf4(self.rows, self.cols, self.block_size, int(self.double_quant),
+                        self.dq_group, 0, _ptr(self.codes), _ptr(self.absmax),
+                        _ptr(self.absmax_q), _ptr(self.absmax_scale2))
+
+
+def empty_nf4(rows: int, cols: int, block_size: int = 64, double_quant: bool = False,
+              dq_group: int = 256, device="cuda") -> NF4Weight:
+    torch = _torch()
+    n = rows * cols
+    nb = n // block_size if block_size > 0 else 0
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=device)
+    if double_quant:
+        ng = (nb + dq_group - 1) // dq_group
+        return NF4Weight(rows, cols, block_size, True, dq_group, codes, None,
+                         torch.empty(nb, dtype=torch.uint8, device=device),
+                         torch.empty(ng, dtype=torch.float32, device=device))
+    return NF4Weight(rows, cols, block_size, False, dq_group, codes,
+                     torch.empty(nb, dtype=torch.float32, device=device))
+
+
+def quantize(w, block_size: int = 64, double_quant: bool = False, dq_group: int = 256) -> NF4Weight:
+    """Blockwise NF4 quantization of a 2-D fp32 GPU tensor (optionally with the block
+    scales double-quantized to u8 + one fp32 scale per dq_group blocks)."""
+    torch = _torch()
+    _need_cuda("w", w, torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [rows, cols]")
+    rows, cols = w.shape
+    if block_size <= 0 or (rows * cols) % block_size:
+        desc_bs = block_size  # let the library produce the status and message
+        q = NF4Weight(rows, cols, desc_bs, double_quant, dq_group,
+                      torch.empty(0, dtype=torch.uint8, device=w.device))
+    else:
+        q = empty_nf4(rows, cols, block_size, double_quant, dq_group, w.device)
+    d = q.descriptor()
+    _lib.check(_lib.lib().qlora_nf4_quantize(_ptr(w), ctypes.byref(d), _stream_ptr(w.device)))
+    return q
+
+
+def dequantize(q: NF4Weight, dtype=None):
+    """w_hat = fl32(level * block scale), rounded to nearest-even into ``dtype``."""
+    torch = _torch()
+    dtype = torch.bfloat16 if dtype is None else dtype
+    out = torch.empty(q.rows, q.cols, dtype=dtype, device=q.device)
+    d = q.descriptor()
+    _lib.check(_lib.lib().qlora_nf4_dequantize(ctypes.byref(d), dtype_code(dtype), _ptr(out),
+                                              _stream_ptr(q.device)))
+    return out
+
+
+def workspace_bytes(op: int, m: int, rows: int, cols: int, r: int, dtype) -> int:
+    return int(_lib.lib().qlora_workspace_bytes(op, m, rows, cols, r, dtype_code(dtype)))
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), nbytes))
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _flatten(x, cols):
+    if x.shape[-1] != cols:
+        raise ValueError("last dim of x must be %d, got %d" % (cols, x.shape[-1]))
+    lead = tuple(x.shape[:-1])
+    return x.reshape(-1, cols), lead
+
+
+def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t: bool = False,
+               rslora: bool = False, workspace=None):
+    """y = x . deq(W)^T + s (x . A^T) . B^T (+ bias), s = alpha / r (alpha / sqrt(r)
+    with rslora).  Leading dims of x are flattened to tokens.  Returns y, or
+    (y, T0) with T0 = x A^T in fp32 when save_t."""
+    torch = _torch()
+    dt = x.dtype
+    x2, lead = _flatten(x, q.cols)
+    x2 = x2.contiguous()
+    for name, t in (("x", x2), ("lora_a", lora_a), ("lora_b", lora_b), ("bias", bias)):
+        _need_cuda(name, t, dt)
+    r = lora_a.shape[0]
+    m = x2.shape[0]
+    y = torch.empty(m, q.rows, dtype=dt, device=x.device)
+    t0 = torch.empty(m, r, dtype=torch.float32, device=x.device) if save_t else None
+    ws = _workspace(workspace_bytes(_lib.QLORA_OP_FWD, m, q.rows, q.cols, r, dt), x.device, workspace)
+    d = q.descriptor()
+    flags = _lib.QLORA_FLAG_RSLORA if rslora else 0
+    _lib.check(_lib.lib().qlora_linear_fwd(
+        ctypes.byref(d), _ptr(x2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
+        _ptr(bias), dtype_code(dt), _ptr(y), _ptr(t0), _ptr(ws), ws.numel(), _stream_ptr(x.device)))
+    y = y.reshape(*lead, q.rows)
+    return (y, t0) if save_t else y
+
+
+def linear_bwd(q: NF4Weight, x, dy, lora_a, lora_b, alpha: float, t_saved=None, need_dx: bool = True,
+               rslora: bool = False, workspace=None):
+    """Gradients with the base frozen: returns (dX or None, dA fp32 [r, cols], dB fp32 [rows, r])."""
+    torch = _torch()
+    dt = x.dtype
+    x2, lead = _flatten(x, q.cols)
+    dy2, _ = _flatten(dy, q.rows)
+    x2, dy2 = x2.contiguous(), dy2.contiguous()
+    for name, t in (("x", x2), ("dy", dy2), ("lora_a", lora_a), ("lora_b", lora_b)):
+        _need_cuda(name, t, dt)
+    _need_cuda("t_saved", t_saved, torch.float32)
+    r = lora_a.shape[0]
+    m = x2.shape[0]
+    dx = torch.empty(m, q.cols, dtype=dt, device=x.device) if need_dx else None
+    da = torch.empty(r, q.cols, dtype=torch.float32, device=x.device)
+    db = torch.empty(q.rows, r, dtype=torch.float32, device=x.device)
+    ws = _workspace(workspace_bytes(_lib.QLORA_OP_BWD, m, q.rows, q.cols, r, dt), x.device, workspace)
+    d = q.descriptor()
+    flags = _lib.QLORA_FLAG_RSLORA if rslora else 0
+    _lib.check(_lib.lib().qlora_linear_bwd(
+        ctypes.byref(d), _ptr(x2), _ptr(dy2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
+        dtype_code(dt), _ptr(t_saved), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), ws.numel(),
+        _stream_ptr(x.device)))
+    if dx is not None:
+        dx = dx.reshape(*lead, q.cols)
+    return dx, da, db
+
+
+def levels():
+    """The 16 fp32 NF4 levels the kernels use (host copy)."""
+    out = (ctypes.c_float * 16)()
+    _lib.check(_lib.lib().qlora_nf4_levels(out))
+    return [float(v) for v in out]

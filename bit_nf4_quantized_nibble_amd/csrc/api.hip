@@ -1,0 +1,285 @@
+// api.hip -- host side of libqlora_nf4.so: the C ABI declared in
+// include/qlora_nf4.h, argument validation, error reporting and the NF4 level
+// table.  Validation happens before anything is launched, so a refused call
+// writes nothing (qlora-rs export refuses invalid layers before writing; the
+// rust_ai_core QLoraConfig validate_for_training returns an error for an
+// invalid configuration).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "common.h"
+
+namespace qnf4 {
+
+namespace {
+thread_local char g_err[512] = "";
+
+// ---------------------------------------------------------------- NF4 levels
+// "LoRA and QLoRA, mathematically", "NF4: quantizing the frozen base": 16 levels at
+// the quantiles of a normal distribution (printed to 3 decimals on the qlora-rs
+// README, "NF4 Quantization").  Construction: with the offset
+// d = (1 - 1/30)/2 + (1 - 1/32)/2, 8 positive levels are the normal quantiles at
+// d - j (d - 1/2) / 8 (j = 0..7), 7 negative levels are minus those at
+// d - j (d - 1/2) / 7 (j = 0..6), plus an exact zero; all divide by the largest and
+// round once to binary32.  The quantile is found by Newton's method on the CDF.
+double normal_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+double normal_pdf(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * M_PI); }
+double normal_quantile_upper(double p) {  // p in (1/2, 1)
+  double x = 0.0;
+  for (int it = 0; it < 200; ++it) {
+    const double dx = (normal_cdf(x) - p) / normal_pdf(x);
+    x -= dx;
+    if (fabs(dx) <= 1e-17 * (1.0 + fabs(x))) break;
+  }
+  return x;
+}
+
+Nf4Tables g_tables;
+bool g_tables_ok = false;
+std::once_flag g_tables_once;
+
+void build_tables() {
+  const double d = 0.5 * (1.0 - 1.0 / 30.0) + 0.5 * (1.0 - 1.0 / 32.0);
+  const double top = normal_quantile_upper(d);
+  double lv[16];
+  int i = 0;
+  for (int j = 0; j <= 6; ++j) lv[i++] = -normal_quantile_upper(d - j * (d - 0.5) / 7.0) / top;
+  lv[i++] = 0.0;
+  for (int j = 7; j >= 0; --j) lv[i++] = normal_quantile_upper(d - j * (d - 0.5) / 8.0) / top;
+  Nf4Tables t;
+  for (int k = 0; k < 16; ++k) t.lv[k] = (float)lv[k];
+  // Nearest level with ties to the lower code: code = #{j : x > mid_j} with the
+  // midpoints exact in fp64; for binary32 x that is #{j : x >= thr_j}, thr_j the
+  // smallest binary32 strictly above mid_j.
+  for (int j = 0; j < 15; ++j) {
+    const double mid = ((double)t.lv[j] + (double)t.lv[j + 1]) / 2.0;
+    float th = (float)mid;
+    if ((double)th <= mid) th = nextafterf(th, INFINITY);
+    t.thr[j] = th;
+  }
+  // Bucket table: bucket b holds x with b <= 16 (x + 1) < b + 1.
+  bool ok = true;
+  for (int b = 0; b < 32; ++b) {
+    const double lo = b / 16.0 - 1.0, hi = (b + 1) / 16.0 - 1.0;
+    int base = 0, inside = 0;
+    float th = INFINITY;
+    for (int j = 0; j < 15; ++j) {
+      if ((double)t.thr[j] <= lo)
+        ++base;
+      else if ((double)t.thr[j] < hi || (b == 31 && (double)t.thr[j] <= 1.0)) {
+        ++inside;
+        th = t.thr[j];
+      }
+      // fl32(16 x + 16) may misplace x by a few 1e-7 near an edge: keep thresholds away.
+      if (fabs((double)t.thr[j] - lo) < 1e-6 || fabs((double)t.thr[j] - hi) < 1e-6) ok = false;
+    }
+    if (inside > 1) ok = false;
+    t.bucket_base[b] = base;
+    t.bucket_thr[b] = th;
+  }
+  g_tables = t;
+  g_tables_ok = ok;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_cd(int32_t cd) { return cd == QLORA_F32 || cd == QLORA_BF16 || cd == QLORA_F16; }
+
+int validate_desc(const qlora_nf4_t* q, bool need_data, const char* who) {
+  if (!q) return set_error(QLORA_ERR_INVALID_ARG, "%s: null descriptor", who);
+  if (q->rows < 0 || q->cols < 0) return set_error(QLORA_ERR_SHAPE, "%s: negative shape", who);
+  if (q->reserved != 0) return set_error(QLORA_ERR_INVALID_ARG, "%s: reserved field must be 0", who);
+  const int64_t n = q->rows * q->cols;
+  const int32_t bs = q->block_size;
+  if (bs <= 0 || (bs & 1)) return set_error(QLORA_ERR_SHAPE, "%s: block_size %d must be positive and even", who, bs);
+  if (n % bs != 0) return set_error(QLORA_ERR_SHAPE, "%s: %lld elements not a multiple of block_size %d", who, (long long)n, bs);
+  if (q->double_quant != 0 && q->double_quant != 1)
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: double_quant must be 0 or 1", who);
+  if (q->double_quant && q->dq_group <= 0)
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: dq_group must be positive", who);
+  if (!need_data || n == 0) return QLORA_OK;
+  if (!q->codes) return set_error(QLORA_ERR_INVALID_ARG, "%s: null codes", who);
+  if (!aligned16(q->codes)) return set_error(QLORA_ERR_INVALID_ARG, "%s: codes must be 16-byte aligned", who);
+  if (q->double_quant) {
+    if (!q->absmax_q || !q->absmax_scale2)
+      return set_error(QLORA_ERR_INVALID_ARG, "%s: double quant needs absmax_q and absmax_scale2", who);
+  } else if (!q->absmax) {
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: null absmax", who);
+  }
+  return QLORA_OK;
+}
+
+int validate_layer(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
+                   const void* lora_b, int32_t r, float alpha, int32_t flags, int32_t cd,
+                   const char* who) {
+  int rc = validate_desc(w, true, who);
+  if (rc) return rc;
+  if (!valid_cd(cd)) return set_error(QLORA_ERR_DTYPE, "%s: bad compute dtype %d", who, cd);
+  if (m < 0) return set_error(QLORA_ERR_SHAPE, "%s: negative m", who);
+  if (r < 1) return set_error(QLORA_ERR_INVALID_ARG, "%s: rank r must be >= 1 (got %d)", who, r);
+  if (!isfinite(alpha)) return set_error(QLORA_ERR_INVALID_ARG, "%s: alpha must be finite", who);
+  if (flags & ~QLORA_FLAG_RSLORA) return set_error(QLORA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", who, flags);
+  if (w->rows < 1 || w->cols < 1) return set_error(QLORA_ERR_SHAPE, "%s: empty weight", who);
+  if (!x || !lora_a || !lora_b) return set_error(QLORA_ERR_INVALID_ARG, "%s: null x / lora_a / lora_b", who);
+  if (w->cols % 64 != 0)
+    return set_error(QLORA_ERR_UNSUPPORTED, "%s: cols (%lld) must be a multiple of 64", who, (long long)w->cols);
+  if (w->block_size % 32 != 0 || w->cols % w->block_size != 0)
+    return set_error(QLORA_ERR_UNSUPPORTED, "%s: block_size %d must be a multiple of 32 dividing cols", who,
+                     w->block_size);
+  return QLORA_OK;
+}
+
+float lora_scale(float alpha, int32_t r, int32_t flags) {
+  if (flags & QLORA_FLAG_RSLORA) return (float)((double)alpha / sqrt((double)r));
+  return (float)((double)alpha / (double)r);
+}
+
+int check_tables(const char* who) {
+  std::call_once(g_tables_once, build_tables);
+  if (!g_tables_ok) return set_error(QLORA_ERR_UNSUPPORTED, "%s: NF4 lookup table failed its self-check", who);
+  return QLORA_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need, const char* who) {
+  if (ws_bytes < need)
+    return set_error(QLORA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu required", who, ws_bytes, need);
+  if (need > 0 && (!ws || ((uintptr_t)ws & 255u)))
+    return set_error(QLORA_ERR_WORKSPACE, "%s: workspace must be non-null and 256-byte aligned", who);
+  return QLORA_OK;
+}
+
+}  // namespace
+
+const Nf4Tables& host_tables() {
+  std::call_once(g_tables_once, build_tables);
+  return g_tables;
+}
+
+int set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(QLORA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return QLORA_OK;
+}
+
+}  // namespace qnf4
+
+using namespace qnf4;
+
+extern "C" {
+
+int qlora_abi_version(void) { return QLORA_NF4_ABI_VERSION; }
+
+const char* qlora_last_error(void) { return g_err; }
+
+int qlora_nf4_levels(float out[16]) {
+  if (!out) return set_error(QLORA_ERR_INVALID_ARG, "levels: null output");
+  const Nf4Tables& t = host_tables();
+  for (int i = 0; i < 16; ++i) out[i] = t.lv[i];
+  return QLORA_OK;
+}
+
+int qlora_nf4_quantize(const float* w, qlora_nf4_t* q, void* stream) {
+  g_err[0] = 0;
+  int rc = validate_desc(q, true, "quantize");
+  if (rc) return rc;
+  const int64_t n = q->rows * q->cols;
+  if (n == 0) return QLORA_OK;
+  if (!w) return set_error(QLORA_ERR_INVALID_ARG, "quantize: null weight");
+  if (!aligned16(w)) return set_error(QLORA_ERR_INVALID_ARG, "quantize: weight must be 16-byte aligned");
+  const int32_t bs = q->block_size;
+  if (bs < 8 || bs > 512 || (bs & (bs - 1)))
+    return set_error(QLORA_ERR_UNSUPPORTED, "quantize: block_size %d (need a power of two in 8..512)", bs);
+  if (q->double_quant && q->dq_group > 4096)
+    return set_error(QLORA_ERR_UNSUPPORTED, "quantize: dq_group %d > 4096", q->dq_group);
+  if ((rc = check_tables("quantize"))) return rc;
+  return launch_quantize(w, q, (hipStream_t)stream);
+}
+
+int qlora_nf4_dequantize(const qlora_nf4_t* q, int32_t out_dtype, void* out, void* stream) {
+  g_err[0] = 0;
+  int rc = validate_desc(q, true, "dequantize");
+  if (rc) return rc;
+  if (!valid_cd(out_dtype)) return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", out_dtype);
+  const int64_t n = q->rows * q->cols;
+  if (n == 0) return QLORA_OK;
+  if (!out) return set_error(QLORA_ERR_INVALID_ARG, "dequantize: null output");
+  if (!aligned16(out)) return set_error(QLORA_ERR_INVALID_ARG, "dequantize: output must be 16-byte aligned");
+  if (q->block_size % 8 != 0)
+    return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: block_size %d must be a multiple of 8", q->block_size);
+  if ((rc = check_tables("dequantize"))) return rc;
+  return launch_dequantize(q, out_dtype, out, (hipStream_t)stream);
+}
+
+size_t qlora_workspace_bytes(int32_t op, int64_t m, int64_t rows, int64_t cols, int32_t r, int32_t cd) {
+  if (m < 0 || rows < 0 || cols < 0 || r < 1 || !valid_cd(cd)) return 0;
+  if (op == QLORA_OP_FWD) return fwd_workspace_bytes(m, rows, cols, r, cd);
+  if (op == QLORA_OP_BWD) return bwd_workspace_bytes(m, rows, cols, r, cd);
+  return 0;
+}
+
+int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
+                     const void* lora_b, int32_t r, float alpha, int32_t flags, const void* bias,
+                     int32_t cd, void* y, float* t_save, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = validate_layer(w, x, m, lora_a, lora_b, r, alpha, flags, cd, "linear_fwd");
+  if (rc) return rc;
+  if (!y) return set_error(QLORA_ERR_INVALID_ARG, "linear_fwd: null y");
+  if (m == 0) return QLORA_OK;
+  if ((rc = check_ws(ws, ws_bytes, fwd_workspace_bytes(m, w->rows, w->cols, r, cd), "linear_fwd"))) return rc;
+  if ((rc = check_tables("linear_fwd"))) return rc;
+  LayerCall c;
+  c.w = make_w(w);
+  c.cd = cd;
+  c.m = m;
+  c.r = r;
+  c.scale = lora_scale(alpha, r, flags);
+  c.x = x;
+  c.lora_a = lora_a;
+  c.lora_b = lora_b;
+  c.bias = bias;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_forward(c, y, t_save);
+}
+
+int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m,
+                     const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,
+                     int32_t cd, const float* t_saved, void* dx, float* d_a, float* d_b, void* ws,
+                     size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = validate_layer(w, x, m, lora_a, lora_b, r, alpha, flags, cd, "linear_bwd");
+  if (rc) return rc;
+  if (!dy || !d_a || !d_b) return set_error(QLORA_ERR_INVALID_ARG, "linear_bwd: null dy / d_a / d_b");
+  if (m == 0) return set_error(QLORA_ERR_SHAPE, "linear_bwd: m must be >= 1 (dA, dB would be all zero)");
+  if ((rc = check_ws(ws, ws_bytes, bwd_workspace_bytes(m, w->rows, w->cols, r, cd), "linear_bwd"))) return rc;
+  if ((rc = check_tables("linear_bwd"))) return rc;
+  LayerCall c;
+  c.w = make_w(w);
+  c.cd = cd;
+  c.m = m;
+  c.r = r;
+  c.scale = lora_scale(alpha, r, flags);
+  c.x = x;
+  c.lora_a = lora_a;
+  c.lora_b = lora_b;
+  c.bias = nullptr;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_backward(c, dy, t_saved, dx, d_a, d_b);
+}
+
+}  // extern "C"

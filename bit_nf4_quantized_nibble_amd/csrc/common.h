@@ -1,0 +1,152 @@
+// common.h -- types and device helpers shared by the gfx950 kernels of
+// libqlora_nf4.so.  Internal: not part of the C ABI (include/qlora_nf4.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qlora_nf4.h"
+
+namespace qnf4 {
+
+// ----------------------------------------------------------------------------
+// Vector types for MFMA operands and 16-byte memory traffic.
+// ----------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef _Float16 f16x8_t __attribute__((__vector_size__(16)));
+typedef float f32x16_t __attribute__((__vector_size__(64)));
+typedef float f32x4_t __attribute__((__vector_size__(16)));
+typedef unsigned int u32x4_t __attribute__((__vector_size__(16)));
+typedef unsigned int u32x2_t __attribute__((__vector_size__(8)));
+
+enum Cd : int { CD_F32 = QLORA_F32, CD_BF16 = QLORA_BF16, CD_F16 = QLORA_F16 };
+
+// Level table and quantization lookups, computed once on the host (api.hip) and
+// passed to kernels by value (kernel arguments land in scalar registers).
+struct Nf4Tables {
+  float lv[16];      // the 16 NF4 levels, ascending, binary32
+  float thr[15];     // thr[j] = smallest binary32 above the midpoint of lv[j], lv[j+1]
+  int bucket_base[32];   // code of the lowest value in bucket b of [-1, 1] (width 1/16)
+  float bucket_thr[32];  // the one threshold inside bucket b, or +inf
+};
+
+// An NF4 weight as the kernels see it.
+struct Nf4W {
+  const uint8_t* codes;      // [rows * cols / 2]
+  const float* absmax;       // [nb] (no double quant)
+  const uint8_t* absmax_q;   // [nb] (double quant)
+  const float* scale2;       // [ng] (double quant)
+  int64_t rows, cols;
+  int32_t bs;                // block size (elements)
+  int32_t dq;                // double quantization on/off
+  int32_t g;                 // blocks per second-level scale
+};
+
+// fl32(a * b), kept as a binary32 value.  Without the register barrier the
+// compiler may fuse the product with a following f16 conversion into one
+// mixed-precision FMA that rounds once to f16, skipping the binary32 rounding the
+// dequantization defines (w_hat = fl32(L[c] * s_b), then rounded to the dtype).
+__device__ __forceinline__ float fl32_mul(float a, float b) {
+  float p = a * b;
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+// Scale of block b: the fp32 absmax, or fl32(q_b * S_group) with double quant.
+__device__ __forceinline__ float block_scale(const Nf4W& w, int64_t b) {
+  if (w.dq) return (float)w.absmax_q[b] * w.scale2[b / w.g];
+  return w.absmax[b];
+}
+
+// ----------------------------------------------------------------------------
+// Compute-dtype conversions (round to nearest even, as the hardware converts).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
+  _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+template <int CD>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (CD == CD_BF16) return pack2_bf16(lo, hi);
+  else return pack2_f16(lo, hi);
+}
+template <int CD>
+__device__ __forceinline__ uint16_t to_cd16(float v) {
+  if constexpr (CD == CD_BF16) return __builtin_bit_cast(uint16_t, (__bf16)v);
+  else return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+template <int CD>
+__device__ __forceinline__ float from_cd16(uint16_t h) {
+  if constexpr (CD == CD_BF16) return __uint_as_float((uint32_t)h << 16);
+  else return (float)__builtin_bit_cast(_Float16, h);
+}
+// Load one element of a compute-dtype array as fp32.
+template <int CD>
+__device__ __forceinline__ float load_cd(const void* p, int64_t i) {
+  if constexpr (CD == CD_F32) return ((const float*)p)[i];
+  else return from_cd16<CD>(((const uint16_t*)p)[i]);
+}
+// Store an fp32 value into a compute-dtype array.
+template <int CD>
+__device__ __forceinline__ void store_cd(void* p, int64_t i, float v) {
+  if constexpr (CD == CD_F32) ((float*)p)[i] = v;
+  else ((uint16_t*)p)[i] = to_cd16<CD>(v);
+}
+
+constexpr int cd_bytes(int cd) { return cd == CD_F32 ? 4 : 2; }
+
+// ----------------------------------------------------------------------------
+// Host-side launch plumbing (defined in api.hip).
+// ----------------------------------------------------------------------------
+const Nf4Tables& host_tables();
+int set_error(int status, const char* fmt, ...);
+int check_launch(const char* what);
+
+inline Nf4W make_w(const qlora_nf4_t* q) {
+  Nf4W w;
+  w.codes = q->codes;
+  w.absmax = q->absmax;
+  w.absmax_q = q->absmax_q;
+  w.scale2 = q->absmax_scale2;
+  w.rows = q->rows;
+  w.cols = q->cols;
+  w.bs = q->block_size;
+  w.dq = q->double_quant;
+  w.g = q->double_quant ? q->dq_group : 1;
+  return w;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Launchers (quant.hip, gemm.hip, gemv.hip).  Each returns a qlora_status_t.
+int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s);
+int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_t s);
+
+struct LayerCall {
+  Nf4W w;
+  int cd;
+  int64_t m;          // tokens
+  int32_t r;
+  float scale;        // alpha / r (or alpha / sqrt(r))
+  const void* x;      // [m, cols]
+  const void* lora_a; // [r, cols]
+  const void* lora_b; // [rows, r]
+  const void* bias;   // [rows] or null
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
+size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
+int launch_forward(const LayerCall& c, void* y, float* t_save);
+int launch_backward(const LayerCall& c, const void* dy, const float* t_saved, void* dx,
+                    float* d_a, float* d_b);
+
+}  // namespace qnf4

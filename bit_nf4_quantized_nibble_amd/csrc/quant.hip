@@ -1,0 +1,224 @@
+// quant.hip -- NF4 quantize (+ double quantization of the scales) and dequantize
+// for gfx950.  Both are HBM streams; the arithmetic is arranged so that every
+// code, scale and dequantized value is bit-identical to the definition:
+//
+//   qlora-rs README, "Honest capability matrix": per-block absmax scales, NF4
+//   pack/unpack, double quant to u8 with a scale-of-scales that replaces the
+//   resident fp32 scales; "NF4 Quantization": the 16 levels.
+//   "LoRA and QLoRA, mathematically", "NF4: quantizing the frozen base": levels at
+//   normal quantiles; each weight takes the nearest level of w / absmax.
+//
+// Quantize layout: each lane owns 8 consecutive fp32 weights (two 16-byte loads)
+// and produces one 32-bit word of packed codes.  A block of BS weights spans
+// BS/8 adjacent lanes, whose absmax is combined with lane shuffles.  One
+// workgroup walks one double-quant group (or a 16384-element span without DQ),
+// so the group max and the u8 encoding need no second pass over HBM.
+#include "common.h"
+
+namespace qnf4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Nearest-level code of a normalised value x in [-1, 1]: a 32-bucket table over
+// [-1, 1] holds, per bucket, the code of its lowest value and the single
+// threshold inside it (the host checks that no bucket holds two thresholds and
+// that no threshold sits within rounding distance of a bucket edge).
+__device__ __forceinline__ uint32_t nearest_code(float x, const int* __restrict__ base,
+                                                 const float* __restrict__ thr) {
+  float u = fmaf(x, 16.0f, 16.0f);
+  int b = (int)fminf(fmaxf(u, 0.0f), 31.0f);
+  return (uint32_t)(base[b] + (x >= thr[b] ? 1 : 0));
+}
+
+template <int BS>
+__global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__ w, int64_t n,
+                                                       uint8_t* __restrict__ codes,
+                                                       float* __restrict__ absmax,
+                                                       uint8_t* __restrict__ absmax_q,
+                                                       float* __restrict__ scale2,
+                                                       int blocks_per_wg, int dq, Nf4Tables tab) {
+  constexpr int LPB = BS / 8;  // lanes per block
+  __shared__ int s_base[32];
+  __shared__ float s_thr[32];
+  __shared__ float s_amax[4096];  // block scales of this group (double quant only)
+  __shared__ float s_red[kThreads / 64];
+
+  const int tid = threadIdx.x;
+  if (tid < 32) {
+    s_base[tid] = tab.bucket_base[tid];
+    s_thr[tid] = tab.bucket_thr[tid];
+  }
+  __syncthreads();
+
+  const int64_t nb = n / BS;
+  const int64_t blk0 = (int64_t)blockIdx.x * blocks_per_wg;
+  const int64_t nblk = (blk0 + blocks_per_wg <= nb) ? blocks_per_wg : nb - blk0;
+  const int64_t e_begin = blk0 * BS;
+  const int64_t e_count = nblk * BS;
+
+  for (int64_t e = (int64_t)tid * 8; e < e_count; e += (int64_t)kThreads * 8) {
+    const f32x4_t* src = (const f32x4_t*)(w + e_begin + e);
+    f32x4_t v0 = __builtin_nontemporal_load(src);
+    f32x4_t v1 = __builtin_nontemporal_load(src + 1);
+    float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+#pragma unroll
+    for (int off = 1; off < LPB; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+
+    const int64_t blk_local = e / BS;
+    if ((tid % LPB) == 0) {
+      if (dq)
+        s_amax[blk_local] = a;
+      else
+        absmax[blk0 + blk_local] = a;
+    }
+
+    // x = fl32(w / a) by Markstein's correction: r = RN(1/a) once per block, then
+    // y = RN(w r) is within an ulp of w / a and RN(y + RN(w - a y) r) = RN(w / a).
+    // Blocks of very small or very large magnitude are rescaled by an exact power
+    // of two first so that 1/a stays a normal number.
+    const float sc = (a < 0x1p-64f) ? 0x1p64f : ((a > 0x1p64f) ? 0x1p-64f : 1.0f);
+    const float as = a * sc;
+    const float rcp = 1.0f / as;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float ws = v[i] * sc;
+      float y = ws * rcp;
+      float rem = fmaf(-as, y, ws);
+      float x = fmaf(rem, rcp, y);
+      if (a == 0.0f) x = 0.0f;
+      uint32_t c = nearest_code(x, s_base, s_thr);
+      // element 2k -> high nibble of byte k
+      word |= c << ((i >> 1) * 8 + ((i & 1) ? 0 : 4));
+    }
+    *(uint32_t*)(codes + (e_begin + e) / 2) = word;
+  }
+
+  if (!dq) return;
+  __syncthreads();
+  // Group max of the block scales, then S = fl32(max / 255) and
+  // q_b = round-half-even(a_b / S) (exact: the fp64 quotient of two binary32
+  // values never rounds onto a half-integer it is not equal to).
+  float c = 0.0f;
+  for (int64_t b = tid; b < nblk; b += kThreads) c = fmaxf(c, s_amax[b]);
+  for (int off = 32; off >= 1; off >>= 1) c = fmaxf(c, __shfl_xor(c, off, 64));
+  if ((tid & 63) == 0) s_red[tid >> 6] = c;
+  __syncthreads();
+  c = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float S = c / 255.0f;
+  if (tid == 0) scale2[blockIdx.x] = S;
+  for (int64_t b = tid; b < nblk; b += kThreads) {
+    double q = 0.0;
+    if (S > 0.0f) {
+      q = __builtin_rint((double)s_amax[b] / (double)S);
+      q = q < 0.0 ? 0.0 : (q > 255.0 ? 255.0 : q);
+    }
+    absmax_q[blk0 + b] = (uint8_t)q;
+  }
+}
+
+// Dequantize: each lane decodes 32 consecutive weights (16 bytes of codes).
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void k_dequantize(Nf4W q, int64_t n, void* __restrict__ out,
+                                                         Nf4Tables tab) {
+  __shared__ float s_lv[16];
+  if (threadIdx.x < 16) s_lv[threadIdx.x] = tab.lv[threadIdx.x];
+  __syncthreads();
+  const int64_t e0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 32;
+  if (e0 >= n) return;
+  const bool full = (e0 + 32 <= n);
+  uint32_t words[4];
+  if (full) {
+    u32x4_t v = *(const u32x4_t*)(q.codes + e0 / 2);
+    words[0] = v[0]; words[1] = v[1]; words[2] = v[2]; words[3] = v[3];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      words[i] = (e0 + 8 * i < n) ? *(const uint32_t*)(q.codes + e0 / 2 + 4 * i) : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t e = e0 + 8 * i;
+    if (e >= n) break;
+    const float s = block_scale(q, e / q.bs);
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // byte j/2 of the word; element 2k sits in the high nibble
+      uint32_t c = (words[i] >> ((j >> 1) * 8 + ((j & 1) ? 0 : 4))) & 15u;
+      f[j] = fl32_mul(s_lv[c], s);
+    }
+    if constexpr (OUT == CD_F32) {
+      float4* o = (float4*)((float*)out + e);
+      o[0] = make_float4(f[0], f[1], f[2], f[3]);
+      o[1] = make_float4(f[4], f[5], f[6], f[7]);
+    } else {
+      u32x4_t o;
+      o[0] = pack2<OUT>(f[0], f[1]);
+      o[1] = pack2<OUT>(f[2], f[3]);
+      o[2] = pack2<OUT>(f[4], f[5]);
+      o[3] = pack2<OUT>(f[6], f[7]);
+      *(u32x4_t*)((uint16_t*)out + e) = o;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s) {
+  const int64_t n = q->rows * q->cols;
+  const int bs = q->block_size;
+  const int64_t nb = n / bs;
+  const int blocks_per_wg = q->double_quant ? q->dq_group : (bs >= 16384 ? 1 : 16384 / bs);
+  const int64_t grid = ceil_div(nb, blocks_per_wg);
+  const Nf4Tables& t = host_tables();
+  if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "quantize: tensor too large");
+#define QNF4_Q(BS)                                                                         \
+  case BS:                                                                                 \
+    k_quantize<BS><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(                        \
+        w, n, q->codes, q->absmax, q->absmax_q, q->absmax_scale2, blocks_per_wg,           \
+        q->double_quant, t);                                                               \
+    break;
+  switch (bs) {
+    QNF4_Q(8)
+    QNF4_Q(16)
+    QNF4_Q(32)
+    QNF4_Q(64)
+    QNF4_Q(128)
+    QNF4_Q(256)
+    QNF4_Q(512)
+    default:
+      return set_error(QLORA_ERR_UNSUPPORTED, "quantize: block_size %d not supported", bs);
+  }
+#undef QNF4_Q
+  return check_launch("k_quantize");
+}
+
+int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_t s) {
+  const int64_t n = q->rows * q->cols;
+  const int64_t grid = ceil_div(ceil_div(n, 32), kThreads);
+  if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
+  Nf4W w = make_w(q);
+  const Nf4Tables& t = host_tables();
+  switch (out_dtype) {
+    case QLORA_F32:
+      k_dequantize<CD_F32><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+      break;
+    case QLORA_BF16:
+      k_dequantize<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+      break;
+    case QLORA_F16:
+      k_dequantize<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+      break;
+    default:
+      return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", out_dtype);
+  }
+  return check_launch("k_dequantize");
+}
+
+}  // namespace qnf4

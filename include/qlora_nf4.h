@@ -1,0 +1,157 @@
+/*
+ * qlora_nf4.h -- C ABI of libqlora_nf4.so: the QLoRA NF4 linear layer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (pages: qlora-rs README "Honest capability matrix" and "Quick Start";
+ * rust_ai_core QLoraConfig docs; "LoRA and QLoRA, mathematically"):
+ *
+ *   W  [rows, cols] fp32, frozen, stored as NF4: the flattened weight is cut into
+ *      blocks of block_size consecutive elements; each block keeps its absmax a_b
+ *      and every element its 4-bit code = the nearest of 16 normal-quantile levels
+ *      L[0..15] to w / a_b (ties to the lower code).  Two codes share a byte,
+ *      element 2k in the high nibble.  With double quantization the block scales
+ *      are themselves stored as u8 q_b with one fp32 scale S per group of dq_group
+ *      consecutive blocks: S = fl32(max a / 255), q_b = round-half-even(a_b / S).
+ *   deq  w_hat = fl32(L[code] * s_b) with s_b = a_b, or fl32(q_b * S) with DQ.
+ *   fwd  y = x W~^T + s (x A^T) B^T (+ bias),  W~ = deq(W) rounded to the compute
+ *        dtype, s = alpha / r (alpha / sqrt(r) with QLORA_FLAG_RSLORA).
+ *   bwd  with W frozen: dT = s dY B, dX = dY W~ + dT A, dA = dT^T x,
+ *        dB = s dY^T T0 where T0 = x A^T.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees device memory.  Matrices are row-major and dense.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = null stream).
+ *   - Arguments are validated on the host before anything is launched: on any
+ *     error nothing is written and no work is queued.  Errors: a negative
+ *     qlora_status_t; qlora_last_error() (thread-local) gives the reason.
+ *   - Launch failures surface as QLORA_ERR_HIP.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_NF4_ABI_VERSION 1
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_ARG = -1, /* null pointer, r < 1, non-finite alpha, bad enum   */
+  QLORA_ERR_SHAPE = -2,       /* n % block_size != 0, odd block_size, empty dims     */
+  QLORA_ERR_DTYPE = -3,       /* dtype not one of qlora_dtype_t                      */
+  QLORA_ERR_UNSUPPORTED = -4, /* valid layer outside what the kernels implement      */
+  QLORA_ERR_WORKSPACE = -5,   /* workspace too small (see qlora_workspace_bytes)     */
+  QLORA_ERR_HIP = -6          /* a HIP launch failed                                 */
+} qlora_status_t;
+
+/* Compute / storage dtype of activations, adapters and outputs. */
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1, QLORA_F16 = 2 } qlora_dtype_t;
+
+/* Flags for the forward / backward calls. */
+enum {
+  QLORA_FLAG_RSLORA = 1 /* scale = alpha / sqrt(r) instead of alpha / r */
+};
+
+/* Workspace queries. */
+enum { QLORA_OP_FWD = 0, QLORA_OP_BWD = 1 };
+
+/*
+ * An NF4-quantized frozen weight W [rows, cols].  Descriptor memory is the
+ * caller's; the pointers inside are device pointers the caller allocated:
+ *   codes          u8   [rows*cols/2]        two 4-bit codes per byte, high nibble first
+ *   absmax         f32  [nb]                 when double_quant == 0 (else NULL)
+ *   absmax_q       u8   [nb]                 when double_quant != 0 (else NULL)
+ *   absmax_scale2  f32  [ceil(nb/dq_group)]  when double_quant != 0 (else NULL)
+ * with nb = rows*cols/block_size.  Blocks run over the flattened tensor.
+ */
+typedef struct {
+  int64_t rows;
+  int64_t cols;
+  int32_t block_size;   /* even; the quantize kernel takes 8..512 with block_size/8 a power of two */
+  int32_t double_quant; /* 0 or 1 */
+  int32_t dq_group;     /* blocks per second-level scale when double_quant (1..4096) */
+  int32_t reserved;     /* must be 0 */
+  uint8_t* codes;
+  float* absmax;
+  uint8_t* absmax_q;
+  float* absmax_scale2;
+} qlora_nf4_t;
+
+/*
+ * Quantize W (device fp32 [q->rows * q->cols], row-major) into *q: per-block absmax,
+ * nearest NF4 level of w / absmax (binary32 division, correctly rounded), nibble
+ * packing and, if q->double_quant, the u8 + fp32 encoding of the block scales.
+ * Pages: qlora-rs README "Honest capability matrix" (NF4 pack/unpack, block absmax,
+ * double quant that drops the resident fp32 scales) and "NF4 Quantization".
+ * Writes q->codes and either q->absmax or q->absmax_q + q->absmax_scale2.
+ * Errors: QLORA_ERR_SHAPE (n % block_size, odd block_size, n == 0),
+ * QLORA_ERR_UNSUPPORTED (block_size outside 8..512 or block_size/8 not a power of
+ * two; dq_group > 4096), QLORA_ERR_INVALID_ARG (null pointers, reserved != 0).
+ * NaN / Inf in W are outside the contract (codes are then unspecified, no fault).
+ */
+int qlora_nf4_quantize(const float* w, qlora_nf4_t* q, void* stream);
+
+/*
+ * Dequantize *q into out [rows, cols] of dtype out_dtype: w_hat = fl32(L[c] * s_b),
+ * then rounded to nearest-even into bf16 / f16 (fp32 is stored as is).
+ * Pages: qlora-rs README "Honest capability matrix" (dequant honours compute_dtype).
+ * Errors: QLORA_ERR_DTYPE, QLORA_ERR_SHAPE, QLORA_ERR_INVALID_ARG.
+ */
+int qlora_nf4_dequantize(const qlora_nf4_t* q, int32_t out_dtype, void* out, void* stream);
+
+/*
+ * Forward of the QLoRA linear layer, fused dequantize + GEMM:
+ *   y [m, rows] = x [m, cols] . W~^T + s (x . A^T) . B^T (+ bias [rows])
+ * x, lora_a [r, cols], lora_b [rows, r], bias, y are in dtype cd; accumulation is
+ * fp32.  t_save (nullable) receives T0 = x A^T in fp32 [m, r] for the backward.
+ * Pages: qlora-rs README "Quick Start" (QuantizedLinear::forward) and "Honest
+ * capability matrix"; rust_ai_core QLoraConfig scale() = alpha / r; "LoRA and QLoRA,
+ * mathematically" eq. (6.3.6) and "Tooling" (dequant fused with the matmul).
+ * ws: device workspace of at least qlora_workspace_bytes(QLORA_OP_FWD, ...) bytes,
+ * 256-byte aligned.  Errors: QLORA_ERR_INVALID_ARG (null x/lora_a/lora_b/y, r < 1,
+ * non-finite alpha, m < 1), QLORA_ERR_DTYPE, QLORA_ERR_UNSUPPORTED (cols % 64 != 0
+ * or block_size not a multiple of 32 dividing cols), QLORA_ERR_WORKSPACE.
+ */
+int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
+                     const void* lora_b, int32_t r, float alpha, int32_t flags,
+                     const void* bias, int32_t cd, void* y, float* t_save, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the same layer with the base weight frozen (only A and B train):
+ *   dT = s dY B,  dX = dY W~ + dT A  [m, cols] (cd; skipped when dx == NULL),
+ *   dA = dT^T x  [r, cols] fp32,  dB = s dY^T T0  [rows, r] fp32.
+ * dA and dB are overwritten, not accumulated.  t_saved (nullable) is T0 from the
+ * forward; when NULL it is recomputed.  Pages: qlora-rs README "Honest capability
+ * matrix" / "Training" (adapters update, base frozen); "LoRA and QLoRA,
+ * mathematically" (only the low-rank factors are trained).
+ * Errors: as qlora_linear_fwd, plus null dy / d_a / d_b.
+ */
+int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m,
+                     const void* lora_a, const void* lora_b, int32_t r, float alpha,
+                     int32_t flags, int32_t cd, const float* t_saved, void* dx, float* d_a,
+                     float* d_b, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace size in bytes for op (QLORA_OP_FWD / QLORA_OP_BWD) on this layer shape;
+ * 0 for an invalid query.  Pure host function. */
+size_t qlora_workspace_bytes(int32_t op, int64_t m, int64_t rows, int64_t cols, int32_t r,
+                             int32_t cd);
+
+/* Thread-local message for the last error returned on this thread ("" if none). */
+const char* qlora_last_error(void);
+
+/* Host copy of the 16 fp32 NF4 levels the kernels use, ascending.  Pure host. */
+int qlora_nf4_levels(float out[16]);
+
+/* QLORA_NF4_ABI_VERSION of the built library. */
+int qlora_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLORA_NF4_H */

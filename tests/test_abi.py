@@ -1,0 +1,163 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, reports its level table, and refuses invalid calls on the host
+before anything is launched (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_nf4_quantized_nibble_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+OK, INVALID, SHAPE, DTYPE, UNSUP, WS = 0, -1, -2, -3, -4, -5
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced by a refused call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def desc(rows=64, cols=64, bs=64, dq=0, g=256, codes=FAKE, absmax=FAKE, aq=FAKE, s2=FAKE, reserved=0):
+    return _lib.QloraNf4(rows, cols, bs, dq, g, reserved, codes, absmax, aq, s2)
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.qlora_abi_version() == 1
+
+
+def test_host_level_table_equals_oracle(lib):
+    out = (ctypes.c_float * 16)()
+    assert lib.qlora_nf4_levels(out) == OK
+    _, lv32 = oracle.levels()
+    assert np.array_equal(np.array(list(out), np.float32), lv32)
+
+
+def last_error(lib):
+    return lib.qlora_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bs=63), SHAPE),                    # odd block size
+    (dict(rows=10, cols=10, bs=64), SHAPE),  # n not a multiple of the block size
+    (dict(rows=24, cols=1, bs=24), UNSUP),   # even, divides n, but not a power of two
+    (dict(bs=1024, rows=64, cols=64), UNSUP),
+    (dict(dq=1, g=5000), UNSUP),
+    (dict(dq=1, g=0), INVALID),
+    (dict(dq=2), INVALID),
+    (dict(reserved=1), INVALID),
+    (dict(codes=FAKE + 4), INVALID),         # misaligned codes
+    (dict(codes=0), INVALID),
+    (dict(absmax=0), INVALID),
+    (dict(dq=1, aq=0), INVALID),
+    (dict(rows=-1), SHAPE),
+])
+def test_quantize_refusals(lib, kw, status):
+    d = desc(**kw)
+    assert lib.qlora_nf4_quantize(FAKE, ctypes.byref(d), None) == status
+    assert last_error(lib)
+
+
+def test_quantize_refuses_null_and_misaligned_weight(lib):
+    d = desc()
+    assert lib.qlora_nf4_quantize(None, ctypes.byref(d), None) == INVALID
+    assert lib.qlora_nf4_quantize(FAKE + 8, ctypes.byref(d), None) == INVALID
+    assert lib.qlora_nf4_quantize(FAKE, None, None) == INVALID
+
+
+def test_empty_tensor_is_a_noop(lib):
+    d = desc(rows=0, cols=64, codes=0, absmax=0)
+    assert lib.qlora_nf4_quantize(None, ctypes.byref(d), None) == OK
+    assert lib.qlora_nf4_dequantize(ctypes.byref(d), 1, None, None) == OK
+
+
+def test_dequantize_refusals(lib):
+    d = desc()
+    assert lib.qlora_nf4_dequantize(ctypes.byref(d), 7, FAKE, None) == DTYPE
+    assert lib.qlora_nf4_dequantize(ctypes.byref(d), 1, None, None) == INVALID
+    assert lib.qlora_nf4_dequantize(ctypes.byref(d), 1, FAKE + 2, None) == INVALID
+    d6 = desc(rows=6, cols=1, bs=6)
+    assert lib.qlora_nf4_dequantize(ctypes.byref(d6), 1, FAKE, None) == UNSUP
+
+
+def fwd(lib, d, x=FAKE, m=128, a=FAKE, b=FAKE, r=8, alpha=16.0, flags=0, bias=None, cd=1, y=FAKE,
+        ws=FAKE, ws_bytes=1 << 40):
+    return lib.qlora_linear_fwd(ctypes.byref(d), x, m, a, b, r, alpha, flags, bias, cd, y, None, ws,
+                                ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(r=0), INVALID),
+    (dict(alpha=float("nan")), INVALID),
+    (dict(alpha=float("inf")), INVALID),
+    (dict(flags=4), INVALID),
+    (dict(x=None), INVALID),
+    (dict(a=None), INVALID),
+    (dict(b=None), INVALID),
+    (dict(y=None), INVALID),
+    (dict(cd=3), DTYPE),
+    (dict(m=-1), SHAPE),
+    (dict(ws_bytes=16), WS),
+    (dict(ws=FAKE + 16), WS),
+])
+def test_forward_refusals(lib, kw, status):
+    assert fwd(lib, desc(), **kw) == status
+    assert last_error(lib)
+
+
+def test_forward_shape_refusals(lib):
+    assert fwd(lib, desc(rows=64, cols=96, bs=32)) == UNSUP     # cols % 64
+    assert fwd(lib, desc(rows=64, cols=128, bs=16)) == UNSUP    # block not a multiple of 32
+    assert fwd(lib, desc(rows=64, cols=192, bs=128)) == UNSUP   # block does not divide cols
+    assert fwd(lib, desc(), m=0) == OK                          # no tokens: nothing to do
+
+
+def test_backward_refusals(lib):
+    d = desc()
+
+    def bwd(dy=FAKE, da=FAKE, db=FAKE, m=128, ws_bytes=1 << 40, r=8):
+        return lib.qlora_linear_bwd(ctypes.byref(d), FAKE, dy, m, FAKE, FAKE, r, 16.0, 0, 1, None,
+                                    FAKE, da, db, FAKE, ws_bytes, None)
+
+    assert bwd(dy=None) == INVALID
+    assert bwd(da=None) == INVALID
+    assert bwd(db=None) == INVALID
+    assert bwd(m=0) == SHAPE
+    assert bwd(r=0) == INVALID
+    assert bwd(ws_bytes=8) == WS
+
+
+def test_workspace_query(lib):
+    assert lib.qlora_workspace_bytes(0, 128, 64, 64, 0, 1) == 0      # r < 1
+    assert lib.qlora_workspace_bytes(9, 128, 64, 64, 8, 1) == 0      # bad op
+    assert lib.qlora_workspace_bytes(0, 128, 64, 64, 8, 5) == 0      # bad dtype
+    small = lib.qlora_workspace_bytes(1, 128, 4096, 4096, 64, 1)
+    big = lib.qlora_workspace_bytes(1, 4096, 4096, 4096, 64, 1)
+    assert 0 < small <= big and big % 256 == 0
+    assert lib.qlora_workspace_bytes(0, 4, 4096, 4096, 16, 1) >= 4 * 16 * 4
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    import bit_nf4_quantized_nibble_amd as q
+    with pytest.raises(ValueError):
+        q.quantize(torch.zeros(64, 64))
+    assert q.dtype_code(torch.bfloat16) == 1 and q.dtype_code(torch.float16) == 2
+    with pytest.raises(TypeError):
+        q.dtype_code(torch.int8)

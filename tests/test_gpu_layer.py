@@ -1,0 +1,222 @@
+"""GPU parity of the QLoRA layer (fused dequant-GEMM forward, decode GEMV and the
+backward) against the fp64 oracle on the same seeded inputs, through the C ABI.
+
+Small cases compare every element (several tiles plus ragged tails in M, N and
+the rank); full-size workloads compare sampled entries the oracle computes one
+by one, in the launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import bit_nf4_quantized_nibble_amd as qn
+import oracle
+from bit_nf4_quantized_nibble_amd import inputs
+from parity import assert_close, oracle_layer, say, to_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(L, g, q, **kw):
+    y = qn.linear_fwd(q, g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+def gpu_q(L, g):
+    return qn.quantize(g["W"], L.block_size, L.double_quant, L.dq_group)
+
+
+# ----------------------------------------------------------------------------- forward
+def test_forward_tiny():
+    L = inputs.tiny()
+    say("fwd tiny")
+    g = to_gpu(L)
+    y = run_fwd(L, g, gpu_q(L, g))
+    o = oracle_layer(L)
+    assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"]), "bf16", "tiny fwd")
+
+
+@pytest.mark.parametrize("cd", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("M,N,K,r,bs,dq,bias", [
+    (300, 200, 320, 8, 64, True, True),     # ragged M and N, 5 K-steps, bias
+    (129, 257, 128, 24, 32, False, False),  # ragged by one, rank not a multiple of 16
+    (64, 96, 256, 64, 128, True, False),
+    (17, 128, 64, 3, 64, False, True),      # smallest GEMM-path M, odd rank
+])
+def test_forward_ragged(cd, M, N, K, r, bs, dq, bias):
+    L = inputs.random_layer(M, N, K, r, seed=M + N + r, cd=cd, block_size=bs, double_quant=dq,
+                            with_bias=bias, with_dy=False)
+    say("fwd ragged", cd, M, N, K, r, bs, dq, bias)
+    g = to_gpu(L)
+    y = run_fwd(L, g, gpu_q(L, g))
+    o = oracle_layer(L)
+    ref = oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"])
+    assert_close(to_np(y), ref, cd, "fwd %s %dx%dx%d r%d" % (cd, M, N, K, r))
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_forward_decode_full(m):
+    L = inputs.decode(m)
+    say("fwd decode m", m)
+    g = to_gpu(L)
+    y = run_fwd(L, g, gpu_q(L, g))
+    o = oracle_layer(L)
+    assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"]), "bf16", "decode m%d" % m)
+
+
+@pytest.mark.parametrize("m", [2, 7, 13])
+@pytest.mark.parametrize("cd", ["f16", "f32"])
+def test_forward_decode_small_shapes(m, cd):
+    L = inputs.random_layer(m, 320, 512, 16, seed=m, cd=cd, with_bias=True, with_dy=False)
+    say("fwd decode small", m, cd)
+    g = to_gpu(L)
+    y = run_fwd(L, g, gpu_q(L, g))
+    o = oracle_layer(L)
+    assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"]), cd, "decode small")
+
+
+def test_forward_save_t_and_leading_dims():
+    L = inputs.random_layer(60, 128, 256, 8, seed=3, with_dy=False)
+    say("fwd save_t")
+    g = to_gpu(L)
+    q = gpu_q(L, g)
+    y, t0 = qn.linear_fwd(q, g["x"].reshape(3, 20, 256), g["A"], g["B"], L.alpha, save_t=True)
+    torch.cuda.synchronize()
+    assert y.shape == (3, 20, 128)
+    o = oracle_layer(L)
+    T0 = o["x"].astype(np.float64) @ o["A"].astype(np.float64).T
+    assert_close(to_np(t0), T0, "f32", "T0")
+    assert_close(to_np(y).reshape(60, 128), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"]), "bf16", "y")
+
+
+def test_forward_b_zero_and_alpha_linearity():
+    L = inputs.random_layer(256, 256, 512, 16, seed=4, with_dy=False)
+    say("fwd B=0 / alpha")
+    g = to_gpu(L)
+    q = gpu_q(L, g)
+    o = oracle_layer(L)
+    base_ref = oracle.forward(o["x"], o["W"], o["A"], np.zeros_like(o["B"]), 0.0)
+    y0 = qn.linear_fwd(q, g["x"], g["A"], torch.zeros_like(g["B"]), L.alpha)
+    yz = qn.linear_fwd(q, g["x"], g["A"], g["B"], 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, yz)  # B = 0 and alpha = 0 both give the base output
+    assert_close(to_np(y0), base_ref, "bf16", "base")
+    # fp32 outputs of the LoRA delta scale with alpha (f32 compute keeps it exact-ish).
+    Lf = inputs.random_layer(128, 128, 256, 8, seed=5, cd="f32", with_dy=False)
+    gf = to_gpu(Lf)
+    qf = gpu_q(Lf, gf)
+    yb = qn.linear_fwd(qf, gf["x"], gf["A"], gf["B"], 0.0)
+    y1 = qn.linear_fwd(qf, gf["x"], gf["A"], gf["B"], 8.0)
+    y2 = qn.linear_fwd(qf, gf["x"], gf["A"], gf["B"], 16.0)
+    torch.cuda.synchronize()
+    d1, d2 = (y1 - yb).double().cpu().numpy(), (y2 - yb).double().cpu().numpy()
+    assert oracle.rel_l2(d2, 2 * d1) < 1e-4
+
+
+def test_forward_rslora():
+    L = inputs.random_layer(130, 64, 128, 16, seed=6, with_dy=False)
+    say("fwd rslora")
+    g = to_gpu(L)
+    y = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, rslora=True)
+    torch.cuda.synchronize()
+    o = oracle_layer(L)
+    ref = oracle.forward(o["x"], o["W"], o["A"], o["B"], L.alpha / np.sqrt(L.r))
+    assert_close(to_np(y), ref, "bf16", "rslora")
+
+
+@pytest.mark.parametrize("name", ["q_proj", "down_proj"])
+def test_forward_prefill_full_size_sampled(name):
+    (L,) = inputs.prefill(projections=[name])
+    say("fwd prefill", name)
+    g = to_gpu(L)
+    q = gpu_q(L, g)
+    y = run_fwd(L, g, q)
+    o = oracle_layer(L)
+    rng = np.random.default_rng(7)
+    ii = rng.integers(0, L.M, 256)
+    jj = rng.integers(0, L.N, 256)
+    ii[:4] = [0, L.M - 1, 0, L.M - 1]
+    jj[:4] = [0, 0, L.N - 1, L.N - 1]
+    ref = oracle.forward_at(o["x"], o["W"], o["A"], o["B"], o["s"], ii, jj)
+    got = to_np(y)[ii, jj]
+    assert_close(got, ref, "bf16", "prefill %s" % name)
+
+
+@pytest.mark.parametrize("cd", ["f16", "f32"])
+def test_forward_prefill_dtype_sweep_sampled(cd):
+    (L,) = inputs.prefill(cd=cd, projections=["k_proj"])
+    say("fwd prefill dtype", cd)
+    g = to_gpu(L)
+    y = run_fwd(L, g, gpu_q(L, g))
+    o = oracle_layer(L)
+    rng = np.random.default_rng(8)
+    ii, jj = rng.integers(0, L.M, 256), rng.integers(0, L.N, 256)
+    ref = oracle.forward_at(o["x"], o["W"], o["A"], o["B"], o["s"], ii, jj)
+    assert_close(to_np(y)[ii, jj], ref, cd, "prefill %s" % cd)
+
+
+# ----------------------------------------------------------------------------- backward
+def run_bwd(L, g, q, **kw):
+    out = qn.linear_bwd(q, g["x"], g["dY"], g["A"], g["B"], L.alpha, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_backward_tiny():
+    L = inputs.tiny()
+    say("bwd tiny")
+    g = to_gpu(L)
+    dx, da, db = run_bwd(L, g, gpu_q(L, g))
+    o = oracle_layer(L)
+    rdx, rda, rdb = oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"])
+    assert_close(to_np(dx), rdx, "bf16", "tiny dX")
+    assert_close(to_np(da), rda, "bf16", "tiny dA")
+    assert_close(to_np(db), rdb, "bf16", "tiny dB")
+
+
+@pytest.mark.parametrize("cd", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("M,N,K,r", [(300, 200, 320, 24), (70, 130, 128, 5), (256, 64, 192, 64)])
+def test_backward_ragged(cd, M, N, K, r):
+    L = inputs.random_layer(M, N, K, r, seed=M * 7 + r, cd=cd)
+    say("bwd ragged", cd, M, N, K, r)
+    g = to_gpu(L)
+    dx, da, db = run_bwd(L, g, gpu_q(L, g))
+    o = oracle_layer(L)
+    rdx, rda, rdb = oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"])
+    assert_close(to_np(dx), rdx, cd, "dX")
+    assert_close(to_np(da), rda, cd, "dA")
+    assert_close(to_np(db), rdb, cd, "dB")
+
+
+def test_backward_saved_t_matches_recompute():
+    L = inputs.random_layer(200, 192, 256, 16, seed=9)
+    say("bwd saved T0")
+    g = to_gpu(L)
+    q = gpu_q(L, g)
+    _, t0 = qn.linear_fwd(q, g["x"], g["A"], g["B"], L.alpha, save_t=True)
+    a = run_bwd(L, g, q, t_saved=t0)
+    b = run_bwd(L, g, q)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    dx, da, db = run_bwd(L, g, q, need_dx=False)
+    assert dx is None and torch.equal(da, a[1]) and torch.equal(db, a[2])
+
+
+@pytest.mark.parametrize("name", ["gate_proj"])
+def test_backward_prefill_full_size_sampled(name):
+    (L,) = inputs.prefill(with_dy=True, projections=[name])
+    say("bwd prefill", name)
+    g = to_gpu(L)
+    dx, da, db = run_bwd(L, g, gpu_q(L, g))
+    o = oracle_layer(L)
+    rng = np.random.default_rng(10)
+    ii, kk = rng.integers(0, L.M, 128), rng.integers(0, L.K, 128)
+    ref = oracle.backward_dx_at(o["dY"], o["W"], o["A"], o["B"], o["s"], ii, kk)
+    assert_close(to_np(dx)[ii, kk], ref, "bf16", "dX sampled")
+    tt = rng.choice(L.r, 3, replace=False)[rng.integers(0, 3, 96)]
+    kk = rng.integers(0, L.K, 96)
+    ref = oracle.backward_da_at(o["x"], o["dY"], o["B"], o["s"], tt, kk)
+    assert_close(to_np(da)[tt, kk], ref, "bf16", "dA sampled")
+    nn = rng.integers(0, L.N, 96)
+    ref = oracle.backward_db_at(o["x"], o["A"], o["dY"], o["s"], nn, tt)
+    assert_close(to_np(db)[nn, tt], ref, "bf16", "dB sampled")
