@@ -1,0 +1,414 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA NF4 linear layer on one MI355X.
+
+Headline: the training step of the seven projections of one Llama-3-8B-shaped
+block (q/o 4096x4096, k/v 1024x4096, gate/up 14336x4096, down 4096x14336; NF4 block
+64 with double quantization; 4096 tokens; LoRA r = 64, alpha = 128; bf16 compute):
+one step = the fused dequant-GEMM forward of all seven projections followed by
+their backward (dX, dA, dB).  value = algorithmic TFLOP/s of that step.
+
+Also reported on the same line, each against its own MI355X roofline:
+  gemv      decode forward at m = 1, 4, 16 (4096x4096, r = 16), GB/s over cold weights
+  quantize  NF4 quantize of a 4096x4096 fp32 weight without / with double quant, GB/s
+  dequantize  the double-quantized weight back to bf16 / fp32, GB/s
+  dtype_sweep  the prefill forward in f16 and f32 compute
+  cpu_baseline  the oracle (plain C, fp64) on a bounded sample of the step's work
+  roofline  the dominant kernel of the step, timed with HIP events on its stream
+
+Inputs are seeded synthetic tensors (bit_nf4_quantized_nibble_amd.inputs): trained
+weights are not needed because cost and numerics depend on shapes and value ranges.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused NF4 QLoRA linear TFLOP/s (prefill/bwd) + GEMV HBM GB/s, % of roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def fwd_flops(m, n, k, r):
+    return 2.0 * m * n * k + 2.0 * m * r * k + 2.0 * m * n * r
+
+
+def bwd_flops(m, n, k, r):
+    # dX base + dT A, plus dT = s dY B, dA = dT^T x, dB = s dY^T T0
+    return 2.0 * m * n * k + 2.0 * m * r * k + 2.0 * m * n * r + 2.0 * r * k * m + 2.0 * n * r * m
+
+
+class Layer:
+    """Device tensors and prebuilt C-ABI argument tuples for one projection."""
+
+    def __init__(self, L, x, ws_f, ws_b, qn, torch, lib):
+        self.name, self.M, self.N, self.K, self.r, self.alpha = L.name, L.M, L.N, L.K, L.r, L.alpha
+        dev = "cuda"
+        W = L.W.to(dev)
+        self.q = qn.quantize(W, L.block_size, L.double_quant, L.dq_group)
+        del W
+        self.A, self.B = L.A.to(dev), L.B.to(dev)
+        self.dY = L.dY.to(dev) if L.dY is not None else None
+        dt = x.dtype
+        self.y = torch.empty(self.M, self.N, dtype=dt, device=dev)
+        self.t0 = torch.empty(self.M, self.r, dtype=torch.float32, device=dev)
+        self.dx = torch.empty(self.M, self.K, dtype=dt, device=dev)
+        self.da = torch.empty(self.r, self.K, dtype=torch.float32, device=dev)
+        self.db = torch.empty(self.N, self.r, dtype=torch.float32, device=dev)
+        self.desc = self.q.descriptor()
+        cd = qn.dtype_code(dt)
+        stream = torch.cuda.current_stream().cuda_stream
+        self.fwd_args = (ctypes.byref(self.desc), x.data_ptr(), self.M, self.A.data_ptr(), self.B.data_ptr(),
+                         self.r, float(self.alpha), 0, None, cd, self.y.data_ptr(), self.t0.data_ptr(),
+                         ws_f.data_ptr(), ws_f.numel(), stream)
+        if self.dY is not None:
+            self.bwd_args = (ctypes.byref(self.desc), x.data_ptr(), self.dY.data_ptr(), self.M,
+                             self.A.data_ptr(), self.B.data_ptr(), self.r, float(self.alpha), 0, cd,
+                             self.t0.data_ptr(), self.dx.data_ptr(), self.da.data_ptr(),
+                             self.db.data_ptr(), ws_b.data_ptr(), ws_b.numel(), stream)
+        self.lib = lib
+
+    def fwd(self):
+        rc = self.lib.qlora_linear_fwd(*self.fwd_args)
+        if rc:
+            raise RuntimeError("fwd %s: %d %s" % (self.name, rc, self.lib.qlora_last_error()))
+
+    def bwd(self):
+        rc = self.lib.qlora_linear_bwd(*self.bwd_args)
+        if rc:
+            raise RuntimeError("bwd %s: %d %s" % (self.name, rc, self.lib.qlora_last_error()))
+
+
+def build_block(cd, with_dy, qn, torch, lib, inputs, m=4096):
+    Ls = inputs.prefill(seed=0, cd=cd, m=m, with_dy=with_dy)
+    xs = {}
+    for L in Ls:
+        if L.K not in xs:
+            xs[L.K] = L.x.to("cuda")
+    op_f, op_b = 0, 1
+    wsf = max(qn.workspace_bytes(op_f, L.M, L.N, L.K, L.r, xs[L.K].dtype) for L in Ls)
+    wsb = max(qn.workspace_bytes(op_b, L.M, L.N, L.K, L.r, xs[L.K].dtype) for L in Ls) if with_dy else 1
+    ws_f = torch.empty(wsf, dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    layers = [Layer(L, xs[L.K], ws_f, ws_b, qn, torch, lib) for L in Ls]
+    del Ls
+    return layers, (xs, ws_f, ws_b)
+
+
+def time_loop(fn, iters, torch):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / iters
+
+
+def bench_step(args, qn, torch, lib, inputs):
+    layers, keep = build_block("bf16", True, qn, torch, lib, inputs)
+    torch.cuda.synchronize()
+    flops = sum(fwd_flops(l.M, l.N, l.K, l.r) + bwd_flops(l.M, l.N, l.K, l.r) for l in layers)
+    ff = {k: 0.0 for k in ("fwd_gemm", "lora_down", "bwd_dx", "bwd_dt", "bwd_da", "bwd_db")}
+    for l in layers:
+        ff["fwd_gemm"] += 2.0 * l.M * l.N * l.K + 2.0 * l.M * l.N * l.r
+        ff["lora_down"] += 2.0 * l.M * l.r * l.K
+        ff["bwd_dx"] += 2.0 * l.M * l.N * l.K + 2.0 * l.M * l.r * l.K
+        ff["bwd_dt"] += 2.0 * l.M * l.N * l.r
+        ff["bwd_da"] += 2.0 * l.r * l.K * l.M
+        ff["bwd_db"] += 2.0 * l.N * l.r * l.M
+
+    def step():
+        for l in layers:
+            l.fwd()
+        for l in layers:
+            l.bwd()
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    qn.profile_enable(True)
+    log("timing", args.steps, "steps")
+    sec = time_loop(step, args.steps, torch)
+    prof = qn.profile_read()
+    qn.profile_enable(False)
+    kernels = {}
+    for kind, (ms, n) in prof.items():
+        if n == 0:
+            continue
+        per_step = ms / args.steps
+        ent = {"ms_per_step": round(per_step, 4), "launches_per_step": n // args.steps}
+        if kind in ff:
+            tf = ff[kind] / (per_step / 1e3) / 1e12
+            ent["tflops"] = round(tf, 2)
+            ent["frac_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+        kernels[kind] = ent
+    # The dominant kernel: the largest share of the step's time.
+    dom = max((k for k in kernels if k in ff), key=lambda k: kernels[k]["ms_per_step"])
+    dom_ms = prof[dom][0] / prof[dom][1]  # average launch duration
+    dom_flops = ff[dom] / (prof[dom][1] / args.steps)  # algorithmic flops per launch
+    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "avg_launch_ms": round(dom_ms, 4),
+                "flops_per_launch": dom_flops}
+    result = dict(sec=sec, flops=flops, kernels=kernels, roofline=roofline,
+                  fwd_ms=sum(kernels.get(k, {}).get("ms_per_step", 0) for k in ("fwd_gemm", "lora_down")),
+                  layers=[(l.name, l.N, l.K) for l in layers])
+    del layers, keep
+    torch.cuda.empty_cache()
+    return result
+
+
+def bench_dtype_sweep(qn, torch, lib, inputs, steps=3):
+    out = {}
+    for cd in ("f16", "f32"):
+        layers, keep = build_block(cd, False, qn, torch, lib, inputs)
+        flops = sum(fwd_flops(l.M, l.N, l.K, l.r) for l in layers)
+
+        def fwd():
+            for l in layers:
+                l.fwd()
+
+        fwd()
+        sec = time_loop(fwd, steps, torch)
+        tf = flops / sec / 1e12
+        peak = PEAK_BF16_TFLOPS if cd == "f16" else PEAK_F32_TFLOPS
+        out[cd] = {"ms": round(sec * 1e3, 3), "tflops": round(tf, 2), "peak": peak, "frac": round(tf / peak, 4)}
+        del layers, keep
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_gemv(qn, torch, lib, inputs, copies=40, iters=400):
+    """Decode GEMV over `copies` independent weights (> the 256 MB last-level cache),
+    so each call streams its weight from HBM."""
+    out = {}
+    for m in (1, 4, 16):
+        L = inputs.decode(m)
+        W = L.W.to("cuda")
+        q0 = qn.quantize(W, 64, True, 256)
+        del W
+        sets = []
+        for c in range(copies):
+            q = qn.NF4Weight(q0.rows, q0.cols, 64, True, 256, q0.codes.clone(), None,
+                             q0.absmax_q.clone(), q0.absmax_scale2.clone())
+            x = L.x.to("cuda").clone()
+            A, B = L.A.to("cuda").clone(), L.B.to("cuda").clone()
+            y = torch.empty(m, 4096, dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(qn.workspace_bytes(0, m, 4096, 4096, 16, torch.bfloat16), dtype=torch.uint8,
+                             device="cuda")
+            d = q.descriptor()
+            args = (ctypes.byref(d), x.data_ptr(), m, A.data_ptr(), B.data_ptr(), 16, 32.0, 0, None, 1,
+                    y.data_ptr(), None, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+            sets.append((q, x, A, B, y, ws, d, args))
+        f = lib.qlora_linear_fwd
+        for s in sets:
+            f(*s[7])
+        torch.cuda.synchronize()
+        qn.profile_enable(True)
+        t0 = time.perf_counter()
+        for i in range(iters):
+            rc = f(*sets[i % copies][7])
+            if rc:
+                raise RuntimeError("gemv rc %d" % rc)
+        torch.cuda.synchronize()
+        call_us = (time.perf_counter() - t0) / iters * 1e6
+        prof = qn.profile_read()
+        qn.profile_enable(False)
+        k_ms, k_n = prof["gemv"]
+        l_ms, l_n = prof["lora_down"]
+        kern_us = k_ms / k_n * 1e3
+        layer_bytes = (4096 * 4096 // 2 + 4096 * 4096 // 64 + 4096 * 4096 // 64 // 256 * 4
+                       + 2 * m * 4096 + 2 * 16 * 4096 * 2 + 2 * m * 4096)
+        kern_bytes = (4096 * 4096 // 2 + 4096 * 4096 // 64 + 4096 * 4096 // 64 // 256 * 4
+                      + 2 * m * 4096 + 2 * 16 * 4096 + 4 * m * 16 + 2 * m * 4096)
+        gbs_kernel = kern_bytes / (kern_us * 1e-6) / 1e9
+        gbs_layer = layer_bytes / ((kern_us + l_ms / l_n * 1e3) * 1e-6) / 1e9
+        out["m%d" % m] = {"kernel_us": round(kern_us, 3), "lora_down_us": round(l_ms / l_n * 1e3, 3),
+                          "call_us_wall": round(call_us, 3), "kernel_bytes": kern_bytes,
+                          "kernel_gbs": round(gbs_kernel, 1), "kernel_frac": round(gbs_kernel / PEAK_HBM_GBS, 4),
+                          "layer_bytes": layer_bytes, "layer_gbs_device": round(gbs_layer, 1),
+                          "layer_frac": round(gbs_layer / PEAK_HBM_GBS, 4)}
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_quant(qn, torch, inputs, copies=5, iters=20):
+    W0 = inputs.roundtrip_weight(0).to("cuda")
+    n = W0.numel()
+    Ws = [W0.clone() for _ in range(copies)]
+    out = {}
+    for dq in (False, True):
+        qs = [qn.empty_nf4(4096, 4096, 64, dq, 256) for _ in range(copies)]
+        ds = [q.descriptor() for q in qs]
+        lib = qn._lib.lib()
+        stream = torch.cuda.current_stream().cuda_stream
+        for i in range(copies):
+            lib.qlora_nf4_quantize(Ws[i].data_ptr(), ctypes.byref(ds[i]), stream)
+        torch.cuda.synchronize()
+        qn.profile_enable(True)
+        for i in range(iters):
+            rc = lib.qlora_nf4_quantize(Ws[i % copies].data_ptr(), ctypes.byref(ds[i % copies]), stream)
+            if rc:
+                raise RuntimeError("quantize rc %d" % rc)
+        torch.cuda.synchronize()
+        ms, k = qn.profile_read()["quantize"]
+        qn.profile_enable(False)
+        nb = n // 64
+        byts = n * 4 + n // 2 + (nb + (nb + 255) // 256 * 4 if dq else nb * 4)
+        us = ms / k * 1e3
+        gbs = byts / (us * 1e-6) / 1e9
+        out["dq" if dq else "no_dq"] = {"us": round(us, 2), "bytes": byts, "gbs": round(gbs, 1),
+                                        "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        if dq:
+            for name, dt, ob in (("bf16", torch.bfloat16, 2), ("f32", torch.float32, 4)):
+                outs = [torch.empty(4096, 4096, dtype=dt, device="cuda") for _ in range(copies)]
+                code = qn.dtype_code(dt)
+                for i in range(copies):
+                    lib.qlora_nf4_dequantize(ctypes.byref(ds[i]), code, outs[i].data_ptr(), stream)
+                torch.cuda.synchronize()
+                qn.profile_enable(True)
+                for i in range(iters):
+                    rc = lib.qlora_nf4_dequantize(ctypes.byref(ds[i % copies]), code, outs[i % copies].data_ptr(),
+                                                  stream)
+                    if rc:
+                        raise RuntimeError("dequantize rc %d" % rc)
+                torch.cuda.synchronize()
+                ms, k = qn.profile_read()["dequantize"]
+                qn.profile_enable(False)
+                byts = n // 2 + nb + (nb + 255) // 256 * 4 + n * ob
+                us = ms / k * 1e3
+                gbs = byts / (us * 1e-6) / 1e9
+                out["dequant_dq_to_" + name] = {"us": round(us, 2), "bytes": byts, "gbs": round(gbs, 1),
+                                                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+                del outs
+        del qs
+    del Ws, W0
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(inputs, target_s):
+    """The oracle as it is (plain C, fp64, OpenMP over output rows) on a bounded
+    sample of the step: forward + backward of q_proj for the first m_s tokens."""
+    import numpy as np
+
+    import oracle
+    (L,) = inputs.prefill(seed=0, cd="bf16", with_dy=True, projections=["q_proj"])
+    q = oracle.quantize(L.W.numpy(), 64, True, 256)
+    W = oracle.weight_operand(q, "bf16")
+    x, A, B, dY = (oracle.operand(t, "bf16") for t in (L.x, L.A, L.B, L.dY))
+    s = L.alpha / L.r
+
+    def run(ms):
+        t0 = time.perf_counter()
+        oracle.forward(x[:ms], W, A, B, s)
+        oracle.backward(x[:ms], W, A, B, dY[:ms], s)
+        return time.perf_counter() - t0
+
+    probe = 8
+    t = run(probe)
+    ms = int(max(8, min(4096, probe * target_s / max(t, 1e-3))))
+    t = run(ms)
+    flops = fwd_flops(ms, L.N, L.K, L.r) + bwd_flops(ms, L.N, L.K, L.r)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(t, 2),
+            "sample": "oracle forward + backward of q_proj (4096x4096, r=64) on the first %d of the "
+                      "4096 tokens (%.1f GFLOP), fp64 scalar C with OpenMP" % (ms, flops / 1e9)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep"], default=None,
+                    help="run one part (for profiling); the JSON line needs the full run")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU; --gpus %d is not supported "
+              "(the layer would shard data-parallel over tokens, see the design notes)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_nf4_quantized_nibble_amd as qn
+    from bit_nf4_quantized_nibble_amd import inputs
+    lib = qn._lib.lib()
+    torch.cuda.set_device(0)
+
+    if args.only == "gemv":
+        print(json.dumps(bench_gemv(qn, torch, lib, inputs)))
+        return
+    if args.only == "quant":
+        print(json.dumps(bench_quant(qn, torch, inputs)))
+        return
+    if args.only == "sweep":
+        print(json.dumps(bench_dtype_sweep(qn, torch, lib, inputs)))
+        return
+
+    st = bench_step(args, qn, torch, lib, inputs)
+    log("step %.3f ms" % (st["sec"] * 1e3))
+    if args.only == "step":
+        print(json.dumps({"ms_per_step": st["sec"] * 1e3, "kernels": st["kernels"], "roofline": st["roofline"]}))
+        return
+    gemv = bench_gemv(qn, torch, lib, inputs)
+    log("gemv done")
+    quant = bench_quant(qn, torch, inputs)
+    log("quant done")
+    sweep = bench_dtype_sweep(qn, torch, lib, inputs)
+    log("sweep done")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (~%.0f s)" % args.cpu_seconds)
+        cpu = cpu_baseline(inputs, args.cpu_seconds)
+
+    ms = st["sec"] * 1e3
+    value = st["flops"] / st["sec"] / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qlora_nf4_block_train_step_llama3_8b_shapes",
+                   "tokens": 4096, "projections": [[n, N, K] for n, N, K in st["layers"]],
+                   "r": 64, "alpha": 128, "block_size": 64, "double_quant": True, "dq_group": 256,
+                   "step": "fused forward of 7 projections + backward (dX, dA, dB)",
+                   "flops_per_step": st["flops"], "parallelism": "single GPU"},
+        "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": st["roofline"],
+        "cpu_baseline": cpu,
+        "kernels": st["kernels"],
+        "gemv": gemv,
+        "quantize": quant,
+        "dtype_sweep_forward": sweep,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import QloraError, QloraNf4  # noqa: F401
 
 __all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "workspace_bytes",
-           "levels", "QloraError", "dtype_code"]
+           "levels", "QloraError", "dtype_code", "profile_enable", "profile_read"]
 
 
 def _torch():
@@ -162,10 +162,11 @@ def _flatten(x, cols):
 
 
 def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t: bool = False,
-               rslora: bool = False, workspace=None):
+               rslora: bool = False, workspace=None, out=None, t_out=None):
     """y = x . deq(W)^T + s (x . A^T) . B^T (+ bias), s = alpha / r (alpha / sqrt(r)
     with rslora).  Leading dims of x are flattened to tokens.  Returns y, or
-    (y, T0) with T0 = x A^T in fp32 when save_t."""
+    (y, T0) with T0 = x A^T in fp32 when save_t.  ``out`` / ``t_out`` may supply
+    preallocated outputs."""
     torch = _torch()
     dt = x.dtype
     x2, lead = _flatten(x, q.cols)
@@ -174,21 +175,30 @@ def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t:
         _need_cuda(name, t, dt)
     r = lora_a.shape[0]
     m = x2.shape[0]
-    y = torch.empty(m, q.rows, dtype=dt, device=x.device)
-    t0 = torch.empty(m, r, dtype=torch.float32, device=x.device) if save_t else None
+    y = out if out is not None else torch.empty(m, q.rows, dtype=dt, device=x.device)
+    _need_cuda("out", y, dt)
+    if y.numel() != m * q.rows:
+        raise ValueError("out must hold %d x %d elements" % (m, q.rows))
+    t0 = t_out if t_out is not None else (
+        torch.empty(m, r, dtype=torch.float32, device=x.device) if save_t else None)
+    _need_cuda("t_out", t0, torch.float32)
+    if t0 is not None and t0.numel() != m * r:
+        raise ValueError("t_out must hold %d x %d fp32 elements" % (m, r))
     ws = _workspace(workspace_bytes(_lib.QLORA_OP_FWD, m, q.rows, q.cols, r, dt), x.device, workspace)
     d = q.descriptor()
     flags = _lib.QLORA_FLAG_RSLORA if rslora else 0
     _lib.check(_lib.lib().qlora_linear_fwd(
         ctypes.byref(d), _ptr(x2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
-        _ptr(bias), dtype_code(dt), _ptr(y), _ptr(t0), _ptr(ws), ws.numel(), _stream_ptr(x.device)))
+        _ptr(bias), dtype_code(dt), _ptr(y), _ptr(t0), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream_ptr(x.device)))
     y = y.reshape(*lead, q.rows)
-    return (y, t0) if save_t else y
+    return (y, t0) if (save_t or t_out is not None) else y
 
 
 def linear_bwd(q: NF4Weight, x, dy, lora_a, lora_b, alpha: float, t_saved=None, need_dx: bool = True,
-               rslora: bool = False, workspace=None):
-    """Gradients with the base frozen: returns (dX or None, dA fp32 [r, cols], dB fp32 [rows, r])."""
+               rslora: bool = False, workspace=None, dx_out=None, da_out=None, db_out=None):
+    """Gradients with the base frozen: returns (dX or None, dA fp32 [r, cols], dB fp32 [rows, r]).
+    ``*_out`` may supply preallocated outputs."""
     torch = _torch()
     dt = x.dtype
     x2, lead = _flatten(x, q.cols)
@@ -199,16 +209,24 @@ def linear_bwd(q: NF4Weight, x, dy, lora_a, lora_b, alpha: float, t_saved=None, 
     _need_cuda("t_saved", t_saved, torch.float32)
     r = lora_a.shape[0]
     m = x2.shape[0]
-    dx = torch.empty(m, q.cols, dtype=dt, device=x.device) if need_dx else None
-    da = torch.empty(r, q.cols, dtype=torch.float32, device=x.device)
-    db = torch.empty(q.rows, r, dtype=torch.float32, device=x.device)
+    dx = dx_out if dx_out is not None else (
+        torch.empty(m, q.cols, dtype=dt, device=x.device) if need_dx else None)
+    da = da_out if da_out is not None else torch.empty(r, q.cols, dtype=torch.float32, device=x.device)
+    db = db_out if db_out is not None else torch.empty(q.rows, r, dtype=torch.float32, device=x.device)
+    _need_cuda("dx_out", dx, dt)
+    _need_cuda("da_out", da, torch.float32)
+    _need_cuda("db_out", db, torch.float32)
+    if (dx is not None and dx.numel() != m * q.cols) or da.numel() != r * q.cols or db.numel() != q.rows * r:
+        raise ValueError("output buffers have the wrong size")
+    if t_saved is not None and t_saved.numel() != m * r:
+        raise ValueError("t_saved must hold %d x %d fp32 elements" % (m, r))
     ws = _workspace(workspace_bytes(_lib.QLORA_OP_BWD, m, q.rows, q.cols, r, dt), x.device, workspace)
     d = q.descriptor()
     flags = _lib.QLORA_FLAG_RSLORA if rslora else 0
     _lib.check(_lib.lib().qlora_linear_bwd(
         ctypes.byref(d), _ptr(x2), _ptr(dy2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
-        dtype_code(dt), _ptr(t_saved), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), ws.numel(),
-        _stream_ptr(x.device)))
+        dtype_code(dt), _ptr(t_saved), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream_ptr(x.device)))
     if dx is not None:
         dx = dx.reshape(*lead, q.cols)
     return dx, da, db
@@ -219,3 +237,19 @@ def levels():
     out = (ctypes.c_float * 16)()
     _lib.check(_lib.lib().qlora_nf4_levels(out))
     return [float(v) for v in out]
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start (resetting the totals) or stop per-kernel event timing in the library."""
+    _lib.check(_lib.lib().qlora_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """{kernel kind: (summed milliseconds, launches)} recorded since profile_enable."""
+    out = {}
+    for kind, name in enumerate(_lib.KERNEL_KINDS):
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        _lib.check(_lib.lib().qlora_profile_read(kind, ctypes.byref(ms), ctypes.byref(n)))
+        out[name] = (ms.value, n.value)
+    return out

@@ -25,7 +25,10 @@ QLORA_OP_FWD, QLORA_OP_BWD = 0, 1
 EXPORTED = (
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_workspace_bytes", "qlora_last_error", "qlora_nf4_levels", "qlora_abi_version",
+    "qlora_profile_enable", "qlora_profile_read", "qlora_kernel_name",
 )
+KERNEL_KINDS = ("quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
+                "bwd_dt", "bwd_dx", "bwd_da", "bwd_db")
 
 
 class QloraNf4(ctypes.Structure):
@@ -67,8 +70,13 @@ def _declare(lib):
     lib.qlora_last_error.restype = ctypes.c_char_p
     lib.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
     lib.qlora_abi_version.argtypes = []
+    lib.qlora_profile_enable.argtypes = [i32]
+    lib.qlora_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.qlora_kernel_name.argtypes = [i32]
+    lib.qlora_kernel_name.restype = ctypes.c_char_p
     for name in ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
-                 "qlora_linear_bwd", "qlora_nf4_levels", "qlora_abi_version"):
+                 "qlora_linear_bwd", "qlora_nf4_levels", "qlora_abi_version",
+                 "qlora_profile_enable", "qlora_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
 
 

@@ -9,7 +9,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "common.h"
 
@@ -173,6 +175,73 @@ int check_launch(const char* what) {
   return QLORA_OK;
 }
 
+// ---------------------------------------------------------------- kernel timing
+namespace {
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<ProfRec*> g_prof_pending, g_prof_free;
+double g_prof_ms[QLORA_K_COUNT];
+int64_t g_prof_n[QLORA_K_COUNT];
+
+const char* kKernelNames[QLORA_K_COUNT] = {
+    "quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
+    "bwd_dt",   "bwd_dx",     "bwd_da",    "bwd_db"};
+
+// Wait for every recorded pair and fold it into the totals (lock held).
+int prof_drain() {
+  int rc = QLORA_OK;
+  for (ProfRec* p : g_prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p->b) != hipSuccess || hipEventElapsedTime(&ms, p->a, p->b) != hipSuccess)
+      rc = QLORA_ERR_HIP;
+    g_prof_ms[p->kind] += ms;
+    g_prof_n[p->kind] += 1;
+    g_prof_free.push_back(p);
+  }
+  g_prof_pending.clear();
+  return rc;
+}
+}  // namespace
+
+void prof_begin(int kind, hipStream_t s, void** token) {
+  *token = nullptr;
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  ProfRec* p;
+  if (!g_prof_free.empty()) {
+    p = g_prof_free.back();
+    g_prof_free.pop_back();
+  } else {
+    p = new ProfRec;
+    if (hipEventCreate(&p->a) != hipSuccess || hipEventCreate(&p->b) != hipSuccess) {
+      delete p;
+      return;
+    }
+  }
+  p->kind = kind;
+  if (hipEventRecord(p->a, s) != hipSuccess) {
+    g_prof_free.push_back(p);
+    return;
+  }
+  *token = p;
+}
+
+void prof_end(void* token, hipStream_t s) {
+  if (!token) return;
+  ProfRec* p = (ProfRec*)token;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (hipEventRecord(p->b, s) != hipSuccess) {
+    g_prof_free.push_back(p);
+    return;
+  }
+  g_prof_pending.push_back(p);
+}
+
 }  // namespace qnf4
 
 using namespace qnf4;
@@ -180,6 +249,33 @@ using namespace qnf4;
 extern "C" {
 
 int qlora_abi_version(void) { return QLORA_NF4_ABI_VERSION; }
+
+int qlora_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int rc = prof_drain();
+  if (on) {
+    for (int k = 0; k < QLORA_K_COUNT; ++k) {
+      g_prof_ms[k] = 0.0;
+      g_prof_n[k] = 0;
+    }
+  }
+  g_prof_on = on != 0;
+  return rc == QLORA_OK ? QLORA_OK : set_error(rc, "profile: event wait failed");
+}
+
+int qlora_profile_read(int32_t kind, double* ms, int64_t* launches) {
+  if (kind < 0 || kind >= QLORA_K_COUNT || !ms || !launches)
+    return set_error(QLORA_ERR_INVALID_ARG, "profile_read: bad kind or null output");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int rc = prof_drain();
+  *ms = g_prof_ms[kind];
+  *launches = g_prof_n[kind];
+  return rc == QLORA_OK ? QLORA_OK : set_error(rc, "profile_read: event wait failed");
+}
+
+const char* qlora_kernel_name(int32_t kind) {
+  return (kind >= 0 && kind < QLORA_K_COUNT) ? kKernelNames[kind] : "";
+}
 
 const char* qlora_last_error(void) { return g_err; }
 

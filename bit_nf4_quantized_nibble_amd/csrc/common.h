@@ -107,6 +107,17 @@ const Nf4Tables& host_tables();
 int set_error(int status, const char* fmt, ...);
 int check_launch(const char* what);
 
+// Opt-in kernel timing (qlora_profile_enable): brackets one launch with a pair of
+// events on its stream when recording is on; a no-op otherwise.
+void prof_begin(int kind, hipStream_t s, void** token);
+void prof_end(void* token, hipStream_t s);
+struct ProfScope {
+  void* token = nullptr;
+  hipStream_t s;
+  ProfScope(int kind, hipStream_t st) : s(st) { prof_begin(kind, st, &token); }
+  ~ProfScope() { prof_end(token, s); }
+};
+
 inline Nf4W make_w(const qlora_nf4_t* q) {
   Nf4W w;
   w.codes = q->codes;

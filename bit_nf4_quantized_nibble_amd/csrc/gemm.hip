@@ -443,14 +443,16 @@ int run_reduce(const float* part, const Split& sp, int64_t rows, int64_t cols, f
   const int64_t width = (outcd && ldcd > cols) ? ldcd : cols;
   const int64_t n = rows * width;
   if (n == 0) return QLORA_OK;
+  ProfScope prof(QLORA_K_REDUCE, s);
   k_reduce<CD><<<dim3((unsigned)ceil_div(n, kThreads)), dim3(kThreads), 0, s>>>(
       part, sp.S, rows * cols, rows, cols, sc32, out32, sccd, outcd, ldcd);
   return check_launch("k_reduce");
 }
 
 template <int CD, int BM, int BN, int LA1, int LB1, int LA2, int LB2, int EPI>
-int run_gemm(GemmParams& p, int S, hipStream_t s) {
+int run_gemm(GemmParams& p, int S, int kind, hipStream_t s) {
   dim3 grid((unsigned)ceil_div(p.N, BN), (unsigned)ceil_div(p.M, BM), (unsigned)S);
+  ProfScope prof(kind, s);
   k_gemm<CD, BM, BN, LA1, LB1, LA2, LB2, EPI><<<grid, dim3(kThreads), 0, s>>>(p, host_tables());
   return check_launch("k_gemm");
 }
@@ -478,7 +480,7 @@ int lora_down(const LayerCall& c, const Split& sp, float* part, float* out32, fl
   p.out = part;
   p.ldo = c.r;
   p.split_stride = c.m * c.r;
-  int rc = run_gemm<CD, 128, 64, LK_ROWS, LK_ROWS, LK_NONE, LK_NONE, EPI_F32_PARTIAL>(p, sp.S, c.stream);
+  int rc = run_gemm<CD, 128, 64, LK_ROWS, LK_ROWS, LK_NONE, LK_NONE, EPI_F32_PARTIAL>(p, sp.S, QLORA_K_LORA_DOWN, c.stream);
   if (rc) return rc;
   return run_reduce<CD>(part, sp, c.m, c.r, sc32, out32, sccd, outcd, r_pad, c.stream);
 }
@@ -506,7 +508,7 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
   p.out = y;
   p.ldo = N;
   p.bias = c.bias;
-  return run_gemm<CD, 128, 128, LK_ROWS, LK_NF4_ROWS, LK_ROWS, LK_ROWS, EPI_CD>(p, 1, c.stream);
+  return run_gemm<CD, 128, 128, LK_ROWS, LK_NF4_ROWS, LK_ROWS, LK_ROWS, EPI_CD>(p, 1, QLORA_K_FWD_GEMM, c.stream);
 }
 
 template <int CD>
@@ -541,7 +543,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     p.out = part;
     p.ldo = r;
     p.split_stride = M * r;
-    rc = run_gemm<CD, 128, 64, LK_ROWS, LK_COLS, LK_NONE, LK_NONE, EPI_F32_PARTIAL>(p, P.sdt.S, c.stream);
+    rc = run_gemm<CD, 128, 64, LK_ROWS, LK_COLS, LK_NONE, LK_NONE, EPI_F32_PARTIAL>(p, P.sdt.S, QLORA_K_BWD_DT, c.stream);
     if (rc) return rc;
     rc = run_reduce<CD>(part, P.sdt, M, r, c.scale, dt, c.scale, dtcd, P.r_pad, c.stream);
     if (rc) return rc;
@@ -561,7 +563,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     p.N = K;
     p.out = dx;
     p.ldo = K;
-    rc = run_gemm<CD, 128, 128, LK_ROWS, LK_NF4_COLS, LK_ROWS, LK_COLS, EPI_CD>(p, 1, c.stream);
+    rc = run_gemm<CD, 128, 128, LK_ROWS, LK_NF4_COLS, LK_ROWS, LK_COLS, EPI_CD>(p, 1, QLORA_K_BWD_DX, c.stream);
     if (rc) return rc;
   }
 
@@ -577,7 +579,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     p.out = part;
     p.ldo = K;
     p.split_stride = r * K;
-    rc = run_gemm<CD, 64, 128, LK_COLS, LK_COLS, LK_NONE, LK_NONE, EPI_F32_PARTIAL>(p, P.sda.S, c.stream);
+    rc = run_gemm<CD, 64, 128, LK_COLS, LK_COLS, LK_NONE, LK_NONE, EPI_F32_PARTIAL>(p, P.sda.S, QLORA_K_BWD_DA, c.stream);
     if (rc) return rc;
     rc = run_reduce<CD>(part, P.sda, r, K, 1.0f, d_a, 0.f, nullptr, 0, c.stream);
     if (rc) return rc;
@@ -595,7 +597,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     p.out = part;
     p.ldo = r;
     p.split_stride = N * r;
-    rc = run_gemm<CD, 128, 64, LK_COLS, LK_COLS_F32, LK_NONE, LK_NONE, EPI_F32_PARTIAL>(p, P.sdb.S, c.stream);
+    rc = run_gemm<CD, 128, 64, LK_COLS, LK_COLS_F32, LK_NONE, LK_NONE, EPI_F32_PARTIAL>(p, P.sdb.S, QLORA_K_BWD_DB, c.stream);
     if (rc) return rc;
     rc = run_reduce<CD>(part, P.sdb, N, r, c.scale, d_b, 0.f, nullptr, 0, c.stream);
     if (rc) return rc;

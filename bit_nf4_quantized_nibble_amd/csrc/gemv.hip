@@ -111,10 +111,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv(Nf4W w, const void* __restric
 template <int CD>
 int gemv_forward_t(const LayerCall& c, void* y, float* t_save) {
   float* T = (float*)c.ws;
+  {
+  ProfScope prof(QLORA_K_LORA_DOWN, c.stream);
   k_lora_down_small<CD><<<dim3((unsigned)ceil_div(c.r, kThreads / 64)), dim3(kThreads), 0, c.stream>>>(
       c.x, c.lora_a, c.m, c.w.cols, c.r, c.scale, T, t_save);
   int rc = check_launch("k_lora_down_small");
   if (rc) return rc;
+  }
+  ProfScope prof(QLORA_K_GEMV, c.stream);
   k_gemv<CD><<<dim3((unsigned)ceil_div(c.w.rows, kThreads / 64)), dim3(kThreads), 0, c.stream>>>(
       c.w, c.x, c.m, T, c.lora_b, c.r, c.bias, y, host_tables());
   return check_launch("k_gemv");

@@ -178,6 +178,7 @@ int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s) {
   const int64_t grid = ceil_div(nb, blocks_per_wg);
   const Nf4Tables& t = host_tables();
   if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "quantize: tensor too large");
+  ProfScope prof(QLORA_K_QUANTIZE, s);
 #define QNF4_Q(BS)                                                                         \
   case BS:                                                                                 \
     k_quantize<BS><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(                        \
@@ -205,6 +206,7 @@ int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_
   if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
   Nf4W w = make_w(q);
   const Nf4Tables& t = host_tables();
+  ProfScope prof(QLORA_K_DEQUANTIZE, s);
   switch (out_dtype) {
     case QLORA_F32:
       k_dequantize<CD_F32><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);

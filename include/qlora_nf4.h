@@ -89,7 +89,8 @@ typedef struct {
  * Pages: qlora-rs README "Honest capability matrix" (NF4 pack/unpack, block absmax,
  * double quant that drops the resident fp32 scales) and "NF4 Quantization".
  * Writes q->codes and either q->absmax or q->absmax_q + q->absmax_scale2.
- * Errors: QLORA_ERR_SHAPE (n % block_size, odd block_size, n == 0),
+ * An empty tensor (rows * cols == 0) is a no-op that returns QLORA_OK.
+ * Errors: QLORA_ERR_SHAPE (n % block_size, odd block_size, negative dims),
  * QLORA_ERR_UNSUPPORTED (block_size outside 8..512 or block_size/8 not a power of
  * two; dq_group > 4096), QLORA_ERR_INVALID_ARG (null pointers, reserved != 0).
  * NaN / Inf in W are outside the contract (codes are then unspecified, no fault).
@@ -113,9 +114,10 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, int32_t out_dtype, void* out, voi
  * capability matrix"; rust_ai_core QLoraConfig scale() = alpha / r; "LoRA and QLoRA,
  * mathematically" eq. (6.3.6) and "Tooling" (dequant fused with the matmul).
  * ws: device workspace of at least qlora_workspace_bytes(QLORA_OP_FWD, ...) bytes,
- * 256-byte aligned.  Errors: QLORA_ERR_INVALID_ARG (null x/lora_a/lora_b/y, r < 1,
- * non-finite alpha, m < 1), QLORA_ERR_DTYPE, QLORA_ERR_UNSUPPORTED (cols % 64 != 0
- * or block_size not a multiple of 32 dividing cols), QLORA_ERR_WORKSPACE.
+ * 256-byte aligned.  m == 0 is a no-op.  Errors: QLORA_ERR_INVALID_ARG (null
+ * x/lora_a/lora_b/y, r < 1, non-finite alpha, unknown flags), QLORA_ERR_SHAPE
+ * (m < 0, empty weight), QLORA_ERR_DTYPE, QLORA_ERR_UNSUPPORTED (cols % 64 != 0 or
+ * block_size not a multiple of 32 dividing cols), QLORA_ERR_WORKSPACE.
  */
 int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
                      const void* lora_b, int32_t r, float alpha, int32_t flags,
@@ -130,7 +132,8 @@ int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void*
  * forward; when NULL it is recomputed.  Pages: qlora-rs README "Honest capability
  * matrix" / "Training" (adapters update, base frozen); "LoRA and QLoRA,
  * mathematically" (only the low-rank factors are trained).
- * Errors: as qlora_linear_fwd, plus null dy / d_a / d_b.
+ * Errors: as qlora_linear_fwd, plus null dy / d_a / d_b and QLORA_ERR_SHAPE for
+ * m == 0 (there is nothing to differentiate).
  */
 int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m,
                      const void* lora_a, const void* lora_b, int32_t r, float alpha,
@@ -150,6 +153,34 @@ int qlora_nf4_levels(float out[16]);
 
 /* QLORA_NF4_ABI_VERSION of the built library. */
 int qlora_abi_version(void);
+
+/*
+ * Kernel timing (off by default).  While enabled, every kernel the library
+ * launches is bracketed by a pair of HIP events recorded on the caller's stream,
+ * and the elapsed times are summed per kernel kind.  Used by the benchmark to time
+ * individual kernels inside a multi-kernel call; costs one event pair per launch.
+ *   qlora_profile_enable(1) resets the totals and starts recording; (0) stops.
+ *   qlora_profile_read(kind, &ms, &launches) waits for the recorded events and
+ *   returns the summed milliseconds and launch count of that kind.
+ *   qlora_kernel_name(kind) names a kind ("" when out of range).
+ * Errors: QLORA_ERR_INVALID_ARG (bad kind / null output), QLORA_ERR_HIP.
+ */
+enum {
+  QLORA_K_QUANTIZE = 0,
+  QLORA_K_DEQUANTIZE,
+  QLORA_K_LORA_DOWN,  /* T = s x A^T (prologue of the forward; T0 in the backward) */
+  QLORA_K_REDUCE,     /* fixed-order sum of split-contraction partials */
+  QLORA_K_FWD_GEMM,   /* fused dequant-GEMM forward, m > 16 */
+  QLORA_K_GEMV,       /* decode forward, m <= 16 (its LoRA prologue counts as LORA_DOWN) */
+  QLORA_K_BWD_DT,     /* dT = s dY B */
+  QLORA_K_BWD_DX,     /* fused dequant-GEMM dX = dY W~ + dT A */
+  QLORA_K_BWD_DA,     /* dA = dT^T x */
+  QLORA_K_BWD_DB,     /* dB = s dY^T T0 */
+  QLORA_K_COUNT
+};
+int qlora_profile_enable(int32_t on);
+int qlora_profile_read(int32_t kind, double* ms, int64_t* launches);
+const char* qlora_kernel_name(int32_t kind);
 
 #ifdef __cplusplus
 }

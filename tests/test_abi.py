@@ -39,6 +39,9 @@ def test_exports_every_declared_function(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert lib.qlora_abi_version() == 1
+    for k, name in enumerate(_lib.KERNEL_KINDS):
+        assert lib.qlora_kernel_name(k).decode() == name
+    assert lib.qlora_kernel_name(99) == b""
 
 
 def test_host_level_table_equals_oracle(lib):
