@@ -41,7 +41,18 @@ struct Nf4W {
   int32_t bs;                // block size (elements)
   int32_t dq;                // double quantization on/off
   int32_t g;                 // blocks per second-level scale
+  int32_t bs_shift;          // log2(bs) when bs is a power of two, else -1
+  int32_t g_shift;           // log2(g) when g is a power of two, else -1
 };
+
+// Block of flat element e, and second-level group of block b.  Shifts when the
+// sizes are powers of two (a 64-bit division costs dozens of instructions).
+__device__ __forceinline__ int64_t block_of(const Nf4W& w, int64_t e) {
+  return w.bs_shift >= 0 ? (e >> w.bs_shift) : e / w.bs;
+}
+__device__ __forceinline__ int64_t group_of(const Nf4W& w, int64_t b) {
+  return w.g_shift >= 0 ? (b >> w.g_shift) : b / w.g;
+}
 
 // fl32(a * b), kept as a binary32 value.  Without the register barrier the
 // compiler may fuse the product with a following f16 conversion into one
@@ -55,20 +66,25 @@ __device__ __forceinline__ float fl32_mul(float a, float b) {
 
 // Scale of block b: the fp32 absmax, or fl32(q_b * S_group) with double quant.
 __device__ __forceinline__ float block_scale(const Nf4W& w, int64_t b) {
-  if (w.dq) return (float)w.absmax_q[b] * w.scale2[b / w.g];
+  if (w.dq) return (float)w.absmax_q[b] * w.scale2[group_of(w, b)];
   return w.absmax[b];
 }
 
 // ----------------------------------------------------------------------------
 // Compute-dtype conversions (round to nearest even, as the hardware converts).
 // ----------------------------------------------------------------------------
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 values -> one word of two 16-bit values (lo in bits 0..15), each
+// rounded to nearest even by a single packed conversion.
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
-  _Float16 a = (_Float16)lo, b = (_Float16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 template <int CD>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -118,6 +134,13 @@ struct ProfScope {
   ~ProfScope() { prof_end(token, s); }
 };
 
+inline int32_t log2_exact(int64_t v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int32_t s = 0;
+  while ((1LL << s) < v) ++s;
+  return s;
+}
+
 inline Nf4W make_w(const qlora_nf4_t* q) {
   Nf4W w;
   w.codes = q->codes;
@@ -129,6 +152,8 @@ inline Nf4W make_w(const qlora_nf4_t* q) {
   w.bs = q->block_size;
   w.dq = q->double_quant;
   w.g = q->double_quant ? q->dq_group : 1;
+  w.bs_shift = log2_exact(w.bs);
+  w.g_shift = log2_exact(w.g);
   return w;
 }
 

@@ -29,6 +29,12 @@
 #include "common.h"
 
 namespace qnf4 {
+
+// gemm256.hip: the 256 x 256 double-buffered fused kernels (bf16 / f16).
+int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* y);
+int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r_pad, void* dx);
+bool fused256_ok(const LayerCall& c, bool dx);
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -94,7 +100,7 @@ __device__ __forceinline__ u32x4_t load_chunk(const void* p, int64_t i, int64_t 
 template <int CD>
 __device__ __forceinline__ void decode32(const Nf4W& w, int64_t e, const float* s_lv, float (&f)[32]) {
   u32x4_t v = *(const u32x4_t*)(w.codes + e / 2);
-  const float s = block_scale(w, e / w.bs);
+  const float s = block_scale(w, block_of(w, e));
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
@@ -494,6 +500,7 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
   float* part = (float*)(ws + P.off_part);
   int rc = lora_down<CD>(c, P.st, part, t_save, 1.0f, tcd, c.scale, P.r_pad);
   if (rc) return rc;
+  if (fused256_ok(c, false)) return fused256_forward(c, tcd, P.r_pad, y);
 
   GemmParams p = base_params(c);
   p.a1 = opnd<CD>(c.x, K, M, K);
@@ -550,7 +557,10 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   }
 
   // dX = dY W~ + dT A (fused dequant; the contraction runs over W's rows).
-  if (dx) {
+  if (dx && fused256_ok(c, true)) {
+    rc = fused256_dx(c, dy, dtcd, P.r_pad, dx);
+    if (rc) return rc;
+  } else if (dx) {
     GemmParams p = base_params(c);
     p.a1 = opnd<CD>(dy, N, M, N);
     p.b1 = opnd<CD>(nullptr, 0, K, N);

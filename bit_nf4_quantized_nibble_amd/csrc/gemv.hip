@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(Nf4W w, const void* __restric
     const int64_t k0 = c * 32;
     const int64_t e = n * K + k0;
     u32x4_t v = *(const u32x4_t*)(w.codes + e / 2);
-    const float s = block_scale(w, e / w.bs);
+    const float s = block_scale(w, block_of(w, e));
     float wt[32];
 #pragma unroll
     for (int d = 0; d < 4; ++d)

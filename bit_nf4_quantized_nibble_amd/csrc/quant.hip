@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(Nf4W q, int64_t n, void
   for (int i = 0; i < 4; ++i) {
     const int64_t e = e0 + 8 * i;
     if (e >= n) break;
-    const float s = block_scale(q, e / q.bs);
+    const float s = block_scale(q, block_of(q, e));
     float f[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
