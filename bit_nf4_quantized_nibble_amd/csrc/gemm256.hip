@@ -12,17 +12,19 @@
 // of the output as 4 x 4 MFMA 32x32x16 tiles (256 fp32 accumulators per lane, in
 // the accumulation registers).  The contraction advances 64 elements per stage;
 // both operand tiles live in LDS as [tile index][contraction] rows of 128 bytes
-// (+16 bytes pad so that the 16-byte fragment reads of 16 consecutive rows hit
-// distinct banks), double buffered (2 x 72 KiB).
+// (XOR-swizzled 16-byte chunks), double buffered (4 x 32 KiB).
 //
-// Pipeline (one wave per SIMD, so all latency hiding is explicit):
-//   * global data for a stage is fetched two stages ahead into one of two
-//     register sets, with buffer loads (32-bit offsets, out-of-range reads
-//     return zero, so ragged tails need no branches);
-//   * while the 64 MFMAs of stage k run from LDS buffer k % 2, the lanes decode
-//     the NF4 codes of stage k+1 and write both tiles of that stage into the other
-//     buffer, a quarter per 16-element MFMA step; fragments for the next MFMA
-//     step are read while the current one issues.
+// Pipeline of stage k (one wave per SIMD, so all latency hiding is explicit and
+// the side work is placed between the MFMAs in program order):
+//   * one barrier per stage; before it each wave waits only for its own copy of
+//     stage k's activations and its LDS writes, never for later prefetches;
+//   * sub-step 0 issues the activation copy of stage k+1 (buffer_load ... lds,
+//     global -> LDS with no register round trip; each row of a stage is one whole
+//     128-byte line), spread over the MFMAs;
+//   * sub-step 1 issues the loads of the NF4 codes (and block scales) of stage
+//     k+2 into registers: they have more than a stage to arrive;
+//   * all four sub-steps decode a quarter of the codes of stage k+1 into the
+//     other W buffer and read the fragments of the next sub-step.
 //
 // NF4 decode (the method's dequantization, exact): code c -> fl32(L[c] * s_b) ->
 // compute dtype; L sits in LDS (16 words in 16 banks: conflict-free lookups).
@@ -70,14 +72,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, kRsrcWord3);
 }
-__device__ __forceinline__ u32x4_t ld128(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+// Buffer loads: byte offset = voff (per lane) + soff (wave-uniform).  Every part
+// that can fall outside a buffer stays in voff, which alone decides the range
+// check; soff only carries offsets that are in bounds by construction.
+__device__ __forceinline__ u32x4_t ld128(rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
-__device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
-__device__ __forceinline__ uint32_t ld8(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+__device__ __forceinline__ uint32_t ld8(rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 // Out-of-range offset: the top bit puts it past every buffer (all are < 2 GiB).
 __device__ __forceinline__ uint32_t oob_unless(bool ok, uint32_t off) {
@@ -115,11 +120,15 @@ __device__ __forceinline__ float scale_of(const CodeRegs& R, int i) {
 }
 
 // Per-lane constant parts of the addresses (all byte offsets fit in 31 bits).
+// Out-of-range lanes have the top bit set (oob_unless) so that their loads
+// return zeros; the per-stage parts are wave-uniform and go in soffset.
 struct Lane {
-  uint32_t a_off[8];     // activation: global byte offset of the chunk this lane copies, stage 0
-  uint32_t a_col[8];     // its element column within a stage (tail check)
-  uint32_t w_row;        // fwd: this lane's W row; dX: first of its 8 W rows within a stage
-  uint32_t w_col;        // dX: first of this lane's 8 W columns
+  uint32_t a_off;        // activation: global byte offset of the first chunk this lane copies
+  uint32_t a_step;       // bytes between its 8 chunks (32 rows apart)
+  uint32_t c_off;        // codes: fwd, start of W row n0 + tid; dX, W row (tid % 8) * 8 of
+                         //   the stage, column n0 + (tid / 8) * 8
+  uint32_t b_idx;        // block index of the same place (fwd: row start; dX: its column block)
+  bool ok;               // fwd: the W row exists; dX: the W columns exist
   uint32_t row_bytes;    // bytes of codes per W row (cols / 2)
   uint32_t row_blocks;   // blocks per W row (cols / block_size)
 };
@@ -128,47 +137,55 @@ struct Lane {
 // instruction i of wave w fills rows 8 (4 i + w) .. +8; lane l lands in physical
 // chunk l % 8 of row l / 8 and so fetches the logical chunk that maps there.
 template <int MODE>
+__device__ __forceinline__ void fetch_a1(const Big& p, const Lane& L, rsrc_t ra, char* dst, int wave, uint32_t kt,
+                                         int i) {
+  // The contraction is a whole number of stages (K for the forward: a multiple of
+  // 64 by the layer's contract; N for dX: required by fused256_ok), so no column
+  // check; rows past M read past the buffer and land as zeros.
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + (4 * i + wave) * 1024), 16,
+                                           (int)(L.a_off + i * L.a_step), (int)(kt * (BK * 2)), 0, 0);
+}
+template <int MODE>
 __device__ __forceinline__ void fetch_a(const Big& p, const Lane& L, rsrc_t ra, char* dst, int wave, uint32_t kt) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bool ok = MODE == MODE_FWD || kt * BK + L.a_col[i] < (uint32_t)p.K1;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + (4 * i + wave) * 1024), 16,
-                                             (int)oob_unless(ok, L.a_off[i] + kt * (BK * 2)), 0, 0, 0);
-  }
+  for (int i = 0; i < 8; ++i) fetch_a1<MODE>(p, L, ra, dst, wave, kt, i);
 }
 
+// Codes of stage kt.  Stages past the last (the prefetch runs two ahead) load
+// the last stage again: the stage offsets travel in soffset and must stay inside
+// the buffers.
 template <int MODE, int DQ>
 __device__ __forceinline__ void fetch_w(CodeRegs& R, const Big& p, const Lane& L, rsrc_t rc, rsrc_t rq,
-                                        rsrc_t rs, uint32_t kt) {
+                                        rsrc_t rs, uint32_t kt, uint32_t KT) {
+  if (kt >= KT) kt = KT - 1;
   const Nf4W& w = p.w;
   const uint32_t bsh = (uint32_t)w.bs_shift, gsh = (uint32_t)w.g_shift;
+  const uint32_t cv = oob_unless(L.ok, L.c_off);
   if constexpr (MODE == MODE_FWD) {
-    const bool ok = L.w_row < (uint32_t)w.rows;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint32_t col = kt * BK + 32 * j;
-      R.c[j] = ld128(rc, oob_unless(ok, L.w_row * L.row_bytes + col / 2));
-      const uint32_t b = L.w_row * L.row_blocks + (col >> bsh);
+      const uint32_t col = kt * BK + 32 * j;  // both 32-code halves lie in one block (bs >= 32)
+      R.c[j] = ld128(rc, cv, col / 2);
+      const uint32_t bu = col >> bsh;
       if constexpr (DQ) {
-        R.sq[j] = ld8(rq, oob_unless(ok, b));
-        R.sf[j] = __uint_as_float(ld32(rs, oob_unless(ok, (b >> gsh) * 4)));
+        R.sq[j] = ld8(rq, oob_unless(L.ok, L.b_idx), bu);
+        R.sf[j] = __uint_as_float(ld32(rs, oob_unless(L.ok, ((L.b_idx + bu) >> gsh) * 4)));
       } else {
-        R.sf[j] = __uint_as_float(ld32(rq, oob_unless(ok, b * 4)));
+        R.sf[j] = __uint_as_float(ld32(rq, oob_unless(L.ok, L.b_idx * 4), bu * 4));
       }
     }
   } else {
-    const bool col_ok = L.w_col < (uint32_t)w.cols;
+    // W rows kt * 64 + (tid % 8) * 8 + i exist: the fused dX path takes W only
+    // when its row count is a multiple of 64.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t n = kt * BK + L.w_row + i;
-      const bool ok = col_ok && n < (uint32_t)w.rows;
-      R.cw[i] = ld32(rc, oob_unless(ok, n * L.row_bytes + L.w_col / 2));
-      const uint32_t b = n * L.row_blocks + (L.w_col >> bsh);
+      const uint32_t nu = kt * BK + i;  // uniform part of the row index
+      R.cw[i] = ld32(rc, cv, nu * L.row_bytes);
       if constexpr (DQ) {
-        R.sq[i] = ld8(rq, oob_unless(ok, b));
-        R.sf[i] = __uint_as_float(ld32(rs, oob_unless(ok, (b >> gsh) * 4)));
+        R.sq[i] = ld8(rq, oob_unless(L.ok, L.b_idx), nu * L.row_blocks);
+        R.sf[i] = __uint_as_float(ld32(rs, oob_unless(L.ok, ((L.b_idx + nu * L.row_blocks) >> gsh) * 4)));
       } else {
-        R.sf[i] = __uint_as_float(ld32(rq, oob_unless(ok, b * 4)));
+        R.sf[i] = __uint_as_float(ld32(rq, oob_unless(L.ok, L.b_idx * 4), nu * L.row_blocks * 4));
       }
     }
   }
@@ -209,11 +226,22 @@ __device__ __forceinline__ void lookup_quarter(const CodeRegs& R, const char* ld
   }
 }
 
-template <int CD, int MODE, int DQ>
-__device__ __forceinline__ void finish_quarter(const CodeRegs& R, const float (&lv)[16], char* Bs, int tid,
+// The block scales of the lane's codes for one stage: fwd 2 (one per 32-code
+// half), dX 8 (one per W row).
+template <int MODE, int DQ>
+__device__ __forceinline__ void stage_scales(const CodeRegs& R, float (&sc)[8]) {
+#pragma unroll
+  for (int i = 0; i < (MODE == MODE_FWD ? 2 : 8); ++i) {
+    sc[i] = scale_of<DQ>(R, i);
+    asm volatile("" : "+v"(sc[i]));  // a register of its own: the loaded set dies here
+  }
+}
+
+template <int CD, int MODE>
+__device__ __forceinline__ void finish_quarter(const float (&sc)[8], const float (&lv)[16], char* Bs, int tid,
                                                int qtr) {
   if constexpr (MODE == MODE_FWD) {
-    const float s = scale_of<DQ>(R, qtr >> 1);
+    const float s = sc[qtr >> 1];
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       u32x4_t o;
@@ -230,8 +258,7 @@ __device__ __forceinline__ void finish_quarter(const CodeRegs& R, const float (&
       u32x4_t o;
 #pragma unroll
       for (int p2 = 0; p2 < 4; ++p2)
-        o[p2] = pack2<CD>(fl32_mul(lv[8 * u + 2 * p2], scale_of<DQ>(R, 2 * p2)),
-                          fl32_mul(lv[8 * u + 2 * p2 + 1], scale_of<DQ>(R, 2 * p2 + 1)));
+        o[p2] = pack2<CD>(fl32_mul(lv[8 * u + 2 * p2], sc[2 * p2]), fl32_mul(lv[8 * u + 2 * p2 + 1], sc[2 * p2 + 1]));
       *(u32x4_t*)(Bs + chunk_addr(kg * 8 + j, ng)) = o;
     }
   }
@@ -239,9 +266,10 @@ __device__ __forceinline__ void finish_quarter(const CodeRegs& R, const float (&
 
 template <int CD, int MODE, int DQ>
 __device__ __forceinline__ void decode_quarter(const CodeRegs& R, const char* lds, char* Bs, int tid, int qtr) {
-  float lv[16];
+  float lv[16], sc[8];
+  stage_scales<MODE, DQ>(R, sc);
   lookup_quarter<MODE>(R, lds, qtr, lv);
-  finish_quarter<CD, MODE, DQ>(R, lv, Bs, tid, qtr);
+  finish_quarter<CD, MODE>(sc, lv, Bs, tid, qtr);
 }
 
 // s_waitcnt vmcnt(n) (expcnt / lgkmcnt left alone).
@@ -290,38 +318,92 @@ __device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const Frags& F) {
     for (int j = 0; j < 4; ++j) acc[i][j] = mfma<CD>(F.a[i], F.b[j], acc[i][j]);
 }
 
-// Interleave hints: after each MFMA, a few VALU / LDS instructions of the decode.
-__device__ __forceinline__ void interleave_hints() {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+// s_waitcnt lgkmcnt(0) alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0x3f | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Workgroup barrier with no implied waits: the callers wait for exactly what the
+// other waves will read (their own copies and LDS writes of the stage).  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// Byte address (4 * code) of element e (0..15) of decode quarter q of the lane's
+// codes: fwd, element 16 q + e of its W row (high nibble first within a byte);
+// dX, row e % 8 of its 8 x 8 block, column 2 q + e / 8.
+template <int MODE>
+__device__ __forceinline__ uint32_t code_addr(const CodeRegs& R, int q, int e) {
+  if constexpr (MODE == MODE_FWD) {
+    const uint32_t word = R.c[q >> 1][2 * (q & 1) + (e >> 3)];
+    const int byte = (e & 7) >> 1;
+    return (word >> (8 * byte + ((e & 1) ? 0 : 4)) << 2) & 0x3cu;
+  } else {
+    const int j = 2 * q + (e >> 3);
+    const uint32_t sh = 8 * (j >> 1) + ((j & 1) ? 0 : 4);
+    return ((R.cw[e & 7] >> sh) << 2) & 0x3cu;
   }
-  __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);    // the 2 LDS writes
 }
 
-// One stage: 64 MFMAs from LDS buffer `cur`; meanwhile the NF4 codes of the next
-// stage (registers R) are decoded into the other buffer, a quarter per step.
+// Part t (0..7) of finishing quarter q: two weights fl32(level * scale) packed into
+// one word of the 16-byte chunk being assembled; parts 3 and 7 write a chunk.
+template <int CD, int MODE>
+__device__ __forceinline__ void finish_part(const float (&sc)[8], const float (&lv)[16], u32x4_t& o, char* Bs,
+                                            int tid, int q, int t) {
+  const int d = t >> 2, e = t & 3;  // chunk d of the quarter, word e of it
+  if constexpr (MODE == MODE_FWD) {
+    const float s = sc[q >> 1];
+    o[e] = pack2<CD>(fl32_mul(lv[8 * d + 2 * e], s), fl32_mul(lv[8 * d + 2 * e + 1], s));
+    if (e == 3) *(u32x4_t*)(Bs + chunk_addr(tid, 2 * q + d)) = o;
+  } else {
+    o[e] = pack2<CD>(fl32_mul(lv[8 * d + 2 * e], sc[2 * e]), fl32_mul(lv[8 * d + 2 * e + 1], sc[2 * e + 1]));
+    if (e == 3) *(u32x4_t*)(Bs + chunk_addr((tid >> 3) * 8 + 2 * q + d, tid & 7)) = o;
+  }
+}
+
+// One stage: 64 MFMAs from LDS buffer `cur`, in 4 sub-steps of 16.  The side work
+// sits at fixed MFMA slots (fences keep the compiler from regrouping it):
+//   every other slot: one fragment read for the next sub-step;
+//   every slot: one level lookup for the next decode quarter (in sub-step 3, for
+//     quarter 0 of the next stage, from Rn);
+//   slots 8..15: one pack of the current quarter (lookups issued a sub-step ago),
+//     its two chunk writes into the other W buffer;
+//   odd slots of sub-step 0: one instruction of the activation copy of stage kn.
+// lv[0] holds the lookups of quarter 0 on entry (and of the next stage's
+// quarter 0 on exit).
 template <int CD, int MODE, int DQ>
-__device__ __forceinline__ void stage(f32x16_t (&acc)[4][4], char* lds, int cur, const CodeRegs& R, int a_row,
-                                      int b_row, int xr, int h, int tid) {
+__device__ __forceinline__ void stage(f32x16_t (&acc)[4][4], char* lds, int cur, const CodeRegs& R,
+                                      const CodeRegs& Rn, float (&lv)[2][16], const Big& p, const Lane& L, rsrc_t ra,
+                                      int wave, uint32_t kn, bool do_a, int a_row, int b_row, int xr, int h, int tid) {
   char* As = lds + cur * TILE_BYTES;
   char* Bs = lds + (2 + cur) * TILE_BYTES;
+  char* An = lds + (cur ^ 1) * TILE_BYTES;
   char* Bn = lds + (2 + (cur ^ 1)) * TILE_BYTES;
   Frags F[2];
-  float lv[2][16];
+  float sc[8];
+  stage_scales<MODE, DQ>(R, sc);
   read_frags(F[0], As, Bs, a_row, b_row, xr, h, 0);
-  lookup_quarter<MODE>(R, lds, 0, lv[0]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    if (ks < 3) {
-      read_frags(F[(ks + 1) & 1], As, Bs, a_row, b_row, xr, h, ks + 1);
-      lookup_quarter<MODE>(R, lds, ks + 1, lv[(ks + 1) & 1]);
+    Frags& C = F[ks & 1];
+    Frags& N = F[(ks + 1) & 1];
+    float (&lc)[16] = lv[ks & 1];
+    float (&ln)[16] = lv[(ks + 1) & 1];
+    const int cphys = ((2 * (ks + 1) + h) ^ xr) << 4;
+    u32x4_t o;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int i = t >> 2, j = t & 3;
+      acc[i][j] = mfma<CD>(C.a[i], C.b[j], acc[i][j]);
+      if (ks < 3 && (t & 1) == 0) {
+        const int r = t >> 1;
+        if (r < 4) N.a[r] = *(const u32x4_t*)(As + (a_row + 32 * r) * ROWB + cphys);
+        else N.b[r - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (r - 4)) * ROWB + cphys);
+      }
+      if (ks < 3) ln[t] = lv_at(lds, code_addr<MODE>(R, ks + 1, t));
+      else ln[t] = lv_at(lds, code_addr<MODE>(Rn, 0, t));
+      if (t >= 8) finish_part<CD, MODE>(sc, lc, o, Bn, tid, ks, t - 8);
+      if (ks == 0 && (t & 1) == 1 && do_a) fetch_a1<MODE>(p, L, ra, An, wave, kn, t >> 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    mfma16<CD>(acc, F[ks & 1]);
-    finish_quarter<CD, MODE, DQ>(R, lv[ks & 1], Bn, tid, ks);
-    interleave_hints();
   }
 }
 
@@ -330,7 +412,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
   // [A0 | A1 | B0 | B1 | levels]
   __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_BYTES + 64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the DMA bases scalar
   if (tid < 16) *(float*)(lds + LV_OFF + 4 * tid) = tab.lv[tid];
   int tm, tn;
   tile_of(p, tm, tn);
@@ -349,21 +432,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
                               DQ ? ((nb + w.g - 1) / w.g) * 4 : nb * 4);
 
   Lane L;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 8 * (4 * i + wave) + (lane >> 3);
+  {
+    // rows 8 (4 i + wave) + lane / 8 for i = 0..7: their swizzle does not depend on i
+    const int row = 8 * wave + (lane >> 3);
     const int c = (lane & 7) ^ swz(row);
-    L.a_col[i] = 8 * c;
-    L.a_off[i] = (uint32_t)(((m0 + row) * p.ld_a1 + 8 * c) * 2);
+    L.a_off = (uint32_t)(((m0 + row) * p.ld_a1 + 8 * c) * 2);
+    L.a_step = (uint32_t)(32 * p.ld_a1 * 2);
   }
   L.row_bytes = (uint32_t)(w.cols / 2);
   L.row_blocks = (uint32_t)(w.cols >> w.bs_shift);
   if constexpr (MODE == MODE_FWD) {
-    L.w_row = (uint32_t)(n0 + tid);
-    L.w_col = 0;
+    const uint32_t row = (uint32_t)(n0 + tid);
+    L.ok = row < (uint32_t)w.rows;
+    L.c_off = row * L.row_bytes;
+    L.b_idx = row * L.row_blocks;
   } else {
-    L.w_row = (uint32_t)((tid & 7) * 8);
-    L.w_col = (uint32_t)(n0 + (tid >> 3) * 8);
+    const uint32_t row = (uint32_t)((tid & 7) * 8), col = (uint32_t)(n0 + (tid >> 3) * 8);
+    L.ok = col < (uint32_t)w.cols;
+    L.c_off = row * L.row_bytes + col / 2;
+    L.b_idx = row * L.row_blocks + (col >> w.bs_shift);
   }
 
   f32x16_t acc[4][4];
@@ -375,36 +462,45 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const uint32_t KT = (uint32_t)((p.K1 + BK - 1) / BK);
+  constexpr int NW = fetch_w_loads<MODE, DQ>();
   CodeRegs R0, R1;
   fetch_a<MODE>(p, L, ra, lds, wave, 0);
-  fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, 0);
-  fetch_w<MODE, DQ>(R1, p, L, rc, rq, rs, 1);
+  fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, 0, KT);
+  fetch_w<MODE, DQ>(R1, p, L, rc, rq, rs, 1, KT);
   __syncthreads();  // level table
 #pragma unroll
   for (int q = 0; q < 4; ++q) decode_quarter<CD, MODE, DQ>(R0, lds, lds + 2 * TILE_BYTES, tid, q);
-  fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, 2);
-  wait_vmcnt<fetch_w_loads<MODE, DQ>()>();  // the activation tile of stage 0 has landed in LDS
-  __syncthreads();
+  fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, 2, KT);
+  wait_vmcnt<NW>();  // the activation tile of stage 0 (and the codes of stage 1) have landed
+  wait_lgkm0();
+  barrier_only();
 
-  // Stage kt reads buffer kt % 2, prefetches the activations of stage kt + 1 into
-  // the other buffer and decodes its codes (fetched two stages ahead) there.
+  // Stage kt computes from buffer kt % 2 while it copies the activations of
+  // stage kt + 1 into the other buffer and decodes there the codes of stage kt + 1
+  // (R1 for even kt, R0 for odd); the set it has decoded then loads the codes of
+  // stage kt + 3.
+  float lv[2][16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) lv[0][t] = lv_at(lds, code_addr<MODE>(R1, 0, t));
   uint32_t kt = 0;
   for (; kt + 2 <= KT; kt += 2) {
-    fetch_a<MODE>(p, L, ra, lds + TILE_BYTES, wave, kt + 1);
-    stage<CD, MODE, DQ>(acc, lds, 0, R1, a_row, b_row, xr, h, tid);
-    fetch_w<MODE, DQ>(R1, p, L, rc, rq, rs, kt + 3);
-    wait_vmcnt<fetch_w_loads<MODE, DQ>()>();  // this stage's activation DMA has landed
-    __syncthreads();
-    fetch_a<MODE>(p, L, ra, lds, wave, kt + 2);
-    stage<CD, MODE, DQ>(acc, lds, 1, R0, a_row, b_row, xr, h, tid);
-    fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, kt + 4);
-    wait_vmcnt<fetch_w_loads<MODE, DQ>()>();
-    __syncthreads();
+    stage<CD, MODE, DQ>(acc, lds, 0, R1, R0, lv, p, L, ra, wave, kt + 1, true, a_row, b_row, xr, h, tid);
+    fetch_w<MODE, DQ>(R1, p, L, rc, rq, rs, kt + 3, KT);
+    wait_vmcnt<NW>();  // this wave's copy of stage kt + 1 has landed (the code loads may still fly)
+    wait_lgkm0();      // and its decode writes are in LDS
+    barrier_only();
+    const bool more = kt + 2 < KT;
+    stage<CD, MODE, DQ>(acc, lds, 1, R0, R1, lv, p, L, ra, wave, kt + 2, more, a_row, b_row, xr, h, tid);
+    fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, kt + 4, KT);
+    if (more) wait_vmcnt<NW>(); else __builtin_amdgcn_s_waitcnt(0);
+    wait_lgkm0();
+    barrier_only();
   }
   if (kt < KT) {
-    stage<CD, MODE, DQ>(acc, lds, 0, R1, a_row, b_row, xr, h, tid);
-    __syncthreads();
+    stage<CD, MODE, DQ>(acc, lds, 0, R1, R0, lv, p, L, ra, wave, kt + 1, false, a_row, b_row, xr, h, tid);
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // LoRA segment: r_pad more contraction steps with [T | B] (fwd) or [dT | A] (dX).
   char* As0 = lds;
@@ -509,8 +605,9 @@ bool fits_buffers(const LayerCall& c, int64_t a1_bytes) {
 // Whether the 256-tile kernels take this layer (else the generic tile engine does).
 bool fused256_ok(const LayerCall& c, bool dx) {
   if (c.cd != CD_BF16 && c.cd != CD_F16) return false;
+  if (c.w.rows <= 0 || c.w.cols <= 0 || c.m <= 0) return false;
   if (c.w.bs_shift < 0 || (c.w.dq && c.w.g_shift < 0)) return false;
-  if (dx) return (c.w.rows % 8 == 0) && fits_buffers(c, c.m * c.w.rows * 2);
+  if (dx) return (c.w.rows % BK == 0) && fits_buffers(c, c.m * c.w.rows * 2);
   return fits_buffers(c, c.m * c.w.cols * 2);
 }
 
