@@ -9,9 +9,14 @@ hand-written HIP kernels; there is no CPU or PyTorch fallback.
 Public API (names follow the pages' problem statement):
     quantize(w, block_size=64, double_quant=False, dq_group=256) -> NF4Weight
     dequantize(q, dtype=torch.bfloat16) -> Tensor [rows, cols]
-    linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False)
-    linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False)
-    workspace_bytes(op, m, rows, cols, r, dtype) ; levels()
+    linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False, path="auto")
+    linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False, path="auto")
+    workspace_bytes(op, m, rows, cols, r, dtype, flags=0) ; levels()
+
+path: "fused" decodes W inside the GEMM kernels; "dequant" writes W~ (or W~^T for
+dX) into the workspace first and runs a dense GEMM; "auto" lets the library pick
+(dequantize-then-GEMM from 1024 tokens up).  Calls with at most 16 tokens take
+the decode GEMV either way.
 """
 from __future__ import annotations
 
@@ -141,8 +146,18 @@ def dequantize(q: NF4Weight, dtype=None):
     return out
 
 
-def workspace_bytes(op: int, m: int, rows: int, cols: int, r: int, dtype) -> int:
-    return int(_lib.lib().qlora_workspace_bytes(op, m, rows, cols, r, dtype_code(dtype)))
+def workspace_bytes(op: int, m: int, rows: int, cols: int, r: int, dtype, flags: int = 0) -> int:
+    return int(_lib.lib().qlora_workspace_bytes(op | (flags << _lib.QLORA_OP_FLAGS_SHIFT), m, rows, cols, r,
+                                               dtype_code(dtype)))
+
+
+_PATHS = {"auto": 0, "fused": _lib.QLORA_FLAG_FUSED, "dequant": _lib.QLORA_FLAG_DEQUANT_GEMM}
+
+
+def _flags(rslora: bool, path: str) -> int:
+    if path not in _PATHS:
+        raise ValueError("path must be one of %s" % sorted(_PATHS))
+    return (_lib.QLORA_FLAG_RSLORA if rslora else 0) | _PATHS[path]
 
 
 def _workspace(nbytes: int, device, workspace=None):
@@ -162,7 +177,7 @@ def _flatten(x, cols):
 
 
 def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t: bool = False,
-               rslora: bool = False, workspace=None, out=None, t_out=None):
+               rslora: bool = False, workspace=None, out=None, t_out=None, path: str = "auto"):
     """y = x . deq(W)^T + s (x . A^T) . B^T (+ bias), s = alpha / r (alpha / sqrt(r)
     with rslora).  Leading dims of x are flattened to tokens.  Returns y, or
     (y, T0) with T0 = x A^T in fp32 when save_t.  ``out`` / ``t_out`` may supply
@@ -184,9 +199,9 @@ def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t:
     _need_cuda("t_out", t0, torch.float32)
     if t0 is not None and t0.numel() != m * r:
         raise ValueError("t_out must hold %d x %d fp32 elements" % (m, r))
-    ws = _workspace(workspace_bytes(_lib.QLORA_OP_FWD, m, q.rows, q.cols, r, dt), x.device, workspace)
+    flags = _flags(rslora, path)
+    ws = _workspace(workspace_bytes(_lib.QLORA_OP_FWD, m, q.rows, q.cols, r, dt, flags), x.device, workspace)
     d = q.descriptor()
-    flags = _lib.QLORA_FLAG_RSLORA if rslora else 0
     _lib.check(_lib.lib().qlora_linear_fwd(
         ctypes.byref(d), _ptr(x2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
         _ptr(bias), dtype_code(dt), _ptr(y), _ptr(t0), _ptr(ws), ws.numel() * ws.element_size(),
@@ -196,7 +211,7 @@ def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t:
 
 
 def linear_bwd(q: NF4Weight, x, dy, lora_a, lora_b, alpha: float, t_saved=None, need_dx: bool = True,
-               rslora: bool = False, workspace=None, dx_out=None, da_out=None, db_out=None):
+               rslora: bool = False, workspace=None, dx_out=None, da_out=None, db_out=None, path: str = "auto"):
     """Gradients with the base frozen: returns (dX or None, dA fp32 [r, cols], dB fp32 [rows, r]).
     ``*_out`` may supply preallocated outputs."""
     torch = _torch()
@@ -220,9 +235,9 @@ def linear_bwd(q: NF4Weight, x, dy, lora_a, lora_b, alpha: float, t_saved=None, 
         raise ValueError("output buffers have the wrong size")
     if t_saved is not None and t_saved.numel() != m * r:
         raise ValueError("t_saved must hold %d x %d fp32 elements" % (m, r))
-    ws = _workspace(workspace_bytes(_lib.QLORA_OP_BWD, m, q.rows, q.cols, r, dt), x.device, workspace)
+    flags = _flags(rslora, path)
+    ws = _workspace(workspace_bytes(_lib.QLORA_OP_BWD, m, q.rows, q.cols, r, dt, flags), x.device, workspace)
     d = q.descriptor()
-    flags = _lib.QLORA_FLAG_RSLORA if rslora else 0
     _lib.check(_lib.lib().qlora_linear_bwd(
         ctypes.byref(d), _ptr(x2), _ptr(dy2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
         dtype_code(dt), _ptr(t_saved), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),

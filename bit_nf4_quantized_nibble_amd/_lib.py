@@ -18,8 +18,8 @@ STATUS_NAMES = {
     -4: "QLORA_ERR_UNSUPPORTED", -5: "QLORA_ERR_WORKSPACE", -6: "QLORA_ERR_HIP",
 }
 QLORA_F32, QLORA_BF16, QLORA_F16 = 0, 1, 2
-QLORA_FLAG_RSLORA = 1
-QLORA_OP_FWD, QLORA_OP_BWD = 0, 1
+QLORA_FLAG_RSLORA, QLORA_FLAG_FUSED, QLORA_FLAG_DEQUANT_GEMM = 1, 2, 4
+QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_FLAGS_SHIFT = 0, 1, 8
 
 # Every function the header declares, for the export check.
 EXPORTED = (

@@ -124,7 +124,10 @@ int validate_layer(const qlora_nf4_t* w, const void* x, int64_t m, const void* l
   if (m < 0) return set_error(QLORA_ERR_SHAPE, "%s: negative m", who);
   if (r < 1) return set_error(QLORA_ERR_INVALID_ARG, "%s: rank r must be >= 1 (got %d)", who, r);
   if (!isfinite(alpha)) return set_error(QLORA_ERR_INVALID_ARG, "%s: alpha must be finite", who);
-  if (flags & ~QLORA_FLAG_RSLORA) return set_error(QLORA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", who, flags);
+  if (flags & ~(QLORA_FLAG_RSLORA | QLORA_FLAG_FUSED | QLORA_FLAG_DEQUANT_GEMM))
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", who, flags);
+  if ((flags & QLORA_FLAG_FUSED) && (flags & QLORA_FLAG_DEQUANT_GEMM))
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: QLORA_FLAG_FUSED and QLORA_FLAG_DEQUANT_GEMM exclude each other", who);
   if (w->rows < 1 || w->cols < 1) return set_error(QLORA_ERR_SHAPE, "%s: empty weight", who);
   if (!x || !lora_a || !lora_b) return set_error(QLORA_ERR_INVALID_ARG, "%s: null x / lora_a / lora_b", who);
   if (w->cols % 64 != 0)
@@ -320,8 +323,11 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, int32_t out_dtype, void* out, voi
 
 size_t qlora_workspace_bytes(int32_t op, int64_t m, int64_t rows, int64_t cols, int32_t r, int32_t cd) {
   if (m < 0 || rows < 0 || cols < 0 || r < 1 || !valid_cd(cd)) return 0;
-  if (op == QLORA_OP_FWD) return fwd_workspace_bytes(m, rows, cols, r, cd);
-  if (op == QLORA_OP_BWD) return bwd_workspace_bytes(m, rows, cols, r, cd);
+  const int32_t flags = op >> QLORA_OP_FLAGS_SHIFT;
+  op &= (1 << QLORA_OP_FLAGS_SHIFT) - 1;
+  if (flags & ~(QLORA_FLAG_RSLORA | QLORA_FLAG_FUSED | QLORA_FLAG_DEQUANT_GEMM)) return 0;
+  if (op == QLORA_OP_FWD) return fwd_workspace_bytes(m, rows, cols, r, cd, flags);
+  if (op == QLORA_OP_BWD) return bwd_workspace_bytes(m, rows, cols, r, cd, flags);
   return 0;
 }
 
@@ -333,7 +339,7 @@ int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void*
   if (rc) return rc;
   if (!y) return set_error(QLORA_ERR_INVALID_ARG, "linear_fwd: null y");
   if (m == 0) return QLORA_OK;
-  if ((rc = check_ws(ws, ws_bytes, fwd_workspace_bytes(m, w->rows, w->cols, r, cd), "linear_fwd"))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, fwd_workspace_bytes(m, w->rows, w->cols, r, cd, flags), "linear_fwd"))) return rc;
   if ((rc = check_tables("linear_fwd"))) return rc;
   LayerCall c;
   c.w = make_w(w);
@@ -341,6 +347,7 @@ int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void*
   c.m = m;
   c.r = r;
   c.scale = lora_scale(alpha, r, flags);
+  c.flags = flags;
   c.x = x;
   c.lora_a = lora_a;
   c.lora_b = lora_b;
@@ -360,7 +367,7 @@ int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_
   if (rc) return rc;
   if (!dy || !d_a || !d_b) return set_error(QLORA_ERR_INVALID_ARG, "linear_bwd: null dy / d_a / d_b");
   if (m == 0) return set_error(QLORA_ERR_SHAPE, "linear_bwd: m must be >= 1 (dA, dB would be all zero)");
-  if ((rc = check_ws(ws, ws_bytes, bwd_workspace_bytes(m, w->rows, w->cols, r, cd), "linear_bwd"))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, bwd_workspace_bytes(m, w->rows, w->cols, r, cd, flags), "linear_bwd"))) return rc;
   if ((rc = check_tables("linear_bwd"))) return rc;
   LayerCall c;
   c.w = make_w(w);
@@ -368,6 +375,7 @@ int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_
   c.m = m;
   c.r = r;
   c.scale = lora_scale(alpha, r, flags);
+  c.flags = flags;
   c.x = x;
   c.lora_a = lora_a;
   c.lora_b = lora_b;

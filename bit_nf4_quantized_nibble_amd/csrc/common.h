@@ -170,6 +170,7 @@ struct LayerCall {
   int64_t m;          // tokens
   int32_t r;
   float scale;        // alpha / r (or alpha / sqrt(r))
+  int32_t flags;      // QLORA_FLAG_* of the call
   const void* x;      // [m, cols]
   const void* lora_a; // [r, cols]
   const void* lora_b; // [rows, r]
@@ -179,8 +180,9 @@ struct LayerCall {
   hipStream_t stream;
 };
 
-size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
-size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
+size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags);
+size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags);
+int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s);
 int launch_forward(const LayerCall& c, void* y, float* t_save);
 int launch_backward(const LayerCall& c, const void* dy, const float* t_saved, void* dx,
                     float* d_a, float* d_b);

@@ -34,6 +34,9 @@ namespace qnf4 {
 int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* y);
 int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r_pad, void* dx);
 bool fused256_ok(const LayerCall& c, bool dx);
+bool dense256_ok(const LayerCall& c, bool dx);
+int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y);
+int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx);
 
 namespace {
 
@@ -400,30 +403,49 @@ Split choose_split(int64_t tiles, int64_t k, int bk) {
 constexpr int64_t kAlign = 256;
 inline int64_t al(int64_t b) { return round_up(b, kAlign); }
 
+// Dequantize-then-GEMM from this many tokens up (unless a path flag decides):
+// there the one-time dequantization (about 4.6 bytes of HBM traffic per weight) costs
+// less than decoding W again in every token tile of the fused kernels.
+constexpr int64_t kDenseMinM = 1024;
+
+// Whether a call takes the dequantize-then-GEMM path, from its shape and flags
+// alone (the workspace query must agree with the launch).  The launch also needs
+// dense256_ok; when that fails the copy's workspace is simply unused.
+bool dense_path(int64_t m, int64_t rows, int64_t cols, int cd, int32_t flags, bool dx) {
+  if (cd != CD_BF16 && cd != CD_F16) return false;
+  if (cols % 64 || (dx && rows % 64)) return false;
+  if (flags & QLORA_FLAG_FUSED) return false;
+  if (flags & QLORA_FLAG_DEQUANT_GEMM) return true;
+  return m >= kDenseMinM;
+}
+
 // Workspace plan shared by the size query and the launchers.
 struct FwdPlan {
   int64_t r_pad;
   Split st;
-  int64_t off_tcd, off_part, total;
+  bool dense;
+  int64_t off_tcd, off_part, off_wd, total;
 };
-FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
-  (void)rows;
+FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   FwdPlan P;
   const int es = cd_bytes(cd), bk = 128 / es;
   P.r_pad = round_up(r, 8);
   P.st = choose_split(ceil_div(m, 128) * ceil_div(r, 64), cols, bk);
   P.off_tcd = 0;
   P.off_part = al(m * P.r_pad * es);
-  P.total = P.off_part + al((int64_t)P.st.S * m * r * 4);
+  P.off_wd = P.off_part + al((int64_t)P.st.S * m * r * 4);
+  P.dense = dense_path(m, rows, cols, cd, flags, false);
+  P.total = P.off_wd + (P.dense ? al(rows * cols * es) : 0);
   return P;
 }
 
 struct BwdPlan {
   int64_t r_pad;
   Split st, sdt, sda, sdb;
-  int64_t off_t0, off_dt, off_dtcd, off_part, total;
+  bool dense;
+  int64_t off_t0, off_dt, off_dtcd, off_part, off_wdt, total;
 };
-BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
+BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   BwdPlan P;
   const int es = cd_bytes(cd), bk = 128 / es;
   P.r_pad = round_up(r, 8);
@@ -439,7 +461,9 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
   part = std::max<int64_t>(part, (int64_t)P.sdt.S * m * r);
   part = std::max<int64_t>(part, (int64_t)P.sda.S * r * cols);
   part = std::max<int64_t>(part, (int64_t)P.sdb.S * rows * r);
-  P.total = P.off_part + al(part * 4);
+  P.off_wdt = P.off_part + al(part * 4);
+  P.dense = dense_path(m, rows, cols, cd, flags, true);
+  P.total = P.off_wdt + (P.dense ? al(rows * cols * es) : 0);
   return P;
 }
 
@@ -494,12 +518,17 @@ int lora_down(const LayerCall& c, const Split& sp, float* part, float* out32, fl
 template <int CD>
 int forward_gemm(const LayerCall& c, void* y, float* t_save) {
   const int64_t M = c.m, N = c.w.rows, K = c.w.cols;
-  FwdPlan P = plan_fwd(M, N, K, c.r, CD);
+  FwdPlan P = plan_fwd(M, N, K, c.r, CD, c.flags);
   char* ws = (char*)c.ws;
   void* tcd = ws + P.off_tcd;
   float* part = (float*)(ws + P.off_part);
   int rc = lora_down<CD>(c, P.st, part, t_save, 1.0f, tcd, c.scale, P.r_pad);
   if (rc) return rc;
+  if (P.dense && dense256_ok(c, false)) {
+    void* wd = ws + P.off_wd;
+    if ((rc = dequant_into(c.w, CD, wd, false, c.stream))) return rc;
+    return dense256_forward(c, wd, tcd, P.r_pad, y);
+  }
   if (fused256_ok(c, false)) return fused256_forward(c, tcd, P.r_pad, y);
 
   GemmParams p = base_params(c);
@@ -522,7 +551,7 @@ template <int CD>
 int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void* dx, float* d_a,
                   float* d_b) {
   const int64_t M = c.m, N = c.w.rows, K = c.w.cols, r = c.r;
-  BwdPlan P = plan_bwd(M, N, K, c.r, CD);
+  BwdPlan P = plan_bwd(M, N, K, c.r, CD, c.flags);
   char* ws = (char*)c.ws;
   float* t0 = (float*)(ws + P.off_t0);
   float* dt = (float*)(ws + P.off_dt);
@@ -556,8 +585,13 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     if (rc) return rc;
   }
 
-  // dX = dY W~ + dT A (fused dequant; the contraction runs over W's rows).
-  if (dx && fused256_ok(c, true)) {
+  // dX = dY W~ + dT A (the contraction runs over W's rows): W~^T written once and a
+  // dense GEMM, or the fused dequant.
+  if (dx && P.dense && dense256_ok(c, true)) {
+    void* wdt = ws + P.off_wdt;
+    if ((rc = dequant_into(c.w, CD, wdt, true, c.stream))) return rc;
+    if ((rc = dense256_dx(c, dy, wdt, dtcd, P.r_pad, dx))) return rc;
+  } else if (dx && fused256_ok(c, true)) {
     rc = fused256_dx(c, dy, dtcd, P.r_pad, dx);
     if (rc) return rc;
   } else if (dx) {
@@ -621,13 +655,13 @@ int gemv_forward(const LayerCall& c, void* y, float* t_save);  // gemv.hip
 size_t gemv_workspace_bytes(int64_t m, int32_t r);
 constexpr int64_t kGemvMaxM = 16;
 
-size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
+size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   if (m <= kGemvMaxM) return gemv_workspace_bytes(m, r);
-  return (size_t)plan_fwd(m, rows, cols, r, cd).total;
+  return (size_t)plan_fwd(m, rows, cols, r, cd, flags).total;
 }
 
-size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
-  return (size_t)plan_bwd(m, rows, cols, r, cd).total;
+size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
+  return (size_t)plan_bwd(m, rows, cols, r, cd, flags).total;
 }
 
 int launch_forward(const LayerCall& c, void* y, float* t_save) {

@@ -407,6 +407,97 @@ __device__ __forceinline__ void stage(f32x16_t (&acc)[4][4], char* lds, int cur,
   }
 }
 
+// LoRA segment: r_pad more contraction steps with [T | B] (fwd) or [dT | A] (dX),
+// appended to the main contraction in the same accumulators.  Entered with every
+// copy drained and the LDS free.
+template <int CD, int MODE>
+__device__ __forceinline__ void lora_segment(f32x16_t (&acc)[4][4], char* lds, const Big& p, int64_t m0, int64_t n0,
+                                             int tid, int wave, int lane, int a_row, int b_row, int xr, int h) {
+  char* As0 = lds;
+  char* Bs0 = lds + 2 * TILE_BYTES;
+  for (int64_t k = 0; k < p.r_pad; k += BK) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + kThreads * i;
+      const int row = q >> 3, c = q & 7;
+      const int64_t grow = m0 + row, col = k + c * 8;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (grow < p.M && col < p.r_pad) v = *(const u32x4_t*)((const uint16_t*)p.a2 + grow * p.r_pad + col);
+      *(u32x4_t*)(As0 + chunk_addr(row, c)) = v;
+    }
+    if constexpr (MODE == MODE_FWD) {
+      // lora_b rows [n][t] as they are
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = tid + kThreads * i;
+        const int row = q >> 3, c = q & 7;
+        const int64_t grow = n0 + row, col = k + c * 8;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (grow < p.NB) {
+          const uint16_t* src = (const uint16_t*)p.b2 + grow * p.r + col;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.r) v[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
+        }
+        *(u32x4_t*)(Bs0 + chunk_addr(row, c)) = v;
+      }
+    } else {
+      // lora_a [t][k] staged as [k][t]: one 8 x 8 block per lane, transposed with permutes
+      const int tg = tid & 7, kg = tid >> 3;
+      u32x4_t in[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t t = k + tg * 8 + i, col = n0 + kg * 8;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (t < p.r) {
+          const uint16_t* src = (const uint16_t*)p.b2 + t * p.NB + col;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.NB) v[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
+        }
+        in[i] = v;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t o;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) o[q2] = __builtin_amdgcn_perm(in[2 * q2 + 1][j >> 1], in[2 * q2][j >> 1], sel);
+        *(u32x4_t*)(Bs0 + chunk_addr(kg * 8 + j, tg)) = o;
+      }
+    }
+    __syncthreads();
+    Frags F;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      read_frags(F, As0, Bs0, a_row, b_row, xr, h, ks);
+      mfma16<CD>(acc, F);
+    }
+    __syncthreads();
+  }
+
+}
+
+// Epilogue: fp32 accumulators (+ bias) -> compute dtype.
+template <int CD>
+__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Big& p, int64_t m0, int64_t n0, int wm,
+                                         int wn, int lane, int h) {
+  const int cl = lane & 31;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t col = n0 + wn + 32 * j + cl;
+    if (col >= p.NB) continue;
+    const float bias = p.bias ? load_cd<CD>(p.bias, col) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row < p.M) store_cd<CD>(p.out, row * p.NB + col, acc[i][j][v] + bias);
+      }
+  }
+}
+
 template <int CD, int MODE, int DQ>
 __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) {
   // [A0 | A1 | B0 | B1 | levels]
@@ -502,85 +593,110 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // LoRA segment: r_pad more contraction steps with [T | B] (fwd) or [dT | A] (dX).
-  char* As0 = lds;
-  char* Bs0 = lds + 2 * TILE_BYTES;
-  for (int64_t k = 0; k < p.r_pad; k += BK) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + kThreads * i;
-      const int row = q >> 3, c = q & 7;
-      const int64_t grow = m0 + row, col = k + c * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (grow < p.M && col < p.r_pad) v = *(const u32x4_t*)((const uint16_t*)p.a2 + grow * p.r_pad + col);
-      *(u32x4_t*)(As0 + chunk_addr(row, c)) = v;
-    }
-    if constexpr (MODE == MODE_FWD) {
-      // lora_b rows [n][t] as they are
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = tid + kThreads * i;
-        const int row = q >> 3, c = q & 7;
-        const int64_t grow = n0 + row, col = k + c * 8;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (grow < p.NB) {
-          const uint16_t* src = (const uint16_t*)p.b2 + grow * p.r + col;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (col + e < p.r) v[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
-        }
-        *(u32x4_t*)(Bs0 + chunk_addr(row, c)) = v;
-      }
-    } else {
-      // lora_a [t][k] staged as [k][t]: one 8 x 8 block per lane, transposed with permutes
-      const int tg = tid & 7, kg = tid >> 3;
-      u32x4_t in[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t t = k + tg * 8 + i, col = n0 + kg * 8;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (t < p.r) {
-          const uint16_t* src = (const uint16_t*)p.b2 + t * p.NB + col;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (col + e < p.NB) v[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
-        }
-        in[i] = v;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t o;
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) o[q2] = __builtin_amdgcn_perm(in[2 * q2 + 1][j >> 1], in[2 * q2][j >> 1], sel);
-        *(u32x4_t*)(Bs0 + chunk_addr(kg * 8 + j, tg)) = o;
-      }
-    }
-    __syncthreads();
-    Frags F;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      read_frags(F, As0, Bs0, a_row, b_row, xr, h, ks);
-      mfma16<CD>(acc, F);
-    }
-    __syncthreads();
-  }
+  lora_segment<CD, MODE>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+  epilogue<CD>(acc, p, m0, n0, wm, wn, lane, h);
+}
 
-  // Epilogue: fp32 accumulators (+ bias) -> compute dtype.
-  const int cl = lane & 31;
+// ---------------------------------------------------------------------------
+// Dense variant (dequantize-then-GEMM): the W operand is a compute-dtype matrix
+// Bd [NB, K1] (W~ for the forward, W~^T for dX, written by the dequantize
+// kernels), copied into LDS by the same DMA as the activations.  Stage k: one
+// barrier (every copy in flight is stage k's), then 64 MFMAs with the copy of
+// stage k + 1 spread over sub-steps 0 (activations) and 1 (W), one instruction
+// per two MFMAs, and the fragment reads of the next sub-step between them.
+// ---------------------------------------------------------------------------
+template <int CD, int DO_COPY>
+__device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][4], char* lds, int cur, rsrc_t ra, rsrc_t rb,
+                                            uint32_t a_off, uint32_t b_off, uint32_t step, int wave, uint32_t kn,
+                                            int a_row, int b_row, int xr, int h) {
+  char* As = lds + cur * TILE_BYTES;
+  char* Bs = lds + (2 + cur) * TILE_BYTES;
+  char* An = lds + (cur ^ 1) * TILE_BYTES;
+  char* Bn = lds + (2 + (cur ^ 1)) * TILE_BYTES;
+  Frags F[2];
+  read_frags(F[0], As, Bs, a_row, b_row, xr, h, 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t col = n0 + wn + 32 * j + cl;
-    if (col >= p.NB) continue;
-    const float bias = p.bias ? load_cd<CD>(p.bias, col) : 0.f;
+  for (int ks = 0; ks < 4; ++ks) {
+    Frags& C = F[ks & 1];
+    Frags& N = F[(ks + 1) & 1];
+    const int cphys = ((2 * (ks + 1) + h) ^ xr) << 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row < p.M) store_cd<CD>(p.out, row * p.NB + col, acc[i][j][v] + bias);
+    for (int t = 0; t < 16; ++t) {
+      const int i = t >> 2, j = t & 3;
+      acc[i][j] = mfma<CD>(C.a[i], C.b[j], acc[i][j]);
+      if (ks < 3 && (t & 1) == 0) {
+        const int r = t >> 1;
+        if (r < 4) N.a[r] = *(const u32x4_t*)(As + (a_row + 32 * r) * ROWB + cphys);
+        else N.b[r - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (r - 4)) * ROWB + cphys);
       }
+      if (DO_COPY && ks < 2 && (t & 1) == 1) {
+        const int d = t >> 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ks == 0 ? ra : rb,
+                                                 (lds_void*)((ks == 0 ? An : Bn) + (4 * d + wave) * 1024), 16,
+                                                 (int)((ks == 0 ? a_off : b_off) + d * step), (int)(kn * (BK * 2)),
+                                                 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+}
+
+template <int CD, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd) {
+  // [A0 | A1 | B0 | B1]
+  __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  tile_of(p, tm, tn);
+  const int64_t m0 = (int64_t)tm * TILE, n0 = (int64_t)tn * TILE;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int h = lane >> 5;
+  const int a_row = wm + (lane & 31), b_row = wn + (lane & 31);
+  const int xr = swz(lane & 31);
+  const rsrc_t ra = make_rsrc(p.a1, p.M * p.ld_a1 * 2);
+  const rsrc_t rb = make_rsrc(bd, p.NB * p.K1 * 2);
+  // rows 8 (4 d + wave) + lane / 8 (d = 0..7) of each tile; rows past M or NB read
+  // past their buffer (the row is in the lane offset) and land as zeros
+  const int row = 8 * wave + (lane >> 3);
+  const int c = (lane & 7) ^ swz(row);
+  const uint32_t a_off = (uint32_t)(((m0 + row) * p.ld_a1 + 8 * c) * 2);
+  const uint32_t b_off = (uint32_t)(((n0 + row) * p.K1 + 8 * c) * 2);
+  const uint32_t a_step = (uint32_t)(32 * p.ld_a1 * 2), b_step = (uint32_t)(32 * p.K1 * 2);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const uint32_t KT = (uint32_t)(p.K1 / BK);  // K1 is a multiple of 64 here
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(lds + (4 * d + wave) * 1024), 16, (int)(a_off + d * a_step),
+                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + 2 * TILE_BYTES + (4 * d + wave) * 1024), 16,
+                                             (int)(b_off + d * b_step), 0, 0, 0);
+  }
+  // a_step == b_step only when ld_a1 == K1, which holds for both uses (x [M, K]
+  // against W~ [N, K]; dY [M, N] against W~^T [K, N]).
+  uint32_t k = 0;
+  for (; k + 1 < KT; ++k) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of stage k and its fragment reads
+    barrier_only();
+    dense_stage<CD, 1>(acc, lds, k & 1, ra, rb, a_off, b_off, a_step, wave, k + 1, a_row, b_row, xr, h);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  barrier_only();
+  dense_stage<CD, 0>(acc, lds, k & 1, ra, rb, a_off, b_off, a_step, wave, 0, a_row, b_row, xr, h);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  lora_segment<CD, MODE>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+  epilogue<CD>(acc, p, m0, n0, wm, wn, lane, h);
 }
 
 template <int CD, int MODE>
@@ -592,6 +708,14 @@ int run(const Big& b, hipStream_t s, int kind) {
   else
     k_fused256<CD, MODE, 0><<<dim3((unsigned)tiles), dim3(kThreads), 0, s>>>(b, host_tables());
   return check_launch(MODE == MODE_FWD ? "k_fused256<fwd>" : "k_fused256<dx>");
+}
+
+template <int CD, int MODE>
+int run_dense(const Big& b, const void* bd, hipStream_t s, int kind) {
+  const int64_t tiles = (int64_t)b.tiles_m * b.tiles_n;
+  ProfScope prof(kind, s);
+  k_dense256<CD, MODE><<<dim3((unsigned)tiles), dim3(kThreads), 0, s>>>(b, bd);
+  return check_launch(MODE == MODE_FWD ? "k_dense256<fwd>" : "k_dense256<dx>");
 }
 
 bool fits_buffers(const LayerCall& c, int64_t a1_bytes) {
@@ -651,6 +775,55 @@ int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r
   b.bias = nullptr;
   if (c.cd == CD_BF16) return run<CD_BF16, MODE_DX>(b, c.stream, QLORA_K_BWD_DX);
   return run<CD_F16, MODE_DX>(b, c.stream, QLORA_K_BWD_DX);
+}
+
+// Whether the dense (dequantize-then-GEMM) kernels take this layer: the same
+// shapes as the fused ones, and the dequantized copy must fit a buffer resource.
+bool dense256_ok(const LayerCall& c, bool dx) {
+  if (!fused256_ok(c, dx)) return false;
+  return c.w.rows * c.w.cols * 2 < 0x7fff0000LL && (c.w.cols % BK == 0) && (c.w.rows % BK == 0 || !dx);
+}
+
+// y = [x | T][W~ | B]^T + bias with W~ [N, K] already in the compute dtype.
+int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y) {
+  Big b = {};
+  b.a1 = c.x;
+  b.ld_a1 = c.w.cols;
+  b.a2 = t_cd;
+  b.r_pad = r_pad;
+  b.b2 = c.lora_b;
+  b.w = c.w;
+  b.M = c.m;
+  b.NB = c.w.rows;
+  b.K1 = c.w.cols;
+  b.r = c.r;
+  b.tiles_m = (int32_t)ceil_div(c.m, TILE);
+  b.tiles_n = (int32_t)ceil_div(c.w.rows, TILE);
+  b.out = y;
+  b.bias = c.bias;
+  if (c.cd == CD_BF16) return run_dense<CD_BF16, MODE_FWD>(b, wd, c.stream, QLORA_K_FWD_GEMM);
+  return run_dense<CD_F16, MODE_FWD>(b, wd, c.stream, QLORA_K_FWD_GEMM);
+}
+
+// dX = [dY | dT][W~ ; A] with W~^T [K, N] already in the compute dtype.
+int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx) {
+  Big b = {};
+  b.a1 = dy;
+  b.ld_a1 = c.w.rows;
+  b.a2 = dt_cd;
+  b.r_pad = r_pad;
+  b.b2 = c.lora_a;
+  b.w = c.w;
+  b.M = c.m;
+  b.NB = c.w.cols;
+  b.K1 = c.w.rows;
+  b.r = c.r;
+  b.tiles_m = (int32_t)ceil_div(c.m, TILE);
+  b.tiles_n = (int32_t)ceil_div(c.w.cols, TILE);
+  b.out = dx;
+  b.bias = nullptr;
+  if (c.cd == CD_BF16) return run_dense<CD_BF16, MODE_DX>(b, wdt, c.stream, QLORA_K_BWD_DX);
+  return run_dense<CD_F16, MODE_DX>(b, wdt, c.stream, QLORA_K_BWD_DX);
 }
 
 }  // namespace qnf4

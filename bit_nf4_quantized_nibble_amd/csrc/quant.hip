@@ -170,6 +170,41 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(Nf4W q, int64_t n, void
 
 }  // namespace
 
+// Transposed dequantize for the dequantize-then-GEMM backward: out [cols, rows] =
+// RNE_cd(fl32(L[c] * s_b))^T, the same values as k_dequantize.  One workgroup per
+// 64 x 64 tile of W: each lane decodes 16 consecutive codes of one W row into an
+// LDS tile [k][n], then writes 16 consecutive elements of one output row.
+// rows and cols are multiples of 64 (checked by the caller).
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restrict__ out, Nf4Tables tab) {
+  __shared__ float s_lv[16];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // [k][n], 144-byte rows
+  const int tid = threadIdx.x;
+  if (tid < 16) s_lv[tid] = tab.lv[tid];
+  __syncthreads();
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  const int nr = tid >> 2, kc = (tid & 3) * 16;
+  const int64_t e0 = (n0 + nr) * q.cols + k0 + kc;
+  const uint2 cw = *(const uint2*)(q.codes + e0 / 2);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const uint32_t word = hf ? cw.y : cw.x;
+    const float s = block_scale(q, block_of(q, e0 + 8 * hf));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t c = (word >> ((j >> 1) * 8 + ((j & 1) ? 0 : 4))) & 15u;
+      tile[kc + 8 * hf + j][nr] = to_cd16<OUT>(fl32_mul(s_lv[c], s));
+    }
+  }
+  __syncthreads();
+  const int kr = tid >> 2, nc = (tid & 3) * 16;
+  const u32x4_t v0 = *(const u32x4_t*)&tile[kr][nc];
+  const u32x4_t v1 = *(const u32x4_t*)&tile[kr][nc + 8];
+  uint16_t* o = (uint16_t*)out + (k0 + kr) * q.rows + n0 + nc;
+  *(u32x4_t*)o = v0;
+  *(u32x4_t*)(o + 8) = v1;
+}
+
 int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s) {
   const int64_t n = q->rows * q->cols;
   const int bs = q->block_size;
@@ -220,6 +255,28 @@ int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_
     default:
       return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", out_dtype);
   }
+  return check_launch("k_dequantize");
+}
+
+// Dequantize W into a compute-dtype buffer inside a layer call: [rows, cols]
+// (forward) or its transpose [cols, rows] (dX).  The transpose needs rows and cols
+// to be multiples of 64.
+int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s) {
+  const Nf4Tables& t = host_tables();
+  ProfScope prof(QLORA_K_DEQUANTIZE, s);
+  if (transposed) {
+    if (w.rows % 64 || w.cols % 64) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: shape not a multiple of 64");
+    const dim3 grid((unsigned)(w.cols / 64), (unsigned)(w.rows / 64));
+    if (cd == CD_BF16) k_dequantize_t<CD_BF16><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+    else if (cd == CD_F16) k_dequantize_t<CD_F16><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+    else return set_error(QLORA_ERR_DTYPE, "dequantize^T: bad dtype %d", cd);
+    return check_launch("k_dequantize_t");
+  }
+  const int64_t n = w.rows * w.cols;
+  const int64_t grid = ceil_div(ceil_div(n, 32), kThreads);
+  if (cd == CD_BF16) k_dequantize<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+  else if (cd == CD_F16) k_dequantize<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+  else return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
   return check_launch("k_dequantize");
 }
 

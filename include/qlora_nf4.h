@@ -52,13 +52,24 @@ typedef enum {
 /* Compute / storage dtype of activations, adapters and outputs. */
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1, QLORA_F16 = 2 } qlora_dtype_t;
 
-/* Flags for the forward / backward calls. */
+/* Flags for the forward / backward calls.  The two path flags (at most one) pick
+ * how W~ meets the activations when m > 16 (m <= 16 always takes the decode GEMV):
+ *   default                  m >= 1024: dequantize-then-GEMM; else fused
+ *   QLORA_FLAG_FUSED         the fused kernels decode W~ on the fly, tile by tile
+ *                            (no dequantized copy of W anywhere)
+ *   QLORA_FLAG_DEQUANT_GEMM  W~ (forward) or W~^T (dX) is first written in cd into
+ *                            the workspace, then a dense GEMM reads it; the copy
+ *                            lives only in the workspace, for the call.
+ * Both paths give the same W~ bits; the sums differ only in accumulation order. */
 enum {
-  QLORA_FLAG_RSLORA = 1 /* scale = alpha / sqrt(r) instead of alpha / r */
+  QLORA_FLAG_RSLORA = 1,       /* scale = alpha / sqrt(r) instead of alpha / r */
+  QLORA_FLAG_FUSED = 2,
+  QLORA_FLAG_DEQUANT_GEMM = 4
 };
 
-/* Workspace queries. */
-enum { QLORA_OP_FWD = 0, QLORA_OP_BWD = 1 };
+/* Workspace queries: op is QLORA_OP_FWD or QLORA_OP_BWD, OR'ed with the call's
+ * flags shifted left by QLORA_OP_FLAGS_SHIFT (the path decides the size). */
+enum { QLORA_OP_FWD = 0, QLORA_OP_BWD = 1, QLORA_OP_FLAGS_SHIFT = 8 };
 
 /*
  * An NF4-quantized frozen weight W [rows, cols].  Descriptor memory is the
@@ -117,7 +128,10 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, int32_t out_dtype, void* out, voi
  * 256-byte aligned.  m == 0 is a no-op.  Errors: QLORA_ERR_INVALID_ARG (null
  * x/lora_a/lora_b/y, r < 1, non-finite alpha, unknown flags), QLORA_ERR_SHAPE
  * (m < 0, empty weight), QLORA_ERR_DTYPE, QLORA_ERR_UNSUPPORTED (cols % 64 != 0 or
- * block_size not a multiple of 32 dividing cols), QLORA_ERR_WORKSPACE.
+ * block_size not a multiple of 32 dividing cols), QLORA_ERR_WORKSPACE.  With both
+ * path flags set: QLORA_ERR_INVALID_ARG.  Shapes the fast paths do not take (f32,
+ * block sizes that are not powers of two, W rows % 64 != 0 for dX) run on a
+ * generic tile kernel with the same results.
  */
 int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
                      const void* lora_b, int32_t r, float alpha, int32_t flags,
@@ -140,8 +154,9 @@ int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_
                      int32_t flags, int32_t cd, const float* t_saved, void* dx, float* d_a,
                      float* d_b, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace size in bytes for op (QLORA_OP_FWD / QLORA_OP_BWD) on this layer shape;
- * 0 for an invalid query.  Pure host function. */
+/* Workspace size in bytes for op (QLORA_OP_FWD / QLORA_OP_BWD, optionally OR'ed
+ * with flags << QLORA_OP_FLAGS_SHIFT) on this layer shape; 0 for an invalid query.
+ * Pure host function. */
 size_t qlora_workspace_bytes(int32_t op, int64_t m, int64_t rows, int64_t cols, int32_t r,
                              int32_t cd);
 

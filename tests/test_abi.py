@@ -108,7 +108,8 @@ def fwd(lib, d, x=FAKE, m=128, a=FAKE, b=FAKE, r=8, alpha=16.0, flags=0, bias=No
     (dict(r=0), INVALID),
     (dict(alpha=float("nan")), INVALID),
     (dict(alpha=float("inf")), INVALID),
-    (dict(flags=4), INVALID),
+    (dict(flags=8), INVALID),
+    (dict(flags=6), INVALID),                # both path flags
     (dict(x=None), INVALID),
     (dict(a=None), INVALID),
     (dict(b=None), INVALID),
@@ -153,6 +154,16 @@ def test_workspace_query(lib):
     big = lib.qlora_workspace_bytes(1, 4096, 4096, 4096, 64, 1)
     assert 0 < small <= big and big % 256 == 0
     assert lib.qlora_workspace_bytes(0, 4, 4096, 4096, 16, 1) >= 4 * 16 * 4
+    # the dequantize-then-GEMM path holds W~ (forward) or W~^T (dX) in the workspace
+    fused = lib.qlora_workspace_bytes(0 | (2 << 8), 2048, 4096, 4096, 64, 1)
+    dense = lib.qlora_workspace_bytes(0 | (4 << 8), 2048, 4096, 4096, 64, 1)
+    assert dense - fused >= 4096 * 4096 * 2
+    assert lib.qlora_workspace_bytes(0, 2048, 4096, 4096, 64, 1) == dense      # default at 2048 tokens
+    assert lib.qlora_workspace_bytes(0, 512, 4096, 4096, 64, 1) == lib.qlora_workspace_bytes(2 << 8, 512, 4096, 4096, 64, 1)
+    assert lib.qlora_workspace_bytes(1 | (4 << 8), 512, 4096, 4096, 64, 1) >= 4096 * 4096 * 2
+    assert lib.qlora_workspace_bytes(0 | (8 << 8), 512, 4096, 4096, 64, 1) == 0  # unknown flag
+    assert lib.qlora_workspace_bytes(0 | (4 << 8), 512, 4096, 4096, 64, 0) == \
+        lib.qlora_workspace_bytes(0 | (2 << 8), 512, 4096, 4096, 64, 0)       # f32 has no dense path
 
 
 def test_binding_rejects_cpu_tensors():
@@ -164,3 +175,6 @@ def test_binding_rejects_cpu_tensors():
     assert q.dtype_code(torch.bfloat16) == 1 and q.dtype_code(torch.float16) == 2
     with pytest.raises(TypeError):
         q.dtype_code(torch.int8)
+    with pytest.raises(ValueError):
+        q._flags(False, "fast")
+    assert q._flags(True, "dequant") == 5 and q._flags(False, "fused") == 2

@@ -1,5 +1,6 @@
-"""GPU parity of the QLoRA layer (fused dequant-GEMM forward, decode GEMV and the
-backward) against the fp64 oracle on the same seeded inputs, through the C ABI.
+"""GPU parity of the QLoRA layer (fused dequant-GEMM and dequantize-then-GEMM
+forward, decode GEMV and the backward) against the fp64 oracle on the same seeded
+inputs, through the C ABI.
 
 Small cases compare every element (several tiles plus ragged tails in M, N and
 the rank); full-size workloads compare sampled entries the oracle computes one
@@ -36,19 +37,22 @@ def test_forward_tiny():
     assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"]), "bf16", "tiny fwd")
 
 
-@pytest.mark.parametrize("cd", ["bf16", "f16", "f32"])
+PATHS = [("bf16", "fused"), ("bf16", "dequant"), ("f16", "fused"), ("f16", "dequant"), ("f32", "auto")]
+
+
+@pytest.mark.parametrize("cd,path", PATHS)
 @pytest.mark.parametrize("M,N,K,r,bs,dq,bias", [
     (300, 200, 320, 8, 64, True, True),     # ragged M and N, 5 K-steps, bias
     (129, 257, 128, 24, 32, False, False),  # ragged by one, rank not a multiple of 16
     (64, 96, 256, 64, 128, True, False),
     (17, 128, 64, 3, 64, False, True),      # smallest GEMM-path M, odd rank
 ])
-def test_forward_ragged(cd, M, N, K, r, bs, dq, bias):
+def test_forward_ragged(cd, path, M, N, K, r, bs, dq, bias):
     L = inputs.random_layer(M, N, K, r, seed=M + N + r, cd=cd, block_size=bs, double_quant=dq,
                             with_bias=bias, with_dy=False)
-    say("fwd ragged", cd, M, N, K, r, bs, dq, bias)
+    say("fwd ragged", cd, path, M, N, K, r, bs, dq, bias)
     g = to_gpu(L)
-    y = run_fwd(L, g, gpu_q(L, g))
+    y = run_fwd(L, g, gpu_q(L, g), path=path)
     o = oracle_layer(L)
     ref = oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"])
     assert_close(to_np(y), ref, cd, "fwd %s %dx%dx%d r%d" % (cd, M, N, K, r))
@@ -124,13 +128,14 @@ def test_forward_rslora():
     assert_close(to_np(y), ref, "bf16", "rslora")
 
 
+@pytest.mark.parametrize("path", ["fused", "dequant"])
 @pytest.mark.parametrize("name", ["q_proj", "down_proj"])
-def test_forward_prefill_full_size_sampled(name):
+def test_forward_prefill_full_size_sampled(name, path):
     (L,) = inputs.prefill(projections=[name])
-    say("fwd prefill", name)
+    say("fwd prefill", name, path)
     g = to_gpu(L)
     q = gpu_q(L, g)
-    y = run_fwd(L, g, q)
+    y = run_fwd(L, g, q, path=path)
     o = oracle_layer(L)
     rng = np.random.default_rng(7)
     ii = rng.integers(0, L.M, 256)
@@ -139,7 +144,7 @@ def test_forward_prefill_full_size_sampled(name):
     jj[:4] = [0, 0, L.N - 1, L.N - 1]
     ref = oracle.forward_at(o["x"], o["W"], o["A"], o["B"], o["s"], ii, jj)
     got = to_np(y)[ii, jj]
-    assert_close(got, ref, "bf16", "prefill %s" % name)
+    assert_close(got, ref, "bf16", "prefill %s %s" % (name, path))
 
 
 @pytest.mark.parametrize("cd", ["f16", "f32"])
@@ -174,13 +179,14 @@ def test_backward_tiny():
     assert_close(to_np(db), rdb, "bf16", "tiny dB")
 
 
-@pytest.mark.parametrize("cd", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("M,N,K,r", [(300, 200, 320, 24), (70, 130, 128, 5), (256, 64, 192, 64)])
-def test_backward_ragged(cd, M, N, K, r):
+@pytest.mark.parametrize("cd,path", PATHS)
+@pytest.mark.parametrize("M,N,K,r", [(300, 200, 320, 24), (70, 130, 128, 5), (256, 64, 192, 64),
+                                     (130, 256, 384, 16)])
+def test_backward_ragged(cd, path, M, N, K, r):
     L = inputs.random_layer(M, N, K, r, seed=M * 7 + r, cd=cd)
-    say("bwd ragged", cd, M, N, K, r)
+    say("bwd ragged", cd, path, M, N, K, r)
     g = to_gpu(L)
-    dx, da, db = run_bwd(L, g, gpu_q(L, g))
+    dx, da, db = run_bwd(L, g, gpu_q(L, g), path=path)
     o = oracle_layer(L)
     rdx, rda, rdb = oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"])
     assert_close(to_np(dx), rdx, cd, "dX")
@@ -202,12 +208,13 @@ def test_backward_saved_t_matches_recompute():
     assert dx is None and torch.equal(da, a[1]) and torch.equal(db, a[2])
 
 
+@pytest.mark.parametrize("path", ["fused", "dequant"])
 @pytest.mark.parametrize("name", ["gate_proj"])
-def test_backward_prefill_full_size_sampled(name):
+def test_backward_prefill_full_size_sampled(name, path):
     (L,) = inputs.prefill(with_dy=True, projections=[name])
-    say("bwd prefill", name)
+    say("bwd prefill", name, path)
     g = to_gpu(L)
-    dx, da, db = run_bwd(L, g, gpu_q(L, g))
+    dx, da, db = run_bwd(L, g, gpu_q(L, g), path=path)
     o = oracle_layer(L)
     rng = np.random.default_rng(10)
     ii, kk = rng.integers(0, L.M, 128), rng.integers(0, L.K, 128)
@@ -220,3 +227,26 @@ def test_backward_prefill_full_size_sampled(name):
     nn = rng.integers(0, L.N, 96)
     ref = oracle.backward_db_at(o["x"], o["A"], o["dY"], o["s"], nn, tt)
     assert_close(to_np(db)[nn, tt], ref, "bf16", "dB sampled")
+
+
+# ----------------------------------------------------------------------------- W~ bits, both paths
+@pytest.mark.parametrize("cd", ["bf16", "f16"])
+@pytest.mark.parametrize("path", ["fused", "dequant"])
+def test_one_hot_reproduces_dequantized_weight_exactly(cd, path):
+    """With one-hot activations and B = 0 every output is one product 1 * W~[n, k]
+    (plus exact zeros), so y = W~^T and dX = W~ bit for bit: both paths use the
+    dequantized weight that qlora_nf4_dequantize writes (W~^T for dX too)."""
+    N, K, r = 256, 384, 16
+    L = inputs.random_layer(K, N, K, r, seed=31, cd=cd, block_size=64, double_quant=True, with_dy=False)
+    say("one-hot", cd, path)
+    g = to_gpu(L)
+    q = gpu_q(L, g)
+    dt = g["x"].dtype
+    w_cd = qn.dequantize(q, dt)                                   # [N, K]
+    zero_b = torch.zeros_like(g["B"])
+    y = qn.linear_fwd(q, torch.eye(K, dtype=dt, device="cuda"), g["A"], zero_b, L.alpha, path=path)
+    dx, _, _ = qn.linear_bwd(q, g["x"][:N], torch.eye(N, dtype=dt, device="cuda"), g["A"], zero_b, L.alpha,
+                             path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(y, w_cd.t().contiguous())
+    assert torch.equal(dx, w_cd)
