@@ -227,21 +227,38 @@ def bench_gemv(qn, torch, lib, inputs, copies=40, iters=400):
         prof = qn.profile_read()
         qn.profile_enable(False)
         k_ms, k_n = prof["gemv"]
-        l_ms, l_n = prof["lora_down"]
+        e_ms = prof["reduce"][0] + prof["lora_down"][0]  # the epilogue (y = partial sums + T B^T + bias)
         kern_us = k_ms / k_n * 1e3
-        layer_bytes = (4096 * 4096 // 2 + 4096 * 4096 // 64 + 4096 * 4096 // 64 // 256 * 4
-                       + 2 * m * 4096 + 2 * 16 * 4096 * 2 + 2 * m * 4096)
-        kern_bytes = (4096 * 4096 // 2 + 4096 * 4096 // 64 + 4096 * 4096 // 64 // 256 * 4
-                      + 2 * m * 4096 + 2 * 16 * 4096 + 4 * m * 16 + 2 * m * 4096)
+        epi_us = e_ms / k_n * 1e3
+        codes = 4096 * 4096 // 2 + 4096 * 4096 // 64 + 4096 * 4096 // 64 // 256 * 4
+        # the GEMV kernel must read the packed weight, x and lora_a (the LoRA down-projection
+        # rides along); the layer also reads lora_b and writes y
+        kern_bytes = codes + 2 * m * 4096 + 2 * 16 * 4096
+        layer_bytes = codes + 2 * m * 4096 + 2 * 16 * 4096 * 2 + 2 * m * 4096
         gbs_kernel = kern_bytes / (kern_us * 1e-6) / 1e9
-        gbs_layer = layer_bytes / ((kern_us + l_ms / l_n * 1e3) * 1e-6) / 1e9
-        out["m%d" % m] = {"kernel_us": round(kern_us, 3), "lora_down_us": round(l_ms / l_n * 1e3, 3),
+        gbs_layer = layer_bytes / ((kern_us + epi_us) * 1e-6) / 1e9
+        out["m%d" % m] = {"kernel_us": round(kern_us, 3), "epilogue_us": round(epi_us, 3),
                           "call_us_wall": round(call_us, 3), "kernel_bytes": kern_bytes,
                           "kernel_gbs": round(gbs_kernel, 1), "kernel_frac": round(gbs_kernel / PEAK_HBM_GBS, 4),
                           "layer_bytes": layer_bytes, "layer_gbs_device": round(gbs_layer, 1),
                           "layer_frac": round(gbs_layer / PEAK_HBM_GBS, 4)}
         del sets
         torch.cuda.empty_cache()
+    # empirical ceiling: a plain read of as many bytes (torch's sum over int32 words), over
+    # the same number of distinct buffers
+    bufs = [torch.ones(8933376 // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    for b in bufs:
+        b.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        bufs[i % copies].sum()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / iters * 1e3
+    out["read_probe_9MB"] = {"us_per_launch_incl_gaps": round(us, 3), "gbs": round(8933376 / (us * 1e-6) / 1e9, 1)}
+    del bufs
     return out
 
 

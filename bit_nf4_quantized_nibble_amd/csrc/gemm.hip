@@ -652,11 +652,11 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
 }  // namespace
 
 int gemv_forward(const LayerCall& c, void* y, float* t_save);  // gemv.hip
-size_t gemv_workspace_bytes(int64_t m, int32_t r);
+size_t gemv_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
 constexpr int64_t kGemvMaxM = 16;
 
 size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
-  if (m <= kGemvMaxM) return gemv_workspace_bytes(m, r);
+  if (m <= kGemvMaxM) return gemv_workspace_bytes(m, rows, cols, r, cd);
   return (size_t)plan_fwd(m, rows, cols, r, cd, flags).total;
 }
 
