@@ -4,8 +4,11 @@
 Headline: the training step of the seven projections of one Llama-3-8B-shaped
 block (q/o 4096x4096, k/v 1024x4096, gate/up 14336x4096, down 4096x14336; NF4 block
 64 with double quantization; 4096 tokens; LoRA r = 64, alpha = 128; bf16 compute):
-one step = the fused dequant-GEMM forward of all seven projections followed by
-their backward (dX, dA, dB).  value = algorithmic TFLOP/s of that step.
+one step = the forward of all seven projections followed by their backward (dX,
+dA, dB), each call on the library's default path (at 4096 tokens: W~ dequantized
+into the workspace, then the dense MFMA GEMM).  value = algorithmic TFLOP/s of
+that step (dequantization is not credited).  The same step forced onto the fused
+dequant-GEMM kernels (QLORA_FLAG_FUSED) is reported beside it.
 
 Also reported on the same line, each against its own MI355X roofline:
   gemv      decode forward at m = 1, 4, 16 (4096x4096, r = 16), GB/s over cold weights
@@ -51,7 +54,7 @@ def bwd_flops(m, n, k, r):
 class Layer:
     """Device tensors and prebuilt C-ABI argument tuples for one projection."""
 
-    def __init__(self, L, x, ws_f, ws_b, qn, torch, lib):
+    def __init__(self, L, x, ws_f, ws_b, qn, torch, lib, flags=0):
         self.name, self.M, self.N, self.K, self.r, self.alpha = L.name, L.M, L.N, L.K, L.r, L.alpha
         dev = "cuda"
         W = L.W.to(dev)
@@ -69,11 +72,11 @@ class Layer:
         cd = qn.dtype_code(dt)
         stream = torch.cuda.current_stream().cuda_stream
         self.fwd_args = (ctypes.byref(self.desc), x.data_ptr(), self.M, self.A.data_ptr(), self.B.data_ptr(),
-                         self.r, float(self.alpha), 0, None, cd, self.y.data_ptr(), self.t0.data_ptr(),
+                         self.r, float(self.alpha), flags, None, cd, self.y.data_ptr(), self.t0.data_ptr(),
                          ws_f.data_ptr(), ws_f.numel(), stream)
         if self.dY is not None:
             self.bwd_args = (ctypes.byref(self.desc), x.data_ptr(), self.dY.data_ptr(), self.M,
-                             self.A.data_ptr(), self.B.data_ptr(), self.r, float(self.alpha), 0, cd,
+                             self.A.data_ptr(), self.B.data_ptr(), self.r, float(self.alpha), flags, cd,
                              self.t0.data_ptr(), self.dx.data_ptr(), self.da.data_ptr(),
                              self.db.data_ptr(), ws_b.data_ptr(), ws_b.numel(), stream)
         self.lib = lib
@@ -89,18 +92,18 @@ class Layer:
             raise RuntimeError("bwd %s: %d %s" % (self.name, rc, self.lib.qlora_last_error()))
 
 
-def build_block(cd, with_dy, qn, torch, lib, inputs, m=4096):
+def build_block(cd, with_dy, qn, torch, lib, inputs, m=4096, flags=0):
     Ls = inputs.prefill(seed=0, cd=cd, m=m, with_dy=with_dy)
     xs = {}
     for L in Ls:
         if L.K not in xs:
             xs[L.K] = L.x.to("cuda")
     op_f, op_b = 0, 1
-    wsf = max(qn.workspace_bytes(op_f, L.M, L.N, L.K, L.r, xs[L.K].dtype) for L in Ls)
-    wsb = max(qn.workspace_bytes(op_b, L.M, L.N, L.K, L.r, xs[L.K].dtype) for L in Ls) if with_dy else 1
+    wsf = max(qn.workspace_bytes(op_f, L.M, L.N, L.K, L.r, xs[L.K].dtype, flags) for L in Ls)
+    wsb = max(qn.workspace_bytes(op_b, L.M, L.N, L.K, L.r, xs[L.K].dtype, flags) for L in Ls) if with_dy else 1
     ws_f = torch.empty(wsf, dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    layers = [Layer(L, xs[L.K], ws_f, ws_b, qn, torch, lib) for L in Ls]
+    layers = [Layer(L, xs[L.K], ws_f, ws_b, qn, torch, lib, flags) for L in Ls]
     del Ls
     return layers, (xs, ws_f, ws_b)
 
@@ -114,8 +117,8 @@ def time_loop(fn, iters, torch):
     return (time.perf_counter() - t0) / iters
 
 
-def bench_step(args, qn, torch, lib, inputs):
-    layers, keep = build_block("bf16", True, qn, torch, lib, inputs)
+def bench_step(args, qn, torch, lib, inputs, flags=0):
+    layers, keep = build_block("bf16", True, qn, torch, lib, inputs, flags=flags)
     torch.cuda.synchronize()
     flops = sum(fwd_flops(l.M, l.N, l.K, l.r) + bwd_flops(l.M, l.N, l.K, l.r) for l in layers)
     ff = {k: 0.0 for k in ("fwd_gemm", "lora_down", "bwd_dx", "bwd_dt", "bwd_da", "bwd_db")}
@@ -244,21 +247,6 @@ def bench_gemv(qn, torch, lib, inputs, copies=40, iters=400):
                           "layer_frac": round(gbs_layer / PEAK_HBM_GBS, 4)}
         del sets
         torch.cuda.empty_cache()
-    # empirical ceiling: a plain read of as many bytes (torch's sum over int32 words), over
-    # the same number of distinct buffers
-    bufs = [torch.ones(8933376 // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
-    for b in bufs:
-        b.sum()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(iters):
-        bufs[i % copies].sum()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / iters * 1e3
-    out["read_probe_9MB"] = {"us_per_launch_incl_gaps": round(us, 3), "gbs": round(8933376 / (us * 1e-6) / 1e9, 1)}
-    del bufs
     return out
 
 
@@ -385,6 +373,8 @@ def main():
     if args.only == "step":
         print(json.dumps({"ms_per_step": st["sec"] * 1e3, "kernels": st["kernels"], "roofline": st["roofline"]}))
         return
+    stf = bench_step(args, qn, torch, lib, inputs, flags=qn._lib.QLORA_FLAG_FUSED)
+    log("fused step %.3f ms" % (stf["sec"] * 1e3))
     gemv = bench_gemv(qn, torch, lib, inputs)
     log("gemv done")
     quant = bench_quant(qn, torch, inputs)
@@ -414,12 +404,17 @@ def main():
         "config": {"workload": "qlora_nf4_block_train_step_llama3_8b_shapes",
                    "tokens": 4096, "projections": [[n, N, K] for n, N, K in st["layers"]],
                    "r": 64, "alpha": 128, "block_size": 64, "double_quant": True, "dq_group": 256,
-                   "step": "fused forward of 7 projections + backward (dX, dA, dB)",
+                   "step": "forward of 7 projections + backward (dX, dA, dB), library default path "
+                           "(dequantize-then-GEMM at 4096 tokens)",
                    "flops_per_step": st["flops"], "parallelism": "single GPU"},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": st["roofline"],
         "cpu_baseline": cpu,
         "kernels": st["kernels"],
+        "fused_path_step": {"ms_per_step": round(stf["sec"] * 1e3, 4),
+                            "tflops": round(stf["flops"] / stf["sec"] / 1e12, 2),
+                            "frac_bf16_peak": round(stf["flops"] / stf["sec"] / 1e12 / PEAK_BF16_TFLOPS, 4),
+                            "roofline": stf["roofline"], "kernels": stf["kernels"]},
         "gemv": gemv,
         "quantize": quant,
         "dtype_sweep_forward": sweep,
