@@ -35,6 +35,15 @@ int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* 
 int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r_pad, void* dx);
 bool fused256_ok(const LayerCall& c, bool dx);
 bool dense256_ok(const LayerCall& c, bool dx);
+// lora.hip: the rank-r products on the skinny MFMA kernel
+bool skinny_ok(int cd, int64_t r);
+size_t skinny_part_bytes(int64_t P, int64_t Kc);
+int skinny(int cd, bool tn, const void* a, int64_t lda, int64_t arows, const void* b, int64_t ldb, int64_t P,
+           int64_t R, int64_t Kc, float* part, int* S_out, hipStream_t s, int kind);
+int skinny_reduce(int cd, const float* part, int S, int64_t P, int64_t R, float sc32, float* out32, bool trans,
+                  float sccd, void* outcd, int64_t ldcd, hipStream_t s);
+int transpose_small(int cd, const void* src, bool src_f32, int64_t ld_src, int64_t rows, int64_t cols, float scale,
+                    void* dst, int64_t ld_dst, hipStream_t s);
 int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y);
 int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx);
 
@@ -433,7 +442,9 @@ FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   P.st = choose_split(ceil_div(m, 128) * ceil_div(r, 64), cols, bk);
   P.off_tcd = 0;
   P.off_part = al(m * P.r_pad * es);
-  P.off_wd = P.off_part + al((int64_t)P.st.S * m * r * 4);
+  int64_t part = (int64_t)P.st.S * m * r * 4;
+  if (skinny_ok(cd, r)) part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(m, cols));
+  P.off_wd = P.off_part + al(part);
   P.dense = dense_path(m, rows, cols, cd, flags, false);
   P.total = P.off_wd + (P.dense ? al(rows * cols * es) : 0);
   return P;
@@ -443,7 +454,9 @@ struct BwdPlan {
   int64_t r_pad;
   Split st, sdt, sda, sdb;
   bool dense;
-  int64_t off_t0, off_dt, off_dtcd, off_part, off_wdt, total;
+  bool sk, sk_n;       // the skinny kernels take the rank products (dT and dB also need rows % 8)
+  int64_t n_pad, m_pad;  // contractions rounded up to whole 64-element stages
+  int64_t off_t0, off_dt, off_dtcd, off_bt, off_dtt, off_t0t, off_part, off_wdt, total;
 };
 BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   BwdPlan P;
@@ -453,15 +466,30 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   P.sdt = choose_split(ceil_div(m, 128) * ceil_div(r, 64), rows, bk);
   P.sda = choose_split(ceil_div(r, 64) * ceil_div(cols, 128), m, bk);
   P.sdb = choose_split(ceil_div(rows, 128) * ceil_div(r, 64), m, bk);
+  P.sk = skinny_ok(cd, r);
+  P.sk_n = P.sk && rows % 8 == 0;
+  P.n_pad = round_up(rows, 64);
+  P.m_pad = round_up(m, 64);
   P.off_t0 = 0;
   P.off_dt = P.off_t0 + al(m * r * 4);
   P.off_dtcd = P.off_dt + al(m * r * 4);
-  P.off_part = P.off_dtcd + al(m * P.r_pad * es);
-  int64_t part = (int64_t)P.st.S * m * r;
-  part = std::max<int64_t>(part, (int64_t)P.sdt.S * m * r);
-  part = std::max<int64_t>(part, (int64_t)P.sda.S * r * cols);
-  part = std::max<int64_t>(part, (int64_t)P.sdb.S * rows * r);
-  P.off_wdt = P.off_part + al(part * 4);
+  P.off_bt = P.off_dtcd + al(m * P.r_pad * es);
+  P.off_dtt = P.off_bt + (P.sk_n ? al(r * P.n_pad * es) : 0);
+  P.off_t0t = P.off_dtt + (P.sk ? al(r * P.m_pad * es) : 0);
+  P.off_part = P.off_t0t + (P.sk_n ? al(r * P.m_pad * es) : 0);
+  int64_t part = (int64_t)P.st.S * m * r * 4;
+  part = std::max<int64_t>(part, (int64_t)P.sdt.S * m * r * 4);
+  part = std::max<int64_t>(part, (int64_t)P.sda.S * r * cols * 4);
+  part = std::max<int64_t>(part, (int64_t)P.sdb.S * rows * r * 4);
+  if (P.sk) {
+    part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(m, cols));        // T0
+    part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(cols, P.m_pad));  // dA
+  }
+  if (P.sk_n) {
+    part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(m, P.n_pad));     // dT
+    part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(rows, P.m_pad));  // dB
+  }
+  P.off_wdt = P.off_part + al(part);
   P.dense = dense_path(m, rows, cols, cd, flags, true);
   P.total = P.off_wdt + (P.dense ? al(rows * cols * es) : 0);
   return P;
@@ -522,8 +550,14 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
   char* ws = (char*)c.ws;
   void* tcd = ws + P.off_tcd;
   float* part = (float*)(ws + P.off_part);
-  int rc = lora_down<CD>(c, P.st, part, t_save, 1.0f, tcd, c.scale, P.r_pad);
-  if (rc) return rc;
+  int rc;
+  if (skinny_ok(CD, c.r)) {
+    int S;
+    if ((rc = skinny(CD, false, c.x, K, M, c.lora_a, K, M, c.r, K, part, &S, c.stream, QLORA_K_LORA_DOWN))) return rc;
+    if ((rc = skinny_reduce(CD, part, S, M, c.r, 1.0f, t_save, false, c.scale, tcd, P.r_pad, c.stream))) return rc;
+  } else if ((rc = lora_down<CD>(c, P.st, part, t_save, 1.0f, tcd, c.scale, P.r_pad))) {
+    return rc;
+  }
   if (P.dense && dense256_ok(c, false)) {
     void* wd = ws + P.off_wd;
     if ((rc = dequant_into(c.w, CD, wd, false, c.stream))) return rc;
@@ -562,13 +596,24 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   // T0 = x A^T (recomputed unless the forward saved it).
   const float* T0 = t_saved;
   if (!T0) {
-    rc = lora_down<CD>(c, P.st, part, t0, 1.0f, nullptr, 0.f, 0);
-    if (rc) return rc;
+    if (P.sk) {
+      int S;
+      if ((rc = skinny(CD, false, c.x, K, M, c.lora_a, K, M, r, K, part, &S, c.stream, QLORA_K_LORA_DOWN))) return rc;
+      if ((rc = skinny_reduce(CD, part, S, M, r, 1.0f, t0, false, 0.f, nullptr, 0, c.stream))) return rc;
+    } else if ((rc = lora_down<CD>(c, P.st, part, t0, 1.0f, nullptr, 0.f, 0))) {
+      return rc;
+    }
     T0 = t0;
   }
 
   // dT = s dY B  -> fp32 [M, r] and a compute-dtype copy [M, r_pad].
-  {
+  if (P.sk_n) {
+    void* bt = ws + P.off_bt;  // B^T [r][n_pad], zero past N
+    if ((rc = transpose_small(CD, c.lora_b, false, r, N, r, 1.0f, bt, P.n_pad, c.stream))) return rc;
+    int S;
+    if ((rc = skinny(CD, false, dy, N, M, bt, P.n_pad, M, r, P.n_pad, part, &S, c.stream, QLORA_K_BWD_DT))) return rc;
+    if ((rc = skinny_reduce(CD, part, S, M, r, c.scale, dt, false, c.scale, dtcd, P.r_pad, c.stream))) return rc;
+  } else {
     GemmParams p = base_params(c);
     p.a1 = opnd<CD>(dy, N, M, N);
     p.b1 = opnd<CD>(c.lora_b, r, r, N);  // source [n][t]: transposed while staging
@@ -612,7 +657,13 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   }
 
   // dA = dT^T x  (contraction over tokens).
-  {
+  if (P.sk) {
+    void* dtt = ws + P.off_dtt;  // dT^T [r][m_pad] in cd (the operand the dX uses), zero past M
+    if ((rc = transpose_small(CD, dtcd, false, P.r_pad, M, r, 1.0f, dtt, P.m_pad, c.stream))) return rc;
+    int S;
+    if ((rc = skinny(CD, true, c.x, K, M, dtt, P.m_pad, K, r, P.m_pad, part, &S, c.stream, QLORA_K_BWD_DA))) return rc;
+    if ((rc = skinny_reduce(CD, part, S, K, r, 1.0f, d_a, true, 0.f, nullptr, 0, c.stream))) return rc;
+  } else {
     GemmParams p = base_params(c);
     p.a1 = opnd<CD>(dtcd, P.r_pad, r, M);  // source [m][t]
     p.b1 = opnd<CD>(c.x, K, K, M);         // source [m][k]
@@ -630,7 +681,13 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   }
 
   // dB = s dY^T T0  (contraction over tokens).
-  {
+  if (P.sk_n) {
+    void* t0t = ws + P.off_t0t;  // T0^T [r][m_pad] rounded to cd, zero past M
+    if ((rc = transpose_small(CD, T0, true, r, M, r, 1.0f, t0t, P.m_pad, c.stream))) return rc;
+    int S;
+    if ((rc = skinny(CD, true, dy, N, M, t0t, P.m_pad, N, r, P.m_pad, part, &S, c.stream, QLORA_K_BWD_DB))) return rc;
+    if ((rc = skinny_reduce(CD, part, S, N, r, c.scale, d_b, false, 0.f, nullptr, 0, c.stream))) return rc;
+  } else {
     GemmParams p = base_params(c);
     p.a1 = opnd<CD>(dy, N, N, M);         // source [m][n]
     p.b1 = opnd<CD>(T0, r, r, M, 4);      // fp32 source [m][t]

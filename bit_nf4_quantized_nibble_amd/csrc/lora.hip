@@ -1,0 +1,333 @@
+// lora.hip -- the rank-r products of the QLoRA layer (bf16 / f16 compute, r <= 64)
+// on gfx950:
+//
+//   forward   T0 = x A^T                 [M, r]   contraction over K
+//   backward  dT = s dY B                [M, r]   contraction over N
+//             dA = dT^T x                [r, K]   contraction over the M tokens
+//             dB = s dY^T T0             [N, r]   contraction over the M tokens
+//
+// ("LoRA and QLoRA, mathematically": only the low-rank factors train; qlora-rs
+// README "Honest capability matrix": the adapters update, the base stays frozen.)
+//
+// All four are C[p, t] = sum_k Aop[p, k] Bop[t, k] with t < r <= 64: one skinny
+// kernel, output tile 128 (p) x 64 (t), 4 waves of 32 x 64 (two MFMA 32x32x16
+// tiles each), 64-element contraction stages in three LDS buffers (the copy runs
+// two stages ahead), and a split of the contraction into S slices whose fp32
+// partial sums a second kernel adds in slice order.  Bop is always a small [t][k]
+// matrix with k contiguous (A, or a transposed copy of B, dT or T0 made by
+// k_transpose).  Every tile is copied global -> LDS by DMA.  Aop is either
+//   NT: a matrix [p][k] with k contiguous (x, dY): 128-byte rows of k, 16-byte
+//       chunk c of row r at chunk c ^ swz(r), or
+//   TN: a matrix X [k][p] with p contiguous (x or dY read along the tokens):
+//       256-byte rows of p, chunk c of row k at chunk c ^ (k % 16); a fragment
+//       (8 consecutive k of one p) is gathered with 16-bit reads, and the swizzle
+//       puts the two row groups a read instruction touches on distinct banks.
+#include "common.h"
+
+namespace qnf4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BP = 128;          // output rows (p) per workgroup
+constexpr int BR = 64;           // rank columns (t) per workgroup
+constexpr int BK = 64;           // contraction elements per stage
+constexpr int ROWB = 128;        // swizzled NT / Bop LDS row: 64 elements
+constexpr int XROW = 2 * BP;     // swizzled TN LDS row: 128 elements (256 bytes)
+constexpr int A_BYTES = 16384;   // NT: 128 rows x 128 B; TN: 64 rows x 256 B
+constexpr int B_BYTES = BR * ROWB;   // 8 KiB
+constexpr int NBUF = 3;
+constexpr int STAGE = A_BYTES + B_BYTES;
+constexpr int kCopies = 6;       // DMA instructions per lane per stage (4 Aop + 2 Bop)
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t oob_unless(bool ok, uint32_t off) { return off | ((uint32_t)(!ok) << 31); }
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int CD>
+__device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (CD == CD_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+struct SkP {
+  const void* a;    // NT: [P][lda], k contiguous; TN: [arows][lda], p contiguous
+  int64_t lda;
+  int64_t arows;    // rows of a (TN: the true token count; rows up to Kc past it read as zeros)
+  const void* b;    // [R][ldb], k contiguous (rows >= R read as zeros)
+  int64_t ldb;
+  int64_t P, R, Kc;
+  int64_t kslice;   // contraction per slice (multiple of 64)
+  float* part;      // [S][P][64] fp32
+};
+
+// Copy of one stage's Bop tile (64 rows of 64 elements): DMA instruction d of wave
+// w fills rows 8 (4 d + w) .. +8; lane l lands in physical chunk l % 8 of row l / 8.
+__device__ __forceinline__ void copy_b(const SkP& p, rsrc_t rb, char* dst, int wave, int lane, int64_t k) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const int row = 8 * (4 * d + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + (4 * d + wave) * 1024), 16,
+                                             (int)oob_unless(row < p.R, (uint32_t)((row * p.ldb + k + 8 * c) * 2)),
+                                             0, 0, 0);
+  }
+}
+
+// NT Aop tile (128 rows of 64 elements) by DMA, like copy_b.
+__device__ __forceinline__ void copy_a_nt(const SkP& p, rsrc_t ra, char* dst, int64_t p0, int wave, int lane,
+                                          int64_t k) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int row = 8 * (4 * d + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    const int64_t gr = p0 + row;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + (4 * d + wave) * 1024), 16,
+                                             (int)oob_unless(gr < p.P, (uint32_t)((gr * p.lda + k + 8 * c) * 2)),
+                                             0, 0, 0);
+  }
+}
+
+// TN Aop tile (X rows k .. k+63, columns p0 .. p0+127) by DMA: instruction d of
+// wave w fills rows 4 (4 d + w) .. +4; lane l lands in physical chunk l % 16 of row
+// l / 16.  Rows past the true token count and columns past P read as zeros.
+__device__ __forceinline__ void copy_a_tn(const SkP& p, rsrc_t ra, char* dst, int64_t p0, int wave, int lane,
+                                          int64_t k) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int row = 4 * (4 * d + wave) + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15);
+    const bool ok = p0 + 8 * c < p.P;  // P is a multiple of 8: a chunk is all in or all out
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ra, (lds_void*)(dst + (4 * d + wave) * 1024), 16,
+        (int)oob_unless(ok, (uint32_t)(((k + row) * p.lda + p0 + 8 * c) * 2)), 0, 0, 0);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int CD, int TN>
+__global__ __launch_bounds__(kThreads) void k_skinny(SkP p) {
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * STAGE];  // stage b: [A | B]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 31, h = lane >> 5;
+  const int64_t p0 = (int64_t)blockIdx.x * BP;
+  const int64_t k0 = (int64_t)blockIdx.y * p.kslice;
+  const int64_t k1 = k0 + p.kslice < p.Kc ? k0 + p.kslice : p.Kc;
+  const int nst = (int)((k1 - k0) / BK);
+  const rsrc_t ra = make_rsrc(p.a, p.arows * p.lda * 2);
+  const rsrc_t rb = make_rsrc(p.b, p.R * p.ldb * 2);
+  const int xr = swz(i);  // swizzle of the 128-byte rows this lane reads (they differ by 32)
+  // TN: column 32 wave + i is chunk pc, element pe of it; rows 8 h + j (j < 8) of
+  // a 16-row step sit at chunk pc ^ ((8 h + j) % 16)
+  const int pc = (32 * wave + i) >> 3, pe = (i & 7) * 2;
+  int tn_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tn_off[j] = (8 * h + j) * XROW + 16 * (pc ^ ((8 * h + j) & 15)) + pe;
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+
+  auto copy = [&](int st) {
+    char* dst = lds + (st % NBUF) * STAGE;
+    const int64_t k = k0 + (int64_t)st * BK;
+    if (TN) copy_a_tn(p, ra, dst, p0, wave, lane, k);
+    else copy_a_nt(p, ra, dst, p0, wave, lane, k);
+    copy_b(p, rb, dst + A_BYTES, wave, lane, k);
+  };
+  copy(0);
+  if (nst > 1) copy(1);
+  for (int s = 0; s < nst; ++s) {
+    // stage s landed in every wave (stage s + 1 may still fly); stage s - 1's reads done
+    if (s + 1 < nst) wait_vm<kCopies>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_waitcnt(0x3f | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    barrier_only();
+    if (s + 2 < nst) copy(s + 2);  // into the buffer stage s - 1 used
+    const char* As = lds + (s % NBUF) * STAGE;
+    const char* Bs = As + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cphys = ((2 * ks + h) ^ xr) << 4;
+      u32x4_t a;
+      if (TN) {
+        // 8 consecutive k (rows 16 ks + 8 h ..) of column 32 wave + i
+        const char* src = As + 16 * ks * XROW;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a[e] = (uint32_t)*(const uint16_t*)(src + tn_off[2 * e]) |
+                 ((uint32_t)*(const uint16_t*)(src + tn_off[2 * e + 1]) << 16);
+      } else {
+        a = *(const u32x4_t*)(As + (32 * wave + i) * ROWB + cphys);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4_t b = *(const u32x4_t*)(Bs + (32 * j + i) * ROWB + cphys);
+        acc[j] = mfma<CD>(a, b, acc[j]);
+      }
+    }
+  }
+
+  // partial sums: lane (i, h) holds rows 32 wave + 8 (v / 4) + 4 h + v % 4, column 32 j + i
+  float* out = p.part + (int64_t)blockIdx.y * p.P * BR;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = p0 + 32 * wave + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (row < p.P) out[row * BR + 32 * j + i] = acc[j][v];
+    }
+}
+
+// out32 = sc32 * sum over slices (in slice order), [P][R] or transposed [R][P];
+// outcd [P][ldcd] = cd(sccd * sum), its columns R .. ldcd-1 zero.
+template <int CD>
+__global__ __launch_bounds__(kThreads) void k_skreduce(const float* __restrict__ part, int S, int64_t P, int64_t R,
+                                                       float sc32, float* __restrict__ out32, int trans, float sccd,
+                                                       void* __restrict__ outcd, int64_t ldcd) {
+  const int64_t width = (outcd && ldcd > R) ? ldcd : R;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= P * width) return;
+  const int64_t pr = idx / width, t = idx % width;
+  if (t >= R) {
+    store_cd<CD>(outcd, pr * ldcd + t, 0.f);
+    return;
+  }
+  float v[8];
+#pragma unroll
+  for (int z = 0; z < 8; ++z) v[z] = z < S ? part[((int64_t)z * P + pr) * BR + t] : 0.f;  // S <= 8
+  float sum = 0.f;
+#pragma unroll
+  for (int z = 0; z < 8; ++z) sum += v[z];  // slice order; the zeros past S do not change it
+  if (out32) out32[trans ? t * P + pr : pr * R + t] = sum * sc32;
+  if (outcd) store_cd<CD>(outcd, pr * ldcd + t, sum * sccd);
+}
+
+// dst [cols][ld_dst] (cd) = cd(scale * src[rows][ld_src]^T), src in cd or fp32;
+// columns rows .. ld_dst-1 of dst are zeros.  Tile 64 x 64 through LDS.
+template <int CD, int SRC32>
+__global__ __launch_bounds__(kThreads) void k_transpose(const void* __restrict__ src, int64_t ld_src, int64_t rows,
+                                                        int64_t cols, float scale, void* __restrict__ dst,
+                                                        int64_t ld_dst) {
+  __shared__ float t[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t r = r0 + y, c = c0 + tx;
+    float v = 0.f;
+    if (r < rows && c < cols) v = SRC32 ? ((const float*)src)[r * ld_src + c] : load_cd<CD>(src, r * ld_src + c);
+    t[y][tx] = v * scale;
+  }
+  __syncthreads();
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t c = c0 + y, r = r0 + tx;
+    if (c < cols && r < ld_dst) store_cd<CD>(dst, c * ld_dst + r, r < rows ? t[tx][y] : 0.f);
+  }
+}
+
+}  // namespace
+
+// The skinny path takes bf16 / f16 layers with r <= 64 whose contractions are whole
+// stages and whose P dimensions are multiples of 8 (16-byte chunks).
+bool skinny_ok(int cd, int64_t r) { return (cd == CD_BF16 || cd == CD_F16) && r >= 1 && r <= BR; }
+
+// Slices of the contraction: about 256 workgroups, at most 8 slices (the partial
+// sums are written and read back once more).
+void skinny_split(int64_t P, int64_t Kc, int* S, int64_t* kslice) {
+  const int64_t tiles = ceil_div(P, BP);
+  int64_t s = ceil_div(256, tiles);
+  const int64_t steps = Kc / BK;
+  if (s > steps) s = steps;
+  if (s > 8) s = 8;
+  if (s < 1) s = 1;
+  const int64_t ks = round_up(ceil_div(Kc, s), BK);
+  *kslice = ks;
+  *S = (int)ceil_div(Kc, ks);
+}
+
+size_t skinny_part_bytes(int64_t P, int64_t Kc) {
+  int S;
+  int64_t ks;
+  skinny_split(P, Kc, &S, &ks);
+  return (size_t)S * P * BR * 4;
+}
+
+// part = per-slice sums of Aop . Bop^T over the contraction 0 .. Kc (a multiple of
+// 64); Aop NT [P][lda] or TN [arows][lda]; Bop [R][ldb] with ldb >= Kc, zero
+// between its true width and Kc.
+int skinny(int cd, bool tn, const void* a, int64_t lda, int64_t arows, const void* b, int64_t ldb, int64_t P,
+           int64_t R, int64_t Kc, float* part, int* S_out, hipStream_t s, int kind) {
+  if (Kc % BK || lda % 8 || ldb % 8 || ldb < Kc || (tn && P % 8))
+    return set_error(QLORA_ERR_UNSUPPORTED, "rank product: shape not supported by the skinny kernel");
+  SkP p = {};
+  p.a = a;
+  p.lda = lda;
+  p.arows = arows;
+  p.b = b;
+  p.ldb = ldb;
+  p.P = P;
+  p.R = R;
+  p.Kc = Kc;
+  p.part = part;
+  int S;
+  skinny_split(P, Kc, &S, &p.kslice);
+  *S_out = S;
+  const dim3 grid((unsigned)ceil_div(P, BP), (unsigned)S);
+  ProfScope prof(kind, s);
+  if (cd == CD_BF16) {
+    if (tn) k_skinny<CD_BF16, 1><<<grid, dim3(kThreads), 0, s>>>(p);
+    else k_skinny<CD_BF16, 0><<<grid, dim3(kThreads), 0, s>>>(p);
+  } else {
+    if (tn) k_skinny<CD_F16, 1><<<grid, dim3(kThreads), 0, s>>>(p);
+    else k_skinny<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(p);
+  }
+  return check_launch("k_skinny");
+}
+
+int skinny_reduce(int cd, const float* part, int S, int64_t P, int64_t R, float sc32, float* out32, bool trans,
+                  float sccd, void* outcd, int64_t ldcd, hipStream_t s) {
+  const int64_t width = (outcd && ldcd > R) ? ldcd : R;
+  const int64_t n = P * width;
+  if (n == 0) return QLORA_OK;
+  ProfScope prof(QLORA_K_REDUCE, s);
+  const dim3 grid((unsigned)ceil_div(n, kThreads));
+  if (cd == CD_BF16)
+    k_skreduce<CD_BF16><<<grid, dim3(kThreads), 0, s>>>(part, S, P, R, sc32, out32, trans ? 1 : 0, sccd, outcd, ldcd);
+  else
+    k_skreduce<CD_F16><<<grid, dim3(kThreads), 0, s>>>(part, S, P, R, sc32, out32, trans ? 1 : 0, sccd, outcd, ldcd);
+  return check_launch("k_skreduce");
+}
+
+// dst [cols][ld_dst] = cd(scale * src^T) for a small matrix src [rows][ld_src].
+int transpose_small(int cd, const void* src, bool src_f32, int64_t ld_src, int64_t rows, int64_t cols, float scale,
+                    void* dst, int64_t ld_dst, hipStream_t s) {
+  if (ld_dst == 0 || cols == 0) return QLORA_OK;
+  const dim3 grid((unsigned)ceil_div(ld_dst, 64), (unsigned)ceil_div(cols, 64));
+  ProfScope prof(QLORA_K_REDUCE, s);
+  if (cd == CD_BF16) {
+    if (src_f32) k_transpose<CD_BF16, 1><<<grid, dim3(kThreads), 0, s>>>(src, ld_src, rows, cols, scale, dst, ld_dst);
+    else k_transpose<CD_BF16, 0><<<grid, dim3(kThreads), 0, s>>>(src, ld_src, rows, cols, scale, dst, ld_dst);
+  } else {
+    if (src_f32) k_transpose<CD_F16, 1><<<grid, dim3(kThreads), 0, s>>>(src, ld_src, rows, cols, scale, dst, ld_dst);
+    else k_transpose<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(src, ld_src, rows, cols, scale, dst, ld_dst);
+  }
+  return check_launch("k_transpose");
+}
+
+}  // namespace qnf4

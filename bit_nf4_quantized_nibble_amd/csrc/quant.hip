@@ -170,6 +170,54 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(Nf4W q, int64_t n, void
 
 }  // namespace
 
+// Dequantize (block size a power of two >= 8, n a multiple of 8): lane l of a
+// workgroup handles the 8-element chunks l + 256 j (j < 8) of the workgroup's
+// 16384 elements, so each load (4 bytes of codes per lane) and each 16-byte store
+// instruction covers contiguous memory across the wave.  Same values as
+// k_dequantize.
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, void* __restrict__ out,
+                                                             Nf4Tables tab) {
+  __shared__ float s_lv[16];
+  if (threadIdx.x < 16) s_lv[threadIdx.x] = tab.lv[threadIdx.x];
+  const int64_t ch0 = (int64_t)blockIdx.x * (kThreads * 8) + threadIdx.x;
+  const int64_t nch = n / 8;
+  uint32_t cw[8];
+  float sc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t ch = ch0 + kThreads * j;
+    cw[j] = 0u;
+    sc[j] = 0.f;
+    if (ch < nch) {
+      cw[j] = *(const uint32_t*)(q.codes + ch * 4);
+      sc[j] = block_scale(q, (ch * 8) >> q.bs_shift);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t ch = ch0 + kThreads * j;
+    if (ch >= nch) break;
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)  // byte i / 2; element 2k in the high nibble
+      f[i] = fl32_mul(s_lv[(cw[j] >> ((i >> 1) * 8 + ((i & 1) ? 0 : 4))) & 15u], sc[j]);
+    if constexpr (OUT == CD_F32) {
+      float4* o = (float4*)((float*)out + ch * 8);
+      o[0] = make_float4(f[0], f[1], f[2], f[3]);
+      o[1] = make_float4(f[4], f[5], f[6], f[7]);
+    } else {
+      u32x4_t o;
+      o[0] = pack2<OUT>(f[0], f[1]);
+      o[1] = pack2<OUT>(f[2], f[3]);
+      o[2] = pack2<OUT>(f[4], f[5]);
+      o[3] = pack2<OUT>(f[6], f[7]);
+      *(u32x4_t*)((uint16_t*)out + ch * 8) = o;
+    }
+  }
+}
+
 // Transposed dequantize for the dequantize-then-GEMM backward: out [cols, rows] =
 // RNE_cd(fl32(L[c] * s_b))^T, the same values as k_dequantize.  One workgroup per
 // 64 x 64 tile of W: each lane decodes 16 consecutive codes of one W row into an
@@ -235,26 +283,33 @@ int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s) {
   return check_launch("k_quantize");
 }
 
+int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s);
+
 int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_t s) {
-  const int64_t n = q->rows * q->cols;
-  const int64_t grid = ceil_div(ceil_div(n, 32), kThreads);
-  if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
-  Nf4W w = make_w(q);
+  const Nf4W w = make_w(q);
+  return dequant_flat(w, out_dtype, out, s);
+}
+
+// Flat dequantize of all rows * cols elements into out (f32 / bf16 / f16).
+int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s) {
+  const int64_t n = w.rows * w.cols;
   const Nf4Tables& t = host_tables();
   ProfScope prof(QLORA_K_DEQUANTIZE, s);
-  switch (out_dtype) {
-    case QLORA_F32:
-      k_dequantize<CD_F32><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
-      break;
-    case QLORA_BF16:
-      k_dequantize<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
-      break;
-    case QLORA_F16:
-      k_dequantize<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
-      break;
-    default:
-      return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", out_dtype);
+  if (w.bs_shift >= 3 && n % 8 == 0) {
+    const int64_t grid = ceil_div(n / 8, kThreads * 8);
+    if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
+    if (cd == CD_BF16) k_dequant_chunks<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+    else if (cd == CD_F16) k_dequant_chunks<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+    else if (cd == CD_F32) k_dequant_chunks<CD_F32><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+    else return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
+    return check_launch("k_dequant_chunks");
   }
+  const int64_t grid = ceil_div(ceil_div(n, 32), kThreads);
+  if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
+  if (cd == CD_BF16) k_dequantize<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+  else if (cd == CD_F16) k_dequantize<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+  else if (cd == CD_F32) k_dequantize<CD_F32><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+  else return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
   return check_launch("k_dequantize");
 }
 
@@ -262,9 +317,9 @@ int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_
 // (forward) or its transpose [cols, rows] (dX).  The transpose needs rows and cols
 // to be multiples of 64.
 int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s) {
-  const Nf4Tables& t = host_tables();
-  ProfScope prof(QLORA_K_DEQUANTIZE, s);
   if (transposed) {
+    const Nf4Tables& t = host_tables();
+    ProfScope prof(QLORA_K_DEQUANTIZE, s);
     if (w.rows % 64 || w.cols % 64) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: shape not a multiple of 64");
     const dim3 grid((unsigned)(w.cols / 64), (unsigned)(w.rows / 64));
     if (cd == CD_BF16) k_dequantize_t<CD_BF16><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
@@ -272,12 +327,7 @@ int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t 
     else return set_error(QLORA_ERR_DTYPE, "dequantize^T: bad dtype %d", cd);
     return check_launch("k_dequantize_t");
   }
-  const int64_t n = w.rows * w.cols;
-  const int64_t grid = ceil_div(ceil_div(n, 32), kThreads);
-  if (cd == CD_BF16) k_dequantize<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
-  else if (cd == CD_F16) k_dequantize<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
-  else return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
-  return check_launch("k_dequantize");
+  return dequant_flat(w, cd, out, s);
 }
 
 }  // namespace qnf4
