@@ -163,8 +163,8 @@ def bench_step(args, qn, torch, lib, inputs, flags=0):
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "avg_launch_ms": round(dom_ms, 4),
-                "flops_per_launch": dom_flops}
+                "traffic": measured_traffic() if (dom == "fwd_gemm" and flags == 0) else None,
+                "avg_launch_ms": round(dom_ms, 4), "flops_per_launch": dom_flops}
     result = dict(sec=sec, flops=flops, kernels=kernels, roofline=roofline,
                   fwd_ms=sum(kernels.get(k, {}).get("ms_per_step", 0) for k in ("fwd_gemm", "lora_down")),
                   layers=[(l.name, l.N, l.K) for l in layers])
@@ -248,6 +248,55 @@ def bench_gemv(qn, torch, lib, inputs, copies=40, iters=400):
         del sets
         torch.cuda.empty_cache()
     return out
+
+
+def copy_probe(torch, mib=512, iters=10):
+    """A plain device copy of known size: the calibration run for the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) and the streaming ceiling of this GPU."""
+    a = torch.ones(mib << 19, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / iters * 1e3
+    return {"bytes_read": mib << 20, "bytes_written": mib << 20, "us": round(us, 2),
+            "gbs": round(2 * (mib << 20) / (us * 1e-6) / 1e9, 1)}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense256_fwd_hbm_traffic_llama3_8b_block.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_nibble_amd", "csrc", f) for f in ("gemm256.hip", "common.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter runs
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the kernel sources changed
+    since the counters were taken."""
+    try:
+        vals = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("traffic_") or line.startswith("kernel_source_hash"):
+                    k, v = line.split(":", 1)
+                    vals[k.strip()] = v.strip()
+        if vals.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def bench_quant(qn, torch, inputs, copies=5, iters=20):
@@ -342,7 +391,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep"], default=None,
+    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep", "copyprobe"], default=None,
                     help="run one part (for profiling); the JSON line needs the full run")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -360,6 +409,9 @@ def main():
 
     if args.only == "gemv":
         print(json.dumps(bench_gemv(qn, torch, lib, inputs)))
+        return
+    if args.only == "copyprobe":
+        print(json.dumps(copy_probe(torch)))
         return
     if args.only == "quant":
         print(json.dumps(bench_quant(qn, torch, inputs)))

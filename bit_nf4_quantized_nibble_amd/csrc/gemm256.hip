@@ -96,13 +96,21 @@ __device__ __forceinline__ uint32_t oob_unless(bool ok, uint32_t off) {
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int chunk_addr(int row, int c) { return row * ROWB + ((c ^ swz(row)) << 4); }
 
+// Workgroup -> output tile.  Workgroups b, b + 8, ... run on the same XCD, so
+// each XCD takes a contiguous chunk of T / 8 tiles of a grouped order: groups of
+// kGroupM tile rows, column-major inside a group.  An XCD then holds a compact
+// block (4 x 8 tiles for a 16 x 16 grid) and its L2 sees fewer distinct operand
+// tiles per stage than with whole tile rows.
+constexpr int kGroupM = 4;
 __device__ __forceinline__ void tile_of(const Big& p, int& tm, int& tn) {
   const int b = blockIdx.x;
   const int T = p.tiles_m * p.tiles_n;
   int t = b;
   if ((T & 7) == 0) t = (b & 7) * (T >> 3) + (b >> 3);  // XCD-contiguous chunks
-  tm = t / p.tiles_n;
-  tn = t % p.tiles_n;
+  const int per = kGroupM * p.tiles_n, g = t / per, u = t % per;
+  const int gm = min(kGroupM, p.tiles_m - g * kGroupM);
+  tm = g * kGroupM + u % gm;
+  tn = u / gm;
 }
 
 // The NF4 codes (and raw block scales) a lane fetches for one stage.
