@@ -72,6 +72,8 @@ def _load():
     lib.orc_qlora_bwd_da_at.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _d,
                                         _i64p, _i64p, _i64, _f64p]
     lib.orc_qlora_bwd_da_at.restype = None
+    lib.orc_qlora_merge.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _d, _i32, _vp]
+    lib.orc_qlora_merge.restype = None
     lib.orc_qlora_bwd_db_at.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _d,
                                         _i64p, _i64p, _i64, _f64p]
     lib.orc_qlora_bwd_db_at.restype = None
@@ -282,3 +284,18 @@ def rel_l2(got, ref) -> float:
     ref = np.asarray(ref, np.float64)
     den = np.linalg.norm(ref.ravel())
     return float(np.linalg.norm((got - ref).ravel()) / (den if den > 0 else 1.0))
+
+
+def merge(what, A, B, s: float, dtype: str) -> np.ndarray:
+    """W_merged = W_hat + s B A, rounded once to dtype ("LoRA and QLoRA, mathematically",
+    "The merge math", eq. 6.3.6).  what: the binary32 dequantized weight [N, K]; A, B the
+    adapter values.  Returns float32 values for "f32", else the 16-bit patterns."""
+    what, A, B = _f32(what), _f32(A), _f32(B)
+    N, K = what.shape
+    r = A.shape[0]
+    assert A.shape == (r, K) and B.shape == (N, r)
+    kind = {"f32": 0, "bf16": 1, "f16": 2}[dtype]
+    out = np.empty((N, K), np.float32 if kind == 0 else np.uint16)
+    _load().orc_qlora_merge(what, A, B, N, K, r, float(s), kind, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+

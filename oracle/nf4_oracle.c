@@ -432,3 +432,51 @@ void orc_qlora_bwd_db_at(const float* x, const float* A, const float* dY, int64_
   }
   free(col);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Merge ([B] "The merge math", eq. 6.3.6): W_merged = W_hat + s B A, rounded  */
+/* once from the exact (fp64) value to the output dtype; never re-quantized.   */
+/* ------------------------------------------------------------------------- */
+
+/* One rounding of a binary64 value to the nearest value with `bits` significant
+ * bits whose quantum is at least 2^qmin (ties to even); the result is exact in
+ * binary64. */
+static double round_sig(double v, int bits, int qmin) {
+  if (v == 0.0 || isnan(v) || isinf(v)) return v;
+  int e;
+  frexp(fabs(v), &e); /* |v| = m 2^e, m in [0.5, 1) */
+  int q = e - bits;
+  if (q < qmin) q = qmin;
+  return ldexp(nearbyint(ldexp(v, -q)), q);
+}
+
+static uint16_t bf16_from_f64(double v) {
+  if (isnan(v)) return 0x7fc0;
+  double r = round_sig(v, 8, -133); /* bf16: 8 significant bits, binary32 exponents */
+  if (fabs(r) > 3.3895313892515355e38) return (uint16_t)(signbit(v) ? 0xff80 : 0x7f80);
+  return bf16_from_f32((float)r); /* exact: r is a bf16 value */
+}
+
+static uint16_t f16_from_f64(double v) {
+  if (isnan(v)) return 0x7e00;
+  double r = round_sig(v, 11, -24); /* f16: 11 significant bits, quantum >= 2^-24 */
+  if (fabs(r) > 65504.0) return (uint16_t)(signbit(v) ? 0xfc00 : 0x7c00);
+  return f16_from_f32((float)r); /* exact */
+}
+
+/* what [N,K] (the binary32 dequantized weight), A [r,K], B [N,r] (adapter values),
+ * kind 0: binary32 out, 1: bf16 bits, 2: f16 bits. */
+void orc_qlora_merge(const float* what, const float* A, const float* B, int64_t N, int64_t K, int64_t r,
+                     double s, int32_t kind, void* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < r; ++t) acc += (double)B[n * r + t] * (double)A[t * K + k];
+      const double v = (double)what[n * K + k] + s * acc;
+      if (kind == 0) ((float*)out)[n * K + k] = (float)v;
+      else if (kind == 1) ((uint16_t*)out)[n * K + k] = bf16_from_f64(v);
+      else ((uint16_t*)out)[n * K + k] = f16_from_f64(v);
+    }
+}
+
