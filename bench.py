@@ -250,6 +250,52 @@ def bench_gemv(qn, torch, lib, inputs, copies=40, iters=400):
     return out
 
 
+def bench_merge(qn, torch, inputs, iters=5):
+    """Adapter merge W_merged = RNE_bf16(w_hat + s B A) of the seven projections of the
+    block (r = 64), cycled so that every call streams its weight from HBM (the seven
+    outputs and codes together exceed the last-level cache)."""
+    layers = inputs.prefill(m=1)
+    sets = []
+    for L in layers:
+        q = qn.quantize(L.W.to("cuda"), 64, True, 256)
+        A, B = L.A.to("cuda"), L.B.to("cuda")
+        out = torch.empty(L.N, L.K, dtype=torch.bfloat16, device="cuda")
+        sets.append((L, q, A, B, out))
+    for L, q, A, B, out in sets:
+        qn.merge(q, A, B, L.alpha, out=out)
+    torch.cuda.synchronize()
+    per = {}
+    total_bytes = 0
+    qn.profile_enable(True)
+    for _ in range(iters):
+        for L, q, A, B, out in sets:
+            qn.merge(q, A, B, L.alpha, out=out)
+    torch.cuda.synchronize()
+    ms, k = qn.profile_read()["merge"]
+    qn.profile_enable(False)
+    # per-projection times from a second, separately profiled pass
+    for L, q, A, B, out in sets:
+        qn.profile_enable(True)
+        for _ in range(iters):
+            qn.merge(q, A, B, L.alpha, out=out)
+        torch.cuda.synchronize()
+        pms, pk = qn.profile_read()["merge"]
+        qn.profile_enable(False)
+        n = L.N * L.K
+        nb = n // 64
+        byts = n // 2 + nb + (nb + 255) // 256 * 4 + 2 * L.r * L.K + 2 * L.N * L.r + 2 * n
+        us = pms / pk * 1e3
+        per[L.name] = {"us": round(us, 2), "bytes": byts, "gbs": round(byts / (us * 1e-6) / 1e9, 1)}
+        total_bytes += byts
+    total_us = ms / k * 1e3 * len(sets)
+    gbs = total_bytes / (total_us * 1e-6) / 1e9
+    del sets
+    torch.cuda.empty_cache()
+    return {"block_us": round(total_us, 2), "block_bytes": total_bytes, "gbs": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "per_projection": per,
+            "bytes_per_element": "0.5 codes + 1/64 u8 scale + 2 bf16 out (+ A, B once)"}
+
+
 def copy_probe(torch, mib=512, iters=10):
     """A plain device copy of known size: the calibration run for the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) and the streaming ceiling of this GPU."""
@@ -391,7 +437,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep", "copyprobe"], default=None,
+    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep", "merge", "copyprobe"], default=None,
                     help="run one part (for profiling); the JSON line needs the full run")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -419,6 +465,9 @@ def main():
     if args.only == "sweep":
         print(json.dumps(bench_dtype_sweep(qn, torch, lib, inputs)))
         return
+    if args.only == "merge":
+        print(json.dumps(bench_merge(qn, torch, inputs)))
+        return
 
     st = bench_step(args, qn, torch, lib, inputs)
     log("step %.3f ms" % (st["sec"] * 1e3))
@@ -433,6 +482,8 @@ def main():
     log("quant done")
     sweep = bench_dtype_sweep(qn, torch, lib, inputs)
     log("sweep done")
+    merge = bench_merge(qn, torch, inputs)
+    log("merge done")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)
@@ -470,6 +521,7 @@ def main():
         "gemv": gemv,
         "quantize": quant,
         "dtype_sweep_forward": sweep,
+        "merge": merge,
     }
     print(json.dumps(line))
 

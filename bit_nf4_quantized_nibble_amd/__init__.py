@@ -11,6 +11,7 @@ Public API (names follow the pages' problem statement):
     dequantize(q, dtype=torch.bfloat16) -> Tensor [rows, cols]
     linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False, path="auto")
     linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False, path="auto")
+    merge(q, lora_a, lora_b, alpha, rslora=False, out=None) -> Tensor [rows, cols]
     workspace_bytes(op, m, rows, cols, r, dtype, flags=0) ; levels()
 
 path: "fused" decodes W inside the GEMM kernels; "dequant" writes W~ (or W~^T for
@@ -27,7 +28,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import QloraError, QloraNf4  # noqa: F401
 
-__all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "workspace_bytes",
+__all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "merge", "workspace_bytes",
            "levels", "QloraError", "dtype_code", "profile_enable", "profile_read"]
 
 
@@ -245,6 +246,29 @@ def linear_bwd(q: NF4Weight, x, dy, lora_a, lora_b, alpha: float, t_saved=None, 
     if dx is not None:
         dx = dx.reshape(*lead, q.cols)
     return dx, da, db
+
+
+def merge(q: NF4Weight, lora_a, lora_b, alpha: float, rslora: bool = False, out=None):
+    """Dense merged weight RNE(w_hat + s B A) [rows, cols] in the adapters' dtype
+    (never re-quantized to NF4).  ``out`` may supply a preallocated output."""
+    torch = _torch()
+    dt = lora_a.dtype
+    _need_cuda("lora_a", lora_a, dt)
+    _need_cuda("lora_b", lora_b, dt)
+    r = lora_a.shape[0]
+    if lora_a.dim() != 2 or lora_a.shape[1] != q.cols:
+        raise ValueError("lora_a must be [r, %d]" % q.cols)
+    if lora_b.dim() != 2 or tuple(lora_b.shape) != (q.rows, r):
+        raise ValueError("lora_b must be [%d, %d]" % (q.rows, r))
+    o = out if out is not None else torch.empty(q.rows, q.cols, dtype=dt, device=lora_a.device)
+    _need_cuda("out", o, dt)
+    if o.numel() != q.rows * q.cols:
+        raise ValueError("out must hold %d x %d elements" % (q.rows, q.cols))
+    d = q.descriptor()
+    _lib.check(_lib.lib().qlora_merge(ctypes.byref(d), _ptr(lora_a), _ptr(lora_b), r, float(alpha),
+                                      _lib.QLORA_FLAG_RSLORA if rslora else 0, dtype_code(dt), _ptr(o),
+                                      _stream_ptr(lora_a.device)))
+    return o.view(q.rows, q.cols)
 
 
 def levels():

@@ -25,10 +25,10 @@ QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_FLAGS_SHIFT = 0, 1, 8
 EXPORTED = (
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_workspace_bytes", "qlora_last_error", "qlora_nf4_levels", "qlora_abi_version",
-    "qlora_profile_enable", "qlora_profile_read", "qlora_kernel_name",
+    "qlora_profile_enable", "qlora_profile_read", "qlora_kernel_name", "qlora_merge",
 )
 KERNEL_KINDS = ("quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
-                "bwd_dt", "bwd_dx", "bwd_da", "bwd_db")
+                "bwd_dt", "bwd_dx", "bwd_da", "bwd_db", "merge")
 
 
 class QloraNf4(ctypes.Structure):
@@ -64,6 +64,7 @@ def _declare(lib):
     lib.qlora_nf4_dequantize.argtypes = [P, i32, vp, vp]
     lib.qlora_linear_fwd.argtypes = [P, vp, i64, vp, vp, i32, f32, i32, vp, i32, vp, vp, vp, sz, vp]
     lib.qlora_linear_bwd.argtypes = [P, vp, vp, i64, vp, vp, i32, f32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.qlora_merge.argtypes = [P, vp, vp, i32, f32, i32, i32, vp, vp]
     lib.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.qlora_workspace_bytes.restype = sz
     lib.qlora_last_error.argtypes = []
@@ -76,7 +77,7 @@ def _declare(lib):
     lib.qlora_kernel_name.restype = ctypes.c_char_p
     for name in ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
                  "qlora_linear_bwd", "qlora_nf4_levels", "qlora_abi_version",
-                 "qlora_profile_enable", "qlora_profile_read"):
+                 "qlora_profile_enable", "qlora_profile_read", "qlora_merge"):
         getattr(lib, name).restype = ctypes.c_int
 
 

@@ -192,7 +192,7 @@ int64_t g_prof_n[QLORA_K_COUNT];
 
 const char* kKernelNames[QLORA_K_COUNT] = {
     "quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
-    "bwd_dt",   "bwd_dx",     "bwd_da",    "bwd_db"};
+    "bwd_dt",   "bwd_dx",     "bwd_da",    "bwd_db", "merge"};
 
 // Wait for every recorded pair and fold it into the totals (lock held).
 int prof_drain() {
@@ -384,6 +384,22 @@ int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;
   return launch_backward(c, dy, t_saved, dx, d_a, d_b);
+}
+
+int qlora_merge(const qlora_nf4_t* w, const void* lora_a, const void* lora_b, int32_t r, float alpha,
+                int32_t flags, int32_t cd, void* out, void* stream) {
+  g_err[0] = 0;
+  int rc = validate_desc(w, true, "merge");
+  if (rc) return rc;
+  if (!valid_cd(cd)) return set_error(QLORA_ERR_DTYPE, "merge: bad dtype %d", cd);
+  if (r < 1) return set_error(QLORA_ERR_INVALID_ARG, "merge: rank r must be >= 1 (got %d)", r);
+  if (!isfinite(alpha)) return set_error(QLORA_ERR_INVALID_ARG, "merge: alpha must be finite");
+  if (flags & ~QLORA_FLAG_RSLORA) return set_error(QLORA_ERR_INVALID_ARG, "merge: unknown flags 0x%x", flags);
+  if (w->rows * w->cols == 0) return QLORA_OK;
+  if (!lora_a || !lora_b || !out) return set_error(QLORA_ERR_INVALID_ARG, "merge: null lora_a / lora_b / out");
+  if (w->rows > 4194240) return set_error(QLORA_ERR_UNSUPPORTED, "merge: %lld rows (at most 4194240)", (long long)w->rows);
+  if ((rc = check_tables("merge"))) return rc;
+  return launch_merge(make_w(w), lora_a, lora_b, r, lora_scale(alpha, r, flags), cd, out, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -42,7 +42,8 @@ struct Nf4W {
   int32_t dq;                // double quantization on/off
   int32_t g;                 // blocks per second-level scale
   int32_t bs_shift;          // log2(bs) when bs is a power of two, else -1
-  int32_t g_shift;           // log2(g) when g is a power of two, else -1
+  int32_t g_shift;           // log2(g) when g is a power of two, 31 when one group holds
+                             // every block (fewer than 2^31), else -1
 };
 
 // Block of flat element e, and second-level group of block b.  Shifts when the
@@ -154,13 +155,16 @@ inline Nf4W make_w(const qlora_nf4_t* q) {
   w.g = q->double_quant ? q->dq_group : 1;
   w.bs_shift = log2_exact(w.bs);
   w.g_shift = log2_exact(w.g);
+  // One group holds every block: b >> 31 is 0 for every block index b < 2^31.
+  const int64_t nb = w.bs > 0 ? q->rows * q->cols / w.bs : 0;
+  if (w.g_shift < 0 && nb <= w.g && nb < (1LL << 31)) w.g_shift = 31;
   return w;
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// Launchers (quant.hip, gemm.hip, gemv.hip).  Each returns a qlora_status_t.
+// Launchers (quant.hip, gemm.hip, gemv.hip, merge.hip).  Each returns a qlora_status_t.
 int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s);
 int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_t s);
 
@@ -186,5 +190,7 @@ int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t 
 int launch_forward(const LayerCall& c, void* y, float* t_save);
 int launch_backward(const LayerCall& c, const void* dy, const float* t_saved, void* dx,
                     float* d_a, float* d_b);
+int launch_merge(const Nf4W& w, const void* a, const void* b, int32_t r, float s, int cd, void* out,
+                 hipStream_t st);
 
 }  // namespace qnf4

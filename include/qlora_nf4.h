@@ -154,6 +154,29 @@ int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_
                      int32_t flags, int32_t cd, const float* t_saved, void* dx, float* d_a,
                      float* d_b, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Fold the trained adapter into a dense weight (the step after training):
+ *   out [rows, cols] = RNE_cd(w_hat + s (B . A)),  s = alpha / r (alpha / sqrt(r)
+ *   with QLORA_FLAG_RSLORA),
+ * w_hat = fl32(L[code] * s_b) exactly as qlora_nf4_dequantize computes it.  B . A is
+ * summed in fp32 (bf16 / f16 products are exact in fp32), added to w_hat with one
+ * fp32 fused multiply-add and rounded to nearest-even into cd.  The result stays
+ * dense and is never re-quantized to NF4, which would round the update away.
+ * lora_a [r, cols], lora_b [rows, r] and out [rows, cols] are row-major device
+ * arrays of dtype cd owned by the caller; out must not overlap the inputs.
+ * Pages: "LoRA and QLoRA, mathematically", "The merge math, and when merging changes
+ * behavior", eq. (6.3.6); qlora-rs README "Honest capability matrix" (dense merge
+ * helper with the LoRA scaling, rsLoRA included) and "Deploy".
+ * bf16 / f16 with r, cols and block_size multiples of 8 and 16-byte aligned arrays
+ * run on the MFMA kernel; other shapes and fp32 on a generic kernel (same w_hat, the
+ * rank sum in another order).  An empty weight is a no-op.
+ * Errors: QLORA_ERR_INVALID_ARG (null pointers, r < 1, non-finite alpha, flags other
+ * than QLORA_FLAG_RSLORA), QLORA_ERR_SHAPE (as qlora_nf4_dequantize), QLORA_ERR_DTYPE,
+ * QLORA_ERR_UNSUPPORTED (more than 4194240 rows).
+ */
+int qlora_merge(const qlora_nf4_t* w, const void* lora_a, const void* lora_b, int32_t r, float alpha,
+                int32_t flags, int32_t cd, void* out, void* stream);
+
 /* Workspace size in bytes for op (QLORA_OP_FWD / QLORA_OP_BWD, optionally OR'ed
  * with flags << QLORA_OP_FLAGS_SHIFT) on this layer shape; 0 for an invalid query.
  * Pure host function. */
@@ -191,6 +214,7 @@ enum {
   QLORA_K_BWD_DX,     /* fused dequant-GEMM dX = dY W~ + dT A */
   QLORA_K_BWD_DA,     /* dA = dT^T x */
   QLORA_K_BWD_DB,     /* dB = s dY^T T0 */
+  QLORA_K_MERGE,      /* adapter merge into the dense weight */
   QLORA_K_COUNT
 };
 int qlora_profile_enable(int32_t on);

@@ -178,3 +178,28 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         q._flags(False, "fast")
     assert q._flags(True, "dequant") == 5 and q._flags(False, "fused") == 2
+
+
+def merge(lib, d, a=FAKE, b=FAKE, r=8, alpha=16.0, flags=0, cd=1, out=FAKE):
+    return lib.qlora_merge(ctypes.byref(d), a, b, r, alpha, flags, cd, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(r=0), INVALID),
+    (dict(alpha=float("nan")), INVALID),
+    (dict(flags=2), INVALID),                # path flags mean nothing to the merge
+    (dict(flags=4), INVALID),
+    (dict(a=None), INVALID),
+    (dict(b=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(cd=5), DTYPE),
+])
+def test_merge_refusals(lib, kw, status):
+    assert merge(lib, desc(), **kw) == status
+    assert last_error(lib)
+
+
+def test_merge_shape_refusals_and_empty(lib):
+    assert merge(lib, desc(rows=3, cols=5, bs=2)) == SHAPE     # 15 elements, block 2
+    assert merge(lib, desc(rows=0, cols=64, codes=0, absmax=0), a=None, b=None, out=None) == OK
+    assert merge(lib, desc(rows=4194241, cols=64, bs=64)) == UNSUP
