@@ -170,39 +170,74 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(Nf4W q, int64_t n, void
 
 }  // namespace
 
-// Dequantize (block size a power of two >= 8, n a multiple of 8): lane l of a
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* ptr, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0, (int)bytes, 0x00020000);
+}
+
+// Raw words of the block scale of element e (converted at use, so that every load of
+// a thread leaves before any is waited on; a read past a buffer returns 0).
+struct ScaleRsrc {
+  rsrc_t q, s2;
+};
+template <int DQ>
+__device__ __forceinline__ ScaleRsrc make_scale_rsrc(const Nf4W& w, int64_t nb) {
+  ScaleRsrc r;
+  r.q = DQ ? make_rsrc(w.absmax_q, nb) : make_rsrc(w.absmax, nb * 4);
+  r.s2 = DQ ? make_rsrc(w.scale2, ((nb + w.g - 1) / w.g) * 4) : r.q;
+  return r;
+}
+template <int DQ>
+__device__ __forceinline__ void load_scale(const ScaleRsrc& r, const Nf4W& w, uint32_t blk, uint32_t& qa,
+                                           uint32_t& s2) {
+  if constexpr (DQ) {
+    qa = __builtin_amdgcn_raw_buffer_load_b8(r.q, (int)blk, 0, 0);
+    s2 = __builtin_amdgcn_raw_buffer_load_b32(r.s2, (int)((blk >> w.g_shift) * 4), 0, 0);
+  } else {
+    qa = __builtin_amdgcn_raw_buffer_load_b32(r.q, (int)(blk * 4), 0, 0);
+    s2 = 0u;
+  }
+}
+// s_b: a_b, or fl32(q_b * S) with double quantization.
+template <int DQ>
+__device__ __forceinline__ float scale_of(uint32_t qa, uint32_t s2) {
+  if constexpr (DQ) return fl32_mul((float)qa, __uint_as_float(s2));
+  else return __uint_as_float(qa);
+}
+
+// Dequantize (block size a power of two >= 8, n a multiple of 8, codes under 2 GiB;
+// with double quantization a power-of-two group or a single group): lane l of a
 // workgroup handles the 8-element chunks l + 256 j (j < 8) of the workgroup's
 // 16384 elements, so each load (4 bytes of codes per lane) and each 16-byte store
-// instruction covers contiguous memory across the wave.  Same values as
-// k_dequantize.
-template <int OUT>
+// instruction covers contiguous memory across the wave.  All 8 chunks' codes and
+// scales are requested before the first is used; chunks past the end read past the
+// buffers (zeros) and store nothing.  Same values as k_dequantize.
+template <int OUT, int DQ>
 __global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, void* __restrict__ out,
                                                              Nf4Tables tab) {
   __shared__ float s_lv[16];
   if (threadIdx.x < 16) s_lv[threadIdx.x] = tab.lv[threadIdx.x];
+  const rsrc_t rc = make_rsrc(q.codes, n / 2);
+  const ScaleRsrc rs = make_scale_rsrc<DQ>(q, n >> q.bs_shift);
   const int64_t ch0 = (int64_t)blockIdx.x * (kThreads * 8) + threadIdx.x;
   const int64_t nch = n / 8;
-  uint32_t cw[8];
-  float sc[8];
+  uint32_t cw[8], qa[8], s2[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t ch = ch0 + kThreads * j;
-    cw[j] = 0u;
-    sc[j] = 0.f;
-    if (ch < nch) {
-      cw[j] = *(const uint32_t*)(q.codes + ch * 4);
-      sc[j] = block_scale(q, (ch * 8) >> q.bs_shift);
-    }
+    cw[j] = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(uint32_t)(ch * 4), 0, 0);
+    load_scale<DQ>(rs, q, (uint32_t)((ch * 8) >> q.bs_shift), qa[j], s2[j]);
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t ch = ch0 + kThreads * j;
     if (ch >= nch) break;
+    const float sc = scale_of<DQ>(qa[j], s2[j]);
     float f[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)  // byte i / 2; element 2k in the high nibble
-      f[i] = fl32_mul(s_lv[(cw[j] >> ((i >> 1) * 8 + ((i & 1) ? 0 : 4))) & 15u], sc[j]);
+      f[i] = fl32_mul(s_lv[(cw[j] >> ((i >> 1) * 8 + ((i & 1) ? 0 : 4))) & 15u], sc);
     if constexpr (OUT == CD_F32) {
       float4* o = (float4*)((float*)out + ch * 8);
       o[0] = make_float4(f[0], f[1], f[2], f[3]);
@@ -221,34 +256,46 @@ __global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, 
 // Transposed dequantize for the dequantize-then-GEMM backward: out [cols, rows] =
 // RNE_cd(fl32(L[c] * s_b))^T, the same values as k_dequantize.  One workgroup per
 // 64 x 64 tile of W: each lane decodes 16 consecutive codes of one W row into an
-// LDS tile [k][n], then writes 16 consecutive elements of one output row.
-// rows and cols are multiples of 64 (checked by the caller).
-template <int OUT>
+// LDS tile [k][n], then writes 16 consecutive elements of one output row.  Tile
+// rows are 128 bytes; 16-byte chunk c of row k sits at c ^ 2 ((k >> 4) & 3), so the
+// four column groups of a 2-byte write instruction land on distinct banks.
+// rows and cols are multiples of 64, the block size a power of two >= 8 (with double
+// quantization a power-of-two group or one group), codes under 2 GiB (checked by
+// the caller).
+template <int OUT, int DQ>
 __global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restrict__ out, Nf4Tables tab) {
   __shared__ float s_lv[16];
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // [k][n], 144-byte rows
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];  // [k][n]
   const int tid = threadIdx.x;
   if (tid < 16) s_lv[tid] = tab.lv[tid];
-  __syncthreads();
+  const int64_t n = q.rows * q.cols;
+  const rsrc_t rc = make_rsrc(q.codes, n / 2);
+  const ScaleRsrc rs = make_scale_rsrc<DQ>(q, n >> q.bs_shift);
   const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
   const int nr = tid >> 2, kc = (tid & 3) * 16;
   const int64_t e0 = (n0 + nr) * q.cols + k0 + kc;
-  const uint2 cw = *(const uint2*)(q.codes + e0 / 2);
+  const uint32_t cw0 = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(uint32_t)(e0 / 2), 0, 0);
+  const uint32_t cw1 = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(uint32_t)(e0 / 2 + 4), 0, 0);
+  uint32_t qa[2], s2[2];
+  load_scale<DQ>(rs, q, (uint32_t)(e0 >> q.bs_shift), qa[0], s2[0]);
+  load_scale<DQ>(rs, q, (uint32_t)((e0 + 8) >> q.bs_shift), qa[1], s2[1]);
+  __syncthreads();
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    const uint32_t word = hf ? cw.y : cw.x;
-    const float s = block_scale(q, block_of(q, e0 + 8 * hf));
+    const uint32_t word = hf ? cw1 : cw0;
+    const float s = scale_of<DQ>(qa[hf], s2[hf]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t c = (word >> ((j >> 1) * 8 + ((j & 1) ? 0 : 4))) & 15u;
-      tile[kc + 8 * hf + j][nr] = to_cd16<OUT>(fl32_mul(s_lv[c], s));
+      const int k = kc + 8 * hf + j;
+      tile[k * 64 + ((((nr >> 3) ^ (2 * ((k >> 4) & 3)))) << 3) + (nr & 7)] = to_cd16<OUT>(fl32_mul(s_lv[c], s));
     }
   }
   __syncthreads();
-  const int kr = tid >> 2, nc = (tid & 3) * 16;
-  const u32x4_t v0 = *(const u32x4_t*)&tile[kr][nc];
-  const u32x4_t v1 = *(const u32x4_t*)&tile[kr][nc + 8];
-  uint16_t* o = (uint16_t*)out + (k0 + kr) * q.rows + n0 + nc;
+  const int kr = tid >> 2, c2 = (tid & 3) * 2, sw = 2 * ((kr >> 4) & 3);
+  const u32x4_t v0 = *(const u32x4_t*)&tile[kr * 64 + ((c2 ^ sw) << 3)];
+  const u32x4_t v1 = *(const u32x4_t*)&tile[kr * 64 + (((c2 + 1) ^ sw) << 3)];
+  uint16_t* o = (uint16_t*)out + (k0 + kr) * q.rows + n0 + 8 * c2;
   *(u32x4_t*)o = v0;
   *(u32x4_t*)(o + 8) = v1;
 }
@@ -295,12 +342,19 @@ int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s) {
   const int64_t n = w.rows * w.cols;
   const Nf4Tables& t = host_tables();
   ProfScope prof(QLORA_K_DEQUANTIZE, s);
-  if (w.bs_shift >= 3 && n % 8 == 0) {
+  if (w.bs_shift >= 3 && n % 8 == 0 && (!w.dq || w.g_shift >= 0) && n / 2 < (1LL << 31)) {
     const int64_t grid = ceil_div(n / 8, kThreads * 8);
-    if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
-    if (cd == CD_BF16) k_dequant_chunks<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
-    else if (cd == CD_F16) k_dequant_chunks<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
-    else if (cd == CD_F32) k_dequant_chunks<CD_F32><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+    const dim3 g((unsigned)grid), blk(kThreads);
+    if (cd == CD_BF16) {
+      if (w.dq) k_dequant_chunks<CD_BF16, 1><<<g, blk, 0, s>>>(w, n, out, t);
+      else k_dequant_chunks<CD_BF16, 0><<<g, blk, 0, s>>>(w, n, out, t);
+    } else if (cd == CD_F16) {
+      if (w.dq) k_dequant_chunks<CD_F16, 1><<<g, blk, 0, s>>>(w, n, out, t);
+      else k_dequant_chunks<CD_F16, 0><<<g, blk, 0, s>>>(w, n, out, t);
+    } else if (cd == CD_F32) {
+      if (w.dq) k_dequant_chunks<CD_F32, 1><<<g, blk, 0, s>>>(w, n, out, t);
+      else k_dequant_chunks<CD_F32, 0><<<g, blk, 0, s>>>(w, n, out, t);
+    }
     else return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
     return check_launch("k_dequant_chunks");
   }
@@ -321,9 +375,16 @@ int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t 
     const Nf4Tables& t = host_tables();
     ProfScope prof(QLORA_K_DEQUANTIZE, s);
     if (w.rows % 64 || w.cols % 64) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: shape not a multiple of 64");
+    if (w.bs_shift < 3 || (w.dq && w.g_shift < 0) || w.rows * w.cols / 2 >= (1LL << 31))
+      return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: block / group sizes or size not supported");
     const dim3 grid((unsigned)(w.cols / 64), (unsigned)(w.rows / 64));
-    if (cd == CD_BF16) k_dequantize_t<CD_BF16><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
-    else if (cd == CD_F16) k_dequantize_t<CD_F16><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+    if (cd == CD_BF16) {
+      if (w.dq) k_dequantize_t<CD_BF16, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+      else k_dequantize_t<CD_BF16, 0><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+    } else if (cd == CD_F16) {
+      if (w.dq) k_dequantize_t<CD_F16, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+      else k_dequantize_t<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+    }
     else return set_error(QLORA_ERR_DTYPE, "dequantize^T: bad dtype %d", cd);
     return check_launch("k_dequantize_t");
   }
