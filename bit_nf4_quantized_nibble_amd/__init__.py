@@ -7,7 +7,7 @@ workspaces with torch.  Every step of the computation runs in the library's
 hand-written HIP kernels; there is no CPU or PyTorch fallback.
 
 Public API (names follow the pages' problem statement):
-    quantize(w, block_size=64, double_quant=False, dq_group=256) -> NF4Weight
+    quantize(w, block_size=64, double_quant=False, dq_group=256 | "global") -> NF4Weight
     dequantize(q, dtype=torch.bfloat16) -> Tensor [rows, cols]
     linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False, path="auto")
     linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False, path="auto")
@@ -117,14 +117,17 @@ def empty_nf4(rows: int, cols: int, block_size: int = 64, double_quant: bool = F
                      torch.empty(nb, dtype=torch.float32, device=device))
 
 
-def quantize(w, block_size: int = 64, double_quant: bool = False, dq_group: int = 256) -> NF4Weight:
+def quantize(w, block_size: int = 64, double_quant: bool = False, dq_group=256) -> NF4Weight:
     """Blockwise NF4 quantization of a 2-D fp32 GPU tensor (optionally with the block
-    scales double-quantized to u8 + one fp32 scale per dq_group blocks)."""
+    scales double-quantized to u8 + one fp32 scale per dq_group blocks; dq_group
+    "global" puts every block in one group)."""
     torch = _torch()
     _need_cuda("w", w, torch.float32)
     if w.dim() != 2:
         raise ValueError("w must be 2-D [rows, cols]")
     rows, cols = w.shape
+    if dq_group == "global":
+        dq_group = max(1, (rows * cols) // block_size) if block_size > 0 else 1
     if block_size <= 0 or (rows * cols) % block_size:
         desc_bs = block_size  # let the library produce the status and message
         q = NF4Weight(rows, cols, desc_bs, double_quant, dq_group,

@@ -300,8 +300,6 @@ int qlora_nf4_quantize(const float* w, qlora_nf4_t* q, void* stream) {
   const int32_t bs = q->block_size;
   if (bs < 8 || bs > 512 || (bs & (bs - 1)))
     return set_error(QLORA_ERR_UNSUPPORTED, "quantize: block_size %d (need a power of two in 8..512)", bs);
-  if (q->double_quant && q->dq_group > 4096)
-    return set_error(QLORA_ERR_UNSUPPORTED, "quantize: dq_group %d > 4096", q->dq_group);
   if ((rc = check_tables("quantize"))) return rc;
   return launch_quantize(w, q, (hipStream_t)stream);
 }

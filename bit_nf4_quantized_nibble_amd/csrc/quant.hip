@@ -38,18 +38,21 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
                                                        float* __restrict__ absmax,
                                                        uint8_t* __restrict__ absmax_q,
                                                        float* __restrict__ scale2,
-                                                       int blocks_per_wg, int dq, Nf4Tables tab) {
+                                                       int blocks_per_wg, int dq, int64_t dq_group,
+                                                       Nf4Tables tab) {
   constexpr int LPB = BS / 8;  // lanes per block
   __shared__ int s_base[32];
   __shared__ float s_thr[32];
   __shared__ float s_amax[4096];  // block scales of this group (double quant only)
   __shared__ float s_red[kThreads / 64];
+  __shared__ uint32_t s_gmax[2];  // dq == 2: bits of the maxima of the (at most two) groups met here
 
   const int tid = threadIdx.x;
   if (tid < 32) {
     s_base[tid] = tab.bucket_base[tid];
     s_thr[tid] = tab.bucket_thr[tid];
   }
+  if (tid < 2) s_gmax[tid] = 0u;
   __syncthreads();
 
   const int64_t nb = n / BS;
@@ -57,6 +60,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
   const int64_t nblk = (blk0 + blocks_per_wg <= nb) ? blocks_per_wg : nb - blk0;
   const int64_t e_begin = blk0 * BS;
   const int64_t e_count = nblk * BS;
+  // dq == 2 (groups larger than a workgroup's span): the span meets group g_first and
+  // possibly the next one, starting at local block `split`.
+  const int64_t g_first = dq == 2 ? blk0 / dq_group : 0;
+  const int64_t split = dq == 2 ? (g_first + 1) * dq_group - blk0 : 0;
 
   for (int64_t e = (int64_t)tid * 8; e < e_count; e += (int64_t)kThreads * 8) {
     const f32x4_t* src = (const f32x4_t*)(w + e_begin + e);
@@ -71,7 +78,9 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
 
     const int64_t blk_local = e / BS;
     if ((tid % LPB) == 0) {
-      if (dq)
+      if (dq == 2)
+        atomicMax(&s_gmax[blk_local >= split ? 1 : 0], __float_as_uint(a));  // a >= 0: bits order as values
+      else if (dq)
         s_amax[blk_local] = a;
       else
         absmax[blk0 + blk_local] = a;
@@ -101,6 +110,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
 
   if (!dq) return;
   __syncthreads();
+  if (dq == 2) {  // fold this span's group maxima into the global ones (k_dq_large_finish divides)
+    if (tid == 0) atomicMax((uint32_t*)scale2 + g_first, s_gmax[0]);
+    if (tid == 1 && split < nblk) atomicMax((uint32_t*)scale2 + g_first + 1, s_gmax[1]);
+    return;
+  }
   // Group max of the block scales, then S = fl32(max / 255) and
   // q_b = round-half-even(a_b / S) (exact: the fp64 quotient of two binary32
   // values never rounds onto a half-integer it is not equal to).
@@ -120,6 +134,58 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
     }
     absmax_q[blk0 + b] = (uint8_t)q;
   }
+}
+
+// Double quantization with groups larger than 4096 blocks (up to one group for the
+// whole tensor): the group maxima need a pass over every block first.  k_quantize
+// (dq == 2) writes the codes and folds the block absmaxes into scale2[g] as a
+// maximum (atomic max on the bits of non-negative floats, from zero); this pass
+// re-reads W, recomputes each block's absmax and encodes q_b = round-half-even(a_b / S)
+// with S = fl32(max / 255); k_dq_large_finish then stores S itself.  Same values as
+// the one-pass kernel.
+__global__ __launch_bounds__(kThreads) void k_fill_zero(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+template <int BS>
+__global__ __launch_bounds__(kThreads) void k_dq_large_q(const float* __restrict__ w, int64_t n,
+                                                         uint8_t* __restrict__ absmax_q,
+                                                         const float* __restrict__ gmax, int blocks_per_wg,
+                                                         int64_t dq_group) {
+  constexpr int LPB = BS / 8;
+  const int tid = threadIdx.x;
+  const int64_t nb = n / BS;
+  const int64_t blk0 = (int64_t)blockIdx.x * blocks_per_wg;
+  const int64_t nblk = (blk0 + blocks_per_wg <= nb) ? blocks_per_wg : nb - blk0;
+  const int64_t g_first = blk0 / dq_group, split = (g_first + 1) * dq_group - blk0;
+  const float S0 = gmax[g_first] / 255.0f;
+  const float S1 = split < nblk ? gmax[g_first + 1] / 255.0f : 0.0f;
+  for (int64_t e = (int64_t)tid * 8; e < nblk * BS; e += (int64_t)kThreads * 8) {
+    const f32x4_t* src = (const f32x4_t*)(w + blk0 * BS + e);
+    const f32x4_t v0 = __builtin_nontemporal_load(src);
+    const f32x4_t v1 = __builtin_nontemporal_load(src + 1);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a = fmaxf(a, fmaxf(fabsf(v0[i]), fabsf(v1[i])));
+#pragma unroll
+    for (int off = 1; off < LPB; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    const int64_t b = e / BS;
+    if ((tid % LPB) == 0) {
+      const float S = b >= split ? S1 : S0;
+      double q = 0.0;
+      if (S > 0.0f) {
+        q = __builtin_rint((double)a / (double)S);
+        q = q < 0.0 ? 0.0 : (q > 255.0 ? 255.0 : q);
+      }
+      absmax_q[blk0 + b] = (uint8_t)q;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_dq_large_finish(float* __restrict__ scale2, int64_t ng) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < ng) scale2[i] = scale2[i] / 255.0f;
 }
 
 // Dequantize: each lane decodes 32 consecutive weights (16 bytes of codes).
@@ -304,16 +370,28 @@ int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s) {
   const int64_t n = q->rows * q->cols;
   const int bs = q->block_size;
   const int64_t nb = n / bs;
-  const int blocks_per_wg = q->double_quant ? q->dq_group : (bs >= 16384 ? 1 : 16384 / bs);
+  // dq: 0 none, 1 groups of up to 4096 blocks (one workgroup each, one pass),
+  // 2 larger groups (spans of 16384 elements, a second pass for the u8 scales).
+  const int dq = !q->double_quant ? 0 : (q->dq_group <= 4096 ? 1 : 2);
+  const int64_t g = q->double_quant ? q->dq_group : 1;
+  const int blocks_per_wg = dq == 1 ? q->dq_group : (bs >= 16384 ? 1 : 16384 / bs);
   const int64_t grid = ceil_div(nb, blocks_per_wg);
+  const int64_t ng = ceil_div(nb, g);
   const Nf4Tables& t = host_tables();
   if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "quantize: tensor too large");
   ProfScope prof(QLORA_K_QUANTIZE, s);
+  if (dq == 2) {
+    k_fill_zero<<<dim3((unsigned)ceil_div(ng, kThreads)), dim3(kThreads), 0, s>>>(q->absmax_scale2, ng);
+    int rc = check_launch("k_fill_zero");
+    if (rc) return rc;
+  }
 #define QNF4_Q(BS)                                                                         \
   case BS:                                                                                 \
     k_quantize<BS><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(                        \
-        w, n, q->codes, q->absmax, q->absmax_q, q->absmax_scale2, blocks_per_wg,           \
-        q->double_quant, t);                                                               \
+        w, n, q->codes, q->absmax, q->absmax_q, q->absmax_scale2, blocks_per_wg, dq, g, t); \
+    if (dq == 2)                                                                           \
+      k_dq_large_q<BS><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(                    \
+          w, n, q->absmax_q, q->absmax_scale2, blocks_per_wg, g);                          \
     break;
   switch (bs) {
     QNF4_Q(8)
@@ -327,6 +405,7 @@ int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s) {
       return set_error(QLORA_ERR_UNSUPPORTED, "quantize: block_size %d not supported", bs);
   }
 #undef QNF4_Q
+  if (dq == 2) k_dq_large_finish<<<dim3((unsigned)ceil_div(ng, kThreads)), dim3(kThreads), 0, s>>>(q->absmax_scale2, ng);
   return check_launch("k_quantize");
 }
 

@@ -85,7 +85,8 @@ typedef struct {
   int64_t cols;
   int32_t block_size;   /* even; the quantize kernel takes 8..512 with block_size/8 a power of two */
   int32_t double_quant; /* 0 or 1 */
-  int32_t dq_group;     /* blocks per second-level scale when double_quant (1..4096) */
+  int32_t dq_group;     /* blocks per second-level scale when double_quant (>= 1; a value
+                           >= rows*cols/block_size gives one scale for the whole tensor) */
   int32_t reserved;     /* must be 0 */
   uint8_t* codes;
   float* absmax;
@@ -99,11 +100,13 @@ typedef struct {
  * packing and, if q->double_quant, the u8 + fp32 encoding of the block scales.
  * Pages: qlora-rs README "Honest capability matrix" (NF4 pack/unpack, block absmax,
  * double quant that drops the resident fp32 scales) and "NF4 Quantization".
- * Writes q->codes and either q->absmax or q->absmax_q + q->absmax_scale2.
+ * Writes q->codes and either q->absmax or q->absmax_q + q->absmax_scale2.  Groups of
+ * up to 4096 blocks are encoded in one pass over W; larger ones (one group for the
+ * whole tensor included: the "global" scale-of-scales) take a second pass.
  * An empty tensor (rows * cols == 0) is a no-op that returns QLORA_OK.
  * Errors: QLORA_ERR_SHAPE (n % block_size, odd block_size, negative dims),
  * QLORA_ERR_UNSUPPORTED (block_size outside 8..512 or block_size/8 not a power of
- * two; dq_group > 4096), QLORA_ERR_INVALID_ARG (null pointers, reserved != 0).
+ * two), QLORA_ERR_INVALID_ARG (null pointers, reserved != 0).
  * NaN / Inf in W are outside the contract (codes are then unspecified, no fault).
  */
 int qlora_nf4_quantize(const float* w, qlora_nf4_t* q, void* stream);

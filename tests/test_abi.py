@@ -60,7 +60,6 @@ def last_error(lib):
     (dict(rows=10, cols=10, bs=64), SHAPE),  # n not a multiple of the block size
     (dict(rows=24, cols=1, bs=24), UNSUP),   # even, divides n, but not a power of two
     (dict(bs=1024, rows=64, cols=64), UNSUP),
-    (dict(dq=1, g=5000), UNSUP),
     (dict(dq=1, g=0), INVALID),
     (dict(dq=2), INVALID),
     (dict(reserved=1), INVALID),

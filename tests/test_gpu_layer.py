@@ -250,3 +250,38 @@ def test_one_hot_reproduces_dequantized_weight_exactly(cd, path):
     torch.cuda.synchronize()
     assert torch.equal(y, w_cd.t().contiguous())
     assert torch.equal(dx, w_cd)
+
+
+# ----------------------------------------------------------------------------- variants
+@pytest.mark.parametrize("path", ["fused", "dequant"])
+@pytest.mark.parametrize("bs,groups,N,K", [(64, "global", 256, 512), (32, "global", 256, 512), (256, 3, 256, 512),
+                                           (128, 64, 256, 512), (32, 5000, 512, 1024)])
+def test_layer_block_sizes_and_global_scale(path, bs, groups, N, K):
+    """Block sizes 32 / 64 / 128 / 256 and the double-quant group variants (one
+    "global" group, a group larger than 4096 blocks, small odd groups) through the
+    forward and the backward on both GEMM paths."""
+    M, r = 200, 16
+    g = N * K // bs if groups == "global" else groups
+    L = inputs.random_layer(M, N, K, r, seed=bs + N, block_size=bs, double_quant=True, dq_group=g)
+    say("variant", path, bs, groups, g)
+    gg = to_gpu(L)
+    q = gpu_q(L, gg)
+    o = oracle_layer(L)
+    y = run_fwd(L, gg, q, path=path)
+    assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"]), "bf16", "fwd")
+    dx, da, db = run_bwd(L, gg, q, path=path)
+    rdx, rda, rdb = oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"])
+    assert_close(to_np(dx), rdx, "bf16", "dX")
+    assert_close(to_np(da), rda, "bf16", "dA")
+    assert_close(to_np(db), rdb, "bf16", "dB")
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_decode_global_scale(m):
+    L = inputs.random_layer(m, 4096, 4096, 16, seed=m + 40, alpha=32.0, double_quant=True,
+                            dq_group=4096 * 4096 // 64, with_dy=False)
+    say("decode global", m)
+    g = to_gpu(L)
+    y = run_fwd(L, g, gpu_q(L, g))
+    o = oracle_layer(L)
+    assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"]), "bf16", "decode global")

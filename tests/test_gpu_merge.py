@@ -162,3 +162,17 @@ def test_merge_rejects_bad_arguments():
                                                 qn._lib.QLORA_BF16, out.data_ptr(), None))
     with pytest.raises(qn.QloraError, match="INVALID_ARG"):
         qn.merge(q, A, B, float("nan"))
+
+
+def test_merge_global_scale():
+    say("merge global")
+    nb = 300 * 512 // 64
+    L2 = inputs.random_layer(1, 300, 512, 64, seed=8, cd="bf16", block_size=64, double_quant=True, dq_group=nb,
+                             with_dy=False)
+    q = qn.quantize(L2.W.cuda(), 64, True, nb)
+    what = oracle.dequantize(oracle.quantize(L2.W.numpy(), 64, True, nb))
+    out = qn.merge(q, L2.A.cuda(), L2.B.cuda(), L2.alpha)
+    torch.cuda.synchronize()
+    A, B = oracle.operand(L2.A, "bf16"), oracle.operand(L2.B, "bf16")
+    ref = oracle.merge(what, A, B, L2.alpha / 64, "bf16")
+    assert_merge_close(out, ref, "bf16", "merge global", A, B, L2.alpha / 64)

@@ -85,6 +85,23 @@ def test_block_sizes_and_groups(bs, g):
     check(W, bs, True, g, what="bs%d-g%d" % (bs, g))
 
 
+@pytest.mark.parametrize("bs,g", [(64, 262144), (64, 5000), (32, 1 << 30), (256, 4097)])
+def test_large_and_global_groups(bs, g):
+    """Groups larger than 4096 blocks take the two-pass encoding; g >= nb (and any
+    larger value) is the single "global" scale-of-scales."""
+    W = inputs.roundtrip_weight(1, outliers=True)
+    q, ref = check(W, bs, True, g, what="bs%d-g%d" % (bs, g), deq=("bf16",))
+    nb = W.numel() // bs
+    assert q.absmax_scale2.numel() == (nb + g - 1) // g
+
+
+def test_global_group_ragged_span():
+    g_ = torch.Generator().manual_seed(9)
+    W = torch.randn(1000, 72, generator=g_)
+    check(W, 8, True, 9000, what="ragged global bs8")     # 9000 blocks, one group
+    check(W, 8, True, 4100, what="ragged bs8 g4100")      # a span crosses a group boundary
+
+
 def test_ragged_spans():
     # 1125 blocks: the last 16384-element span and the last DQ group are partial.
     g_ = torch.Generator().manual_seed(5)
