@@ -47,6 +47,8 @@ def _load():
 
         _build.build()
     lib = ctypes.CDLL(_LIB_PATH)
+    lib.orc_round_f64.argtypes = [_f64p, _i64, _i32, _vp]
+    lib.orc_round_f64.restype = None
     lib.orc_nf4_levels.argtypes = [_f64p, _f32p]
     lib.orc_nf4_levels.restype = None
     lib.orc_nf4_quantize.argtypes = [_f32p, _i64, _i32, _i32, _i32, _u8p, _vp, _vp, _vp, _vp]
@@ -173,6 +175,15 @@ def round_to(a, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return _f32(a).copy()
     return from_bits(to_bits(a, dtype), dtype)
+
+
+def round64_to(a, dtype: str) -> np.ndarray:
+    """fp64 values rounded once (RNE) to the dtype, returned as exact fp32 values."""
+    a = np.ascontiguousarray(a, np.float64)
+    kind = {"f32": 0, "bf16": 1, "f16": 2}[dtype]
+    out = np.empty(a.shape, np.float32 if kind == 0 else np.uint16)
+    _load().orc_round_f64(a.reshape(-1), a.size, kind, out.ctypes.data_as(ctypes.c_void_p))
+    return out if kind == 0 else from_bits(out, dtype)
 
 
 # --------------------------------------------------------------------------- layer

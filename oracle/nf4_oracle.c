@@ -480,3 +480,13 @@ void orc_qlora_merge(const float* what, const float* A, const float* B, int64_t 
     }
 }
 
+
+/* One rounding of binary64 values to binary32 (kind 0, as float), bf16 (1) or f16 (2)
+ * bits: the storage of activations and gradients between the layers of a stack. */
+void orc_round_f64(const double* in, int64_t n, int32_t kind, void* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    if (kind == 0) ((float*)out)[i] = (float)in[i];
+    else if (kind == 1) ((uint16_t*)out)[i] = bf16_from_f64(in[i]);
+    else ((uint16_t*)out)[i] = f16_from_f64(in[i]);
+  }
+}
