@@ -12,6 +12,8 @@ Public API (names follow the pages' problem statement):
     linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False, path="auto")
     linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False, path="auto")
     merge(q, lora_a, lora_b, alpha, rslora=False, out=None) -> Tensor [rows, cols]
+    mse_loss_grad(y, target) -> (loss [1] fp32, dy) ; adamw_step(param, grad, m, v, step, ...)
+    StackLayer.create(q, a32, b32, dtype) ; stack_train_step(layers, x, target, alpha, step, ...)
     workspace_bytes(op, m, rows, cols, r, dtype, flags=0) ; levels()
 
 path: "fused" decodes W inside the GEMM kernels; "dequant" writes W~ (or W~^T for
@@ -29,7 +31,8 @@ from . import _lib
 from ._lib import QloraError, QloraNf4  # noqa: F401
 
 __all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "merge", "workspace_bytes",
-           "levels", "QloraError", "dtype_code", "profile_enable", "profile_read"]
+           "levels", "QloraError", "dtype_code", "profile_enable", "profile_read", "mse_loss_grad",
+           "adamw_step", "StackLayer", "stack_train_step", "stack_workspace_bytes"]
 
 
 def _torch():
@@ -272,6 +275,126 @@ def merge(q: NF4Weight, lora_a, lora_b, alpha: float, rslora: bool = False, out=
                                       _lib.QLORA_FLAG_RSLORA if rslora else 0, dtype_code(dt), _ptr(o),
                                       _stream_ptr(lora_a.device)))
     return o.view(q.rows, q.cols)
+
+
+def mse_loss_grad(y, target, dy=None):
+    """loss = mean((y - target)^2) (a 1-element fp32 GPU tensor) and dy = 2 (y - target) / n
+    in y's dtype."""
+    torch = _torch()
+    dt = y.dtype
+    _need_cuda("y", y, dt)
+    _need_cuda("target", target, dt)
+    if y.numel() != target.numel():
+        raise ValueError("y and target differ in size")
+    dy = dy if dy is not None else torch.empty_like(y)
+    _need_cuda("dy", dy, dt)
+    loss = torch.empty(1, dtype=torch.float32, device=y.device)
+    ws = torch.empty(_lib.QLORA_MSE_WORKSPACE_BYTES, dtype=torch.uint8, device=y.device)
+    _lib.check(_lib.lib().qlora_mse_loss_grad(_ptr(y), _ptr(target), y.numel(), dtype_code(dt), _ptr(loss),
+                                              _ptr(dy), _ptr(ws), ws.numel(), _stream_ptr(y.device)))
+    return loss, dy
+
+
+def _adamw(lr, beta1, beta2, eps, weight_decay):
+    return _lib.QloraAdamW(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay))
+
+
+def adamw_step(param, grad, m, v, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+               eps: float = 1e-8, weight_decay: float = 0.0, param_cd=None):
+    """One in-place AdamW update of fp32 ``param`` (moments ``m``, ``v``; 1-based ``step``);
+    ``param_cd`` (bf16 / f16 / fp32, optional) receives the rounded copy."""
+    torch = _torch()
+    for name, t in (("param", param), ("grad", grad), ("m", m), ("v", v)):
+        _need_cuda(name, t, torch.float32)
+        if t.numel() != param.numel():
+            raise ValueError("%s has %d elements, param %d" % (name, t.numel(), param.numel()))
+    cd = _lib.QLORA_F32
+    if param_cd is not None:
+        _need_cuda("param_cd", param_cd)
+        cd = dtype_code(param_cd.dtype)
+        if param_cd.numel() != param.numel():
+            raise ValueError("param_cd has the wrong size")
+    o = _adamw(lr, beta1, beta2, eps, weight_decay)
+    _lib.check(_lib.lib().qlora_adamw_step(_ptr(param), _ptr(grad), _ptr(m), _ptr(v), param.numel(),
+                                           ctypes.byref(o), int(step), _ptr(param_cd), cd,
+                                           _stream_ptr(param.device)))
+
+
+@dataclass
+class StackLayer:
+    """One layer of a trainable stack: frozen NF4 base, fp32 master adapters, their
+    compute-dtype copies, AdamW moments and the gradient buffers the step writes."""
+    q: NF4Weight
+    lora_a: "object"
+    lora_b: "object"
+    a32: "object"
+    b32: "object"
+    m_a: "object"
+    v_a: "object"
+    m_b: "object"
+    v_b: "object"
+    grad_a: "object"
+    grad_b: "object"
+
+    @staticmethod
+    def create(q: NF4Weight, a32, b32, dtype) -> "StackLayer":
+        torch = _torch()
+        a32 = a32.to(device=q.device, dtype=torch.float32).contiguous().clone()
+        b32 = b32.to(device=q.device, dtype=torch.float32).contiguous().clone()
+        z = torch.zeros_like
+        return StackLayer(q, a32.to(dtype), b32.to(dtype), a32, b32, z(a32), z(a32), z(b32), z(b32), z(a32),
+                          z(b32))
+
+    @property
+    def r(self) -> int:
+        return self.a32.shape[0]
+
+    def _struct(self, desc):
+        return _lib.QloraStackLayer(ctypes.pointer(desc), *[_ptr(t) for t in (
+            self.lora_a, self.lora_b, self.a32, self.b32, self.m_a, self.v_a, self.m_b, self.v_b,
+            self.grad_a, self.grad_b)])
+
+
+def _stack_structs(layers):
+    descs = [L.q.descriptor() for L in layers]
+    arr = (_lib.QloraStackLayer * len(layers))(*[L._struct(d) for L, d in zip(layers, descs)])
+    return arr, descs
+
+
+def stack_workspace_bytes(layers, m: int, dtype, rslora: bool = False, path: str = "auto") -> int:
+    arr, _descs = _stack_structs(layers)
+    return int(_lib.lib().qlora_stack_workspace_bytes(arr, len(layers), m, layers[0].r, dtype_code(dtype),
+                                                      _flags(rslora, path)))
+
+
+def stack_train_step(layers, x, target, alpha: float, step: int, lr: float, beta1: float = 0.9,
+                     beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0, rslora: bool = False,
+                     path: str = "auto", workspace=None, loss=None):
+    """Forward through the stack, MSE loss against ``target``, backward, AdamW on every
+    adapter (in place).  Returns the loss as a 1-element fp32 GPU tensor."""
+    torch = _torch()
+    dt = x.dtype
+    x2, _ = _flatten(x, layers[0].q.cols)
+    t2, _ = _flatten(target, layers[-1].q.rows)
+    x2, t2 = x2.contiguous(), t2.contiguous()
+    _need_cuda("x", x2, dt)
+    _need_cuda("target", t2, dt)
+    m = x2.shape[0]
+    if t2.shape[0] != m:
+        raise ValueError("target has %d rows, x %d" % (t2.shape[0], m))
+    for L in layers:
+        _need_cuda("lora_a", L.lora_a, dt)
+        _need_cuda("lora_b", L.lora_b, dt)
+    arr, _descs = _stack_structs(layers)
+    flags = _flags(rslora, path)
+    nbytes = int(_lib.lib().qlora_stack_workspace_bytes(arr, len(layers), m, layers[0].r, dtype_code(dt), flags))
+    ws = _workspace(nbytes, x.device, workspace)
+    loss = loss if loss is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    o = _adamw(lr, beta1, beta2, eps, weight_decay)
+    _lib.check(_lib.lib().qlora_stack_train_step(arr, len(layers), _ptr(x2), m, _ptr(t2), layers[0].r, float(alpha),
+                                                 flags, dtype_code(dt), ctypes.byref(o), int(step), _ptr(loss),
+                                                 _ptr(ws), ws.numel() * ws.element_size(), _stream_ptr(x.device)))
+    return loss
 
 
 def levels():

@@ -26,9 +26,11 @@ EXPORTED = (
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_workspace_bytes", "qlora_last_error", "qlora_nf4_levels", "qlora_abi_version",
     "qlora_profile_enable", "qlora_profile_read", "qlora_kernel_name", "qlora_merge",
+    "qlora_mse_loss_grad", "qlora_adamw_step", "qlora_stack_train_step", "qlora_stack_workspace_bytes",
 )
+QLORA_MSE_WORKSPACE_BYTES = 4096
 KERNEL_KINDS = ("quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
-                "bwd_dt", "bwd_dx", "bwd_da", "bwd_db", "merge")
+                "bwd_dt", "bwd_dx", "bwd_da", "bwd_db", "merge", "loss", "optim")
 
 
 class QloraNf4(ctypes.Structure):
@@ -45,6 +47,19 @@ class QloraNf4(ctypes.Structure):
         ("absmax_q", ctypes.c_void_p),
         ("absmax_scale2", ctypes.c_void_p),
     ]
+
+
+class QloraAdamW(ctypes.Structure):
+    """Mirror of qlora_adamw_t."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
+
+
+class QloraStackLayer(ctypes.Structure):
+    """Mirror of qlora_stack_layer_t."""
+    _fields_ = [("w", ctypes.POINTER(QloraNf4))] + [
+        (name, ctypes.c_void_p) for name in ("lora_a", "lora_b", "a32", "b32", "m_a", "v_a", "m_b", "v_b",
+                                             "grad_a", "grad_b")]
 
 
 class QloraError(RuntimeError):
@@ -65,6 +80,13 @@ def _declare(lib):
     lib.qlora_linear_fwd.argtypes = [P, vp, i64, vp, vp, i32, f32, i32, vp, i32, vp, vp, vp, sz, vp]
     lib.qlora_linear_bwd.argtypes = [P, vp, vp, i64, vp, vp, i32, f32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.qlora_merge.argtypes = [P, vp, vp, i32, f32, i32, i32, vp, vp]
+    PA = ctypes.POINTER(QloraAdamW)
+    PS = ctypes.POINTER(QloraStackLayer)
+    lib.qlora_mse_loss_grad.argtypes = [vp, vp, i64, i32, vp, vp, vp, sz, vp]
+    lib.qlora_adamw_step.argtypes = [vp, vp, vp, vp, i64, PA, i32, vp, i32, vp]
+    lib.qlora_stack_train_step.argtypes = [PS, i32, vp, i64, vp, i32, f32, i32, i32, PA, i32, vp, vp, sz, vp]
+    lib.qlora_stack_workspace_bytes.argtypes = [PS, i32, i64, i32, i32, i32]
+    lib.qlora_stack_workspace_bytes.restype = sz
     lib.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.qlora_workspace_bytes.restype = sz
     lib.qlora_last_error.argtypes = []
@@ -77,7 +99,8 @@ def _declare(lib):
     lib.qlora_kernel_name.restype = ctypes.c_char_p
     for name in ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
                  "qlora_linear_bwd", "qlora_nf4_levels", "qlora_abi_version",
-                 "qlora_profile_enable", "qlora_profile_read", "qlora_merge"):
+                 "qlora_profile_enable", "qlora_profile_read", "qlora_merge", "qlora_mse_loss_grad",
+                 "qlora_adamw_step", "qlora_stack_train_step"):
         getattr(lib, name).restype = ctypes.c_int
 
 

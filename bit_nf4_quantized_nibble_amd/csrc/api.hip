@@ -192,7 +192,7 @@ int64_t g_prof_n[QLORA_K_COUNT];
 
 const char* kKernelNames[QLORA_K_COUNT] = {
     "quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
-    "bwd_dt",   "bwd_dx",     "bwd_da",    "bwd_db", "merge"};
+    "bwd_dt",   "bwd_dx",     "bwd_da",    "bwd_db", "merge", "loss", "optim"};
 
 // Wait for every recorded pair and fold it into the totals (lock held).
 int prof_drain() {
@@ -398,6 +398,87 @@ int qlora_merge(const qlora_nf4_t* w, const void* lora_a, const void* lora_b, in
   if (w->rows > 4194240) return set_error(QLORA_ERR_UNSUPPORTED, "merge: %lld rows (at most 4194240)", (long long)w->rows);
   if ((rc = check_tables("merge"))) return rc;
   return launch_merge(make_w(w), lora_a, lora_b, r, lora_scale(alpha, r, flags), cd, out, (hipStream_t)stream);
+}
+
+namespace {
+int check_adamw(const qlora_adamw_t* o, int32_t step, const char* who) {
+  if (!o) return set_error(QLORA_ERR_INVALID_ARG, "%s: null optimizer settings", who);
+  if (step < 1) return set_error(QLORA_ERR_INVALID_ARG, "%s: step must be >= 1 (got %d)", who, step);
+  const bool ok = isfinite(o->lr) && o->lr >= 0.f && isfinite(o->beta1) && o->beta1 >= 0.f && o->beta1 < 1.f &&
+                  isfinite(o->beta2) && o->beta2 >= 0.f && o->beta2 < 1.f && isfinite(o->eps) && o->eps > 0.f &&
+                  isfinite(o->weight_decay) && o->weight_decay >= 0.f;
+  if (!ok) return set_error(QLORA_ERR_INVALID_ARG, "%s: AdamW settings out of range", who);
+  return QLORA_OK;
+}
+}  // namespace
+
+int qlora_mse_loss_grad(const void* y, const void* target, int64_t n, int32_t cd, float* loss, void* dy,
+                        void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!valid_cd(cd)) return set_error(QLORA_ERR_DTYPE, "mse: bad dtype %d", cd);
+  if (n < 0) return set_error(QLORA_ERR_INVALID_ARG, "mse: negative n");
+  if (n == 0) return QLORA_OK;
+  if (!y || !target || !loss || !dy) return set_error(QLORA_ERR_INVALID_ARG, "mse: null pointer");
+  int rc = check_ws(ws, ws_bytes, QLORA_MSE_WORKSPACE_BYTES, "mse");
+  if (rc) return rc;
+  return launch_mse(y, target, n, cd, loss, dy, (float*)ws, (hipStream_t)stream);
+}
+
+int qlora_adamw_step(float* param, const float* grad, float* m, float* v, int64_t n, const qlora_adamw_t* opt,
+                     int32_t step, void* param_cd, int32_t cd, void* stream) {
+  g_err[0] = 0;
+  if (!valid_cd(cd)) return set_error(QLORA_ERR_DTYPE, "adamw: bad dtype %d", cd);
+  if (n < 0) return set_error(QLORA_ERR_INVALID_ARG, "adamw: negative n");
+  int rc = check_adamw(opt, step, "adamw");
+  if (rc) return rc;
+  if (n == 0) return QLORA_OK;
+  if (!param || !grad || !m || !v) return set_error(QLORA_ERR_INVALID_ARG, "adamw: null pointer");
+  return launch_adamw(param, grad, m, v, n, *opt, step, param_cd, cd, (hipStream_t)stream);
+}
+
+namespace {
+int check_stack(const qlora_stack_layer_t* layers, int32_t L, int64_t m, int32_t r, int32_t cd, const char* who) {
+  if (!layers || L < 1) return set_error(QLORA_ERR_SHAPE, "%s: need at least one layer", who);
+  if (m < 1) return set_error(QLORA_ERR_SHAPE, "%s: m must be >= 1", who);
+  if (r < 1) return set_error(QLORA_ERR_INVALID_ARG, "%s: rank r must be >= 1", who);
+  if (!valid_cd(cd)) return set_error(QLORA_ERR_DTYPE, "%s: bad dtype %d", who, cd);
+  for (int l = 0; l < L; ++l) {
+    if (!layers[l].w) return set_error(QLORA_ERR_INVALID_ARG, "%s: layer %d has no weight", who, l);
+    if (l && layers[l].w->cols != layers[l - 1].w->rows)
+      return set_error(QLORA_ERR_SHAPE, "%s: layer %d takes %lld inputs, layer %d gives %lld", who, l,
+                       (long long)layers[l].w->cols, l - 1, (long long)layers[l - 1].w->rows);
+  }
+  return QLORA_OK;
+}
+}  // namespace
+
+size_t qlora_stack_workspace_bytes(const qlora_stack_layer_t* layers, int32_t n_layers, int64_t m, int32_t r,
+                                   int32_t cd, int32_t flags) {
+  if (check_stack(layers, n_layers, m, r, cd, "stack_workspace")) return 0;
+  if (flags & ~(QLORA_FLAG_RSLORA | QLORA_FLAG_FUSED | QLORA_FLAG_DEQUANT_GEMM)) return 0;
+  return stack_workspace_bytes(layers, n_layers, m, r, cd, flags);
+}
+
+int qlora_stack_train_step(const qlora_stack_layer_t* layers, int32_t n_layers, const void* x, int64_t m,
+                           const void* target, int32_t r, float alpha, int32_t flags, int32_t cd,
+                           const qlora_adamw_t* opt, int32_t step, float* loss, void* ws, size_t ws_bytes,
+                           void* stream) {
+  g_err[0] = 0;
+  int rc = check_stack(layers, n_layers, m, r, cd, "stack_step");
+  if (rc) return rc;
+  if (!x || !target || !loss) return set_error(QLORA_ERR_INVALID_ARG, "stack_step: null x / target / loss");
+  if ((rc = check_adamw(opt, step, "stack_step"))) return rc;
+  for (int l = 0; l < n_layers; ++l) {
+    const qlora_stack_layer_t& S = layers[l];
+    if ((rc = validate_layer(S.w, x, m, S.lora_a, S.lora_b, r, alpha, flags, cd, "stack_step"))) return rc;
+    if (!S.a32 || !S.b32 || !S.m_a || !S.v_a || !S.m_b || !S.v_b || !S.grad_a || !S.grad_b)
+      return set_error(QLORA_ERR_INVALID_ARG, "stack_step: layer %d has a null adapter buffer", l);
+  }
+  if ((rc = check_ws(ws, ws_bytes, stack_workspace_bytes(layers, n_layers, m, r, cd, flags), "stack_step")))
+    return rc;
+  if ((rc = check_tables("stack_step"))) return rc;
+  return launch_stack_step(layers, n_layers, x, m, target, r, lora_scale(alpha, r, flags), flags, cd, *opt, step,
+                           loss, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

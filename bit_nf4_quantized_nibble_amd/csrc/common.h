@@ -164,7 +164,7 @@ inline Nf4W make_w(const qlora_nf4_t* q) {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// Launchers (quant.hip, gemm.hip, gemv.hip, merge.hip).  Each returns a qlora_status_t.
+// Launchers (quant.hip, gemm.hip, gemv.hip, merge.hip, train.hip).  Each returns a qlora_status_t.
 int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s);
 int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_t s);
 
@@ -192,5 +192,14 @@ int launch_backward(const LayerCall& c, const void* dy, const float* t_saved, vo
                     float* d_a, float* d_b);
 int launch_merge(const Nf4W& w, const void* a, const void* b, int32_t r, float s, int cd, void* out,
                  hipStream_t st);
+int launch_mse(const void* y, const void* t, int64_t n, int cd, float* loss, void* dy, float* partial,
+               hipStream_t s);
+int launch_adamw(float* theta, const float* g, float* m, float* v, int64_t n, const qlora_adamw_t& o, int32_t step,
+                 void* theta_cd, int cd, hipStream_t s);
+size_t stack_workspace_bytes(const qlora_stack_layer_t* layers, int32_t L, int64_t m, int32_t r, int cd,
+                             int32_t flags);
+int launch_stack_step(const qlora_stack_layer_t* layers, int32_t L, const void* x, int64_t m, const void* target,
+                      int32_t r, float scale, int32_t flags, int cd, const qlora_adamw_t& opt, int32_t step,
+                      float* loss, void* ws, hipStream_t s);
 
 }  // namespace qnf4

@@ -151,3 +151,32 @@ def random_layer(M: int, N: int, K: int, r: int, seed: int = 0, cd: str = "bf16"
     return LayerInputs("random_%dx%dx%d_r%d" % (M, N, K, r), W, x, A, B, r,
                        float(2 * r if alpha is None else alpha), block_size, double_quant,
                        dq_group, cd, dY, bias)
+
+
+@dataclass
+class StackInputs:
+    """A stack of QLoRA layers for the training step (CPU tensors): layer l maps
+    dims[l] features to dims[l + 1]."""
+    Ws: List[torch.Tensor]          # fp32 [dims[l+1], dims[l]] frozen weights (to be quantized)
+    As: List[torch.Tensor]          # fp32 master adapters [r, dims[l]]
+    Bs: List[torch.Tensor]          # fp32 master adapters [dims[l+1], r]
+    x: torch.Tensor                 # cd [M, dims[0]]
+    target: torch.Tensor            # cd [M, dims[-1]]
+    r: int
+    alpha: float
+    cd: str = "bf16"
+
+
+def stack(dims: List[int], M: int, r: int = 16, seed: int = 0, cd: str = "bf16", alpha: Optional[float] = None,
+          w_sigma: float = 0.02, t_sigma: float = 0.1) -> StackInputs:
+    """Synthetic stack: W ~ N(0, w_sigma^2), A ~ N(0, 1/r), B ~ N(0, 0.01^2) per layer in
+    order, then x ~ N(0, 1) and the regression target ~ N(0, t_sigma^2)."""
+    g = _gen(seed)
+    Ws, As, Bs = [], [], []
+    for K, N in zip(dims[:-1], dims[1:]):
+        Ws.append(randn(g, (N, K), w_sigma))
+        As.append(randn(g, (r, K), r ** -0.5))
+        Bs.append(randn(g, (N, r), 0.01))
+    x = randn(g, (M, dims[0]), 1.0, cd)
+    target = randn(g, (M, dims[-1]), t_sigma, cd)
+    return StackInputs(Ws, As, Bs, x, target, r, float(2 * r if alpha is None else alpha), cd)

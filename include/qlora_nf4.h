@@ -180,6 +180,87 @@ int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_
 int qlora_merge(const qlora_nf4_t* w, const void* lora_a, const void* lora_b, int32_t r, float alpha,
                 int32_t flags, int32_t cd, void* out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Training a stack of QLoRA layers (qlora-rs README, "Training (layer stack)": stacked
+ * QuantizedLinear layers, an MSE training_step, AdamW updating the adapters while the
+ * NF4 bases stay frozen).
+ * ------------------------------------------------------------------------- */
+
+/* AdamW hyper-parameters (decoupled weight decay). */
+typedef struct {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+} qlora_adamw_t;
+
+/* Bytes of workspace qlora_mse_loss_grad needs (a fixed small size). */
+#define QLORA_MSE_WORKSPACE_BYTES 4096
+
+/*
+ * loss = mean((y - target)^2) over n elements and dy = dL/dy = 2 (y - target) / n.
+ * y, target, dy: device arrays of n elements of dtype cd (dy may alias y); loss: one
+ * device float.  The squares are summed in fp32 in a fixed order (deterministic);
+ * dy is rounded once more from fp32 into cd.  ws: device workspace of at least
+ * QLORA_MSE_WORKSPACE_BYTES bytes, 256-byte aligned.  n == 0 is a no-op.
+ * Errors: QLORA_ERR_INVALID_ARG (null pointers, n < 0), QLORA_ERR_DTYPE,
+ * QLORA_ERR_WORKSPACE.
+ */
+int qlora_mse_loss_grad(const void* y, const void* target, int64_t n, int32_t cd, float* loss, void* dy,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One AdamW step on n fp32 parameters in place, step t >= 1 (1-based):
+ *   m = b1 m + (1 - b1) g,  v = b2 v + (1 - b2) g^2,
+ *   param = param (1 - lr wd) - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps),
+ * all in fp32 (the bias corrections are formed in fp64 and rounded once).  When
+ * param_cd is not NULL it receives RNE_cd(param) (the copy the layer kernels read).
+ * m and v start at zero.  Errors: QLORA_ERR_INVALID_ARG (null pointers, n < 0,
+ * step < 1, non-finite or out-of-range hyper-parameters), QLORA_ERR_DTYPE.
+ */
+int qlora_adamw_step(float* param, const float* grad, float* m, float* v, int64_t n, const qlora_adamw_t* opt,
+                     int32_t step, void* param_cd, int32_t cd, void* stream);
+
+/* One layer of a stack: its frozen base and its adapter state (all device memory,
+ * owned by the caller; shapes from w: A [r, cols], B [rows, r]). */
+typedef struct {
+  const qlora_nf4_t* w;  /* frozen NF4 base [rows, cols] (host descriptor) */
+  void* lora_a;          /* [r, cols] cd: the copy the kernels read, rewritten by each step */
+  void* lora_b;          /* [rows, r] cd */
+  float* a32;            /* [r, cols] fp32 master copy of A (updated by AdamW) */
+  float* b32;            /* [rows, r] fp32 master copy of B */
+  float* m_a;            /* AdamW moments of A and B, fp32, zero before the first step */
+  float* v_a;
+  float* m_b;
+  float* v_b;
+  float* grad_a;         /* [r, cols] fp32: dL/dA of the step, written by the step */
+  float* grad_b;         /* [rows, r] fp32: dL/dB */
+} qlora_stack_layer_t;
+
+/*
+ * One training step of a stack of n_layers QLoRA layers, h_{l+1} = layer_l(h_l) with
+ * h_0 = x [m, cols_0] and layer l's cols equal to layer l-1's rows (no activation
+ * between layers):  forward through the stack (qlora_linear_fwd, keeping T0),
+ * loss = mean((h_L - target)^2) into *loss (device float), backward through the stack
+ * (qlora_linear_bwd; dX of layer 0 is skipped), then AdamW (qlora_adamw_step) on every
+ * A and B with step t, refreshing the cd copies.  Activations and the gradients
+ * between layers are stored in cd.  All layers share r, alpha, flags and cd.
+ * ws: at least qlora_stack_workspace_bytes(...) bytes, 256-byte aligned.
+ * Errors: those of qlora_linear_fwd / _bwd for any layer, QLORA_ERR_SHAPE (layers
+ * that do not chain, m < 1, n_layers < 1), QLORA_ERR_INVALID_ARG (null pointers, bad
+ * hyper-parameters), QLORA_ERR_WORKSPACE.
+ */
+int qlora_stack_train_step(const qlora_stack_layer_t* layers, int32_t n_layers, const void* x, int64_t m,
+                           const void* target, int32_t r, float alpha, int32_t flags, int32_t cd,
+                           const qlora_adamw_t* opt, int32_t step, float* loss, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Workspace bytes of qlora_stack_train_step (reads only the layers' shapes); 0 for an
+ * invalid query.  Pure host function. */
+size_t qlora_stack_workspace_bytes(const qlora_stack_layer_t* layers, int32_t n_layers, int64_t m, int32_t r,
+                                   int32_t cd, int32_t flags);
+
 /* Workspace size in bytes for op (QLORA_OP_FWD / QLORA_OP_BWD, optionally OR'ed
  * with flags << QLORA_OP_FLAGS_SHIFT) on this layer shape; 0 for an invalid query.
  * Pure host function. */
@@ -218,6 +299,8 @@ enum {
   QLORA_K_BWD_DA,     /* dA = dT^T x */
   QLORA_K_BWD_DB,     /* dB = s dY^T T0 */
   QLORA_K_MERGE,      /* adapter merge into the dense weight */
+  QLORA_K_LOSS,       /* MSE loss and its gradient */
+  QLORA_K_OPTIM,      /* AdamW update of an adapter */
   QLORA_K_COUNT
 };
 int qlora_profile_enable(int32_t on);

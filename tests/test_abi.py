@@ -202,3 +202,24 @@ def test_merge_shape_refusals_and_empty(lib):
     assert merge(lib, desc(rows=3, cols=5, bs=2)) == SHAPE     # 15 elements, block 2
     assert merge(lib, desc(rows=0, cols=64, codes=0, absmax=0), a=None, b=None, out=None) == OK
     assert merge(lib, desc(rows=4194241, cols=64, bs=64)) == UNSUP
+
+
+def test_training_entry_points_refuse_on_the_host(lib):
+    o = _lib.QloraAdamW(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    bad = _lib.QloraAdamW(1e-3, 1.0, 0.999, 1e-8, 0.0)
+    assert lib.qlora_mse_loss_grad(FAKE, FAKE, 10, 7, FAKE, FAKE, FAKE, 4096, None) == DTYPE
+    assert lib.qlora_mse_loss_grad(FAKE, None, 10, 1, FAKE, FAKE, FAKE, 4096, None) == INVALID
+    assert lib.qlora_mse_loss_grad(FAKE, FAKE, 10, 1, FAKE, FAKE, FAKE, 16, None) == WS
+    assert lib.qlora_mse_loss_grad(None, None, 0, 1, None, None, None, 0, None) == OK
+    assert lib.qlora_adamw_step(FAKE, FAKE, FAKE, FAKE, 10, ctypes.byref(o), 0, None, 1, None) == INVALID
+    assert lib.qlora_adamw_step(FAKE, FAKE, FAKE, FAKE, 10, ctypes.byref(bad), 1, None, 1, None) == INVALID
+    assert lib.qlora_adamw_step(FAKE, None, FAKE, FAKE, 10, ctypes.byref(o), 1, None, 1, None) == INVALID
+    assert lib.qlora_adamw_step(FAKE, FAKE, FAKE, FAKE, 10, None, 1, None, 1, None) == INVALID
+    d0, d1 = desc(rows=128, cols=64), desc(rows=64, cols=96)
+    L = (_lib.QloraStackLayer * 2)(_lib.QloraStackLayer(ctypes.pointer(d0), *([FAKE] * 10)),
+                                   _lib.QloraStackLayer(ctypes.pointer(d1), *([FAKE] * 10)))
+    args = lambda n: (L, n, FAKE, 16, FAKE, 8, 16.0, 0, 1, ctypes.byref(o), 1, FAKE, FAKE, 1 << 40, None)
+    assert lib.qlora_stack_train_step(*args(2)) == SHAPE              # 64 outputs feed 96 inputs
+    assert lib.qlora_stack_workspace_bytes(L, 2, 16, 8, 1, 0) == 0
+    assert lib.qlora_stack_workspace_bytes(L, 1, 16, 8, 1, 0) > 0
+    assert lib.qlora_stack_train_step(*args(0)) == SHAPE
