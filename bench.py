@@ -15,6 +15,8 @@ Also reported on the same line, each against its own MI355X roofline:
   quantize  NF4 quantize of a 4096x4096 fp32 weight without / with double quant, GB/s
   dequantize  the double-quantized weight back to bf16 / fp32, GB/s
   dtype_sweep  the prefill forward in f16 and f32 compute
+  merge     the adapter merge of the block's seven projections, GB/s
+  stack_train_step  forward + MSE + backward + AdamW of a 3-layer stack of projection shapes
   cpu_baseline  the oracle (plain C, fp64) on a bounded sample of the step's work
   roofline  the dominant kernel of the step, timed with HIP events on its stream
 
@@ -296,6 +298,47 @@ def bench_merge(qn, torch, inputs, iters=5):
             "bytes_per_element": "0.5 codes + 1/64 u8 scale + 2 bf16 out (+ A, B once)"}
 
 
+STACK_DIMS = [4096, 14336, 4096, 4096]  # up_proj, down_proj and o_proj shapes, chained
+
+
+def bench_stack(qn, torch, inputs, steps=5, warmup=2, m=4096):
+    """Training step of a stack of QLoRA layers (forward, MSE loss, backward, AdamW on
+    every adapter) on Llama-3-8B projection shapes 4096 -> 14336 -> 4096 -> 4096,
+    4096 tokens, r = 64, bf16, NF4 block 64 with double quantization."""
+    S = inputs.stack(STACK_DIMS, m, r=64, seed=5, alpha=128.0)
+    layers = []
+    for W, A, B in zip(S.Ws, S.As, S.Bs):
+        q = qn.quantize(W.to("cuda"), 64, True, 256)
+        layers.append(qn.StackLayer.create(q, A, B, torch.bfloat16))
+    del S.Ws[:]
+    x, t = S.x.to("cuda"), S.target.to("cuda")
+    ws = torch.empty(qn.stack_workspace_bytes(layers, m, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    opt = dict(lr=1e-4, weight_decay=0.01)
+    for k in range(warmup):
+        qn.stack_train_step(layers, x, t, S.alpha, k + 1, workspace=ws, loss=loss, **opt)
+    torch.cuda.synchronize()
+    first = float(loss.item())
+    qn.profile_enable(True)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        qn.stack_train_step(layers, x, t, S.alpha, warmup + k + 1, workspace=ws, loss=loss, **opt)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    prof = qn.profile_read()
+    qn.profile_enable(False)
+    flops = 0.0
+    for l, (K, N) in enumerate(zip(STACK_DIMS[:-1], STACK_DIMS[1:])):
+        flops += fwd_flops(m, N, K, 64) + bwd_flops(m, N, K, 64) - (2.0 * m * N * K + 2.0 * m * 64 * K if l == 0 else 0)
+    out = {"workload": "stack 4096-14336-4096-4096, 4096 tokens, r 64, bf16", "ms_per_step": round(sec * 1e3, 4),
+           "tflops": round(flops / sec / 1e12, 2), "frac_bf16_peak": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "loss_first_timed": first, "loss_last": float(loss.item()),
+           "kernels_ms_per_step": {k: round(ms / steps, 4) for k, (ms, n) in prof.items() if n}}
+    del layers, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_probe(torch, mib=512, iters=10):
     """A plain device copy of known size: the calibration run for the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) and the streaming ceiling of this GPU."""
@@ -437,7 +480,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep", "merge", "copyprobe"], default=None,
+    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep", "merge", "stack", "copyprobe"], default=None,
                     help="run one part (for profiling); the JSON line needs the full run")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -468,6 +511,9 @@ def main():
     if args.only == "merge":
         print(json.dumps(bench_merge(qn, torch, inputs)))
         return
+    if args.only == "stack":
+        print(json.dumps(bench_stack(qn, torch, inputs)))
+        return
 
     st = bench_step(args, qn, torch, lib, inputs)
     log("step %.3f ms" % (st["sec"] * 1e3))
@@ -484,6 +530,8 @@ def main():
     log("sweep done")
     merge = bench_merge(qn, torch, inputs)
     log("merge done")
+    stack = bench_stack(qn, torch, inputs)
+    log("stack done")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)
@@ -522,6 +570,7 @@ def main():
         "quantize": quant,
         "dtype_sweep_forward": sweep,
         "merge": merge,
+        "stack_train_step": stack,
     }
     print(json.dumps(line))
 
