@@ -9,8 +9,10 @@ hand-written HIP kernels; there is no CPU or PyTorch fallback.
 Public API (names follow the pages' problem statement):
     quantize(w, block_size=64, double_quant=False, dq_group=256 | "global") -> NF4Weight
     dequantize(q, dtype=torch.bfloat16) -> Tensor [rows, cols]
-    linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False, path="auto")
-    linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False, path="auto")
+    linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False, path="auto",
+               dropout_mask=None, dropout_p=0.0)
+    linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False, path="auto",
+               dropout_mask=None, dropout_p=0.0)
     merge(q, lora_a, lora_b, alpha, rslora=False, out=None) -> Tensor [rows, cols]
     mse_loss_grad(y, target) -> (loss [1] fp32, dy) ; adamw_step(param, grad, m, v, step, ...)
     StackLayer.create(q, a32, b32, dtype) ; stack_train_step(layers, x, target, alpha, step, ...)
@@ -183,12 +185,25 @@ def _flatten(x, cols):
     return x.reshape(-1, cols), lead
 
 
+def _dropout_args(dropout_mask, dropout_p, x2):
+    torch = _torch()
+    if dropout_mask is None:
+        return None, 0.0
+    mk = dropout_mask.reshape(-1, x2.shape[1]).contiguous()
+    _need_cuda("dropout_mask", mk, torch.uint8)
+    if mk.shape != x2.shape:
+        raise ValueError("dropout_mask must have x's shape")
+    return mk, float(dropout_p)
+
+
 def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t: bool = False,
-               rslora: bool = False, workspace=None, out=None, t_out=None, path: str = "auto"):
+               rslora: bool = False, workspace=None, out=None, t_out=None, path: str = "auto",
+               dropout_mask=None, dropout_p: float = 0.0):
     """y = x . deq(W)^T + s (x . A^T) . B^T (+ bias), s = alpha / r (alpha / sqrt(r)
     with rslora).  Leading dims of x are flattened to tokens.  Returns y, or
     (y, T0) with T0 = x A^T in fp32 when save_t.  ``out`` / ``t_out`` may supply
-    preallocated outputs."""
+    preallocated outputs.  With ``dropout_mask`` (uint8, x's shape, nonzero = kept)
+    the low-rank branch reads x * mask / (1 - dropout_p) (LoRA dropout)."""
     torch = _torch()
     dt = x.dtype
     x2, lead = _flatten(x, q.cols)
@@ -207,20 +222,30 @@ def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t:
     if t0 is not None and t0.numel() != m * r:
         raise ValueError("t_out must hold %d x %d fp32 elements" % (m, r))
     flags = _flags(rslora, path)
-    ws = _workspace(workspace_bytes(_lib.QLORA_OP_FWD, m, q.rows, q.cols, r, dt, flags), x.device, workspace)
+    mk, p = _dropout_args(dropout_mask, dropout_p, x2)
+    qflags = flags | (_lib.QLORA_FLAG_DROPOUT if mk is not None else 0)
+    ws = _workspace(workspace_bytes(_lib.QLORA_OP_FWD, m, q.rows, q.cols, r, dt, qflags), x.device, workspace)
     d = q.descriptor()
-    _lib.check(_lib.lib().qlora_linear_fwd(
-        ctypes.byref(d), _ptr(x2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
-        _ptr(bias), dtype_code(dt), _ptr(y), _ptr(t0), _ptr(ws), ws.numel() * ws.element_size(),
-        _stream_ptr(x.device)))
+    if mk is None:
+        _lib.check(_lib.lib().qlora_linear_fwd(
+            ctypes.byref(d), _ptr(x2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
+            _ptr(bias), dtype_code(dt), _ptr(y), _ptr(t0), _ptr(ws), ws.numel() * ws.element_size(),
+            _stream_ptr(x.device)))
+    else:
+        _lib.check(_lib.lib().qlora_linear_fwd_dropout(
+            ctypes.byref(d), _ptr(x2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
+            _ptr(bias), dtype_code(dt), _ptr(mk), p, _ptr(y), _ptr(t0), _ptr(ws), ws.numel() * ws.element_size(),
+            _stream_ptr(x.device)))
     y = y.reshape(*lead, q.rows)
     return (y, t0) if (save_t or t_out is not None) else y
 
 
 def linear_bwd(q: NF4Weight, x, dy, lora_a, lora_b, alpha: float, t_saved=None, need_dx: bool = True,
-               rslora: bool = False, workspace=None, dx_out=None, da_out=None, db_out=None, path: str = "auto"):
+               rslora: bool = False, workspace=None, dx_out=None, da_out=None, db_out=None, path: str = "auto",
+               dropout_mask=None, dropout_p: float = 0.0):
     """Gradients with the base frozen: returns (dX or None, dA fp32 [r, cols], dB fp32 [rows, r]).
-    ``*_out`` may supply preallocated outputs."""
+    ``*_out`` may supply preallocated outputs; ``dropout_mask`` / ``dropout_p`` as in
+    the forward (the same mask)."""
     torch = _torch()
     dt = x.dtype
     x2, lead = _flatten(x, q.cols)
@@ -243,12 +268,20 @@ def linear_bwd(q: NF4Weight, x, dy, lora_a, lora_b, alpha: float, t_saved=None, 
     if t_saved is not None and t_saved.numel() != m * r:
         raise ValueError("t_saved must hold %d x %d fp32 elements" % (m, r))
     flags = _flags(rslora, path)
-    ws = _workspace(workspace_bytes(_lib.QLORA_OP_BWD, m, q.rows, q.cols, r, dt, flags), x.device, workspace)
+    mk, p = _dropout_args(dropout_mask, dropout_p, x2)
+    qflags = flags | (_lib.QLORA_FLAG_DROPOUT if mk is not None else 0)
+    ws = _workspace(workspace_bytes(_lib.QLORA_OP_BWD, m, q.rows, q.cols, r, dt, qflags), x.device, workspace)
     d = q.descriptor()
-    _lib.check(_lib.lib().qlora_linear_bwd(
-        ctypes.byref(d), _ptr(x2), _ptr(dy2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
-        dtype_code(dt), _ptr(t_saved), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),
-        ws.numel() * ws.element_size(), _stream_ptr(x.device)))
+    if mk is None:
+        _lib.check(_lib.lib().qlora_linear_bwd(
+            ctypes.byref(d), _ptr(x2), _ptr(dy2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
+            dtype_code(dt), _ptr(t_saved), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream_ptr(x.device)))
+    else:
+        _lib.check(_lib.lib().qlora_linear_bwd_dropout(
+            ctypes.byref(d), _ptr(x2), _ptr(dy2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
+            dtype_code(dt), _ptr(mk), p, _ptr(t_saved), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream_ptr(x.device)))
     if dx is not None:
         dx = dx.reshape(*lead, q.cols)
     return dx, da, db

@@ -18,7 +18,7 @@ STATUS_NAMES = {
     -4: "QLORA_ERR_UNSUPPORTED", -5: "QLORA_ERR_WORKSPACE", -6: "QLORA_ERR_HIP",
 }
 QLORA_F32, QLORA_BF16, QLORA_F16 = 0, 1, 2
-QLORA_FLAG_RSLORA, QLORA_FLAG_FUSED, QLORA_FLAG_DEQUANT_GEMM = 1, 2, 4
+QLORA_FLAG_RSLORA, QLORA_FLAG_FUSED, QLORA_FLAG_DEQUANT_GEMM, QLORA_FLAG_DROPOUT = 1, 2, 4, 8
 QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_FLAGS_SHIFT = 0, 1, 8
 
 # Every function the header declares, for the export check.
@@ -27,6 +27,7 @@ EXPORTED = (
     "qlora_workspace_bytes", "qlora_last_error", "qlora_nf4_levels", "qlora_abi_version",
     "qlora_profile_enable", "qlora_profile_read", "qlora_kernel_name", "qlora_merge",
     "qlora_mse_loss_grad", "qlora_adamw_step", "qlora_stack_train_step", "qlora_stack_workspace_bytes",
+    "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
 )
 QLORA_MSE_WORKSPACE_BYTES = 4096
 KERNEL_KINDS = ("quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
@@ -87,6 +88,9 @@ def _declare(lib):
     lib.qlora_stack_train_step.argtypes = [PS, i32, vp, i64, vp, i32, f32, i32, i32, PA, i32, vp, vp, sz, vp]
     lib.qlora_stack_workspace_bytes.argtypes = [PS, i32, i64, i32, i32, i32]
     lib.qlora_stack_workspace_bytes.restype = sz
+    lib.qlora_linear_fwd_dropout.argtypes = [P, vp, i64, vp, vp, i32, f32, i32, vp, i32, vp, f32, vp, vp, vp, sz, vp]
+    lib.qlora_linear_bwd_dropout.argtypes = [P, vp, vp, i64, vp, vp, i32, f32, i32, i32, vp, f32, vp, vp, vp, vp, vp,
+                                             sz, vp]
     lib.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.qlora_workspace_bytes.restype = sz
     lib.qlora_last_error.argtypes = []
@@ -100,7 +104,8 @@ def _declare(lib):
     for name in ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
                  "qlora_linear_bwd", "qlora_nf4_levels", "qlora_abi_version",
                  "qlora_profile_enable", "qlora_profile_read", "qlora_merge", "qlora_mse_loss_grad",
-                 "qlora_adamw_step", "qlora_stack_train_step"):
+                 "qlora_adamw_step", "qlora_stack_train_step", "qlora_linear_fwd_dropout",
+                 "qlora_linear_bwd_dropout"):
         getattr(lib, name).restype = ctypes.c_int
 
 

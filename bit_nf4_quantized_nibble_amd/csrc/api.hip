@@ -124,7 +124,7 @@ int validate_layer(const qlora_nf4_t* w, const void* x, int64_t m, const void* l
   if (m < 0) return set_error(QLORA_ERR_SHAPE, "%s: negative m", who);
   if (r < 1) return set_error(QLORA_ERR_INVALID_ARG, "%s: rank r must be >= 1 (got %d)", who, r);
   if (!isfinite(alpha)) return set_error(QLORA_ERR_INVALID_ARG, "%s: alpha must be finite", who);
-  if (flags & ~(QLORA_FLAG_RSLORA | QLORA_FLAG_FUSED | QLORA_FLAG_DEQUANT_GEMM))
+  if (flags & ~(QLORA_FLAG_RSLORA | QLORA_FLAG_FUSED | QLORA_FLAG_DEQUANT_GEMM | QLORA_FLAG_DROPOUT))
     return set_error(QLORA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", who, flags);
   if ((flags & QLORA_FLAG_FUSED) && (flags & QLORA_FLAG_DEQUANT_GEMM))
     return set_error(QLORA_ERR_INVALID_ARG, "%s: QLORA_FLAG_FUSED and QLORA_FLAG_DEQUANT_GEMM exclude each other", who);
@@ -323,30 +323,32 @@ size_t qlora_workspace_bytes(int32_t op, int64_t m, int64_t rows, int64_t cols, 
   if (m < 0 || rows < 0 || cols < 0 || r < 1 || !valid_cd(cd)) return 0;
   const int32_t flags = op >> QLORA_OP_FLAGS_SHIFT;
   op &= (1 << QLORA_OP_FLAGS_SHIFT) - 1;
-  if (flags & ~(QLORA_FLAG_RSLORA | QLORA_FLAG_FUSED | QLORA_FLAG_DEQUANT_GEMM)) return 0;
+  if (flags & ~(QLORA_FLAG_RSLORA | QLORA_FLAG_FUSED | QLORA_FLAG_DEQUANT_GEMM | QLORA_FLAG_DROPOUT)) return 0;
   if (op == QLORA_OP_FWD) return fwd_workspace_bytes(m, rows, cols, r, cd, flags);
   if (op == QLORA_OP_BWD) return bwd_workspace_bytes(m, rows, cols, r, cd, flags);
   return 0;
 }
 
-int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
-                     const void* lora_b, int32_t r, float alpha, int32_t flags, const void* bias,
-                     int32_t cd, void* y, float* t_save, void* ws, size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
-  int rc = validate_layer(w, x, m, lora_a, lora_b, r, alpha, flags, cd, "linear_fwd");
+namespace {
+int fwd_impl(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a, const void* lora_b, int32_t r,
+             float alpha, int32_t flags, const void* bias, int32_t cd, const uint8_t* mask, float p, void* y,
+             float* t_save, void* ws, size_t ws_bytes, void* stream, const char* who) {
+  int rc = validate_layer(w, x, m, lora_a, lora_b, r, alpha, flags, cd, who);
   if (rc) return rc;
-  if (!y) return set_error(QLORA_ERR_INVALID_ARG, "linear_fwd: null y");
+  if (!y) return set_error(QLORA_ERR_INVALID_ARG, "%s: null y", who);
   if (m == 0) return QLORA_OK;
-  if ((rc = check_ws(ws, ws_bytes, fwd_workspace_bytes(m, w->rows, w->cols, r, cd, flags), "linear_fwd"))) return rc;
-  if ((rc = check_tables("linear_fwd"))) return rc;
+  if (mask) flags |= QLORA_FLAG_DROPOUT;
+  if ((rc = check_ws(ws, ws_bytes, fwd_workspace_bytes(m, w->rows, w->cols, r, cd, flags), who))) return rc;
+  if ((rc = check_tables(who))) return rc;
   LayerCall c;
   c.w = make_w(w);
   c.cd = cd;
   c.m = m;
   c.r = r;
-  c.scale = lora_scale(alpha, r, flags);
+  c.scale = mask ? (float)((double)lora_scale(alpha, r, flags) / (1.0 - (double)p)) : lora_scale(alpha, r, flags);
   c.flags = flags;
   c.x = x;
+  c.drop_mask = mask;
   c.lora_a = lora_a;
   c.lora_b = lora_b;
   c.bias = bias;
@@ -356,25 +358,26 @@ int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void*
   return launch_forward(c, y, t_save);
 }
 
-int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m,
-                     const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,
-                     int32_t cd, const float* t_saved, void* dx, float* d_a, float* d_b, void* ws,
-                     size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
-  int rc = validate_layer(w, x, m, lora_a, lora_b, r, alpha, flags, cd, "linear_bwd");
+int bwd_impl(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m, const void* lora_a,
+             const void* lora_b, int32_t r, float alpha, int32_t flags, int32_t cd, const uint8_t* mask, float p,
+             const float* t_saved, void* dx, float* d_a, float* d_b, void* ws, size_t ws_bytes, void* stream,
+             const char* who) {
+  int rc = validate_layer(w, x, m, lora_a, lora_b, r, alpha, flags, cd, who);
   if (rc) return rc;
-  if (!dy || !d_a || !d_b) return set_error(QLORA_ERR_INVALID_ARG, "linear_bwd: null dy / d_a / d_b");
-  if (m == 0) return set_error(QLORA_ERR_SHAPE, "linear_bwd: m must be >= 1 (dA, dB would be all zero)");
-  if ((rc = check_ws(ws, ws_bytes, bwd_workspace_bytes(m, w->rows, w->cols, r, cd, flags), "linear_bwd"))) return rc;
-  if ((rc = check_tables("linear_bwd"))) return rc;
+  if (!dy || !d_a || !d_b) return set_error(QLORA_ERR_INVALID_ARG, "%s: null dy / d_a / d_b", who);
+  if (m == 0) return set_error(QLORA_ERR_SHAPE, "%s: m must be >= 1 (dA, dB would be all zero)", who);
+  if (mask) flags |= QLORA_FLAG_DROPOUT;
+  if ((rc = check_ws(ws, ws_bytes, bwd_workspace_bytes(m, w->rows, w->cols, r, cd, flags), who))) return rc;
+  if ((rc = check_tables(who))) return rc;
   LayerCall c;
   c.w = make_w(w);
   c.cd = cd;
   c.m = m;
   c.r = r;
-  c.scale = lora_scale(alpha, r, flags);
+  c.scale = mask ? (float)((double)lora_scale(alpha, r, flags) / (1.0 - (double)p)) : lora_scale(alpha, r, flags);
   c.flags = flags;
   c.x = x;
+  c.drop_mask = mask;
   c.lora_a = lora_a;
   c.lora_b = lora_b;
   c.bias = nullptr;
@@ -382,6 +385,56 @@ int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_
   c.ws_bytes = ws_bytes;
   c.stream = (hipStream_t)stream;
   return launch_backward(c, dy, t_saved, dx, d_a, d_b);
+}
+
+int check_dropout(const uint8_t* mask, float p, const char* who) {
+  if (!mask) return set_error(QLORA_ERR_INVALID_ARG, "%s: null dropout mask", who);
+  if (!(p >= 0.f && p < 1.f)) return set_error(QLORA_ERR_INVALID_ARG, "%s: dropout rate %g outside [0, 1)", who, p);
+  return QLORA_OK;
+}
+}  // namespace
+
+int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
+                     const void* lora_b, int32_t r, float alpha, int32_t flags, const void* bias,
+                     int32_t cd, void* y, float* t_save, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (flags & QLORA_FLAG_DROPOUT)
+    return set_error(QLORA_ERR_INVALID_ARG, "linear_fwd: QLORA_FLAG_DROPOUT belongs to qlora_linear_fwd_dropout");
+  return fwd_impl(w, x, m, lora_a, lora_b, r, alpha, flags, bias, cd, nullptr, 0.f, y, t_save, ws, ws_bytes, stream,
+                  "linear_fwd");
+}
+
+int qlora_linear_fwd_dropout(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
+                             const void* lora_b, int32_t r, float alpha, int32_t flags, const void* bias,
+                             int32_t cd, const uint8_t* mask, float p, void* y, float* t_save, void* ws,
+                             size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = check_dropout(mask, p, "linear_fwd_dropout");
+  if (rc) return rc;
+  return fwd_impl(w, x, m, lora_a, lora_b, r, alpha, flags, bias, cd, mask, p, y, t_save, ws, ws_bytes, stream,
+                  "linear_fwd_dropout");
+}
+
+int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m,
+                     const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,
+                     int32_t cd, const float* t_saved, void* dx, float* d_a, float* d_b, void* ws,
+                     size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (flags & QLORA_FLAG_DROPOUT)
+    return set_error(QLORA_ERR_INVALID_ARG, "linear_bwd: QLORA_FLAG_DROPOUT belongs to qlora_linear_bwd_dropout");
+  return bwd_impl(w, x, dy, m, lora_a, lora_b, r, alpha, flags, cd, nullptr, 0.f, t_saved, dx, d_a, d_b, ws, ws_bytes,
+                  stream, "linear_bwd");
+}
+
+int qlora_linear_bwd_dropout(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m,
+                             const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,
+                             int32_t cd, const uint8_t* mask, float p, const float* t_saved, void* dx,
+                             float* d_a, float* d_b, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = check_dropout(mask, p, "linear_bwd_dropout");
+  if (rc) return rc;
+  return bwd_impl(w, x, dy, m, lora_a, lora_b, r, alpha, flags, cd, mask, p, t_saved, dx, d_a, d_b, ws, ws_bytes,
+                  stream, "linear_bwd_dropout");
 }
 
 int qlora_merge(const qlora_nf4_t* w, const void* lora_a, const void* lora_b, int32_t r, float alpha,
@@ -467,6 +520,7 @@ int qlora_stack_train_step(const qlora_stack_layer_t* layers, int32_t n_layers, 
   int rc = check_stack(layers, n_layers, m, r, cd, "stack_step");
   if (rc) return rc;
   if (!x || !target || !loss) return set_error(QLORA_ERR_INVALID_ARG, "stack_step: null x / target / loss");
+  if (flags & QLORA_FLAG_DROPOUT) return set_error(QLORA_ERR_INVALID_ARG, "stack_step: no dropout in the stack step");
   if ((rc = check_adamw(opt, step, "stack_step"))) return rc;
   for (int l = 0; l < n_layers; ++l) {
     const qlora_stack_layer_t& S = layers[l];

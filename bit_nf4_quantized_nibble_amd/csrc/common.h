@@ -176,6 +176,8 @@ struct LayerCall {
   float scale;        // alpha / r (or alpha / sqrt(r))
   int32_t flags;      // QLORA_FLAG_* of the call
   const void* x;      // [m, cols]
+  const uint8_t* drop_mask;  // [m, cols] keep mask of LoRA dropout, or null (no dropout);
+                             // with dropout, scale already holds s / (1 - p)
   const void* lora_a; // [r, cols]
   const void* lora_b; // [rows, r]
   const void* bias;   // [rows] or null
@@ -184,6 +186,10 @@ struct LayerCall {
   hipStream_t stream;
 };
 
+int apply_mask(int cd, const void* x, const uint8_t* mask, int64_t n, void* out, hipStream_t s);
+int zero_fill(void* p, int64_t bytes, hipStream_t s);
+int rank_add_masked(int cd, void* dx, const uint8_t* mask, const void* dt, int64_t ld_dt, const void* a, int32_t r,
+                    int64_t M, int64_t K, hipStream_t s);
 size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags);
 size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags);
 int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s);

@@ -433,7 +433,7 @@ struct FwdPlan {
   int64_t r_pad;
   Split st;
   bool dense;
-  int64_t off_tcd, off_part, off_wd, total;
+  int64_t off_tcd, off_part, off_wd, off_xm, total;
 };
 FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   FwdPlan P;
@@ -446,7 +446,8 @@ FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   if (skinny_ok(cd, r)) part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(m, cols));
   P.off_wd = P.off_part + al(part);
   P.dense = dense_path(m, rows, cols, cd, flags, false);
-  P.total = P.off_wd + (P.dense ? al(rows * cols * es) : 0);
+  P.off_xm = P.off_wd + (P.dense ? al(rows * cols * es) : 0);  // x M with LoRA dropout
+  P.total = P.off_xm + ((flags & QLORA_FLAG_DROPOUT) ? al(m * cols * es) : 0);
   return P;
 }
 
@@ -456,7 +457,7 @@ struct BwdPlan {
   bool dense;
   bool sk, sk_n;       // the skinny kernels take the rank products (dT and dB also need rows % 8)
   int64_t n_pad, m_pad;  // contractions rounded up to whole 64-element stages
-  int64_t off_t0, off_dt, off_dtcd, off_bt, off_dtt, off_t0t, off_part, off_wdt, total;
+  int64_t off_t0, off_dt, off_dtcd, off_bt, off_dtt, off_t0t, off_part, off_wdt, off_xm, off_zero, total;
 };
 BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   BwdPlan P;
@@ -491,7 +492,11 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   }
   P.off_wdt = P.off_part + al(part);
   P.dense = dense_path(m, rows, cols, cd, flags, true);
-  P.total = P.off_wdt + (P.dense ? al(rows * cols * es) : 0);
+  // with LoRA dropout: x M, and a zero [m, r_pad] operand for the base-only dX GEMM
+  P.off_xm = P.off_wdt + (P.dense ? al(rows * cols * es) : 0);
+  const bool drop = (flags & QLORA_FLAG_DROPOUT) != 0;
+  P.off_zero = P.off_xm + (drop ? al(m * cols * es) : 0);
+  P.total = P.off_zero + (drop ? al(m * P.r_pad * es) : 0);
   return P;
 }
 
@@ -525,11 +530,11 @@ GemmParams base_params(const LayerCall& c) {
 // T0 (or s T0) = x A^T as fp32 partials, reduced into out32 (scale sc32) and a
 // compute-dtype copy outcd [m, r_pad] (scale sccd).
 template <int CD>
-int lora_down(const LayerCall& c, const Split& sp, float* part, float* out32, float sc32, void* outcd,
-              float sccd, int64_t r_pad) {
+int lora_down(const LayerCall& c, const void* lx, const Split& sp, float* part, float* out32, float sc32,
+              void* outcd, float sccd, int64_t r_pad) {
   const int64_t K = c.w.cols;
   GemmParams p = base_params(c);
-  p.a1 = opnd<CD>(c.x, K, c.m, K);
+  p.a1 = opnd<CD>(lx, K, c.m, K);
   p.b1 = opnd<CD>(c.lora_a, K, c.r, K);
   p.k1 = K;
   p.k1_chunk = sp.chunk;
@@ -551,11 +556,17 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
   void* tcd = ws + P.off_tcd;
   float* part = (float*)(ws + P.off_part);
   int rc;
+  // input of the low-rank branch: x, or x M with LoRA dropout
+  const void* lx = c.x;
+  if (c.drop_mask) {
+    if ((rc = apply_mask(CD, c.x, c.drop_mask, M * K, ws + P.off_xm, c.stream))) return rc;
+    lx = ws + P.off_xm;
+  }
   if (skinny_ok(CD, c.r)) {
     int S;
-    if ((rc = skinny(CD, false, c.x, K, M, c.lora_a, K, M, c.r, K, part, &S, c.stream, QLORA_K_LORA_DOWN))) return rc;
+    if ((rc = skinny(CD, false, lx, K, M, c.lora_a, K, M, c.r, K, part, &S, c.stream, QLORA_K_LORA_DOWN))) return rc;
     if ((rc = skinny_reduce(CD, part, S, M, c.r, 1.0f, t_save, false, c.scale, tcd, P.r_pad, c.stream))) return rc;
-  } else if ((rc = lora_down<CD>(c, P.st, part, t_save, 1.0f, tcd, c.scale, P.r_pad))) {
+  } else if ((rc = lora_down<CD>(c, lx, P.st, part, t_save, 1.0f, tcd, c.scale, P.r_pad))) {
     return rc;
   }
   if (P.dense && dense256_ok(c, false)) {
@@ -592,15 +603,21 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   void* dtcd = ws + P.off_dtcd;
   float* part = (float*)(ws + P.off_part);
   int rc;
+  // input of the low-rank branch: x, or x M with LoRA dropout
+  const void* lx = c.x;
+  if (c.drop_mask) {
+    if ((rc = apply_mask(CD, c.x, c.drop_mask, M * K, ws + P.off_xm, c.stream))) return rc;
+    lx = ws + P.off_xm;
+  }
 
   // T0 = x A^T (recomputed unless the forward saved it).
   const float* T0 = t_saved;
   if (!T0) {
     if (P.sk) {
       int S;
-      if ((rc = skinny(CD, false, c.x, K, M, c.lora_a, K, M, r, K, part, &S, c.stream, QLORA_K_LORA_DOWN))) return rc;
+      if ((rc = skinny(CD, false, lx, K, M, c.lora_a, K, M, r, K, part, &S, c.stream, QLORA_K_LORA_DOWN))) return rc;
       if ((rc = skinny_reduce(CD, part, S, M, r, 1.0f, t0, false, 0.f, nullptr, 0, c.stream))) return rc;
-    } else if ((rc = lora_down<CD>(c, P.st, part, t0, 1.0f, nullptr, 0.f, 0))) {
+    } else if ((rc = lora_down<CD>(c, lx, P.st, part, t0, 1.0f, nullptr, 0.f, 0))) {
       return rc;
     }
     T0 = t0;
@@ -631,13 +648,19 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   }
 
   // dX = dY W~ + dT A (the contraction runs over W's rows): W~^T written once and a
-  // dense GEMM, or the fused dequant.
+  // dense GEMM, or the fused dequant.  With LoRA dropout the GEMM gets a zero dT
+  // (base product only) and the masked low-rank term is added afterwards.
+  const void* dt_gemm = dtcd;
+  if (dx && c.drop_mask) {
+    if ((rc = zero_fill(ws + P.off_zero, M * P.r_pad * cd_bytes(CD), c.stream))) return rc;
+    dt_gemm = ws + P.off_zero;
+  }
   if (dx && P.dense && dense256_ok(c, true)) {
     void* wdt = ws + P.off_wdt;
     if ((rc = dequant_into(c.w, CD, wdt, true, c.stream))) return rc;
-    if ((rc = dense256_dx(c, dy, wdt, dtcd, P.r_pad, dx))) return rc;
+    if ((rc = dense256_dx(c, dy, wdt, dt_gemm, P.r_pad, dx))) return rc;
   } else if (dx && fused256_ok(c, true)) {
-    rc = fused256_dx(c, dy, dtcd, P.r_pad, dx);
+    rc = fused256_dx(c, dy, dt_gemm, P.r_pad, dx);
     if (rc) return rc;
   } else if (dx) {
     GemmParams p = base_params(c);
@@ -645,7 +668,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     p.b1 = opnd<CD>(nullptr, 0, K, N);
     p.k1 = N;
     p.k1_chunk = round_up(N, Cfg<CD>::BK);
-    p.a2 = opnd<CD>(dtcd, P.r_pad, M, P.r_pad);
+    p.a2 = opnd<CD>(dt_gemm, P.r_pad, M, P.r_pad);
     p.b2 = opnd<CD>(c.lora_a, K, K, r);  // source [t][k]: transposed while staging
     p.k2 = P.r_pad;
     p.M = M;
@@ -655,18 +678,21 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     rc = run_gemm<CD, 128, 128, LK_ROWS, LK_NF4_COLS, LK_ROWS, LK_COLS, EPI_CD>(p, 1, QLORA_K_BWD_DX, c.stream);
     if (rc) return rc;
   }
+  if (dx && c.drop_mask &&
+      (rc = rank_add_masked(CD, dx, c.drop_mask, dtcd, P.r_pad, c.lora_a, r, M, K, c.stream)))
+    return rc;
 
   // dA = dT^T x  (contraction over tokens).
   if (P.sk) {
     void* dtt = ws + P.off_dtt;  // dT^T [r][m_pad] in cd (the operand the dX uses), zero past M
     if ((rc = transpose_small(CD, dtcd, false, P.r_pad, M, r, 1.0f, dtt, P.m_pad, c.stream))) return rc;
     int S;
-    if ((rc = skinny(CD, true, c.x, K, M, dtt, P.m_pad, K, r, P.m_pad, part, &S, c.stream, QLORA_K_BWD_DA))) return rc;
+    if ((rc = skinny(CD, true, lx, K, M, dtt, P.m_pad, K, r, P.m_pad, part, &S, c.stream, QLORA_K_BWD_DA))) return rc;
     if ((rc = skinny_reduce(CD, part, S, K, r, 1.0f, d_a, true, 0.f, nullptr, 0, c.stream))) return rc;
   } else {
     GemmParams p = base_params(c);
     p.a1 = opnd<CD>(dtcd, P.r_pad, r, M);  // source [m][t]
-    p.b1 = opnd<CD>(c.x, K, K, M);         // source [m][k]
+    p.b1 = opnd<CD>(lx, K, K, M);          // source [m][k]
     p.k1 = M;
     p.k1_chunk = P.sda.chunk;
     p.M = r;
@@ -713,7 +739,7 @@ size_t gemv_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, in
 constexpr int64_t kGemvMaxM = 16;
 
 size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
-  if (m <= kGemvMaxM) return gemv_workspace_bytes(m, rows, cols, r, cd);
+  if (m <= kGemvMaxM && !(flags & QLORA_FLAG_DROPOUT)) return gemv_workspace_bytes(m, rows, cols, r, cd);
   return (size_t)plan_fwd(m, rows, cols, r, cd, flags).total;
 }
 
@@ -722,7 +748,7 @@ size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int
 }
 
 int launch_forward(const LayerCall& c, void* y, float* t_save) {
-  if (c.m <= kGemvMaxM) return gemv_forward(c, y, t_save);
+  if (c.m <= kGemvMaxM && !c.drop_mask) return gemv_forward(c, y, t_save);
   switch (c.cd) {
     case CD_BF16: return forward_gemm<CD_BF16>(c, y, t_save);
     case CD_F16: return forward_gemm<CD_F16>(c, y, t_save);

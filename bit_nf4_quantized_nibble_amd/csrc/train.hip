@@ -180,6 +180,7 @@ int launch_stack_step(const qlora_stack_layer_t* layers, int32_t L, const void* 
     c.scale = scale;
     c.flags = flags;
     c.x = in;
+    c.drop_mask = nullptr;
     c.lora_a = layers[l].lora_a;
     c.lora_b = layers[l].lora_b;
     c.bias = nullptr;

@@ -180,3 +180,9 @@ def stack(dims: List[int], M: int, r: int = 16, seed: int = 0, cd: str = "bf16",
     x = randn(g, (M, dims[0]), 1.0, cd)
     target = randn(g, (M, dims[-1]), t_sigma, cd)
     return StackInputs(Ws, As, Bs, x, target, r, float(2 * r if alpha is None else alpha), cd)
+
+
+def dropout_mask(M: int, K: int, p: float, seed: int = 0) -> torch.Tensor:
+    """Keep mask of LoRA dropout: uint8 [M, K], 1 with probability 1 - p (uniform draws)."""
+    g = _gen(seed)
+    return (torch.rand(M, K, generator=g) >= p).to(torch.uint8)

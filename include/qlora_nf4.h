@@ -64,7 +64,8 @@ typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1, QLORA_F16 = 2 } qlora_dtype_t;
 enum {
   QLORA_FLAG_RSLORA = 1,       /* scale = alpha / sqrt(r) instead of alpha / r */
   QLORA_FLAG_FUSED = 2,
-  QLORA_FLAG_DEQUANT_GEMM = 4
+  QLORA_FLAG_DEQUANT_GEMM = 4,
+  QLORA_FLAG_DROPOUT = 8       /* workspace queries only: size for the *_dropout calls */
 };
 
 /* Workspace queries: op is QLORA_OP_FWD or QLORA_OP_BWD, OR'ed with the call's
@@ -260,6 +261,31 @@ int qlora_stack_train_step(const qlora_stack_layer_t* layers, int32_t n_layers, 
  * invalid query.  Pure host function. */
 size_t qlora_stack_workspace_bytes(const qlora_stack_layer_t* layers, int32_t n_layers, int64_t m, int32_t r,
                                    int32_t cd, int32_t flags);
+
+/*
+ * The layer with LoRA dropout (rust_ai_core QLoraConfig "Fields": the LoRA
+ * configuration holds rank, alpha and dropout; "LoRA and QLoRA, mathematically",
+ * "Tooling": PEFT's LoraConfig dropout).  Dropout acts on the input of the low-rank
+ * branch only, as inverted dropout with the caller's keep mask M and rate p:
+ *   y  = x W~^T + s (x_d A^T) B^T (+ bias),  x_d = x M / (1 - p),
+ *   dX = dY W~ + (dT A) M / (1 - p),  dA = dT^T x_d,  dB = s dY^T (x_d A^T),
+ * with dT = s dY B.  mask: device u8 [m, cols], nonzero = kept (the caller draws it,
+ * e.g. Bernoulli(1 - p), and passes the same mask to both calls); 0 <= p < 1.
+ * t_save / t_saved hold x_d A^T (1 - p), i.e. (x M) A^T.  The arguments are otherwise
+ * those of qlora_linear_fwd / qlora_linear_bwd; the workspace is
+ * qlora_workspace_bytes(op | (flags | QLORA_FLAG_DROPOUT) << QLORA_OP_FLAGS_SHIFT, ...)
+ * (x M is staged there; calls with m <= 16 take the GEMM path, not the decode GEMV).
+ * Errors: those of qlora_linear_fwd / _bwd, plus QLORA_ERR_INVALID_ARG for a null
+ * mask or p outside [0, 1).
+ */
+int qlora_linear_fwd_dropout(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
+                             const void* lora_b, int32_t r, float alpha, int32_t flags, const void* bias,
+                             int32_t cd, const uint8_t* mask, float p, void* y, float* t_save, void* ws,
+                             size_t ws_bytes, void* stream);
+int qlora_linear_bwd_dropout(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m,
+                             const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,
+                             int32_t cd, const uint8_t* mask, float p, const float* t_saved, void* dx,
+                             float* d_a, float* d_b, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace size in bytes for op (QLORA_OP_FWD / QLORA_OP_BWD, optionally OR'ed
  * with flags << QLORA_OP_FLAGS_SHIFT) on this layer shape; 0 for an invalid query.

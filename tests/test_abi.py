@@ -107,7 +107,8 @@ def fwd(lib, d, x=FAKE, m=128, a=FAKE, b=FAKE, r=8, alpha=16.0, flags=0, bias=No
     (dict(r=0), INVALID),
     (dict(alpha=float("nan")), INVALID),
     (dict(alpha=float("inf")), INVALID),
-    (dict(flags=8), INVALID),
+    (dict(flags=8), INVALID),                # the dropout flag needs the dropout entry point
+    (dict(flags=16), INVALID),
     (dict(flags=6), INVALID),                # both path flags
     (dict(x=None), INVALID),
     (dict(a=None), INVALID),
@@ -160,7 +161,12 @@ def test_workspace_query(lib):
     assert lib.qlora_workspace_bytes(0, 2048, 4096, 4096, 64, 1) == dense      # default at 2048 tokens
     assert lib.qlora_workspace_bytes(0, 512, 4096, 4096, 64, 1) == lib.qlora_workspace_bytes(2 << 8, 512, 4096, 4096, 64, 1)
     assert lib.qlora_workspace_bytes(1 | (4 << 8), 512, 4096, 4096, 64, 1) >= 4096 * 4096 * 2
-    assert lib.qlora_workspace_bytes(0 | (8 << 8), 512, 4096, 4096, 64, 1) == 0  # unknown flag
+    assert lib.qlora_workspace_bytes(0 | (16 << 8), 512, 4096, 4096, 64, 1) == 0  # unknown flag
+    # LoRA dropout stages x M (and, in the backward, a zero dT operand) in the workspace
+    for op in (0, 1):
+        plain = lib.qlora_workspace_bytes(op, 512, 4096, 4096, 64, 1)
+        assert lib.qlora_workspace_bytes(op | (8 << 8), 512, 4096, 4096, 64, 1) >= plain + 512 * 4096 * 2
+    assert lib.qlora_workspace_bytes(0 | (8 << 8), 4, 4096, 4096, 16, 1) >= 4 * 4096 * 2  # GEMM path, not GEMV
     assert lib.qlora_workspace_bytes(0 | (4 << 8), 512, 4096, 4096, 64, 0) == \
         lib.qlora_workspace_bytes(0 | (2 << 8), 512, 4096, 4096, 64, 0)       # f32 has no dense path
 
@@ -223,3 +229,20 @@ def test_training_entry_points_refuse_on_the_host(lib):
     assert lib.qlora_stack_workspace_bytes(L, 2, 16, 8, 1, 0) == 0
     assert lib.qlora_stack_workspace_bytes(L, 1, 16, 8, 1, 0) > 0
     assert lib.qlora_stack_train_step(*args(0)) == SHAPE
+
+
+def test_dropout_entry_points_refuse_on_the_host(lib):
+    d = desc()
+    f = lambda **kw: lib.qlora_linear_fwd_dropout(
+        ctypes.byref(d), FAKE, 128, FAKE, FAKE, 8, 16.0, 0, None, 1, kw.get("mask", FAKE), kw.get("p", 0.1), FAKE,
+        None, FAKE, 1 << 40, None)
+    assert f(mask=None) == INVALID
+    assert f(p=1.0) == INVALID
+    assert f(p=-0.1) == INVALID
+    assert f(p=float("nan")) == INVALID
+    b = lambda **kw: lib.qlora_linear_bwd_dropout(
+        ctypes.byref(d), FAKE, FAKE, 128, FAKE, FAKE, 8, 16.0, 0, 1, kw.get("mask", FAKE), kw.get("p", 0.1), None,
+        FAKE, FAKE, FAKE, FAKE, kw.get("ws_bytes", 1 << 40), None)
+    assert b(mask=None) == INVALID
+    assert b(p=1.5) == INVALID
+    assert b(ws_bytes=16) == WS
