@@ -201,22 +201,25 @@ template <int CD>
 __global__ __launch_bounds__(kThreads) void k_skreduce(const float* __restrict__ part, int S, int64_t P, int64_t R,
                                                        float sc32, float* __restrict__ out32, int trans, float sccd,
                                                        void* __restrict__ outcd, int64_t ldcd) {
-  const int64_t width = (outcd && ldcd > R) ? ldcd : R;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= P * width) return;
-  const int64_t pr = idx / width, t = idx % width;
-  if (t >= R) {
-    store_cd<CD>(outcd, pr * ldcd + t, 0.f);
+  // 32-bit indexing (the launcher checks P * width < 2^31)
+  const uint32_t width = (uint32_t)((outcd && ldcd > R) ? ldcd : R);
+  const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (uint32_t)P * width) return;
+  const uint32_t pr = idx / width, t = idx - pr * width;
+  if (t >= (uint32_t)R) {
+    store_cd<CD>(outcd, (int64_t)pr * ldcd + t, 0.f);
     return;
   }
+  // every slice's load leaves before the first add (slices past S read slice 0 and
+  // are dropped)
   float v[8];
 #pragma unroll
-  for (int z = 0; z < 8; ++z) v[z] = z < S ? part[((int64_t)z * P + pr) * BR + t] : 0.f;  // S <= 8
+  for (int z = 0; z < 8; ++z) v[z] = part[((uint32_t)(z < S ? z : 0) * (uint32_t)P + pr) * BR + t];  // S <= 8
   float sum = 0.f;
 #pragma unroll
-  for (int z = 0; z < 8; ++z) sum += v[z];  // slice order; the zeros past S do not change it
-  if (out32) out32[trans ? t * P + pr : pr * R + t] = sum * sc32;
-  if (outcd) store_cd<CD>(outcd, pr * ldcd + t, sum * sccd);
+  for (int z = 0; z < 8; ++z) sum += z < S ? v[z] : 0.f;  // slice order
+  if (out32) out32[trans ? (int64_t)t * P + pr : (int64_t)pr * R + t] = sum * sc32;
+  if (outcd) store_cd<CD>(outcd, (int64_t)pr * ldcd + t, sum * sccd);
 }
 
 // dst [cols][ld_dst] (cd) = cd(scale * src[rows][ld_src]^T), src in cd or fp32;
@@ -228,14 +231,24 @@ __global__ __launch_bounds__(kThreads) void k_transpose(const void* __restrict__
   __shared__ float t[64][65];
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int y = ty; y < 64; y += 4) {
-    const int64_t r = r0 + y, c = c0 + tx;
-    float v = 0.f;
-    if (r < rows && c < cols) v = SRC32 ? ((const float*)src)[r * ld_src + c] : load_cd<CD>(src, r * ld_src + c);
-    t[y][tx] = v * scale;
+  // all 16 loads of a thread leave before the first is used: out-of-range elements
+  // read element 0 and are replaced by zero afterwards
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
+    const int64_t at = (r < rows && c < cols) ? r * ld_src + c : 0;
+    v[i] = SRC32 ? ((const float*)src)[at] : load_cd<CD>(src, at);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
+    t[ty + 4 * i][tx] = (r < rows && c < cols) ? v[i] * scale : 0.f;
   }
   __syncthreads();
-  for (int y = ty; y < 64; y += 4) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int y = ty + 4 * i;
     const int64_t c = c0 + y, r = r0 + tx;
     if (c < cols && r < ld_dst) store_cd<CD>(dst, c * ld_dst + r, r < rows ? t[tx][y] : 0.f);
   }
@@ -305,6 +318,8 @@ int skinny_reduce(int cd, const float* part, int S, int64_t P, int64_t R, float 
   const int64_t width = (outcd && ldcd > R) ? ldcd : R;
   const int64_t n = P * width;
   if (n == 0) return QLORA_OK;
+  if (n >= (1LL << 31) || 8 * P * BR >= (1LL << 32))
+    return set_error(QLORA_ERR_UNSUPPORTED, "rank product: %lld x %lld too large", (long long)P, (long long)R);
   ProfScope prof(QLORA_K_REDUCE, s);
   const dim3 grid((unsigned)ceil_div(n, kThreads));
   if (cd == CD_BF16)
