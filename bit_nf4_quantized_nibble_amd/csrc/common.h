@@ -164,6 +164,17 @@ inline Nf4W make_w(const qlora_nf4_t* q) {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// Compute units of the current device (cached per device).
+int cu_count();
+
+// How the dense 256 x 256 GEMM spreads its tiles over the compute units: the
+// first `full` workgroups take whole tiles (whole rounds of one tile per CU); the
+// `rem` tiles of an incomplete last round are each cut into `split` contraction
+// slices (split 1, rem 0: no cut).
+struct DenseSplit {
+  int32_t full, rem, split;
+};
+
 // Launchers (quant.hip, gemm.hip, gemv.hip, merge.hip, train.hip).  Each returns a qlora_status_t.
 int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s);
 int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_t s);

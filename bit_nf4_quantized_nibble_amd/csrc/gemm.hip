@@ -44,8 +44,12 @@ int skinny_reduce(int cd, const float* part, int S, int64_t P, int64_t R, float 
                   float sccd, void* outcd, int64_t ldcd, hipStream_t s);
 int transpose_small(int cd, const void* src, bool src_f32, int64_t ld_src, int64_t rows, int64_t cols, float scale,
                     void* dst, int64_t ld_dst, hipStream_t s);
-int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y);
-int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx);
+int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y,
+                     const DenseSplit& sp, void* split_ws);
+int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx,
+                const DenseSplit& sp, void* split_ws);
+DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1);
+size_t dense_split_bytes(const DenseSplit& sp);
 
 namespace {
 
@@ -433,7 +437,8 @@ struct FwdPlan {
   int64_t r_pad;
   Split st;
   bool dense;
-  int64_t off_tcd, off_part, off_wd, off_xm, total;
+  DenseSplit dsp;  // cut of the dense GEMM's last round
+  int64_t off_tcd, off_part, off_wd, off_xm, off_split, total;
 };
 FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   FwdPlan P;
@@ -447,7 +452,9 @@ FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   P.off_wd = P.off_part + al(part);
   P.dense = dense_path(m, rows, cols, cd, flags, false);
   P.off_xm = P.off_wd + (P.dense ? al(rows * cols * es) : 0);  // x M with LoRA dropout
-  P.total = P.off_xm + ((flags & QLORA_FLAG_DROPOUT) ? al(m * cols * es) : 0);
+  P.off_split = P.off_xm + ((flags & QLORA_FLAG_DROPOUT) ? al(m * cols * es) : 0);
+  P.dsp = dense_split(m, rows, cols);
+  P.total = P.off_split + (P.dense ? al(dense_split_bytes(P.dsp)) : 0);
   return P;
 }
 
@@ -457,7 +464,8 @@ struct BwdPlan {
   bool dense;
   bool sk, sk_n;       // the skinny kernels take the rank products (dT and dB also need rows % 8)
   int64_t n_pad, m_pad;  // contractions rounded up to whole 64-element stages
-  int64_t off_t0, off_dt, off_dtcd, off_bt, off_dtt, off_t0t, off_part, off_wdt, off_xm, off_zero, total;
+  DenseSplit dsp;        // cut of the dense dX GEMM's last round
+  int64_t off_t0, off_dt, off_dtcd, off_bt, off_dtt, off_t0t, off_part, off_wdt, off_xm, off_zero, off_split, total;
 };
 BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   BwdPlan P;
@@ -496,7 +504,9 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   P.off_xm = P.off_wdt + (P.dense ? al(rows * cols * es) : 0);
   const bool drop = (flags & QLORA_FLAG_DROPOUT) != 0;
   P.off_zero = P.off_xm + (drop ? al(m * cols * es) : 0);
-  P.total = P.off_zero + (drop ? al(m * P.r_pad * es) : 0);
+  P.off_split = P.off_zero + (drop ? al(m * P.r_pad * es) : 0);
+  P.dsp = dense_split(m, cols, rows);
+  P.total = P.off_split + (P.dense ? al(dense_split_bytes(P.dsp)) : 0);
   return P;
 }
 
@@ -572,7 +582,7 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
   if (P.dense && dense256_ok(c, false)) {
     void* wd = ws + P.off_wd;
     if ((rc = dequant_into(c.w, CD, wd, false, c.stream))) return rc;
-    return dense256_forward(c, wd, tcd, P.r_pad, y);
+    return dense256_forward(c, wd, tcd, P.r_pad, y, P.dsp, ws + P.off_split);
   }
   if (fused256_ok(c, false)) return fused256_forward(c, tcd, P.r_pad, y);
 
@@ -658,7 +668,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   if (dx && P.dense && dense256_ok(c, true)) {
     void* wdt = ws + P.off_wdt;
     if ((rc = dequant_into(c.w, CD, wdt, true, c.stream))) return rc;
-    if ((rc = dense256_dx(c, dy, wdt, dt_gemm, P.r_pad, dx))) return rc;
+    if ((rc = dense256_dx(c, dy, wdt, dt_gemm, P.r_pad, dx, P.dsp, ws + P.off_split))) return rc;
   } else if (dx && fused256_ok(c, true)) {
     rc = fused256_dx(c, dy, dt_gemm, P.r_pad, dx);
     if (rc) return rc;

@@ -35,6 +35,8 @@
 // The workgroup -> tile map keeps the tiles that run concurrently on one XCD
 // (workgroups b, b + 8, ... share an XCD) in the same row block, so their common
 // activation tile stays in that XCD's L2.
+#include <algorithm>
+
 #include "common.h"
 
 namespace qnf4 {
@@ -63,7 +65,13 @@ struct Big {
   int32_t tiles_m, tiles_n;
   void* out;          // [M, NB] cd
   const void* bias;   // [NB] cd (fwd) or null
+  // Dense kernel only: workgroups [0, full) take whole tiles; the next rem * split
+  // take one contraction slice each of the tiles full .. full + rem - 1 (an
+  // incomplete last round) and leave fp32 partial sums for k_split_sum.
+  int32_t full, rem, split;
+  float* part;        // [rem][split][kTileAcc] fp32, in accumulator order
 };
+constexpr int kTileAcc = TILE * TILE;  // accumulators of one tile
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;
@@ -102,15 +110,34 @@ __device__ __forceinline__ int chunk_addr(int row, int c) { return row * ROWB + 
 // block (4 x 8 tiles for a 16 x 16 grid) and its L2 sees fewer distinct operand
 // tiles per stage than with whole tile rows.
 constexpr int kGroupM = 4;
-__device__ __forceinline__ void tile_of(const Big& p, int& tm, int& tn) {
-  const int b = blockIdx.x;
-  const int T = p.tiles_m * p.tiles_n;
-  int t = b;
-  if ((T & 7) == 0) t = (b & 7) * (T >> 3) + (b >> 3);  // XCD-contiguous chunks
+// Position of workgroup b among n consecutive ones when each XCD takes a
+// contiguous chunk of n / 8 positions.
+__device__ __forceinline__ int xcd_chunk(int b, int n) { return (n & 7) == 0 ? (b & 7) * (n >> 3) + (b >> 3) : b; }
+// Tile t of the grouped order.
+__device__ __forceinline__ void grouped_tile(const Big& p, int t, int& tm, int& tn) {
   const int per = kGroupM * p.tiles_n, g = t / per, u = t % per;
   const int gm = min(kGroupM, p.tiles_m - g * kGroupM);
   tm = g * kGroupM + u % gm;
   tn = u / gm;
+}
+__device__ __forceinline__ void tile_of(const Big& p, int& tm, int& tn) {
+  grouped_tile(p, xcd_chunk(blockIdx.x, p.tiles_m * p.tiles_n), tm, tn);
+}
+// Dense kernel: workgroup -> (tile, contraction slice, index among the cut tiles
+// or -1).  The slices of the cut tiles follow the whole tiles; each XCD's chunk of
+// them is one slice of a run of consecutive tiles of the grouped order.
+__device__ __forceinline__ void item_of(const Big& p, int& tm, int& tn, int& slice, int& rt) {
+  const int b = blockIdx.x;
+  slice = 0;
+  rt = -1;
+  if (b < p.full) {
+    grouped_tile(p, xcd_chunk(b, p.full), tm, tn);
+    return;
+  }
+  const int u = xcd_chunk(b - p.full, p.rem * p.split);
+  slice = u / p.rem;
+  rt = u - slice * p.rem;
+  grouped_tile(p, p.full + rt, tm, tn);
 }
 
 // The NF4 codes (and raw block scales) a lane fetches for one stage.
@@ -506,6 +533,46 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Big&
   }
 }
 
+__device__ __forceinline__ f32x4_t acc4(const f32x16_t& a, int q) {
+  f32x4_t v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+  return v;
+}
+
+// Partial sums of a cut tile's slice: block b = 16 i + 4 j + q of the wave
+// accumulators (rows 8 q + 4 h .. + 3 of MFMA block (i, j)) of thread tid at
+// float (b * 256 + tid) * 4, so every 16-byte store instruction is contiguous.
+__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[4][4], float* dst, int tid) {
+  const rsrc_t r = make_rsrc(dst, kTileAcc * 4);
+#pragma unroll
+  for (int b = 0; b < 64; ++b)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc4(acc[b >> 4][(b >> 2) & 3], b & 3)), r,
+                                           tid * 16, b * 4096, 0);
+}
+
+// The cut tiles' outputs: workgroup (b, rt) sums block b of cut tile rt over its
+// slices in slice order, adds the bias and writes the compute dtype.
+template <int CD, int S>
+__global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
+  const int b = blockIdx.x, rt = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* src = p.part + (size_t)rt * S * kTileAcc + (b * 256 + tid) * 4;
+  f32x4_t v[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) v[s] = *(const f32x4_t*)(src + (size_t)s * kTileAcc);
+  f32x4_t t = v[0];
+#pragma unroll
+  for (int s = 1; s < S; ++s) t = t + v[s];
+  int tm, tn;
+  grouped_tile(p, p.full + rt, tm, tn);
+  const int i = b >> 4, j = (b >> 2) & 3, q = b & 3;
+  const int64_t col = (int64_t)tn * TILE + (wave & 1) * 128 + 32 * j + (lane & 31);
+  if (col >= p.NB) return;
+  const float bias = p.bias ? load_cd<CD>(p.bias, col) : 0.f;
+  const int64_t row0 = (int64_t)tm * TILE + (wave >> 1) * 128 + 32 * i + 8 * q + 4 * (lane >> 5);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (row0 + e < p.M) store_cd<CD>(p.out, (row0 + e) * p.NB + col, t[e] + bias);
+}
+
 template <int CD, int MODE, int DQ>
 __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) {
   // [A0 | A1 | B0 | B1 | levels]
@@ -656,8 +723,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
   __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int tm, tn;
-  tile_of(p, tm, tn);
+  int tm, tn, slice, rt;
+  item_of(p, tm, tn, slice, rt);
   const int64_t m0 = (int64_t)tm * TILE, n0 = (int64_t)tn * TILE;
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int h = lane >> 5;
@@ -681,30 +748,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const uint32_t KT = (uint32_t)(p.K1 / BK);  // K1 is a multiple of 64 here
+  // Stages [k0, k1) of the contraction (K1 is a multiple of 64 here): all of them
+  // for a whole tile, slice `slice` of split for a cut one.
+  const uint32_t KT = (uint32_t)(p.K1 / BK);
+  uint32_t k0 = 0, k1 = KT;
+  if (rt >= 0) {
+    k0 = (uint32_t)slice * KT / (uint32_t)p.split;
+    k1 = (uint32_t)(slice + 1) * KT / (uint32_t)p.split;
+  }
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(lds + (4 * d + wave) * 1024), 16, (int)(a_off + d * a_step),
-                                             0, 0, 0);
+                                             (int)(k0 * (BK * 2)), 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + 2 * TILE_BYTES + (4 * d + wave) * 1024), 16,
-                                             (int)(b_off + d * b_step), 0, 0, 0);
+                                             (int)(b_off + d * b_step), (int)(k0 * (BK * 2)), 0, 0);
   }
   // a_step == b_step only when ld_a1 == K1, which holds for both uses (x [M, K]
   // against W~ [N, K]; dY [M, N] against W~^T [K, N]).
-  uint32_t k = 0;
-  for (; k + 1 < KT; ++k) {
+  uint32_t k = k0;
+  for (; k + 1 < k1; ++k) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of stage k and its fragment reads
     barrier_only();
-    dense_stage<CD, 1>(acc, lds, k & 1, ra, rb, a_off, b_off, a_step, wave, k + 1, a_row, b_row, xr, h);
+    dense_stage<CD, 1>(acc, lds, (k - k0) & 1, ra, rb, a_off, b_off, a_step, wave, k + 1, a_row, b_row, xr, h);
   }
   __builtin_amdgcn_s_waitcnt(0);
   barrier_only();
-  dense_stage<CD, 0>(acc, lds, k & 1, ra, rb, a_off, b_off, a_step, wave, 0, a_row, b_row, xr, h);
+  dense_stage<CD, 0>(acc, lds, (k - k0) & 1, ra, rb, a_off, b_off, a_step, wave, 0, a_row, b_row, xr, h);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  lora_segment<CD, MODE>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
-  epilogue<CD>(acc, p, m0, n0, wm, wn, lane, h);
+  // the low-rank tail joins the last slice (or the whole tile)
+  if (rt < 0 || slice == p.split - 1) lora_segment<CD, MODE>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+  if (rt < 0) epilogue<CD>(acc, p, m0, n0, wm, wn, lane, h);
+  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, tid);
 }
 
 template <int CD, int MODE>
@@ -718,12 +794,26 @@ int run(const Big& b, hipStream_t s, int kind) {
   return check_launch(MODE == MODE_FWD ? "k_fused256<fwd>" : "k_fused256<dx>");
 }
 
+// The dense GEMM, and for a cut last round the sum of its slices (both inside one
+// profiling scope: together they are the GEMM).
 template <int CD, int MODE>
 int run_dense(const Big& b, const void* bd, hipStream_t s, int kind) {
-  const int64_t tiles = (int64_t)b.tiles_m * b.tiles_n;
+  const int64_t items = (int64_t)b.full + (int64_t)b.rem * b.split;
   ProfScope prof(kind, s);
-  k_dense256<CD, MODE><<<dim3((unsigned)tiles), dim3(kThreads), 0, s>>>(b, bd);
-  return check_launch(MODE == MODE_FWD ? "k_dense256<fwd>" : "k_dense256<dx>");
+  k_dense256<CD, MODE><<<dim3((unsigned)items), dim3(kThreads), 0, s>>>(b, bd);
+  int rc = check_launch(MODE == MODE_FWD ? "k_dense256<fwd>" : "k_dense256<dx>");
+  if (rc || !b.rem) return rc;
+  const dim3 g(kTileAcc / (4 * kThreads), (unsigned)b.rem);
+  if (b.split == 2) k_split_sum<CD, 2><<<g, dim3(kThreads), 0, s>>>(b);
+  else k_split_sum<CD, 4><<<g, dim3(kThreads), 0, s>>>(b);
+  return check_launch("k_split_sum");
+}
+
+void set_split(Big& b, const DenseSplit& sp, void* split_ws) {
+  b.full = sp.full;
+  b.rem = sp.rem;
+  b.split = sp.split;
+  b.part = (float*)split_ws;
 }
 
 bool fits_buffers(const LayerCall& c, int64_t a1_bytes) {
@@ -785,6 +875,27 @@ int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r
   return run<CD_F16, MODE_DX>(b, c.stream, QLORA_K_BWD_DX);
 }
 
+// One round is a tile per compute unit (the kernel needs most of a CU's LDS).  When
+// the last round is incomplete, its rem tiles are cut into split = 2 or 4
+// contraction slices (the largest that keeps rem * split within one round and at
+// least 4 stages per slice), so the round's workgroups run about 1 / split as long.
+DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1) {
+  const int64_t C = cu_count();
+  const int64_t tiles = ceil_div(m, TILE) * ceil_div(nb, TILE);
+  DenseSplit d = {(int32_t)tiles, 0, 1};
+  const int64_t F = tiles / C, R = tiles - F * C;
+  if (R == 0) return d;
+  const int64_t cap = std::min<int64_t>(C / R, (k1 / BK) / 4);
+  const int32_t S = cap >= 4 ? 4 : (cap >= 2 ? 2 : 1);
+  if (S == 1) return d;
+  d.full = (int32_t)(F * C);
+  d.rem = (int32_t)R;
+  d.split = S;
+  return d;
+}
+
+size_t dense_split_bytes(const DenseSplit& sp) { return (size_t)sp.rem * sp.split * kTileAcc * 4; }
+
 // Whether the dense (dequantize-then-GEMM) kernels take this layer: the same
 // shapes as the fused ones, and the dequantized copy must fit a buffer resource.
 bool dense256_ok(const LayerCall& c, bool dx) {
@@ -792,8 +903,10 @@ bool dense256_ok(const LayerCall& c, bool dx) {
   return c.w.rows * c.w.cols * 2 < 0x7fff0000LL && (c.w.cols % BK == 0) && (c.w.rows % BK == 0 || !dx);
 }
 
-// y = [x | T][W~ | B]^T + bias with W~ [N, K] already in the compute dtype.
-int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y) {
+// y = [x | T][W~ | B]^T + bias with W~ [N, K] already in the compute dtype.  sp:
+// dense_split(m, rows, cols); split_ws: dense_split_bytes(sp) bytes.
+int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y,
+                     const DenseSplit& sp, void* split_ws) {
   Big b = {};
   b.a1 = c.x;
   b.ld_a1 = c.w.cols;
@@ -809,12 +922,15 @@ int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64
   b.tiles_n = (int32_t)ceil_div(c.w.rows, TILE);
   b.out = y;
   b.bias = c.bias;
+  set_split(b, sp, split_ws);
   if (c.cd == CD_BF16) return run_dense<CD_BF16, MODE_FWD>(b, wd, c.stream, QLORA_K_FWD_GEMM);
   return run_dense<CD_F16, MODE_FWD>(b, wd, c.stream, QLORA_K_FWD_GEMM);
 }
 
-// dX = [dY | dT][W~ ; A] with W~^T [K, N] already in the compute dtype.
-int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx) {
+// dX = [dY | dT][W~ ; A] with W~^T [K, N] already in the compute dtype.  sp:
+// dense_split(m, cols, rows); split_ws as for the forward.
+int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx,
+                const DenseSplit& sp, void* split_ws) {
   Big b = {};
   b.a1 = dy;
   b.ld_a1 = c.w.rows;
@@ -830,6 +946,7 @@ int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void*
   b.tiles_n = (int32_t)ceil_div(c.w.cols, TILE);
   b.out = dx;
   b.bias = nullptr;
+  set_split(b, sp, split_ws);
   if (c.cd == CD_BF16) return run_dense<CD_BF16, MODE_DX>(b, wdt, c.stream, QLORA_K_BWD_DX);
   return run_dense<CD_F16, MODE_DX>(b, wdt, c.stream, QLORA_K_BWD_DX);
 }

@@ -363,20 +363,6 @@ __global__ __launch_bounds__(256) void k_merge_generic(GenP p, Nf4Tables tab) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-// Compute units of the current device (cached per device).
-int cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev >= 0 && dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 }  // namespace
 
