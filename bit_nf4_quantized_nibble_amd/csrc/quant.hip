@@ -246,11 +246,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* ptr, int64_t bytes) {
 struct ScaleRsrc {
   rsrc_t q, s2;
 };
+// With double quantization the group size is a power of two (g_shift) or one group
+// holds every block (g_shift 31): ceil(nb / g) = ((nb - 1) >> g_shift) + 1.
 template <int DQ>
 __device__ __forceinline__ ScaleRsrc make_scale_rsrc(const Nf4W& w, int64_t nb) {
   ScaleRsrc r;
   r.q = DQ ? make_rsrc(w.absmax_q, nb) : make_rsrc(w.absmax, nb * 4);
-  r.s2 = DQ ? make_rsrc(w.scale2, ((nb + w.g - 1) / w.g) * 4) : r.q;
+  r.s2 = DQ ? make_rsrc(w.scale2, (((nb - 1) >> w.g_shift) + 1) * 4) : r.q;
   return r;
 }
 template <int DQ>
@@ -321,49 +323,69 @@ __global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, 
 
 // Transposed dequantize for the dequantize-then-GEMM backward: out [cols, rows] =
 // RNE_cd(fl32(L[c] * s_b))^T, the same values as k_dequantize.  One workgroup per
-// 64 x 64 tile of W: each lane decodes 16 consecutive codes of one W row into an
-// LDS tile [k][n], then writes 16 consecutive elements of one output row.  Tile
-// rows are 128 bytes; 16-byte chunk c of row k sits at c ^ 2 ((k >> 4) & 3), so the
-// four column groups of a 2-byte write instruction land on distinct banks.
-// rows and cols are multiples of 64, the block size a power of two >= 8 (with double
-// quantization a power-of-two group or one group), codes under 2 GiB (checked by
-// the caller).
-template <int OUT, int DQ>
+// 64 x 64 T slab of W (T tiles of 64 x 64 along its columns).  Each lane requests
+// the codes (16 consecutive codes of one W row per tile) and block scales of all
+// T tiles before it decodes the first, decodes them into LDS tiles [k][n], and
+// after one barrier writes 16 elements of one output row per tile.
+// Tile rows are 128 bytes; 16-byte chunk c of row k sits at c ^ 2 ((k >> 4) & 3),
+// so the four column groups of a 2-byte write instruction land on distinct banks.
+// rows and cols are multiples of 64, the block size a power of two >= 8 (with
+// double quantization a power-of-two group or one group), codes under 2 GiB
+// (checked by the caller).  Tiles past the last column load the first codes
+// (unused) and write nothing.
+template <int OUT, int DQ, int T>
 __global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restrict__ out, Nf4Tables tab) {
   __shared__ float s_lv[16];
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];  // [k][n]
+  __shared__ __attribute__((aligned(16))) uint16_t tile[T][64 * 64];  // [k][n] per tile
   const int tid = threadIdx.x;
   if (tid < 16) s_lv[tid] = tab.lv[tid];
   const int64_t n = q.rows * q.cols;
   const rsrc_t rc = make_rsrc(q.codes, n / 2);
   const ScaleRsrc rs = make_scale_rsrc<DQ>(q, n >> q.bs_shift);
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  const int64_t n0 = (int64_t)blockIdx.y * 64, kb = (int64_t)blockIdx.x * (64 * T);
   const int nr = tid >> 2, kc = (tid & 3) * 16;
-  const int64_t e0 = (n0 + nr) * q.cols + k0 + kc;
-  const uint32_t cw0 = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(uint32_t)(e0 / 2), 0, 0);
-  const uint32_t cw1 = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(uint32_t)(e0 / 2 + 4), 0, 0);
-  uint32_t qa[2], s2[2];
-  load_scale<DQ>(rs, q, (uint32_t)(e0 >> q.bs_shift), qa[0], s2[0]);
-  load_scale<DQ>(rs, q, (uint32_t)((e0 + 8) >> q.bs_shift), qa[1], s2[1]);
+  uint32_t cw[T][2], qa[T][2], s2[T][2];
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    const bool ok = kb + 64 * u < q.cols;  // the same for the whole workgroup
+    const int64_t e0 = (n0 + nr) * q.cols + kb + 64 * u + kc;
+    const uint32_t co = ok ? (uint32_t)(e0 / 2) : 0u;
+    cw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)co, 0, 0);
+    cw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(co + 4), 0, 0);
+    const uint32_t b0 = ok ? (uint32_t)(e0 >> q.bs_shift) : 0u;
+    const uint32_t b1 = ok ? (uint32_t)((e0 + 8) >> q.bs_shift) : 0u;
+    load_scale<DQ>(rs, q, b0, qa[u][0], s2[u][0]);
+    load_scale<DQ>(rs, q, b1, qa[u][1], s2[u][1]);
+  }
   __syncthreads();
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const uint32_t word = hf ? cw1 : cw0;
-    const float s = scale_of<DQ>(qa[hf], s2[hf]);
+  for (int u = 0; u < T; ++u) {
+    if (kb + 64 * u >= q.cols) break;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t c = (word >> ((j >> 1) * 8 + ((j & 1) ? 0 : 4))) & 15u;
-      const int k = kc + 8 * hf + j;
-      tile[k * 64 + ((((nr >> 3) ^ (2 * ((k >> 4) & 3)))) << 3) + (nr & 7)] = to_cd16<OUT>(fl32_mul(s_lv[c], s));
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint32_t word = cw[u][hf];
+      const float s = scale_of<DQ>(qa[u][hf], s2[u][hf]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t c = (word >> ((j >> 1) * 8 + ((j & 1) ? 0 : 4))) & 15u;
+        const int k = kc + 8 * hf + j;
+        tile[u][k * 64 + ((((nr >> 3) ^ (2 * ((k >> 4) & 3)))) << 3) + (nr & 7)] = to_cd16<OUT>(fl32_mul(s_lv[c], s));
+      }
     }
   }
   __syncthreads();
-  const int kr = tid >> 2, c2 = (tid & 3) * 2, sw = 2 * ((kr >> 4) & 3);
-  const u32x4_t v0 = *(const u32x4_t*)&tile[kr * 64 + ((c2 ^ sw) << 3)];
-  const u32x4_t v1 = *(const u32x4_t*)&tile[kr * 64 + (((c2 + 1) ^ sw) << 3)];
-  uint16_t* o = (uint16_t*)out + (k0 + kr) * q.rows + n0 + 8 * c2;
-  *(u32x4_t*)o = v0;
-  *(u32x4_t*)(o + 8) = v1;
+  // lanes 4 kr .. 4 kr + 3 write output row kr: chunks 0..3 (64 contiguous bytes)
+  // with one instruction, chunks 4..7 with the next
+  const int kr = tid >> 2, ca = tid & 3, sw = 2 * ((kr >> 4) & 3);
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    if (kb + 64 * u >= q.cols) break;
+    const u32x4_t v0 = *(const u32x4_t*)&tile[u][kr * 64 + ((ca ^ sw) << 3)];
+    const u32x4_t v1 = *(const u32x4_t*)&tile[u][kr * 64 + (((ca + 4) ^ sw) << 3)];
+    uint16_t* o = (uint16_t*)out + (kb + 64 * u + kr) * q.rows + n0 + 8 * ca;
+    *(u32x4_t*)o = v0;
+    *(u32x4_t*)(o + 32) = v1;
+  }
 }
 
 int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s) {
@@ -446,6 +468,12 @@ int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s) {
   return check_launch("k_dequantize");
 }
 
+template <int OUT, int DQ>
+void run_dqt(bool four, dim3 grid, const Nf4W& w, void* out, const Nf4Tables& t, hipStream_t s) {
+  if (four) k_dequantize_t<OUT, DQ, 4><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+  else k_dequantize_t<OUT, DQ, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+}
+
 // Dequantize W into a compute-dtype buffer inside a layer call: [rows, cols]
 // (forward) or its transpose [cols, rows] (dX).  The transpose needs rows and cols
 // to be multiples of 64.
@@ -456,13 +484,15 @@ int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t 
     if (w.rows % 64 || w.cols % 64) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: shape not a multiple of 64");
     if (w.bs_shift < 3 || (w.dq && w.g_shift < 0) || w.rows * w.cols / 2 >= (1LL << 31))
       return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: block / group sizes or size not supported");
-    const dim3 grid((unsigned)(w.cols / 64), (unsigned)(w.rows / 64));
+    // four tiles per workgroup while that still leaves >= 1024 workgroups, else one
+    const int T4 = (w.rows / 64) * ceil_div(w.cols, 256) >= 1024;
+    const dim3 grid((unsigned)ceil_div(w.cols, T4 ? 256 : 64), (unsigned)(w.rows / 64));
     if (cd == CD_BF16) {
-      if (w.dq) k_dequantize_t<CD_BF16, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
-      else k_dequantize_t<CD_BF16, 0><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+      if (w.dq) run_dqt<CD_BF16, 1>(T4, grid, w, out, t, s);
+      else run_dqt<CD_BF16, 0>(T4, grid, w, out, t, s);
     } else if (cd == CD_F16) {
-      if (w.dq) k_dequantize_t<CD_F16, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
-      else k_dequantize_t<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+      if (w.dq) run_dqt<CD_F16, 1>(T4, grid, w, out, t, s);
+      else run_dqt<CD_F16, 0>(T4, grid, w, out, t, s);
     }
     else return set_error(QLORA_ERR_DTYPE, "dequantize^T: bad dtype %d", cd);
     return check_launch("k_dequantize_t");
