@@ -197,6 +197,30 @@ struct LayerCall {
   hipStream_t stream;
 };
 
+// One reduction of the skinny kernel's per-slice partial sums part [S][P][64] (fp32,
+// summed in slice order): out32 = sc32 * sum as [P][R] (or [R][P] with trans);
+// outcd [P][ldcd] = cd(sccd * sum) with zero columns R .. ldcd-1; outt [R][ldt] =
+// the transpose of that cd value with zero columns P .. ldt-1; side_t [R][ldt] =
+// cd(side [P][R])^T with zero columns P .. ldt-1 (a transpose that shares the
+// launch).  Null outputs are skipped.
+struct SkRed {
+  const float* part = nullptr;
+  int S = 1;
+  int64_t P = 0, R = 0;
+  float sc32 = 1.f;
+  float* out32 = nullptr;
+  bool trans = false;
+  float sccd = 1.f;
+  void* outcd = nullptr;
+  int64_t ldcd = 0;
+  void* outt = nullptr;
+  int64_t ldt = 0;
+  const float* side = nullptr;
+  void* side_t = nullptr;
+};
+// One launch for one or two reductions (b may be null).
+int skinny_reduce_jobs(int cd, const SkRed& a, const SkRed* b, hipStream_t s);
+
 int apply_mask(int cd, const void* x, const uint8_t* mask, int64_t n, void* out, hipStream_t s);
 int zero_fill(void* p, int64_t bytes, hipStream_t s);
 int rank_add_masked(int cd, void* dx, const uint8_t* mask, const void* dt, int64_t ld_dt, const void* a, int32_t r,

@@ -465,7 +465,8 @@ struct BwdPlan {
   bool sk, sk_n;       // the skinny kernels take the rank products (dT and dB also need rows % 8)
   int64_t n_pad, m_pad;  // contractions rounded up to whole 64-element stages
   DenseSplit dsp;        // cut of the dense dX GEMM's last round
-  int64_t off_t0, off_dt, off_dtcd, off_bt, off_dtt, off_t0t, off_part, off_wdt, off_xm, off_zero, off_split, total;
+  int64_t off_t0, off_dt, off_dtcd, off_bt, off_dtt, off_t0t, off_part, off_part2, off_wdt, off_xm, off_zero, off_split,
+      total;
 };
 BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   BwdPlan P;
@@ -498,7 +499,9 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
     part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(m, P.n_pad));     // dT
     part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(rows, P.m_pad));  // dB
   }
-  P.off_wdt = P.off_part + al(part);
+  // dB's partial sums live beside dA's so that one launch reduces both
+  P.off_part2 = P.off_part + al(part);
+  P.off_wdt = P.off_part2 + (P.sk_n ? al((int64_t)skinny_part_bytes(rows, P.m_pad)) : 0);
   P.dense = dense_path(m, rows, cols, cd, flags, true);
   // with LoRA dropout: x M, and a zero [m, r_pad] operand for the base-only dX GEMM
   P.off_xm = P.off_wdt + (P.dense ? al(rows * cols * es) : 0);
@@ -633,13 +636,31 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     T0 = t0;
   }
 
-  // dT = s dY B  -> fp32 [M, r] and a compute-dtype copy [M, r_pad].
+  // dT = s dY B  -> fp32 [M, r] and a compute-dtype copy [M, r_pad].  On the skinny
+  // path the same launch writes the operands of dA and dB: dT^T [r][m_pad] (the cd
+  // copy transposed) and T0^T [r][m_pad] rounded to cd, both zero past M.
+  void* dtt = ws + P.off_dtt;
+  void* t0t = ws + P.off_t0t;
   if (P.sk_n) {
     void* bt = ws + P.off_bt;  // B^T [r][n_pad], zero past N
     if ((rc = transpose_small(CD, c.lora_b, false, r, N, r, 1.0f, bt, P.n_pad, c.stream))) return rc;
     int S;
     if ((rc = skinny(CD, false, dy, N, M, bt, P.n_pad, M, r, P.n_pad, part, &S, c.stream, QLORA_K_BWD_DT))) return rc;
-    if ((rc = skinny_reduce(CD, part, S, M, r, c.scale, dt, false, c.scale, dtcd, P.r_pad, c.stream))) return rc;
+    SkRed red;
+    red.part = part;
+    red.S = S;
+    red.P = M;
+    red.R = r;
+    red.sc32 = c.scale;
+    red.out32 = dt;
+    red.sccd = c.scale;
+    red.outcd = dtcd;
+    red.ldcd = P.r_pad;
+    red.outt = dtt;
+    red.ldt = P.m_pad;
+    red.side = T0;
+    red.side_t = t0t;
+    if ((rc = skinny_reduce_jobs(CD, red, nullptr, c.stream))) return rc;
   } else {
     GemmParams p = base_params(c);
     p.a1 = opnd<CD>(dy, N, M, N);
@@ -692,9 +713,32 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
       (rc = rank_add_masked(CD, dx, c.drop_mask, dtcd, P.r_pad, c.lora_a, r, M, K, c.stream)))
     return rc;
 
+  // dA = dT^T x and dB = s dY^T T0 (contractions over tokens): on the skinny path
+  // both products, then one launch that reduces both.
+  if (P.sk_n) {
+    float* part2 = (float*)(ws + P.off_part2);
+    int Sa, Sb;
+    if ((rc = skinny(CD, true, lx, K, M, dtt, P.m_pad, K, r, P.m_pad, part, &Sa, c.stream, QLORA_K_BWD_DA))) return rc;
+    if ((rc = skinny(CD, true, dy, N, M, t0t, P.m_pad, N, r, P.m_pad, part2, &Sb, c.stream, QLORA_K_BWD_DB)))
+      return rc;
+    SkRed ra, rb;
+    ra.part = part;
+    ra.S = Sa;
+    ra.P = K;
+    ra.R = r;
+    ra.out32 = d_a;
+    ra.trans = true;
+    rb.part = part2;
+    rb.S = Sb;
+    rb.P = N;
+    rb.R = r;
+    rb.sc32 = c.scale;
+    rb.out32 = d_b;
+    return skinny_reduce_jobs(CD, ra, &rb, c.stream);
+  }
   // dA = dT^T x  (contraction over tokens).
   if (P.sk) {
-    void* dtt = ws + P.off_dtt;  // dT^T [r][m_pad] in cd (the operand the dX uses), zero past M
+    // dT^T [r][m_pad] in cd (the operand the dX uses), zero past M
     if ((rc = transpose_small(CD, dtcd, false, P.r_pad, M, r, 1.0f, dtt, P.m_pad, c.stream))) return rc;
     int S;
     if ((rc = skinny(CD, true, lx, K, M, dtt, P.m_pad, K, r, P.m_pad, part, &S, c.stream, QLORA_K_BWD_DA))) return rc;
@@ -716,14 +760,8 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     if (rc) return rc;
   }
 
-  // dB = s dY^T T0  (contraction over tokens).
-  if (P.sk_n) {
-    void* t0t = ws + P.off_t0t;  // T0^T [r][m_pad] rounded to cd, zero past M
-    if ((rc = transpose_small(CD, T0, true, r, M, r, 1.0f, t0t, P.m_pad, c.stream))) return rc;
-    int S;
-    if ((rc = skinny(CD, true, dy, N, M, t0t, P.m_pad, N, r, P.m_pad, part, &S, c.stream, QLORA_K_BWD_DB))) return rc;
-    if ((rc = skinny_reduce(CD, part, S, N, r, c.scale, d_b, false, 0.f, nullptr, 0, c.stream))) return rc;
-  } else {
+  // dB = s dY^T T0  (contraction over tokens; the skinny case returned above).
+  {
     GemmParams p = base_params(c);
     p.a1 = opnd<CD>(dy, N, N, M);         // source [m][n]
     p.b1 = opnd<CD>(T0, r, r, M, 4);      // fp32 source [m][t]

@@ -195,31 +195,56 @@ __global__ __launch_bounds__(kThreads) void k_skinny(SkP p) {
     }
 }
 
-// out32 = sc32 * sum over slices (in slice order), [P][R] or transposed [R][P];
-// outcd [P][ldcd] = cd(sccd * sum), its columns R .. ldcd-1 zero.
+// Reductions of per-slice partial sums (see SkRed), one thread per element of a
+// rows x width grid (rows: P, or ldt with a transposed output; width: R, or ldcd
+// with a padded cd output); workgroups [0, nblk of job 0) take job 0, the rest
+// job 1.  32-bit indexing (the launcher checks the sizes).
+struct RedJob {
+  const float* part;
+  const float* side;
+  float* out32;
+  void* outcd;
+  void* outt;
+  void* side_t;
+  uint32_t S, P, R, ldcd, ldt, width, rows, nblk;
+  float sc32, sccd;
+  int trans;
+};
+struct RedJobs {
+  RedJob j[2];
+};
+
 template <int CD>
-__global__ __launch_bounds__(kThreads) void k_skreduce(const float* __restrict__ part, int S, int64_t P, int64_t R,
-                                                       float sc32, float* __restrict__ out32, int trans, float sccd,
-                                                       void* __restrict__ outcd, int64_t ldcd) {
-  // 32-bit indexing (the launcher checks P * width < 2^31)
-  const uint32_t width = (uint32_t)((outcd && ldcd > R) ? ldcd : R);
-  const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (uint32_t)P * width) return;
-  const uint32_t pr = idx / width, t = idx - pr * width;
-  if (t >= (uint32_t)R) {
-    store_cd<CD>(outcd, (int64_t)pr * ldcd + t, 0.f);
+__global__ __launch_bounds__(kThreads) void k_skreduce(RedJobs js) {
+  const int w = blockIdx.x >= js.j[0].nblk ? 1 : 0;
+  const RedJob& j = js.j[w];
+  const uint32_t idx = (blockIdx.x - (w ? js.j[0].nblk : 0u)) * kThreads + threadIdx.x;
+  if (idx >= j.rows * j.width) return;
+  const uint32_t pr = idx / j.width, t = idx - pr * j.width;
+  if (pr >= j.P) {  // zero columns P .. ldt-1 of the transposed copies
+    if (t < j.R) {
+      if (j.outt) store_cd<CD>(j.outt, (int64_t)(t * j.ldt + pr), 0.f);
+      if (j.side_t) store_cd<CD>(j.side_t, (int64_t)(t * j.ldt + pr), 0.f);
+    }
     return;
   }
-  // every slice's load leaves before the first add (slices past S read slice 0 and
-  // are dropped)
+  if (t >= j.R) {  // width > R only with a padded cd output
+    store_cd<CD>(j.outcd, (int64_t)(pr * j.ldcd + t), 0.f);
+    return;
+  }
+  // every load leaves before the first add (slices past S read slice 0 and are
+  // dropped; without a side input the side load reads the first partial sum)
   float v[8];
 #pragma unroll
-  for (int z = 0; z < 8; ++z) v[z] = part[((uint32_t)(z < S ? z : 0) * (uint32_t)P + pr) * BR + t];  // S <= 8
+  for (int z = 0; z < 8; ++z) v[z] = j.part[((uint32_t)(z < (int)j.S ? z : 0) * j.P + pr) * BR + t];  // S <= 8
+  const float sv = *(j.side ? j.side + pr * j.R + t : j.part);
   float sum = 0.f;
 #pragma unroll
-  for (int z = 0; z < 8; ++z) sum += z < S ? v[z] : 0.f;  // slice order
-  if (out32) out32[trans ? (int64_t)t * P + pr : (int64_t)pr * R + t] = sum * sc32;
-  if (outcd) store_cd<CD>(outcd, (int64_t)pr * ldcd + t, sum * sccd);
+  for (int z = 0; z < 8; ++z) sum += z < (int)j.S ? v[z] : 0.f;  // slice order
+  if (j.out32) j.out32[j.trans ? t * j.P + pr : pr * j.R + t] = sum * j.sc32;
+  if (j.outcd) store_cd<CD>(j.outcd, (int64_t)(pr * j.ldcd + t), sum * j.sccd);
+  if (j.outt) store_cd<CD>(j.outt, (int64_t)(t * j.ldt + pr), sum * j.sccd);
+  if (j.side_t) store_cd<CD>(j.side_t, (int64_t)(t * j.ldt + pr), sv);
 }
 
 // dst [cols][ld_dst] (cd) = cd(scale * src[rows][ld_src]^T), src in cd or fp32;
@@ -313,20 +338,61 @@ int skinny(int cd, bool tn, const void* a, int64_t lda, int64_t arows, const voi
   return check_launch("k_skinny");
 }
 
+namespace {
+// The device form of a reduction; false if it does not fit 32-bit indexing.
+bool red_job(const SkRed& r, RedJob& j) {
+  const int64_t width = (r.outcd && r.ldcd > r.R) ? r.ldcd : r.R;
+  const int64_t rows = ((r.outt || r.side_t) && r.ldt > r.P) ? r.ldt : r.P;
+  const int64_t lim = 1LL << 31;
+  if (rows * width >= lim || 8 * r.P * BR >= 2 * lim || r.R * r.ldt >= lim || r.P * r.ldcd >= lim || r.S > 8)
+    return false;
+  j.part = r.part;
+  j.side = r.side;
+  j.out32 = r.out32;
+  j.outcd = r.outcd;
+  j.outt = r.outt;
+  j.side_t = r.side_t;
+  j.S = (uint32_t)r.S;
+  j.P = (uint32_t)r.P;
+  j.R = (uint32_t)r.R;
+  j.ldcd = (uint32_t)r.ldcd;
+  j.ldt = (uint32_t)r.ldt;
+  j.width = (uint32_t)width;
+  j.rows = (uint32_t)rows;
+  j.nblk = (uint32_t)ceil_div(rows * width, kThreads);
+  j.sc32 = r.sc32;
+  j.sccd = r.sccd;
+  j.trans = r.trans ? 1 : 0;
+  return true;
+}
+}  // namespace
+
+int skinny_reduce_jobs(int cd, const SkRed& a, const SkRed* b, hipStream_t s) {
+  RedJobs js = {};
+  if (!red_job(a, js.j[0]) || (b && !red_job(*b, js.j[1])))
+    return set_error(QLORA_ERR_UNSUPPORTED, "rank product: %lld x %lld too large", (long long)a.P, (long long)a.R);
+  const int64_t blocks = (int64_t)js.j[0].nblk + (b ? js.j[1].nblk : 0);
+  if (blocks == 0) return QLORA_OK;
+  ProfScope prof(QLORA_K_REDUCE, s);
+  if (cd == CD_BF16) k_skreduce<CD_BF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(js);
+  else k_skreduce<CD_F16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(js);
+  return check_launch("k_skreduce");
+}
+
 int skinny_reduce(int cd, const float* part, int S, int64_t P, int64_t R, float sc32, float* out32, bool trans,
                   float sccd, void* outcd, int64_t ldcd, hipStream_t s) {
-  const int64_t width = (outcd && ldcd > R) ? ldcd : R;
-  const int64_t n = P * width;
-  if (n == 0) return QLORA_OK;
-  if (n >= (1LL << 31) || 8 * P * BR >= (1LL << 32))
-    return set_error(QLORA_ERR_UNSUPPORTED, "rank product: %lld x %lld too large", (long long)P, (long long)R);
-  ProfScope prof(QLORA_K_REDUCE, s);
-  const dim3 grid((unsigned)ceil_div(n, kThreads));
-  if (cd == CD_BF16)
-    k_skreduce<CD_BF16><<<grid, dim3(kThreads), 0, s>>>(part, S, P, R, sc32, out32, trans ? 1 : 0, sccd, outcd, ldcd);
-  else
-    k_skreduce<CD_F16><<<grid, dim3(kThreads), 0, s>>>(part, S, P, R, sc32, out32, trans ? 1 : 0, sccd, outcd, ldcd);
-  return check_launch("k_skreduce");
+  SkRed r;
+  r.part = part;
+  r.S = S;
+  r.P = P;
+  r.R = R;
+  r.sc32 = sc32;
+  r.out32 = out32;
+  r.trans = trans;
+  r.sccd = sccd;
+  r.outcd = outcd;
+  r.ldcd = ldcd;
+  return skinny_reduce_jobs(cd, r, nullptr, s);
 }
 
 // dst [cols][ld_dst] = cd(scale * src^T) for a small matrix src [rows][ld_src].
