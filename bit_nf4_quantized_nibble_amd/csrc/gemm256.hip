@@ -345,12 +345,16 @@ __device__ __forceinline__ void read_frags(Frags& F, const char* As, const char*
   for (int j = 0; j < 4; ++j) F.b[j] = *(const u32x4_t*)(Bs + (b_row + 32 * j) * ROWB + cphys);
 }
 
-template <int CD>
+// SWAP: the W-side fragment goes in as the MFMA's row operand, so block (i, j) is
+// accumulated transposed (lane % 32 indexes the activation row; the 16 values of a
+// lane are W-side columns).  The dense kernel works this way round.
+template <int CD, bool SWAP>
 __device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const Frags& F) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma<CD>(F.a[i], F.b[j], acc[i][j]);
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = SWAP ? mfma<CD>(F.b[j], F.a[i], acc[i][j]) : mfma<CD>(F.a[i], F.b[j], acc[i][j]);
 }
 
 // s_waitcnt lgkmcnt(0) alone.
@@ -445,7 +449,7 @@ __device__ __forceinline__ void stage(f32x16_t (&acc)[4][4], char* lds, int cur,
 // LoRA segment: r_pad more contraction steps with [T | B] (fwd) or [dT | A] (dX),
 // appended to the main contraction in the same accumulators.  Entered with every
 // copy drained and the LDS free.
-template <int CD, int MODE>
+template <int CD, int MODE, bool SWAP>
 __device__ __forceinline__ void lora_segment(f32x16_t (&acc)[4][4], char* lds, const Big& p, int64_t m0, int64_t n0,
                                              int tid, int wave, int lane, int a_row, int b_row, int xr, int h) {
   char* As0 = lds;
@@ -506,7 +510,7 @@ __device__ __forceinline__ void lora_segment(f32x16_t (&acc)[4][4], char* lds, c
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       read_frags(F, As0, Bs0, a_row, b_row, xr, h, ks);
-      mfma16<CD>(acc, F);
+      mfma16<CD, SWAP>(acc, F);
     }
     __syncthreads();
   }
@@ -538,23 +542,32 @@ __device__ __forceinline__ f32x4_t acc4(const f32x16_t& a, int q) {
   return v;
 }
 
-// Partial sums of a cut tile's slice: block b = 16 i + 4 j + q of the wave
-// accumulators (rows 8 q + 4 h .. + 3 of MFMA block (i, j)) of thread tid at
-// float (b * 256 + tid) * 4, so every 16-byte store instruction is contiguous.
-__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[4][4], float* dst, int tid) {
+// Partial sums of a cut tile's slice, fp32 [256][256] row-major: the wave's
+// (transposed) block (i, j) gives row wm + 32 i + lane % 32 the four columns
+// wn + 32 j + 8 q + 4 (lane / 32) .. + 3 from elements 4 q .. 4 q + 3 (one 16-byte
+// store; lanes l and l + 32 fill 32 contiguous bytes of a row).
+__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[4][4], float* dst, int wm, int wn, int lane) {
   const rsrc_t r = make_rsrc(dst, kTileAcc * 4);
+  const uint32_t base = (uint32_t)(((wm + (lane & 31)) * TILE + wn + 4 * (lane >> 5)) * 4);
 #pragma unroll
-  for (int b = 0; b < 64; ++b)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc4(acc[b >> 4][(b >> 2) & 3], b & 3)), r,
-                                           tid * 16, b * 4096, 0);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc4(acc[i][j], q)), r, (int)base,
+                                               (32 * i * TILE + 32 * j + 8 * q) * 4, 0);
 }
 
-// The cut tiles' outputs: workgroup (b, rt) sums block b of cut tile rt over its
-// slices in slice order, adds the bias and writes the compute dtype.
+// The cut tiles' outputs: thread (b, t) of cut tile rt sums the four columns
+// 4 (256 b + t) % 256 .. + 3 of tile row (256 b + t) / 64 over the slices in slice
+// order, adds the bias and writes the compute dtype (a wave covers one whole tile
+// row: 512 contiguous bytes).
 template <int CD, int S>
 __global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
-  const int b = blockIdx.x, rt = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* src = p.part + (size_t)rt * S * kTileAcc + (b * 256 + tid) * 4;
+  const int rt = blockIdx.y;
+  const int idx = blockIdx.x * kThreads + threadIdx.x;
+  const float* src = p.part + (size_t)rt * S * kTileAcc + 4 * idx;
   f32x4_t v[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) v[s] = *(const f32x4_t*)(src + (size_t)s * kTileAcc);
@@ -563,14 +576,20 @@ __global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
   for (int s = 1; s < S; ++s) t = t + v[s];
   int tm, tn;
   grouped_tile(p, p.full + rt, tm, tn);
-  const int i = b >> 4, j = (b >> 2) & 3, q = b & 3;
-  const int64_t col = (int64_t)tn * TILE + (wave & 1) * 128 + 32 * j + (lane & 31);
-  if (col >= p.NB) return;
-  const float bias = p.bias ? load_cd<CD>(p.bias, col) : 0.f;
-  const int64_t row0 = (int64_t)tm * TILE + (wave >> 1) * 128 + 32 * i + 8 * q + 4 * (lane >> 5);
+  const int64_t row = (int64_t)tm * TILE + (4 * idx) / TILE;
+  const int64_t col = (int64_t)tn * TILE + (4 * idx) % TILE;
+  if (row >= p.M) return;
+  float o[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (row0 + e < p.M) store_cd<CD>(p.out, (row0 + e) * p.NB + col, t[e] + bias);
+  for (int e = 0; e < 4; ++e) o[e] = t[e] + (p.bias ? load_cd<CD>(p.bias, col + e < p.NB ? col + e : 0) : 0.f);
+  uint16_t* dst = (uint16_t*)p.out + row * p.NB + col;
+  if ((p.NB & 3) == 0 && col + 4 <= p.NB) {
+    *(uint2*)dst = make_uint2(pack2<CD>(o[0], o[1]), pack2<CD>(o[2], o[3]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < p.NB) store_cd<CD>(p.out, row * p.NB + col + e, o[e]);
+  }
 }
 
 template <int CD, int MODE, int DQ>
@@ -668,8 +687,72 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  lora_segment<CD, MODE>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+  lora_segment<CD, MODE, false>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
   epilogue<CD>(acc, p, m0, n0, wm, wn, lane, h);
+}
+
+// Epilogue of the dense kernel, whose blocks are accumulated transposed: lane
+// (r = lane % 32, h = lane / 32) of block (i, j) holds output row 32 i + r, columns
+// 32 j + 8 q + 4 h + e in element 4 q + e.  Each wave rounds its 128 x 128 block
+// (+ bias) to the compute dtype in its own 32 KiB of LDS (rows of 256 bytes; 16-byte
+// chunk c of row m at chunk c ^ (m % 16), so neither the 8-byte writes nor the
+// 16-byte row reads collide on banks), then writes whole rows: 16 lanes per row, 4
+// rows of 256 contiguous bytes per store instruction.  Entered with the LDS free.
+template <int CD>
+__device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][4], const Big& p, char* lds, int64_t m0,
+                                             int64_t n0, int wave, int wm, int wn, int lane, int h) {
+  char* W = lds + wave * 32768;
+  const int r = lane & 31;
+  float bv[4][4][4];  // bias of the lane's columns (j, q, e)
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[j][q][e] = 0.f;
+  if (p.bias) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t col = n0 + wn + 32 * j + 8 * q + 4 * h + e;
+          bv[j][q][e] = load_cd<CD>(p.bias, col < p.NB ? col : 0);
+        }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 32 * i + r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t w2[2];
+        w2[0] = pack2<CD>(acc[i][j][4 * q] + bv[j][q][0], acc[i][j][4 * q + 1] + bv[j][q][1]);
+        w2[1] = pack2<CD>(acc[i][j][4 * q + 2] + bv[j][q][2], acc[i][j][4 * q + 3] + bv[j][q][3]);
+        *(uint2*)(W + m * 256 + (((4 * j + q) ^ (m & 15)) << 4) + 8 * h) = make_uint2(w2[0], w2[1]);
+      }
+  }
+  wait_lgkm0();  // the wave reads back only what it wrote
+  const int c = lane & 15;
+  const int64_t col = n0 + wn + 8 * c;
+  const bool vec = (p.NB & 7) == 0;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int m = 4 * it + (lane >> 4);
+    const u32x4_t v = *(const u32x4_t*)(W + m * 256 + ((c ^ (m & 15)) << 4));
+    const int64_t row = m0 + wm + m;
+    if (row >= p.M) continue;
+    uint16_t* dst = (uint16_t*)p.out + row * p.NB + col;
+    if (vec && col + 8 <= p.NB) {
+      *(u32x4_t*)dst = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < p.NB) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -699,7 +782,7 @@ __device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][4], char* lds, in
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int i = t >> 2, j = t & 3;
-      acc[i][j] = mfma<CD>(C.a[i], C.b[j], acc[i][j]);
+      acc[i][j] = mfma<CD>(C.b[j], C.a[i], acc[i][j]);  // block (i, j) transposed
       if (ks < 3 && (t & 1) == 0) {
         const int r = t >> 1;
         if (r < 4) N.a[r] = *(const u32x4_t*)(As + (a_row + 32 * r) * ROWB + cphys);
@@ -725,6 +808,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn, slice, rt;
   item_of(p, tm, tn, slice, rt);
+  // all four are uniform: keep them (and every address derived from them) scalar
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  slice = __builtin_amdgcn_readfirstlane(slice);
+  rt = __builtin_amdgcn_readfirstlane(rt);
   const int64_t m0 = (int64_t)tm * TILE, n0 = (int64_t)tn * TILE;
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int h = lane >> 5;
@@ -778,9 +866,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
   __syncthreads();
 
   // the low-rank tail joins the last slice (or the whole tile)
-  if (rt < 0 || slice == p.split - 1) lora_segment<CD, MODE>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
-  if (rt < 0) epilogue<CD>(acc, p, m0, n0, wm, wn, lane, h);
-  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, tid);
+  if (rt < 0 || slice == p.split - 1)
+    lora_segment<CD, MODE, true>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+  if (rt < 0) epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
+  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
 }
 
 template <int CD, int MODE>
