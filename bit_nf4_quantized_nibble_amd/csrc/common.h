@@ -221,6 +221,18 @@ struct SkRed {
 // One launch for one or two reductions (b may be null).
 int skinny_reduce_jobs(int cd, const SkRed& a, const SkRed* b, hipStream_t s);
 
+// dst [cols][ld_dst] = cd(scale * src[rows][ld_src]^T) (src in the compute dtype or
+// fp32), columns rows .. ld_dst-1 of dst zero; one launch carries one or two.
+struct TransposeSpec {
+  const void* src = nullptr;
+  bool src_f32 = false;
+  int64_t ld_src = 0, rows = 0, cols = 0;
+  float scale = 1.f;
+  void* dst = nullptr;
+  int64_t ld_dst = 0;
+};
+int transpose_jobs(int cd, const TransposeSpec& a, const TransposeSpec* b, hipStream_t s);
+
 int apply_mask(int cd, const void* x, const uint8_t* mask, int64_t n, void* out, hipStream_t s);
 int zero_fill(void* p, int64_t bytes, hipStream_t s);
 int rank_add_masked(int cd, void* dx, const uint8_t* mask, const void* dt, int64_t ld_dt, const void* a, int32_t r,

@@ -47,7 +47,7 @@ int transpose_small(int cd, const void* src, bool src_f32, int64_t ld_src, int64
 int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y,
                      const DenseSplit& sp, void* split_ws);
 int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx,
-                const DenseSplit& sp, void* split_ws);
+                const DenseSplit& sp, void* split_ws, const void* a_t);
 DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1);
 size_t dense_split_bytes(const DenseSplit& sp);
 
@@ -466,7 +466,7 @@ struct BwdPlan {
   int64_t n_pad, m_pad;  // contractions rounded up to whole 64-element stages
   DenseSplit dsp;        // cut of the dense dX GEMM's last round
   int64_t off_t0, off_dt, off_dtcd, off_bt, off_dtt, off_t0t, off_part, off_part2, off_wdt, off_xm, off_zero, off_split,
-      total;
+      off_at, total;
 };
 BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
   BwdPlan P;
@@ -509,7 +509,9 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   P.off_zero = P.off_xm + (drop ? al(m * cols * es) : 0);
   P.off_split = P.off_zero + (drop ? al(m * P.r_pad * es) : 0);
   P.dsp = dense_split(m, cols, rows);
-  P.total = P.off_split + (P.dense ? al(dense_split_bytes(P.dsp)) : 0);
+  // A^T [cols][r_pad] in cd: the W-side rows of the dense dX GEMM's low-rank tail
+  P.off_at = P.off_split + (P.dense ? al(dense_split_bytes(P.dsp)) : 0);
+  P.total = P.off_at + (P.dense ? al(cols * P.r_pad * es) : 0);
   return P;
 }
 
@@ -641,9 +643,27 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   // copy transposed) and T0^T [r][m_pad] rounded to cd, both zero past M.
   void* dtt = ws + P.off_dtt;
   void* t0t = ws + P.off_t0t;
+  // A^T [K][r_pad] (zero past r) for the low-rank tail of the dense dX GEMM; its
+  // transpose shares a launch with B^T's on the skinny path.
+  const bool dense_dx = dx && P.dense && dense256_ok(c, true);
+  void* at = dense_dx ? (void*)(ws + P.off_at) : nullptr;
+  TransposeSpec ta;
+  ta.src = c.lora_a;
+  ta.ld_src = K;
+  ta.rows = r;
+  ta.cols = K;
+  ta.dst = at;
+  ta.ld_dst = P.r_pad;
   if (P.sk_n) {
     void* bt = ws + P.off_bt;  // B^T [r][n_pad], zero past N
-    if ((rc = transpose_small(CD, c.lora_b, false, r, N, r, 1.0f, bt, P.n_pad, c.stream))) return rc;
+    TransposeSpec tb;
+    tb.src = c.lora_b;
+    tb.ld_src = r;
+    tb.rows = N;
+    tb.cols = r;
+    tb.dst = bt;
+    tb.ld_dst = P.n_pad;
+    if ((rc = transpose_jobs(CD, tb, at ? &ta : nullptr, c.stream))) return rc;
     int S;
     if ((rc = skinny(CD, false, dy, N, M, bt, P.n_pad, M, r, P.n_pad, part, &S, c.stream, QLORA_K_BWD_DT))) return rc;
     SkRed red;
@@ -662,6 +682,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     red.side_t = t0t;
     if ((rc = skinny_reduce_jobs(CD, red, nullptr, c.stream))) return rc;
   } else {
+    if (at && (rc = transpose_jobs(CD, ta, nullptr, c.stream))) return rc;
     GemmParams p = base_params(c);
     p.a1 = opnd<CD>(dy, N, M, N);
     p.b1 = opnd<CD>(c.lora_b, r, r, N);  // source [n][t]: transposed while staging
@@ -686,10 +707,10 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     if ((rc = zero_fill(ws + P.off_zero, M * P.r_pad * cd_bytes(CD), c.stream))) return rc;
     dt_gemm = ws + P.off_zero;
   }
-  if (dx && P.dense && dense256_ok(c, true)) {
+  if (dense_dx) {
     void* wdt = ws + P.off_wdt;
     if ((rc = dequant_into(c.w, CD, wdt, true, c.stream))) return rc;
-    if ((rc = dense256_dx(c, dy, wdt, dt_gemm, P.r_pad, dx, P.dsp, ws + P.off_split))) return rc;
+    if ((rc = dense256_dx(c, dy, wdt, dt_gemm, P.r_pad, dx, P.dsp, ws + P.off_split, at))) return rc;
   } else if (dx && fused256_ok(c, true)) {
     rc = fused256_dx(c, dy, dt_gemm, P.r_pad, dx);
     if (rc) return rc;

@@ -70,6 +70,12 @@ struct Big {
   // incomplete last round) and leave fp32 partial sums for k_split_sum.
   int32_t full, rem, split;
   float* part;        // [rem][split][kTileAcc] fp32, in accumulator order
+  // Dense kernel only: the low-rank tail as pipelined stages when b2_rows is set:
+  // the W-side tail operand as rows [NB][ld_b2] (fwd: lora_b, ld r; dX: A^T
+  // [K][r_pad]); the r_b2 valid columns of a row (r fwd, r_pad dX; a multiple of 8).
+  const void* b2_rows;
+  int64_t ld_b2;
+  int32_t r_b2;
 };
 constexpr int kTileAcc = TILE * TILE;  // accumulators of one tile
 
@@ -763,9 +769,24 @@ __device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][4], const 
 // stage k + 1 spread over sub-steps 0 (activations) and 1 (W), one instruction
 // per two MFMAs, and the fragment reads of the next sub-step between them.
 // ---------------------------------------------------------------------------
+// The copy of one stage into LDS: rows 8 (4 d + w) + lane / 8 of each tile (d =
+// 0..7 by instruction, w the wave); byte offset voffset + d * step + soff.
+struct Copy {
+  rsrc_t ra, rb;
+  uint32_t a_off, b_off, a_step, b_step, soff;
+};
+
+__device__ __forceinline__ void copy_one(const Copy& cp, char* dst_a, char* dst_b, int wave, int d, bool b_side) {
+  if (!b_side)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.ra, (lds_void*)(dst_a + (4 * d + wave) * 1024), 16,
+                                             (int)(cp.a_off + d * cp.a_step), (int)cp.soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.rb, (lds_void*)(dst_b + (4 * d + wave) * 1024), 16,
+                                             (int)(cp.b_off + d * cp.b_step), (int)cp.soff, 0, 0);
+}
+
 template <int CD, int DO_COPY>
-__device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][4], char* lds, int cur, rsrc_t ra, rsrc_t rb,
-                                            uint32_t a_off, uint32_t b_off, uint32_t step, int wave, uint32_t kn,
+__device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][4], char* lds, int cur, const Copy& cp, int wave,
                                             int a_row, int b_row, int xr, int h) {
   char* As = lds + cur * TILE_BYTES;
   char* Bs = lds + (2 + cur) * TILE_BYTES;
@@ -788,13 +809,7 @@ __device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][4], char* lds, in
         if (r < 4) N.a[r] = *(const u32x4_t*)(As + (a_row + 32 * r) * ROWB + cphys);
         else N.b[r - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (r - 4)) * ROWB + cphys);
       }
-      if (DO_COPY && ks < 2 && (t & 1) == 1) {
-        const int d = t >> 1;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ks == 0 ? ra : rb,
-                                                 (lds_void*)((ks == 0 ? An : Bn) + (4 * d + wave) * 1024), 16,
-                                                 (int)((ks == 0 ? a_off : b_off) + d * step), (int)(kn * (BK * 2)),
-                                                 0, 0);
-      }
+      if (DO_COPY && ks < 2 && (t & 1) == 1) copy_one(cp, An, Bn, wave, t >> 1, ks == 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -818,15 +833,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
   const int h = lane >> 5;
   const int a_row = wm + (lane & 31), b_row = wn + (lane & 31);
   const int xr = swz(lane & 31);
-  const rsrc_t ra = make_rsrc(p.a1, p.M * p.ld_a1 * 2);
-  const rsrc_t rb = make_rsrc(bd, p.NB * p.K1 * 2);
   // rows 8 (4 d + wave) + lane / 8 (d = 0..7) of each tile; rows past M or NB read
   // past their buffer (the row is in the lane offset) and land as zeros
   const int row = 8 * wave + (lane >> 3);
-  const int c = (lane & 7) ^ swz(row);
-  const uint32_t a_off = (uint32_t)(((m0 + row) * p.ld_a1 + 8 * c) * 2);
-  const uint32_t b_off = (uint32_t)(((n0 + row) * p.K1 + 8 * c) * 2);
-  const uint32_t a_step = (uint32_t)(32 * p.ld_a1 * 2), b_step = (uint32_t)(32 * p.K1 * 2);
+  const int c = (lane & 7) ^ swz(row);  // the logical chunk this lane's copies fetch
+  Copy main_cp;
+  main_cp.ra = make_rsrc(p.a1, p.M * p.ld_a1 * 2);
+  main_cp.rb = make_rsrc(bd, p.NB * p.K1 * 2);
+  main_cp.a_off = (uint32_t)(((m0 + row) * p.ld_a1 + 8 * c) * 2);
+  main_cp.b_off = (uint32_t)(((n0 + row) * p.K1 + 8 * c) * 2);
+  main_cp.a_step = (uint32_t)(32 * p.ld_a1 * 2);
+  main_cp.b_step = (uint32_t)(32 * p.K1 * 2);
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -836,37 +853,61 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // Stages [k0, k1) of the contraction (K1 is a multiple of 64 here): all of them
-  // for a whole tile, slice `slice` of split for a cut one.
+  // Stages: [k0, k1) of the main contraction (K1 is a multiple of 64 here; all of
+  // it for a whole tile, slice `slice` of split for a cut one), then, for a whole
+  // tile or the last slice, the low-rank tail: ceil(r_pad / 64) stages of [T | B]
+  // (fwd) or [dT | A] (dX), chunks past the valid columns read as zeros.
   const uint32_t KT = (uint32_t)(p.K1 / BK);
   uint32_t k0 = 0, k1 = KT;
   if (rt >= 0) {
     k0 = (uint32_t)slice * KT / (uint32_t)p.split;
     k1 = (uint32_t)(slice + 1) * KT / (uint32_t)p.split;
   }
+  const bool has_tail = rt < 0 || slice == p.split - 1;
+  const bool dma_tail = has_tail && p.b2_rows != nullptr;
+  const uint32_t nmain = k1 - k0;
+  const uint32_t n_st = nmain + (dma_tail ? (uint32_t)((p.r_pad + BK - 1) / BK) : 0u);
+  const rsrc_t ra2 = make_rsrc(p.a2, p.M * p.r_pad * 2);
+  const rsrc_t rb2 = make_rsrc(p.b2_rows, p.NB * p.ld_b2 * 2);
+  auto copy_of = [&](uint32_t u) {
+    if (u < nmain) {
+      Copy cp = main_cp;
+      cp.soff = (k0 + u) * (BK * 2);
+      return cp;
+    }
+    const uint32_t t0 = (u - nmain) * BK + 8 * c;  // first tail column of this lane's chunk
+    Copy cp;
+    cp.ra = ra2;
+    cp.rb = rb2;
+    cp.a_off = oob_unless(t0 < (uint32_t)p.r_pad, (uint32_t)(((m0 + row) * p.r_pad + t0) * 2));
+    cp.b_off = oob_unless(t0 < (uint32_t)p.r_b2, (uint32_t)(((n0 + row) * p.ld_b2 + t0) * 2));
+    cp.a_step = (uint32_t)(32 * p.r_pad * 2);
+    cp.b_step = (uint32_t)(32 * p.ld_b2 * 2);
+    cp.soff = 0;
+    return cp;
+  };
+  {
+    const Copy cp = copy_of(0);
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(lds + (4 * d + wave) * 1024), 16, (int)(a_off + d * a_step),
-                                             (int)(k0 * (BK * 2)), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds + 2 * TILE_BYTES + (4 * d + wave) * 1024), 16,
-                                             (int)(b_off + d * b_step), (int)(k0 * (BK * 2)), 0, 0);
+    for (int d = 0; d < 8; ++d) {
+      copy_one(cp, lds, lds + 2 * TILE_BYTES, wave, d, false);
+      copy_one(cp, lds, lds + 2 * TILE_BYTES, wave, d, true);
+    }
   }
-  // a_step == b_step only when ld_a1 == K1, which holds for both uses (x [M, K]
-  // against W~ [N, K]; dY [M, N] against W~^T [K, N]).
-  uint32_t k = k0;
-  for (; k + 1 < k1; ++k) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of stage k and its fragment reads
+  uint32_t u = 0;
+  for (; u + 1 < n_st; ++u) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of stage u and its fragment reads
     barrier_only();
-    dense_stage<CD, 1>(acc, lds, (k - k0) & 1, ra, rb, a_off, b_off, a_step, wave, k + 1, a_row, b_row, xr, h);
+    dense_stage<CD, 1>(acc, lds, u & 1, copy_of(u + 1), wave, a_row, b_row, xr, h);
   }
   __builtin_amdgcn_s_waitcnt(0);
   barrier_only();
-  dense_stage<CD, 0>(acc, lds, (k - k0) & 1, ra, rb, a_off, b_off, a_step, wave, 0, a_row, b_row, xr, h);
+  dense_stage<CD, 0>(acc, lds, u & 1, main_cp, wave, a_row, b_row, xr, h);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // the low-rank tail joins the last slice (or the whole tile)
-  if (rt < 0 || slice == p.split - 1)
+  // a tail whose W-side operand cannot be copied row by row (fwd with r % 8 != 0)
+  if (has_tail && !dma_tail)
     lora_segment<CD, MODE, true>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
   if (rt < 0) epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
   else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
@@ -1012,14 +1053,20 @@ int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64
   b.out = y;
   b.bias = c.bias;
   set_split(b, sp, split_ws);
+  if (c.r % 8 == 0) {  // lora_b rows [N][r] copy whole 16-byte chunks: the tail is pipelined
+    b.b2_rows = c.lora_b;
+    b.ld_b2 = c.r;
+    b.r_b2 = c.r;
+  }
   if (c.cd == CD_BF16) return run_dense<CD_BF16, MODE_FWD>(b, wd, c.stream, QLORA_K_FWD_GEMM);
   return run_dense<CD_F16, MODE_FWD>(b, wd, c.stream, QLORA_K_FWD_GEMM);
 }
 
 // dX = [dY | dT][W~ ; A] with W~^T [K, N] already in the compute dtype.  sp:
-// dense_split(m, cols, rows); split_ws as for the forward.
+// dense_split(m, cols, rows); split_ws as for the forward; a_t: A^T [K][r_pad] in the
+// compute dtype, zero past r (the tail's W-side rows), or null.
 int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx,
-                const DenseSplit& sp, void* split_ws) {
+                const DenseSplit& sp, void* split_ws, const void* a_t) {
   Big b = {};
   b.a1 = dy;
   b.ld_a1 = c.w.rows;
@@ -1036,6 +1083,11 @@ int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void*
   b.out = dx;
   b.bias = nullptr;
   set_split(b, sp, split_ws);
+  if (a_t) {
+    b.b2_rows = a_t;
+    b.ld_b2 = r_pad;
+    b.r_b2 = (int32_t)r_pad;
+  }
   if (c.cd == CD_BF16) return run_dense<CD_BF16, MODE_DX>(b, wdt, c.stream, QLORA_K_BWD_DX);
   return run_dense<CD_F16, MODE_DX>(b, wdt, c.stream, QLORA_K_BWD_DX);
 }

@@ -248,13 +248,27 @@ __global__ __launch_bounds__(kThreads) void k_skreduce(RedJobs js) {
 }
 
 // dst [cols][ld_dst] (cd) = cd(scale * src[rows][ld_src]^T), src in cd or fp32;
-// columns rows .. ld_dst-1 of dst are zeros.  Tile 64 x 64 through LDS.
+// columns rows .. ld_dst-1 of dst are zeros.  Tiles of 64 x 64 through LDS; one
+// launch can carry two such jobs (workgroups [0, tiles of job 0) take job 0).
+struct TrJob {
+  const void* src;
+  int64_t ld_src, rows, cols;
+  float scale;
+  void* dst;
+  int64_t ld_dst;
+  int32_t tiles_x, tiles;
+};
+struct TrJobs {
+  TrJob j[2];
+};
+
 template <int CD, int SRC32>
-__global__ __launch_bounds__(kThreads) void k_transpose(const void* __restrict__ src, int64_t ld_src, int64_t rows,
-                                                        int64_t cols, float scale, void* __restrict__ dst,
-                                                        int64_t ld_dst) {
+__global__ __launch_bounds__(kThreads) void k_transpose(TrJobs js) {
   __shared__ float t[64][65];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int w = (int)blockIdx.x >= js.j[0].tiles ? 1 : 0;
+  const TrJob& j = js.j[w];
+  const int b = blockIdx.x - (w ? js.j[0].tiles : 0);
+  const int64_t r0 = (int64_t)(b % j.tiles_x) * 64, c0 = (int64_t)(b / j.tiles_x) * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   // all 16 loads of a thread leave before the first is used: out-of-range elements
   // read element 0 and are replaced by zero afterwards
@@ -262,20 +276,20 @@ __global__ __launch_bounds__(kThreads) void k_transpose(const void* __restrict__
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
-    const int64_t at = (r < rows && c < cols) ? r * ld_src + c : 0;
-    v[i] = SRC32 ? ((const float*)src)[at] : load_cd<CD>(src, at);
+    const int64_t at = (r < j.rows && c < j.cols) ? r * j.ld_src + c : 0;
+    v[i] = SRC32 ? ((const float*)j.src)[at] : load_cd<CD>(j.src, at);
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
-    t[ty + 4 * i][tx] = (r < rows && c < cols) ? v[i] * scale : 0.f;
+    t[ty + 4 * i][tx] = (r < j.rows && c < j.cols) ? v[i] * j.scale : 0.f;
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int y = ty + 4 * i;
     const int64_t c = c0 + y, r = r0 + tx;
-    if (c < cols && r < ld_dst) store_cd<CD>(dst, c * ld_dst + r, r < rows ? t[tx][y] : 0.f);
+    if (c < j.cols && r < j.ld_dst) store_cd<CD>(j.dst, c * j.ld_dst + r, r < j.rows ? t[tx][y] : 0.f);
   }
 }
 
@@ -395,20 +409,56 @@ int skinny_reduce(int cd, const float* part, int S, int64_t P, int64_t R, float 
   return skinny_reduce_jobs(cd, r, nullptr, s);
 }
 
-// dst [cols][ld_dst] = cd(scale * src^T) for a small matrix src [rows][ld_src].
-int transpose_small(int cd, const void* src, bool src_f32, int64_t ld_src, int64_t rows, int64_t cols, float scale,
-                    void* dst, int64_t ld_dst, hipStream_t s) {
-  if (ld_dst == 0 || cols == 0) return QLORA_OK;
-  const dim3 grid((unsigned)ceil_div(ld_dst, 64), (unsigned)ceil_div(cols, 64));
+// dst [cols][ld_dst] = cd(scale * src^T) for small matrices src [rows][ld_src]: one
+// launch for the first job and, if given, a second one with the same source type.
+int transpose_jobs(int cd, const TransposeSpec& a, const TransposeSpec* b, hipStream_t s) {
+  if (b && b->src_f32 != a.src_f32) {
+    const int rc = transpose_jobs(cd, a, nullptr, s);
+    return rc ? rc : transpose_jobs(cd, *b, nullptr, s);
+  }
+  TrJobs js = {};
+  const TransposeSpec* specs[2] = {&a, b};
+  int64_t total = 0;
+  for (int k = 0; k < 2; ++k) {
+    const TransposeSpec* t = specs[k];
+    if (!t || t->ld_dst == 0 || t->cols == 0) continue;
+    TrJob& j = js.j[k];
+    j.src = t->src;
+    j.ld_src = t->ld_src;
+    j.rows = t->rows;
+    j.cols = t->cols;
+    j.scale = t->scale;
+    j.dst = t->dst;
+    j.ld_dst = t->ld_dst;
+    j.tiles_x = (int32_t)ceil_div(t->ld_dst, 64);
+    j.tiles = (int32_t)(j.tiles_x * ceil_div(t->cols, 64));
+    total += j.tiles;
+  }
+  if (total == 0) return QLORA_OK;
   ProfScope prof(QLORA_K_REDUCE, s);
+  const dim3 g((unsigned)total), blk(kThreads);
   if (cd == CD_BF16) {
-    if (src_f32) k_transpose<CD_BF16, 1><<<grid, dim3(kThreads), 0, s>>>(src, ld_src, rows, cols, scale, dst, ld_dst);
-    else k_transpose<CD_BF16, 0><<<grid, dim3(kThreads), 0, s>>>(src, ld_src, rows, cols, scale, dst, ld_dst);
+    if (a.src_f32) k_transpose<CD_BF16, 1><<<g, blk, 0, s>>>(js);
+    else k_transpose<CD_BF16, 0><<<g, blk, 0, s>>>(js);
   } else {
-    if (src_f32) k_transpose<CD_F16, 1><<<grid, dim3(kThreads), 0, s>>>(src, ld_src, rows, cols, scale, dst, ld_dst);
-    else k_transpose<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(src, ld_src, rows, cols, scale, dst, ld_dst);
+    if (a.src_f32) k_transpose<CD_F16, 1><<<g, blk, 0, s>>>(js);
+    else k_transpose<CD_F16, 0><<<g, blk, 0, s>>>(js);
   }
   return check_launch("k_transpose");
+}
+
+int transpose_small(int cd, const void* src, bool src_f32, int64_t ld_src, int64_t rows, int64_t cols, float scale,
+                    void* dst, int64_t ld_dst, hipStream_t s) {
+  TransposeSpec t;
+  t.src = src;
+  t.src_f32 = src_f32;
+  t.ld_src = ld_src;
+  t.rows = rows;
+  t.cols = cols;
+  t.scale = scale;
+  t.dst = dst;
+  t.ld_dst = ld_dst;
+  return transpose_jobs(cd, t, nullptr, s);
 }
 
 }  // namespace qnf4
