@@ -437,7 +437,7 @@ __device__ __forceinline__ void stage(f32x16_t (&acc)[4][4], char* lds, int cur,
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int i = t >> 2, j = t & 3;
-      acc[i][j] = mfma<CD>(C.a[i], C.b[j], acc[i][j]);
+      acc[i][j] = mfma<CD>(C.b[j], C.a[i], acc[i][j]);  // block (i, j) transposed
       if (ks < 3 && (t & 1) == 0) {
         const int r = t >> 1;
         if (r < 4) N.a[r] = *(const u32x4_t*)(As + (a_row + 32 * r) * ROWB + cphys);
@@ -523,25 +523,6 @@ __device__ __forceinline__ void lora_segment(f32x16_t (&acc)[4][4], char* lds, c
 
 }
 
-// Epilogue: fp32 accumulators (+ bias) -> compute dtype.
-template <int CD>
-__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[4][4], const Big& p, int64_t m0, int64_t n0, int wm,
-                                         int wn, int lane, int h) {
-  const int cl = lane & 31;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t col = n0 + wn + 32 * j + cl;
-    if (col >= p.NB) continue;
-    const float bias = p.bias ? load_cd<CD>(p.bias, col) : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row < p.M) store_cd<CD>(p.out, row * p.NB + col, acc[i][j][v] + bias);
-      }
-  }
-}
 
 __device__ __forceinline__ f32x4_t acc4(const f32x16_t& a, int q) {
   f32x4_t v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
@@ -598,6 +579,70 @@ __global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
   }
 }
 
+// Epilogue of the 256-tile kernels, whose blocks are accumulated transposed: lane
+// (r = lane % 32, h = lane / 32) of block (i, j) holds output row 32 i + r, columns
+// 32 j + 8 q + 4 h + e in element 4 q + e.  Each wave rounds its 128 x 128 block
+// (+ bias) to the compute dtype in its own 32 KiB of LDS (rows of 256 bytes; 16-byte
+// chunk c of row m at chunk c ^ (m % 16), so neither the 8-byte writes nor the
+// 16-byte row reads collide on banks), then writes whole rows: 16 lanes per row, 4
+// rows of 256 contiguous bytes per store instruction.  Entered with the LDS free.
+template <int CD>
+__device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][4], const Big& p, char* lds, int64_t m0,
+                                             int64_t n0, int wave, int wm, int wn, int lane, int h) {
+  char* W = lds + wave * 32768;
+  const int r = lane & 31;
+  float bv[4][4][4];  // bias of the lane's columns (j, q, e)
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[j][q][e] = 0.f;
+  if (p.bias) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t col = n0 + wn + 32 * j + 8 * q + 4 * h + e;
+          bv[j][q][e] = load_cd<CD>(p.bias, col < p.NB ? col : 0);
+        }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 32 * i + r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t w2[2];
+        w2[0] = pack2<CD>(acc[i][j][4 * q] + bv[j][q][0], acc[i][j][4 * q + 1] + bv[j][q][1]);
+        w2[1] = pack2<CD>(acc[i][j][4 * q + 2] + bv[j][q][2], acc[i][j][4 * q + 3] + bv[j][q][3]);
+        *(uint2*)(W + m * 256 + (((4 * j + q) ^ (m & 15)) << 4) + 8 * h) = make_uint2(w2[0], w2[1]);
+      }
+  }
+  wait_lgkm0();  // the wave reads back only what it wrote
+  const int c = lane & 15;
+  const int64_t col = n0 + wn + 8 * c;
+  const bool vec = (p.NB & 7) == 0;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int m = 4 * it + (lane >> 4);
+    const u32x4_t v = *(const u32x4_t*)(W + m * 256 + ((c ^ (m & 15)) << 4));
+    const int64_t row = m0 + wm + m;
+    if (row >= p.M) continue;
+    uint16_t* dst = (uint16_t*)p.out + row * p.NB + col;
+    if (vec && col + 8 <= p.NB) {
+      *(u32x4_t*)dst = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < p.NB) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
 template <int CD, int MODE, int DQ>
 __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) {
   // [A0 | A1 | B0 | B1 | levels]
@@ -620,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
   const int64_t nb = w.rows * w.cols / w.bs;
   const rsrc_t rq = DQ ? make_rsrc(w.absmax_q, nb) : make_rsrc(w.absmax, nb * 4);
   const rsrc_t rs = make_rsrc(DQ ? (const void*)w.scale2 : (const void*)w.absmax,
-                              DQ ? ((nb + w.g - 1) / w.g) * 4 : nb * 4);
+                              DQ ? (((nb - 1) >> w.g_shift) + 1) * 4 : nb * 4);
 
   Lane L;
   {
@@ -693,73 +738,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  lora_segment<CD, MODE, false>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
-  epilogue<CD>(acc, p, m0, n0, wm, wn, lane, h);
+  lora_segment<CD, MODE, true>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+  epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
 }
 
-// Epilogue of the dense kernel, whose blocks are accumulated transposed: lane
-// (r = lane % 32, h = lane / 32) of block (i, j) holds output row 32 i + r, columns
-// 32 j + 8 q + 4 h + e in element 4 q + e.  Each wave rounds its 128 x 128 block
-// (+ bias) to the compute dtype in its own 32 KiB of LDS (rows of 256 bytes; 16-byte
-// chunk c of row m at chunk c ^ (m % 16), so neither the 8-byte writes nor the
-// 16-byte row reads collide on banks), then writes whole rows: 16 lanes per row, 4
-// rows of 256 contiguous bytes per store instruction.  Entered with the LDS free.
-template <int CD>
-__device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][4], const Big& p, char* lds, int64_t m0,
-                                             int64_t n0, int wave, int wm, int wn, int lane, int h) {
-  char* W = lds + wave * 32768;
-  const int r = lane & 31;
-  float bv[4][4][4];  // bias of the lane's columns (j, q, e)
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bv[j][q][e] = 0.f;
-  if (p.bias) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t col = n0 + wn + 32 * j + 8 * q + 4 * h + e;
-          bv[j][q][e] = load_cd<CD>(p.bias, col < p.NB ? col : 0);
-        }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 32 * i + r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t w2[2];
-        w2[0] = pack2<CD>(acc[i][j][4 * q] + bv[j][q][0], acc[i][j][4 * q + 1] + bv[j][q][1]);
-        w2[1] = pack2<CD>(acc[i][j][4 * q + 2] + bv[j][q][2], acc[i][j][4 * q + 3] + bv[j][q][3]);
-        *(uint2*)(W + m * 256 + (((4 * j + q) ^ (m & 15)) << 4) + 8 * h) = make_uint2(w2[0], w2[1]);
-      }
-  }
-  wait_lgkm0();  // the wave reads back only what it wrote
-  const int c = lane & 15;
-  const int64_t col = n0 + wn + 8 * c;
-  const bool vec = (p.NB & 7) == 0;
-#pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int m = 4 * it + (lane >> 4);
-    const u32x4_t v = *(const u32x4_t*)(W + m * 256 + ((c ^ (m & 15)) << 4));
-    const int64_t row = m0 + wm + m;
-    if (row >= p.M) continue;
-    uint16_t* dst = (uint16_t*)p.out + row * p.NB + col;
-    if (vec && col + 8 <= p.NB) {
-      *(u32x4_t*)dst = v;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (col + e < p.NB) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Dense variant (dequantize-then-GEMM): the W operand is a compute-dtype matrix

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvP p, Nf4Tables t
     const int64_t nb = N * K / w.bs;
     const rsrc_t rq = DQ ? make_rsrc(w.absmax_q, nb) : make_rsrc(w.absmax, nb * 4);
     const rsrc_t rs = make_rsrc(DQ ? (const void*)w.scale2 : (const void*)w.absmax,
-                                DQ ? ((nb + w.g - 1) / w.g) * 4 : nb * 4);
+                                DQ ? (((nb - 1) >> w.g_shift) + 1) * 4 : nb * 4);
     // codes: DMA instruction i of wave w fills rows 4 (8 i + w) .. +4, 256 bytes each:
     // lane l lands in physical chunk l % 16 of row l / 16 and fetches the logical
     // chunk that maps there (rows past N read past the buffer: zeros)

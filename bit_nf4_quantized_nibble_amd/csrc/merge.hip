@@ -71,7 +71,7 @@ __device__ __forceinline__ MergeRsrc make_merge_rsrc(const MergeP& p) {
   MergeRsrc r;
   r.codes = make_rsrc(w.codes, n / 2);
   r.scale = DQ ? make_rsrc(w.absmax_q, nb) : make_rsrc(w.absmax, nb * 4);
-  r.scale2 = DQ ? make_rsrc(w.scale2, ((nb + w.g - 1) / w.g) * 4) : r.scale;
+  r.scale2 = DQ ? make_rsrc(w.scale2, (((nb - 1) >> w.g_shift) + 1) * 4) : r.scale;
   r.b = make_rsrc(p.b, w.rows * p.r * 2);
   r.a = make_rsrc(p.a, p.r * w.cols * 2);
   return r;
