@@ -94,8 +94,19 @@ class Layer:
             raise RuntimeError("bwd %s: %d %s" % (self.name, rc, self.lib.qlora_last_error()))
 
 
-def build_block(cd, with_dy, qn, torch, lib, inputs, m=4096, flags=0):
+def tensor_sha256(t):
+    import hashlib
+    return hashlib.sha256(t.contiguous().view(-1).view(__import__("torch").uint8).numpy().tobytes()).hexdigest()
+
+
+def build_block(cd, with_dy, qn, torch, lib, inputs, m=4096, flags=0, hashes=None):
     Ls = inputs.prefill(seed=0, cd=cd, m=m, with_dy=with_dy)
+    if hashes is not None:  # SHA-256 of every input tensor, as generated on the host
+        for L in Ls:
+            hashes.setdefault("x_K%d" % L.K, tensor_sha256(L.x))
+            for name, t in (("W", L.W), ("A", L.A), ("B", L.B), ("dY", L.dY)):
+                if t is not None:
+                    hashes["%s_%s" % (L.name, name)] = tensor_sha256(t)
     xs = {}
     for L in Ls:
         if L.K not in xs:
@@ -110,17 +121,35 @@ def build_block(cd, with_dy, qn, torch, lib, inputs, m=4096, flags=0):
     return layers, (xs, ws_f, ws_b)
 
 
-def time_loop(fn, iters, torch):
+def time_loop(fn, iters, torch, per_step=None):
+    """Mean seconds per call over `iters` calls between two synchronizations; with
+    `per_step` (a list) also the device time of each call from event pairs recorded
+    between the calls (no synchronization inside the loop)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)] if per_step is not None else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(iters):
+    for i in range(iters):
+        if evs:
+            evs[i].record()
         fn()
+    if evs:
+        evs[iters].record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / iters
+    sec = (time.perf_counter() - t0) / iters
+    if evs:
+        per_step.extend(evs[i].elapsed_time(evs[i + 1]) for i in range(iters))
+    return sec
 
 
-def bench_step(args, qn, torch, lib, inputs, flags=0):
-    layers, keep = build_block("bf16", True, qn, torch, lib, inputs, flags=flags)
+def percentiles(ms):
+    """median, p10 and p90 of a list of milliseconds (nearest rank)."""
+    v = sorted(ms)
+    pick = lambda q: v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4), "n": len(v)}
+
+
+def bench_step(args, qn, torch, lib, inputs, flags=0, hashes=None):
+    layers, keep = build_block("bf16", True, qn, torch, lib, inputs, flags=flags, hashes=hashes)
     torch.cuda.synchronize()
     flops = sum(fwd_flops(l.M, l.N, l.K, l.r) + bwd_flops(l.M, l.N, l.K, l.r) for l in layers)
     ff = {k: 0.0 for k in ("fwd_gemm", "lora_down", "bwd_dx", "bwd_dt", "bwd_da", "bwd_db")}
@@ -143,7 +172,8 @@ def bench_step(args, qn, torch, lib, inputs, flags=0):
         step()
     torch.cuda.synchronize()
     log("timing", args.steps, "steps")
-    sec = time_loop(step, args.steps, torch)
+    step_ms = []
+    sec = time_loop(step, args.steps, torch, per_step=step_ms)
     # per-kernel times from a second, profiled pass (the event pairs it records around
     # each launch stay out of the timed steps above)
     qn.profile_enable(True)
@@ -170,7 +200,7 @@ def bench_step(args, qn, torch, lib, inputs, flags=0):
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic() if (dom == "fwd_gemm" and flags == 0) else None,
                 "avg_launch_ms": round(dom_ms, 4), "flops_per_launch": dom_flops}
-    result = dict(sec=sec, flops=flops, kernels=kernels, roofline=roofline,
+    result = dict(sec=sec, flops=flops, kernels=kernels, roofline=roofline, step_ms=percentiles(step_ms),
                   fwd_ms=sum(kernels.get(k, {}).get("ms_per_step", 0) for k in ("fwd_gemm", "lora_down")),
                   layers=[(l.name, l.N, l.K) for l in layers])
     del layers, keep
@@ -249,10 +279,77 @@ def bench_gemv(qn, torch, lib, inputs, copies=40, iters=400):
                           "call_us_wall": round(call_us, 3), "kernel_bytes": kern_bytes,
                           "kernel_gbs": round(gbs_kernel, 1), "kernel_frac": round(gbs_kernel / PEAK_HBM_GBS, 4),
                           "layer_bytes": layer_bytes, "layer_gbs_device": round(gbs_layer, 1),
-                          "layer_frac": round(gbs_layer / PEAK_HBM_GBS, 4)}
+                          "layer_frac": round(gbs_layer / PEAK_HBM_GBS, 4),
+                          "stream": gemv_stream(torch, f, sets, layer_bytes)}
         del sets
         torch.cuda.empty_cache()
+    out["move_probe_9mb"] = move_probe(torch)
     return out
+
+
+def gemv_stream(torch, f, sets, layer_bytes, replays=10):
+    """Back-to-back stream of distinct decode GEMVs: one call per weight copy captured
+    in a HIP graph (no host launch gaps, no event pairs), replayed; every replay's
+    outputs must equal the eager outputs bit for bit."""
+    eager = [s[4].clone() for s in sets]  # y of each copy from the eager calls above
+    st = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        h = torch.cuda.current_stream().cuda_stream
+        for s in sets:
+            a = s[7]
+            rc = f(*(a[:-1] + (h,)))
+            if rc:
+                raise RuntimeError("gemv capture rc %d" % rc)
+    for s in sets:
+        s[4].zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    ok = all(torch.equal(s[4], e) for s, e in zip(sets, eager))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ok = ok and all(torch.equal(s[4], e) for s, e in zip(sets, eager))
+    us = e0.elapsed_time(e1) / (replays * len(sets)) * 1e3
+    del g
+    gbs = layer_bytes / (us * 1e-6) / 1e9
+    return {"us_per_call": round(us, 3), "layer_gbs": round(gbs, 1), "layer_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "replays_match_eager": ok}
+
+
+def move_probe(torch, nbytes=8933376, copies=40, replays=10):
+    """Empirical ceiling of one small launch that moves ~9 MB through HBM: a plain
+    device copy of nbytes / 2 into another nbytes / 2 (read + write = nbytes), 40
+    distinct buffer pairs in a HIP graph, so every copy misses the last-level cache."""
+    half = nbytes // 4  # int16 elements in nbytes / 2
+    srcs = [torch.ones(half, dtype=torch.int16, device="cuda") for _ in range(copies)]
+    dsts = [torch.empty_like(t) for t in srcs]
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        for a, b in zip(srcs, dsts):
+            b.copy_(a)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for a, b in zip(srcs, dsts):
+            b.copy_(a)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (replays * copies) * 1e3
+    moved = 4 * half
+    del g, srcs, dsts
+    torch.cuda.empty_cache()
+    gbs = moved / (us * 1e-6) / 1e9
+    return {"bytes_moved": moved, "us": round(us, 3), "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def bench_merge(qn, torch, inputs, iters=5):
@@ -521,7 +618,8 @@ def main():
         print(json.dumps(bench_stack(qn, torch, inputs)))
         return
 
-    st = bench_step(args, qn, torch, lib, inputs)
+    hashes = {} if args.only is None else None
+    st = bench_step(args, qn, torch, lib, inputs, hashes=hashes)
     log("step %.3f ms" % (st["sec"] * 1e3))
     if args.only == "step":
         print(json.dumps({"ms_per_step": st["sec"] * 1e3, "kernels": st["kernels"], "roofline": st["roofline"]}))
@@ -565,6 +663,7 @@ def main():
                            "(dequantize-then-GEMM at 4096 tokens)",
                    "flops_per_step": st["flops"], "parallelism": "single GPU"},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "step_ms_device": st["step_ms"],
         "roofline": st["roofline"],
         "cpu_baseline": cpu,
         "kernels": st["kernels"],
@@ -577,6 +676,7 @@ def main():
         "dtype_sweep_forward": sweep,
         "merge": merge,
         "stack_train_step": stack,
+        "inputs_sha256": hashes,
     }
     print(json.dumps(line))
 
