@@ -244,49 +244,90 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvP p, Nf4Tables t
 
 // y[m, n] = sum over slices of the partials + T[m, :] . B[n, :] + bias[n], with
 // T = s (sum over slices of the lora_a rows).  Workgroup (256 columns, token m)
-// forms T[m, :] in LDS first; the workgroups of column block 0 also write
-// t0 = x A^T when asked.  S is a template parameter so that every load of a sum
-// is issued before the first add.
+// forms T[m, :] in LDS; the workgroups of column block 0 also write t0 = x A^T
+// when asked.  For r <= 64, r % 8 == 0 every global load of a thread (its
+// column's S partial sums, bias, lora_b row, and its share of the r x S partial
+// sums of T) is issued before the first is used, so the kernel waits on memory
+// once; T's slices are then added in slice order through LDS.  Other ranks take
+// the same sums in two dependent rounds.
 template <int CD, int S>
 __global__ __launch_bounds__(kThreads) void k_gemv_epi(GemvP p) {
-  extern __shared__ float s_t[];  // [r]
+  extern __shared__ float s_t[];  // [r] sums, then (fast path) [S][64] staged partial sums
   const int tid = threadIdx.x;
   const int m = blockIdx.y;
   const int64_t N = p.w.rows;
   const float* pm = p.part + (int64_t)m * p.ld;
   const int64_t ss = (int64_t)kMaxM * p.ld;
-  for (int t = tid; t < p.r; t += kThreads) {
+  const int64_t n = (int64_t)blockIdx.x * kThreads + tid;
+  const int64_t nc = n < N ? n : N - 1;  // clamped: every lane loads, out-of-range lanes store nothing
+  float v = 0.f, lora = 0.f;
+  if (p.r <= 64 && (p.r & 7) == 0) {
     float pv[S];
 #pragma unroll
-    for (int i = 0; i < S; ++i) pv[i] = pm[i * ss + p.n_pad + t];
-    float v = 0.f;
+    for (int i = 0; i < S; ++i) pv[i] = pm[i * ss + nc];
+    // bias through a buffer of zero size when absent: the load returns 0, no branch
+    const rsrc_t rb = make_rsrc(p.bias, p.bias ? N * 2 : 0);
+    const uint32_t braw = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(nc * 2), 0, 0);
+    const rsrc_t rB = make_rsrc(p.B, N * p.r * 2);
+    u32x4_t bv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      bv[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rB, (int)(uint32_t)(q * 8 < p.r ? (nc * p.r + 8 * q) * 2 : 0), 0, 0));
+    // T's partial sums: slice i = tid / 64 + 4 k, rank column t = tid % 64
+    const int t = tid & 63;
+    float tp[(S + 3) / 4];
+#pragma unroll
+    for (int k = 0; k < (S + 3) / 4; ++k) {
+      const int i = (tid >> 6) + 4 * k;
+      tp[k] = pm[(i < S ? i : 0) * ss + p.n_pad + (t < p.r ? t : 0)];
+    }
+#pragma unroll
+    for (int k = 0; k < (S + 3) / 4; ++k) {
+      const int i = (tid >> 6) + 4 * k;
+      if (i < S) s_t[64 + i * 64 + t] = tp[k];
+    }
+    __syncthreads();
+    if (tid < p.r) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < S; ++i) sum += s_t[64 + i * 64 + tid];
+      s_t[tid] = sum * p.scale;
+      if (p.t0 && blockIdx.x == 0) p.t0[(int64_t)m * p.r + tid] = sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q * 8 < p.r) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          lora = fmaf(s_t[8 * q + e], from_cd16<CD>((uint16_t)(bv[q][e >> 1] >> (16 * (e & 1)))), lora);
+      }
 #pragma unroll
     for (int i = 0; i < S; ++i) v += pv[i];
-    s_t[t] = v * p.scale;
-    if (p.t0 && blockIdx.x == 0) p.t0[(int64_t)m * p.r + t] = v;
-  }
-  __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * kThreads + tid;
-  if (n >= N) return;
-  float pv[S];
-#pragma unroll
-  for (int i = 0; i < S; ++i) pv[i] = pm[i * ss + n];
-  const float bias = p.bias ? load_cd<CD>(p.bias, n) : 0.f;
-  float lora = 0.f;
-  if ((p.r & 7) == 0) {
-    for (int t = 0; t < p.r; t += 8) {
-      const u32x4_t bv = *(const u32x4_t*)((const uint16_t*)p.B + n * p.r + t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        lora = fmaf(s_t[t + e], from_cd16<CD>((uint16_t)(bv[e >> 1] >> (16 * (e & 1)))), lora);
-    }
+    v += lora + (p.bias ? from_cd16<CD>((uint16_t)braw) : 0.f);
   } else {
-    for (int t = 0; t < p.r; ++t) lora = fmaf(s_t[t], load_cd<CD>(p.B, n * p.r + t), lora);
-  }
-  float v = 0.f;
+    for (int t = tid; t < p.r; t += kThreads) {
+      float tv[S];
 #pragma unroll
-  for (int i = 0; i < S; ++i) v += pv[i];
-  store_cd<CD>(p.y, m * N + n, v + lora + bias);
+      for (int i = 0; i < S; ++i) tv[i] = pm[i * ss + p.n_pad + t];
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < S; ++i) sum += tv[i];
+      s_t[t] = sum * p.scale;
+      if (p.t0 && blockIdx.x == 0) p.t0[(int64_t)m * p.r + t] = sum;
+    }
+    __syncthreads();
+    float pv[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) pv[i] = pm[i * ss + nc];
+    const float bias = p.bias ? load_cd<CD>(p.bias, nc) : 0.f;
+    for (int t = 0; t < p.r; ++t) lora = fmaf(s_t[t], load_cd<CD>(p.B, nc * p.r + t), lora);
+#pragma unroll
+    for (int i = 0; i < S; ++i) v += pv[i];
+    v += lora + bias;
+  }
+  if (n < N) store_cd<CD>(p.y, m * N + n, v);
 }
 
 // VALU decode GEMV: one wavefront per output row (f32, and other shapes).
@@ -401,7 +442,7 @@ int gemv_forward_t(const LayerCall& c, void* y, float* t_save) {
         if (rc) return rc;
       }
       ProfScope prof(QLORA_K_REDUCE, c.stream);
-      const size_t lds = (size_t)c.r * sizeof(float);
+      const size_t lds = (size_t)(c.r <= 64 && c.r % 8 == 0 ? 64 * (1 + P.S) : c.r) * sizeof(float);
       if (lds > 65536) return set_error(QLORA_ERR_UNSUPPORTED, "decode: rank %d too large", c.r);
       const dim3 eg((unsigned)ceil_div(c.w.rows, kThreads), (unsigned)c.m);
       switch (P.S) {

@@ -79,6 +79,26 @@ def test_forward_decode_small_shapes(m, cd):
     assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"]), cd, "decode small")
 
 
+@pytest.mark.parametrize("m,N,K,r,bias", [
+    (3, 200, 512, 5, True),     # odd rank: the epilogue's general path; ragged N
+    (16, 264, 1024, 64, True),  # rank 64: the single-round path at its limit
+    (1, 136, 512, 24, False),   # rank 24 (a multiple of 8, not of 16)
+])
+def test_forward_decode_epilogue_paths(m, N, K, r, bias):
+    """Decode (m <= 16) in bf16 with the saved T0 = x A^T, bias on and off, ranks that
+    take either path of the split-K GEMV's epilogue."""
+    L = inputs.random_layer(m, N, K, r, seed=m * 100 + r, cd="bf16", with_bias=bias, with_dy=False)
+    say("fwd decode epilogue", m, N, K, r, bias)
+    g = to_gpu(L)
+    y, t0 = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], save_t=True)
+    torch.cuda.synchronize()
+    o = oracle_layer(L)
+    assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"]), "bf16", "decode y")
+    ref_t0 = np.asarray(o["x"], np.float64) @ np.asarray(o["A"], np.float64).T
+    got = to_np(t0).astype(np.float64)
+    assert oracle.rel_l2(got, ref_t0) <= 1e-5, "decode T0"
+
+
 def test_forward_save_t_and_leading_dims():
     L = inputs.random_layer(60, 128, 256, 8, seed=3, with_dy=False)
     say("fwd save_t")
