@@ -220,6 +220,25 @@ struct SkRed {
 };
 // One launch for one or two reductions (b may be null).
 int skinny_reduce_jobs(int cd, const SkRed& a, const SkRed* b, hipStream_t s);
+// The device form of one or two reductions (workgroups of kRedThreads threads, one
+// thread per element; job 1 takes the workgroups after job 0's nblk).
+constexpr int kRedThreads = 256;
+constexpr int kRedBR = 64;  // rank columns of the skinny kernel's partial sums
+struct RedJob {
+  const float* part;
+  const float* side;
+  float* out32;
+  void* outcd;
+  void* outt;
+  void* side_t;
+  uint32_t S, P, R, ldcd, ldt, width, rows, nblk;
+  float sc32, sccd;
+  int trans;
+};
+struct RedJobs {
+  RedJob j[2];
+};
+int make_red_jobs(const SkRed& a, const SkRed* b, RedJobs& js, int64_t& blocks);
 
 // dst [cols][ld_dst] = cd(scale * src[rows][ld_src]^T) (src in the compute dtype or
 // fp32), columns rows .. ld_dst-1 of dst zero; one launch carries one or two.
@@ -239,7 +258,9 @@ int rank_add_masked(int cd, void* dx, const uint8_t* mask, const void* dt, int64
                     int64_t M, int64_t K, hipStream_t s);
 size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags);
 size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags);
-int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s);
+// red: a reduction that rides on the same launch (its workgroups follow the
+// dequantize ones), or null.
+int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s, const SkRed* red = nullptr);
 int launch_forward(const LayerCall& c, void* y, float* t_save);
 int launch_backward(const LayerCall& c, const void* dy, const float* t_saved, void* dx,
                     float* d_a, float* d_b);

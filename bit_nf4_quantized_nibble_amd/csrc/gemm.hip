@@ -577,16 +577,31 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
     if ((rc = apply_mask(CD, c.x, c.drop_mask, M * K, ws + P.off_xm, c.stream))) return rc;
     lx = ws + P.off_xm;
   }
+  // T0 = x A^T (fp32, saved on request) and T = s T0 in cd for the GEMM's tail.  On
+  // the dequantize-then-GEMM path the reduction of the skinny kernel's slices rides
+  // on the dequantize launch.
+  const bool dense = P.dense && dense256_ok(c, false);
+  SkRed red;
+  bool red_pending = false;
   if (skinny_ok(CD, c.r)) {
     int S;
     if ((rc = skinny(CD, false, lx, K, M, c.lora_a, K, M, c.r, K, part, &S, c.stream, QLORA_K_LORA_DOWN))) return rc;
-    if ((rc = skinny_reduce(CD, part, S, M, c.r, 1.0f, t_save, false, c.scale, tcd, P.r_pad, c.stream))) return rc;
+    red.part = part;
+    red.S = S;
+    red.P = M;
+    red.R = c.r;
+    red.out32 = t_save;
+    red.sccd = c.scale;
+    red.outcd = tcd;
+    red.ldcd = P.r_pad;
+    if (dense) red_pending = true;
+    else if ((rc = skinny_reduce_jobs(CD, red, nullptr, c.stream))) return rc;
   } else if ((rc = lora_down<CD>(c, lx, P.st, part, t_save, 1.0f, tcd, c.scale, P.r_pad))) {
     return rc;
   }
-  if (P.dense && dense256_ok(c, false)) {
+  if (dense) {
     void* wd = ws + P.off_wd;
-    if ((rc = dequant_into(c.w, CD, wd, false, c.stream))) return rc;
+    if ((rc = dequant_into(c.w, CD, wd, false, c.stream, red_pending ? &red : nullptr))) return rc;
     return dense256_forward(c, wd, tcd, P.r_pad, y, P.dsp, ws + P.off_split);
   }
   if (fused256_ok(c, false)) return fused256_forward(c, tcd, P.r_pad, y);
@@ -654,6 +669,8 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   ta.cols = K;
   ta.dst = at;
   ta.ld_dst = P.r_pad;
+  SkRed red_dt;  // the dT reduction, launched here or riding on W~^T's dequantize
+  bool red_dt_pending = false;
   if (P.sk_n) {
     void* bt = ws + P.off_bt;  // B^T [r][n_pad], zero past N
     TransposeSpec tb;
@@ -666,21 +683,21 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     if ((rc = transpose_jobs(CD, tb, at ? &ta : nullptr, c.stream))) return rc;
     int S;
     if ((rc = skinny(CD, false, dy, N, M, bt, P.n_pad, M, r, P.n_pad, part, &S, c.stream, QLORA_K_BWD_DT))) return rc;
-    SkRed red;
-    red.part = part;
-    red.S = S;
-    red.P = M;
-    red.R = r;
-    red.sc32 = c.scale;
-    red.out32 = dt;
-    red.sccd = c.scale;
-    red.outcd = dtcd;
-    red.ldcd = P.r_pad;
-    red.outt = dtt;
-    red.ldt = P.m_pad;
-    red.side = T0;
-    red.side_t = t0t;
-    if ((rc = skinny_reduce_jobs(CD, red, nullptr, c.stream))) return rc;
+    red_dt.part = part;
+    red_dt.S = S;
+    red_dt.P = M;
+    red_dt.R = r;
+    red_dt.sc32 = c.scale;
+    red_dt.out32 = dt;
+    red_dt.sccd = c.scale;
+    red_dt.outcd = dtcd;
+    red_dt.ldcd = P.r_pad;
+    red_dt.outt = dtt;
+    red_dt.ldt = P.m_pad;
+    red_dt.side = T0;
+    red_dt.side_t = t0t;
+    if (dense_dx) red_dt_pending = true;
+    else if ((rc = skinny_reduce_jobs(CD, red_dt, nullptr, c.stream))) return rc;
   } else {
     if (at && (rc = transpose_jobs(CD, ta, nullptr, c.stream))) return rc;
     GemmParams p = base_params(c);
@@ -709,7 +726,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   }
   if (dense_dx) {
     void* wdt = ws + P.off_wdt;
-    if ((rc = dequant_into(c.w, CD, wdt, true, c.stream))) return rc;
+    if ((rc = dequant_into(c.w, CD, wdt, true, c.stream, red_dt_pending ? &red_dt : nullptr))) return rc;
     if ((rc = dense256_dx(c, dy, wdt, dt_gemm, P.r_pad, dx, P.dsp, ws + P.off_split, at))) return rc;
   } else if (dx && fused256_ok(c, true)) {
     rc = fused256_dx(c, dy, dt_gemm, P.r_pad, dx);

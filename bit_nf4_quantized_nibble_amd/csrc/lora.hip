@@ -23,6 +23,7 @@
 //       (8 consecutive k of one p) is gathered with 16-bit reads, and the swizzle
 //       puts the two row groups a read instruction touches on distinct banks.
 #include "common.h"
+#include "reduce_dev.h"
 
 namespace qnf4 {
 namespace {
@@ -38,6 +39,7 @@ constexpr int B_BYTES = BR * ROWB;   // 8 KiB
 constexpr int NBUF = 3;
 constexpr int STAGE = A_BYTES + B_BYTES;
 constexpr int kCopies = 6;       // DMA instructions per lane per stage (4 Aop + 2 Bop)
+static_assert(BR == kRedBR && kThreads == kRedThreads, "the partial-sum layout the reduction reads");
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -195,56 +197,9 @@ __global__ __launch_bounds__(kThreads) void k_skinny(SkP p) {
     }
 }
 
-// Reductions of per-slice partial sums (see SkRed), one thread per element of a
-// rows x width grid (rows: P, or ldt with a transposed output; width: R, or ldcd
-// with a padded cd output); workgroups [0, nblk of job 0) take job 0, the rest
-// job 1.  32-bit indexing (the launcher checks the sizes).
-struct RedJob {
-  const float* part;
-  const float* side;
-  float* out32;
-  void* outcd;
-  void* outt;
-  void* side_t;
-  uint32_t S, P, R, ldcd, ldt, width, rows, nblk;
-  float sc32, sccd;
-  int trans;
-};
-struct RedJobs {
-  RedJob j[2];
-};
-
 template <int CD>
 __global__ __launch_bounds__(kThreads) void k_skreduce(RedJobs js) {
-  const int w = blockIdx.x >= js.j[0].nblk ? 1 : 0;
-  const RedJob& j = js.j[w];
-  const uint32_t idx = (blockIdx.x - (w ? js.j[0].nblk : 0u)) * kThreads + threadIdx.x;
-  if (idx >= j.rows * j.width) return;
-  const uint32_t pr = idx / j.width, t = idx - pr * j.width;
-  if (pr >= j.P) {  // zero columns P .. ldt-1 of the transposed copies
-    if (t < j.R) {
-      if (j.outt) store_cd<CD>(j.outt, (int64_t)(t * j.ldt + pr), 0.f);
-      if (j.side_t) store_cd<CD>(j.side_t, (int64_t)(t * j.ldt + pr), 0.f);
-    }
-    return;
-  }
-  if (t >= j.R) {  // width > R only with a padded cd output
-    store_cd<CD>(j.outcd, (int64_t)(pr * j.ldcd + t), 0.f);
-    return;
-  }
-  // every load leaves before the first add (slices past S read slice 0 and are
-  // dropped; without a side input the side load reads the first partial sum)
-  float v[8];
-#pragma unroll
-  for (int z = 0; z < 8; ++z) v[z] = j.part[((uint32_t)(z < (int)j.S ? z : 0) * j.P + pr) * BR + t];  // S <= 8
-  const float sv = *(j.side ? j.side + pr * j.R + t : j.part);
-  float sum = 0.f;
-#pragma unroll
-  for (int z = 0; z < 8; ++z) sum += z < (int)j.S ? v[z] : 0.f;  // slice order
-  if (j.out32) j.out32[j.trans ? t * j.P + pr : pr * j.R + t] = sum * j.sc32;
-  if (j.outcd) store_cd<CD>(j.outcd, (int64_t)(pr * j.ldcd + t), sum * j.sccd);
-  if (j.outt) store_cd<CD>(j.outt, (int64_t)(t * j.ldt + pr), sum * j.sccd);
-  if (j.side_t) store_cd<CD>(j.side_t, (int64_t)(t * j.ldt + pr), sv);
+  skreduce_block<CD>(js, blockIdx.x);
 }
 
 // dst [cols][ld_dst] (cd) = cd(scale * src[rows][ld_src]^T), src in cd or fp32;
@@ -373,7 +328,7 @@ bool red_job(const SkRed& r, RedJob& j) {
   j.ldt = (uint32_t)r.ldt;
   j.width = (uint32_t)width;
   j.rows = (uint32_t)rows;
-  j.nblk = (uint32_t)ceil_div(rows * width, kThreads);
+  j.nblk = (uint32_t)ceil_div(rows * width, kRedThreads);
   j.sc32 = r.sc32;
   j.sccd = r.sccd;
   j.trans = r.trans ? 1 : 0;
@@ -381,11 +336,20 @@ bool red_job(const SkRed& r, RedJob& j) {
 }
 }  // namespace
 
-int skinny_reduce_jobs(int cd, const SkRed& a, const SkRed* b, hipStream_t s) {
-  RedJobs js = {};
+// The device form of one or two reductions and the workgroups they take.
+int make_red_jobs(const SkRed& a, const SkRed* b, RedJobs& js, int64_t& blocks) {
+  js = RedJobs{};
   if (!red_job(a, js.j[0]) || (b && !red_job(*b, js.j[1])))
     return set_error(QLORA_ERR_UNSUPPORTED, "rank product: %lld x %lld too large", (long long)a.P, (long long)a.R);
-  const int64_t blocks = (int64_t)js.j[0].nblk + (b ? js.j[1].nblk : 0);
+  blocks = (int64_t)js.j[0].nblk + (b ? js.j[1].nblk : 0);
+  return QLORA_OK;
+}
+
+int skinny_reduce_jobs(int cd, const SkRed& a, const SkRed* b, hipStream_t s) {
+  RedJobs js;
+  int64_t blocks;
+  int rc = make_red_jobs(a, b, js, blocks);
+  if (rc) return rc;
   if (blocks == 0) return QLORA_OK;
   ProfScope prof(QLORA_K_REDUCE, s);
   if (cd == CD_BF16) k_skreduce<CD_BF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(js);

@@ -14,6 +14,7 @@
 // workgroup walks one double-quant group (or a 16384-element span without DQ),
 // so the group max and the u8 encoding need no second pass over HBM.
 #include "common.h"
+#include "reduce_dev.h"
 
 namespace qnf4 {
 
@@ -280,9 +281,14 @@ __device__ __forceinline__ float scale_of(uint32_t qa, uint32_t s2) {
 // instruction covers contiguous memory across the wave.  All 8 chunks' codes and
 // scales are requested before the first is used; chunks past the end read past the
 // buffers (zeros) and store nothing.  Same values as k_dequantize.
+// Workgroups from nmain on run the reduction `red` instead (see reduce_dev.h).
 template <int OUT, int DQ>
 __global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, void* __restrict__ out,
-                                                             Nf4Tables tab) {
+                                                             Nf4Tables tab, RedJobs red, uint32_t nmain) {
+  if (blockIdx.x >= nmain) {
+    skreduce_block<OUT == CD_F16 ? CD_F16 : CD_BF16>(red, blockIdx.x - nmain);
+    return;
+  }
   __shared__ float s_lv[16];
   if (threadIdx.x < 16) s_lv[threadIdx.x] = tab.lv[threadIdx.x];
   const rsrc_t rc = make_rsrc(q.codes, n / 2);
@@ -333,8 +339,15 @@ __global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, 
 // double quantization a power-of-two group or one group), codes under 2 GiB
 // (checked by the caller).  Tiles past the last column load the first codes
 // (unused) and write nothing.
+// Workgroup b < gx * (rows / 64) takes slab (b % gx, b / gx); the ones from there
+// on run the reduction `red` instead (see reduce_dev.h).
 template <int OUT, int DQ, int T>
-__global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restrict__ out, Nf4Tables tab) {
+__global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restrict__ out, Nf4Tables tab,
+                                                           RedJobs red, uint32_t gx, uint32_t nmain) {
+  if (blockIdx.x >= nmain) {
+    skreduce_block<OUT>(red, blockIdx.x - nmain);
+    return;
+  }
   __shared__ float s_lv[16];
   __shared__ __attribute__((aligned(16))) uint16_t tile[T][64 * 64];  // [k][n] per tile
   const int tid = threadIdx.x;
@@ -342,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restr
   const int64_t n = q.rows * q.cols;
   const rsrc_t rc = make_rsrc(q.codes, n / 2);
   const ScaleRsrc rs = make_scale_rsrc<DQ>(q, n >> q.bs_shift);
-  const int64_t n0 = (int64_t)blockIdx.y * 64, kb = (int64_t)blockIdx.x * (64 * T);
+  const int64_t n0 = (int64_t)(blockIdx.x / gx) * 64, kb = (int64_t)(blockIdx.x % gx) * (64 * T);
   const int nr = tid >> 2, kc = (tid & 3) * 16;
   uint32_t cw[T][2], qa[T][2], s2[T][2];
 #pragma unroll
@@ -431,34 +444,50 @@ int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s) {
   return check_launch("k_quantize");
 }
 
-int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s);
+int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s, const SkRed* red);
 
 int launch_dequantize(const qlora_nf4_t* q, int out_dtype, void* out, hipStream_t s) {
   const Nf4W w = make_w(q);
-  return dequant_flat(w, out_dtype, out, s);
+  return dequant_flat(w, out_dtype, out, s, nullptr);
 }
 
-// Flat dequantize of all rows * cols elements into out (f32 / bf16 / f16).
-int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s) {
+// The device form of an optional reduction riding on a dequantize launch.
+int ride_along(const SkRed* red, RedJobs& js, int64_t& blocks) {
+  js = RedJobs{};
+  blocks = 0;
+  return red ? make_red_jobs(*red, nullptr, js, blocks) : QLORA_OK;
+}
+
+// Flat dequantize of all rows * cols elements into out (f32 / bf16 / f16); `red`
+// (bf16 / f16 only) rides on the same launch.
+int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s, const SkRed* red) {
   const int64_t n = w.rows * w.cols;
   const Nf4Tables& t = host_tables();
+  RedJobs js;
+  int64_t nred;
+  int rc = ride_along(red, js, nred);
+  if (rc) return rc;
   ProfScope prof(QLORA_K_DEQUANTIZE, s);
-  if (w.bs_shift >= 3 && n % 8 == 0 && (!w.dq || w.g_shift >= 0) && n / 2 < (1LL << 31)) {
+  if (w.bs_shift >= 3 && n % 8 == 0 && (!w.dq || w.g_shift >= 0) && n / 2 < (1LL << 31) &&
+      !(red && cd == CD_F32)) {
     const int64_t grid = ceil_div(n / 8, kThreads * 8);
-    const dim3 g((unsigned)grid), blk(kThreads);
+    if (grid + nred > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
+    const dim3 g((unsigned)(grid + nred)), blk(kThreads);
+    const uint32_t nm = (uint32_t)grid;
     if (cd == CD_BF16) {
-      if (w.dq) k_dequant_chunks<CD_BF16, 1><<<g, blk, 0, s>>>(w, n, out, t);
-      else k_dequant_chunks<CD_BF16, 0><<<g, blk, 0, s>>>(w, n, out, t);
+      if (w.dq) k_dequant_chunks<CD_BF16, 1><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
+      else k_dequant_chunks<CD_BF16, 0><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
     } else if (cd == CD_F16) {
-      if (w.dq) k_dequant_chunks<CD_F16, 1><<<g, blk, 0, s>>>(w, n, out, t);
-      else k_dequant_chunks<CD_F16, 0><<<g, blk, 0, s>>>(w, n, out, t);
+      if (w.dq) k_dequant_chunks<CD_F16, 1><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
+      else k_dequant_chunks<CD_F16, 0><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
     } else if (cd == CD_F32) {
-      if (w.dq) k_dequant_chunks<CD_F32, 1><<<g, blk, 0, s>>>(w, n, out, t);
-      else k_dequant_chunks<CD_F32, 0><<<g, blk, 0, s>>>(w, n, out, t);
+      if (w.dq) k_dequant_chunks<CD_F32, 1><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
+      else k_dequant_chunks<CD_F32, 0><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
     }
     else return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
     return check_launch("k_dequant_chunks");
   }
+  if (red && (rc = skinny_reduce_jobs(cd, *red, nullptr, s))) return rc;
   const int64_t grid = ceil_div(ceil_div(n, 32), kThreads);
   if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
   if (cd == CD_BF16) k_dequantize<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
@@ -469,35 +498,42 @@ int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s) {
 }
 
 template <int OUT, int DQ>
-void run_dqt(bool four, dim3 grid, const Nf4W& w, void* out, const Nf4Tables& t, hipStream_t s) {
-  if (four) k_dequantize_t<OUT, DQ, 4><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
-  else k_dequantize_t<OUT, DQ, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, t);
+void run_dqt(bool four, uint32_t gx, uint32_t nmain, int64_t nred, const Nf4W& w, void* out, const Nf4Tables& t,
+             const RedJobs& js, hipStream_t s) {
+  const dim3 grid((unsigned)(nmain + nred));
+  if (four) k_dequantize_t<OUT, DQ, 4><<<grid, dim3(kThreads), 0, s>>>(w, out, t, js, gx, nmain);
+  else k_dequantize_t<OUT, DQ, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, t, js, gx, nmain);
 }
 
 // Dequantize W into a compute-dtype buffer inside a layer call: [rows, cols]
 // (forward) or its transpose [cols, rows] (dX).  The transpose needs rows and cols
 // to be multiples of 64.
-int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s) {
+int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s, const SkRed* red) {
   if (transposed) {
     const Nf4Tables& t = host_tables();
+    RedJobs js;
+    int64_t nred;
+    int rc = ride_along(red, js, nred);
+    if (rc) return rc;
     ProfScope prof(QLORA_K_DEQUANTIZE, s);
     if (w.rows % 64 || w.cols % 64) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: shape not a multiple of 64");
     if (w.bs_shift < 3 || (w.dq && w.g_shift < 0) || w.rows * w.cols / 2 >= (1LL << 31))
       return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: block / group sizes or size not supported");
     // four tiles per workgroup while that still leaves >= 1024 workgroups, else one
     const int T4 = (w.rows / 64) * ceil_div(w.cols, 256) >= 1024;
-    const dim3 grid((unsigned)ceil_div(w.cols, T4 ? 256 : 64), (unsigned)(w.rows / 64));
+    const int64_t gx = ceil_div(w.cols, T4 ? 256 : 64), nmain = gx * (w.rows / 64);
+    if (nmain + nred > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: tensor too large");
     if (cd == CD_BF16) {
-      if (w.dq) run_dqt<CD_BF16, 1>(T4, grid, w, out, t, s);
-      else run_dqt<CD_BF16, 0>(T4, grid, w, out, t, s);
+      if (w.dq) run_dqt<CD_BF16, 1>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, t, js, s);
+      else run_dqt<CD_BF16, 0>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, t, js, s);
     } else if (cd == CD_F16) {
-      if (w.dq) run_dqt<CD_F16, 1>(T4, grid, w, out, t, s);
-      else run_dqt<CD_F16, 0>(T4, grid, w, out, t, s);
+      if (w.dq) run_dqt<CD_F16, 1>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, t, js, s);
+      else run_dqt<CD_F16, 0>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, t, js, s);
     }
     else return set_error(QLORA_ERR_DTYPE, "dequantize^T: bad dtype %d", cd);
     return check_launch("k_dequantize_t");
   }
-  return dequant_flat(w, cd, out, s);
+  return dequant_flat(w, cd, out, s, red);
 }
 
 }  // namespace qnf4
