@@ -220,6 +220,16 @@ struct SkRed {
 };
 // One launch for one or two reductions (b may be null).
 int skinny_reduce_jobs(int cd, const SkRed& a, const SkRed* b, hipStream_t s);
+
+// One rank product of the skinny kernel (see skinny() in lora.hip).
+struct SkSpec {
+  const void* a = nullptr;
+  int64_t lda = 0, arows = 0;
+  const void* b = nullptr;
+  int64_t ldb = 0, P = 0, R = 0, Kc = 0;
+};
+int skinny_jobs(int cd, bool tn, const SkSpec& a, float* part, int* S_out, const SkSpec* b2, float* part2,
+                int* S2, hipStream_t s, int kind);
 // The device form of one or two reductions (workgroups of kRedThreads threads, one
 // thread per element; job 1 takes the workgroups after job 0's nblk).
 constexpr int kRedThreads = 256;

@@ -756,9 +756,24 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   if (P.sk_n) {
     float* part2 = (float*)(ws + P.off_part2);
     int Sa, Sb;
-    if ((rc = skinny(CD, true, lx, K, M, dtt, P.m_pad, K, r, P.m_pad, part, &Sa, c.stream, QLORA_K_BWD_DA))) return rc;
-    if ((rc = skinny(CD, true, dy, N, M, t0t, P.m_pad, N, r, P.m_pad, part2, &Sb, c.stream, QLORA_K_BWD_DB)))
-      return rc;
+    SkSpec pa, pb;  // dA: x^T against dT^T;  dB: dY^T against T0^T (one launch)
+    pa.a = lx;
+    pa.lda = K;
+    pa.arows = M;
+    pa.b = dtt;
+    pa.ldb = P.m_pad;
+    pa.P = K;
+    pa.R = r;
+    pa.Kc = P.m_pad;
+    pb.a = dy;
+    pb.lda = N;
+    pb.arows = M;
+    pb.b = t0t;
+    pb.ldb = P.m_pad;
+    pb.P = N;
+    pb.R = r;
+    pb.Kc = P.m_pad;
+    if ((rc = skinny_jobs(CD, true, pa, part, &Sa, &pb, part2, &Sb, c.stream, QLORA_K_BWD_DA))) return rc;
     SkRed ra, rb;
     ra.part = part;
     ra.S = Sa;

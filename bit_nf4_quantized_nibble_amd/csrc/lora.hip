@@ -22,6 +22,8 @@
 //       256-byte rows of p, chunk c of row k at chunk c ^ (k % 16); a fragment
 //       (8 consecutive k of one p) is gathered with 16-bit reads, and the swizzle
 //       puts the two row groups a read instruction touches on distinct banks.
+#include <algorithm>
+
 #include "common.h"
 #include "reduce_dev.h"
 
@@ -120,8 +122,18 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
+// One launch carries one or two products (blockIdx.z picks the job; workgroups
+// outside a job's own grid leave at once).
+struct SkP2 {
+  SkP j[2];
+  uint32_t nx[2], ny[2];
+};
+
 template <int CD, int TN>
-__global__ __launch_bounds__(kThreads) void k_skinny(SkP p) {
+__global__ __launch_bounds__(kThreads) void k_skinny(SkP2 ps) {
+  const int jb = blockIdx.z;
+  if (blockIdx.x >= ps.nx[jb] || blockIdx.y >= ps.ny[jb]) return;
+  const SkP& p = ps.j[jb];
   __shared__ __attribute__((aligned(1024))) char lds[NBUF * STAGE];  // stage b: [A | B]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -278,33 +290,65 @@ size_t skinny_part_bytes(int64_t P, int64_t Kc) {
 // part = per-slice sums of Aop . Bop^T over the contraction 0 .. Kc (a multiple of
 // 64); Aop NT [P][lda] or TN [arows][lda]; Bop [R][ldb] with ldb >= Kc, zero
 // between its true width and Kc.
-int skinny(int cd, bool tn, const void* a, int64_t lda, int64_t arows, const void* b, int64_t ldb, int64_t P,
-           int64_t R, int64_t Kc, float* part, int* S_out, hipStream_t s, int kind) {
-  if (Kc % BK || lda % 8 || ldb % 8 || ldb < Kc || (tn && P % 8))
+namespace {
+int skinny_params(bool tn, const SkSpec& sp, float* part, SkP& p, int* S_out) {
+  if (sp.Kc % BK || sp.lda % 8 || sp.ldb % 8 || sp.ldb < sp.Kc || (tn && sp.P % 8))
     return set_error(QLORA_ERR_UNSUPPORTED, "rank product: shape not supported by the skinny kernel");
-  SkP p = {};
-  p.a = a;
-  p.lda = lda;
-  p.arows = arows;
-  p.b = b;
-  p.ldb = ldb;
-  p.P = P;
-  p.R = R;
-  p.Kc = Kc;
+  p = SkP{};
+  p.a = sp.a;
+  p.lda = sp.lda;
+  p.arows = sp.arows;
+  p.b = sp.b;
+  p.ldb = sp.ldb;
+  p.P = sp.P;
+  p.R = sp.R;
+  p.Kc = sp.Kc;
   p.part = part;
-  int S;
-  skinny_split(P, Kc, &S, &p.kslice);
-  *S_out = S;
-  const dim3 grid((unsigned)ceil_div(P, BP), (unsigned)S);
+  skinny_split(sp.P, sp.Kc, S_out, &p.kslice);
+  return QLORA_OK;
+}
+}  // namespace
+
+// part = per-slice sums of Aop . Bop^T over the contraction 0 .. Kc (a multiple of
+// 64); Aop NT [P][lda] or TN [arows][lda]; Bop [R][ldb] with ldb >= Kc, zero
+// between its true width and Kc.  With b2 a second product of the same kind
+// shares the launch (its slice count in *S2).
+int skinny_jobs(int cd, bool tn, const SkSpec& a, float* part, int* S_out, const SkSpec* b2, float* part2,
+                int* S2, hipStream_t s, int kind) {
+  SkP2 ps = {};
+  int rc = skinny_params(tn, a, part, ps.j[0], S_out);
+  if (rc) return rc;
+  ps.nx[0] = (uint32_t)ceil_div(a.P, BP);
+  ps.ny[0] = (uint32_t)*S_out;
+  if (b2) {
+    if ((rc = skinny_params(tn, *b2, part2, ps.j[1], S2))) return rc;
+    ps.nx[1] = (uint32_t)ceil_div(b2->P, BP);
+    ps.ny[1] = (uint32_t)*S2;
+  }
+  const dim3 grid(std::max(ps.nx[0], ps.nx[1]), std::max(ps.ny[0], ps.ny[1]), b2 ? 2 : 1);
   ProfScope prof(kind, s);
   if (cd == CD_BF16) {
-    if (tn) k_skinny<CD_BF16, 1><<<grid, dim3(kThreads), 0, s>>>(p);
-    else k_skinny<CD_BF16, 0><<<grid, dim3(kThreads), 0, s>>>(p);
+    if (tn) k_skinny<CD_BF16, 1><<<grid, dim3(kThreads), 0, s>>>(ps);
+    else k_skinny<CD_BF16, 0><<<grid, dim3(kThreads), 0, s>>>(ps);
   } else {
-    if (tn) k_skinny<CD_F16, 1><<<grid, dim3(kThreads), 0, s>>>(p);
-    else k_skinny<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(p);
+    if (tn) k_skinny<CD_F16, 1><<<grid, dim3(kThreads), 0, s>>>(ps);
+    else k_skinny<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(ps);
   }
   return check_launch("k_skinny");
+}
+
+int skinny(int cd, bool tn, const void* a, int64_t lda, int64_t arows, const void* b, int64_t ldb, int64_t P,
+           int64_t R, int64_t Kc, float* part, int* S_out, hipStream_t s, int kind) {
+  SkSpec sp;
+  sp.a = a;
+  sp.lda = lda;
+  sp.arows = arows;
+  sp.b = b;
+  sp.ldb = ldb;
+  sp.P = P;
+  sp.R = R;
+  sp.Kc = Kc;
+  return skinny_jobs(cd, tn, sp, part, S_out, nullptr, nullptr, nullptr, s, kind);
 }
 
 namespace {
