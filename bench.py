@@ -230,6 +230,85 @@ def bench_dtype_sweep(qn, torch, lib, inputs, steps=3):
     return out
 
 
+def bench_path_sweep(qn, torch, lib, inputs, copies=8, replays=5):
+    """Forward of q_proj and gate_proj (r 64, bf16) at several token counts on both
+    dequant-GEMM paths: fused (decode inside the GEMM) and dequantize-then-GEMM (W~
+    written once into the call's workspace).  The calls cycle through `copies`
+    copies of the two quantized weights (about 300 MB of codes and scales, more than
+    the 256 MB last-level cache), so each call reads its weight from HBM as a block
+    of a real model would.  Reports time per q + gate pair, TFLOP/s and the
+    workspace each path needs (the memory side of the trade-off)."""
+    ms = (32, 64, 128, 256, 512, 1024, 2048, 4096)
+    Ls = inputs.prefill(seed=0, cd="bf16", m=max(ms), projections=["q_proj", "gate_proj"])
+    x = Ls[0].x.to("cuda")
+    cd = qn.dtype_code(x.dtype)
+    stream = torch.cuda.current_stream().cuda_stream
+    projs = []
+    for L in Ls:
+        W = L.W.to("cuda")
+        q0 = qn.quantize(W, L.block_size, L.double_quant, L.dq_group)
+        del W
+        qs = [qn.NF4Weight(q0.rows, q0.cols, q0.block_size, True, q0.dq_group, q0.codes.clone(), None,
+                           q0.absmax_q.clone(), q0.absmax_scale2.clone()) for _ in range(copies)]
+        projs.append((L, qs, [q.descriptor() for q in qs], L.A.to("cuda"), L.B.to("cuda"),
+                      torch.empty(max(ms), L.N, dtype=x.dtype, device="cuda")))
+        del q0
+    paths = (("fused", qn._lib.QLORA_FLAG_FUSED), ("dequant", qn._lib.QLORA_FLAG_DEQUANT_GEMM))
+    wsb = max(qn.workspace_bytes(0, m, L.N, L.K, L.r, x.dtype, f) for m in ms for L in Ls for _, f in paths)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    f = lib.qlora_linear_fwd
+    st = torch.cuda.Stream()
+    out = {"weights_cycled": copies, "timing": "HIP graph of the 2 x copies calls, replayed %d times" % replays}
+    for m in ms:
+        flops = sum(fwd_flops(m, L.N, L.K, L.r) for L in Ls)
+        res = {}
+        for path, flag in paths:
+            calls = [(ctypes.byref(d), x.data_ptr(), m, A.data_ptr(), B.data_ptr(), L.r, float(L.alpha), flag, None,
+                      cd, y.data_ptr(), None, ws.data_ptr(), ws.numel(), st.cuda_stream)
+                     for c in range(copies) for (L, qs, ds, A, B, y) in projs for d in (ds[c],)]
+
+            def fwd():
+                for a in calls:
+                    rc = f(*a)
+                    if rc:
+                        raise RuntimeError("fwd %s m=%d: %d %s" % (path, m, rc, lib.qlora_last_error()))
+
+            # eager once (the reference outputs), then the same calls as one graph, so
+            # that host launch gaps do not hide the kernels' time at small m
+            torch.cuda.synchronize()
+            with torch.cuda.stream(st):
+                fwd()
+            st.synchronize()
+            eager = [p[5][:m].clone() for p in projs]
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st):
+                fwd()
+            for p in projs:
+                p[5][:m].fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            same = all(torch.equal(e, p[5][:m]) for e, p in zip(eager, projs))
+            # replay() launches on the current stream: the events go there too
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            same = same and all(torch.equal(e, p[5][:m]) for e, p in zip(eager, projs))
+            sec = e0.elapsed_time(e1) / 1e3 / (replays * copies)
+            del g
+            need = max(qn.workspace_bytes(0, m, L.N, L.K, L.r, x.dtype, flag) for L in Ls)
+            res[path] = {"ms": round(sec * 1e3, 4), "tflops": round(flops / sec / 1e12, 1),
+                         "workspace_mb": round(need / 2 ** 20, 1), "replay_matches_eager": same}
+        res["faster"] = min(("fused", "dequant"), key=lambda k: res[k]["ms"])
+        out["m%d" % m] = res
+    del projs, ws, x
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_gemv(qn, torch, lib, inputs, copies=40, iters=400):
     """Decode GEMV over `copies` independent weights (> the 256 MB last-level cache),
     so each call streams its weight from HBM."""
@@ -585,7 +664,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep", "merge", "stack", "copyprobe"], default=None,
+    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep", "merge", "stack", "copyprobe", "paths"],
+                    default=None,
                     help="run one part (for profiling); the JSON line needs the full run")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -616,6 +696,9 @@ def main():
     if args.only == "merge":
         print(json.dumps(bench_merge(qn, torch, inputs)))
         return
+    if args.only == "paths":
+        print(json.dumps(bench_path_sweep(qn, torch, lib, inputs)))
+        return
     if args.only == "stack":
         print(json.dumps(bench_stack(qn, torch, inputs)))
         return
@@ -638,6 +721,8 @@ def main():
     log("merge done")
     stack = bench_stack(qn, torch, inputs)
     log("stack done")
+    paths = bench_path_sweep(qn, torch, lib, inputs)
+    log("path sweep done")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)
@@ -678,6 +763,7 @@ def main():
         "dtype_sweep_forward": sweep,
         "merge": merge,
         "stack_train_step": stack,
+        "fused_vs_dequant_forward": paths,
         "inputs_sha256": hashes,
     }
     print(json.dumps(line))

@@ -20,8 +20,8 @@ Public API (names follow the pages' problem statement):
 
 path: "fused" decodes W inside the GEMM kernels; "dequant" writes W~ (or W~^T for
 dX) into the workspace first and runs a dense GEMM; "auto" lets the library pick
-(dequantize-then-GEMM from 1024 tokens up).  Calls with at most 16 tokens take
-the decode GEMV either way.
+(dequantize-then-GEMM for bf16 / f16; "fused" saves the rows x cols copy in the
+workspace).  Calls with at most 16 tokens take the decode GEMV either way.
 """
 from __future__ import annotations
 

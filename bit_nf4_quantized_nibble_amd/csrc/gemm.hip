@@ -31,8 +31,10 @@
 namespace qnf4 {
 
 // gemm256.hip: the 256 x 256 double-buffered fused kernels (bf16 / f16).
-int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* y);
-int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r_pad, void* dx);
+int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* y, const DenseSplit& sp,
+                     void* split_ws);
+int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r_pad, void* dx, const DenseSplit& sp,
+                void* split_ws);
 bool fused256_ok(const LayerCall& c, bool dx);
 bool dense256_ok(const LayerCall& c, bool dx);
 // lora.hip: the rank-r products on the skinny MFMA kernel
@@ -416,28 +418,32 @@ Split choose_split(int64_t tiles, int64_t k, int bk) {
 constexpr int64_t kAlign = 256;
 inline int64_t al(int64_t b) { return round_up(b, kAlign); }
 
-// Dequantize-then-GEMM from this many tokens up (unless a path flag decides):
-// there the one-time dequantization (about 4.6 bytes of HBM traffic per weight) costs
-// less than decoding W again in every token tile of the fused kernels.
-constexpr int64_t kDenseMinM = 1024;
-
 // Whether a call takes the dequantize-then-GEMM path, from its shape and flags
 // alone (the workspace query must agree with the launch).  The launch also needs
-// dense256_ok; when that fails the copy's workspace is simply unused.
+// dense256_ok; when that fails the copy's workspace is simply unused.  Unless a
+// path flag decides, every call the GEMV does not take goes this way: with each
+// weight read from HBM, writing W~ once and running the dense GEMM was as fast as
+// the fused kernels or faster at every token count from 32 to 4096 (q_proj and
+// gate_proj shapes, r 64, bf16); the fused kernels need no rows x cols copy in the
+// workspace, which is their reason to exist.
 bool dense_path(int64_t m, int64_t rows, int64_t cols, int cd, int32_t flags, bool dx) {
+  (void)m;
   if (cd != CD_BF16 && cd != CD_F16) return false;
   if (cols % 64 || (dx && rows % 64)) return false;
   if (flags & QLORA_FLAG_FUSED) return false;
-  if (flags & QLORA_FLAG_DEQUANT_GEMM) return true;
-  return m >= kDenseMinM;
+  return true;
 }
+
+// Whether the 256 x 256 GEMMs (dense or fused) may take a call of this dtype: their
+// cut last round needs its slices' partial sums in the workspace.
+inline bool big_tiles(int cd) { return cd == CD_BF16 || cd == CD_F16; }
 
 // Workspace plan shared by the size query and the launchers.
 struct FwdPlan {
   int64_t r_pad;
   Split st;
   bool dense;
-  DenseSplit dsp;  // cut of the dense GEMM's last round
+  DenseSplit dsp;  // cut of the 256 x 256 GEMM's last round (dense or fused)
   int64_t off_tcd, off_part, off_wd, off_xm, off_split, total;
 };
 FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
@@ -454,7 +460,7 @@ FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   P.off_xm = P.off_wd + (P.dense ? al(rows * cols * es) : 0);  // x M with LoRA dropout
   P.off_split = P.off_xm + ((flags & QLORA_FLAG_DROPOUT) ? al(m * cols * es) : 0);
   P.dsp = dense_split(m, rows, cols);
-  P.total = P.off_split + (P.dense ? al(dense_split_bytes(P.dsp)) : 0);
+  P.total = P.off_split + (big_tiles(cd) ? al(dense_split_bytes(P.dsp)) : 0);
   return P;
 }
 
@@ -464,7 +470,7 @@ struct BwdPlan {
   bool dense;
   bool sk, sk_n;       // the skinny kernels take the rank products (dT and dB also need rows % 8)
   int64_t n_pad, m_pad;  // contractions rounded up to whole 64-element stages
-  DenseSplit dsp;        // cut of the dense dX GEMM's last round
+  DenseSplit dsp;        // cut of the 256 x 256 dX GEMM's last round (dense or fused)
   int64_t off_t0, off_dt, off_dtcd, off_bt, off_dtt, off_t0t, off_part, off_part2, off_wdt, off_xm, off_zero, off_split,
       off_at, total;
 };
@@ -510,7 +516,7 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   P.off_split = P.off_zero + (drop ? al(m * P.r_pad * es) : 0);
   P.dsp = dense_split(m, cols, rows);
   // A^T [cols][r_pad] in cd: the W-side rows of the dense dX GEMM's low-rank tail
-  P.off_at = P.off_split + (P.dense ? al(dense_split_bytes(P.dsp)) : 0);
+  P.off_at = P.off_split + (big_tiles(cd) ? al(dense_split_bytes(P.dsp)) : 0);
   P.total = P.off_at + (P.dense ? al(cols * P.r_pad * es) : 0);
   return P;
 }
@@ -604,7 +610,7 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
     if ((rc = dequant_into(c.w, CD, wd, false, c.stream, red_pending ? &red : nullptr))) return rc;
     return dense256_forward(c, wd, tcd, P.r_pad, y, P.dsp, ws + P.off_split);
   }
-  if (fused256_ok(c, false)) return fused256_forward(c, tcd, P.r_pad, y);
+  if (fused256_ok(c, false)) return fused256_forward(c, tcd, P.r_pad, y, P.dsp, ws + P.off_split);
 
   GemmParams p = base_params(c);
   p.a1 = opnd<CD>(c.x, K, M, K);
@@ -729,7 +735,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     if ((rc = dequant_into(c.w, CD, wdt, true, c.stream, red_dt_pending ? &red_dt : nullptr))) return rc;
     if ((rc = dense256_dx(c, dy, wdt, dt_gemm, P.r_pad, dx, P.dsp, ws + P.off_split, at))) return rc;
   } else if (dx && fused256_ok(c, true)) {
-    rc = fused256_dx(c, dy, dt_gemm, P.r_pad, dx);
+    rc = fused256_dx(c, dy, dt_gemm, P.r_pad, dx, P.dsp, ws + P.off_split);
     if (rc) return rc;
   } else if (dx) {
     GemmParams p = base_params(c);

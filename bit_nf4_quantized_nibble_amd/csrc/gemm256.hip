@@ -651,8 +651,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the DMA bases scalar
   if (tid < 16) *(float*)(lds + LV_OFF + 4 * tid) = tab.lv[tid];
-  int tm, tn;
-  tile_of(p, tm, tn);
+  int tm, tn, slice, rt;
+  item_of(p, tm, tn, slice, rt);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  slice = __builtin_amdgcn_readfirstlane(slice);
+  rt = __builtin_amdgcn_readfirstlane(rt);
   const int64_t m0 = (int64_t)tm * TILE, n0 = (int64_t)tn * TILE;
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int h = lane >> 5;
@@ -697,16 +701,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // Stages [k0, k1) of the contraction: all of it for a whole tile, slice `slice`
+  // of split for a cut one (the fetches take absolute stage indices; loads past
+  // k1 - 1 repeat it).
   const uint32_t KT = (uint32_t)((p.K1 + BK - 1) / BK);
+  uint32_t k0 = 0, k1 = KT;
+  if (rt >= 0) {
+    k0 = (uint32_t)slice * KT / (uint32_t)p.split;
+    k1 = (uint32_t)(slice + 1) * KT / (uint32_t)p.split;
+  }
+  const uint32_t nst = k1 - k0;
   constexpr int NW = fetch_w_loads<MODE, DQ>();
   CodeRegs R0, R1;
-  fetch_a<MODE>(p, L, ra, lds, wave, 0);
-  fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, 0, KT);
-  fetch_w<MODE, DQ>(R1, p, L, rc, rq, rs, 1, KT);
+  fetch_a<MODE>(p, L, ra, lds, wave, k0);
+  fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, k0, k1);
+  fetch_w<MODE, DQ>(R1, p, L, rc, rq, rs, k0 + 1, k1);
   __syncthreads();  // level table
 #pragma unroll
   for (int q = 0; q < 4; ++q) decode_quarter<CD, MODE, DQ>(R0, lds, lds + 2 * TILE_BYTES, tid, q);
-  fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, 2, KT);
+  fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, k0 + 2, k1);
   wait_vmcnt<NW>();  // the activation tile of stage 0 (and the codes of stage 1) have landed
   wait_lgkm0();
   barrier_only();
@@ -718,28 +731,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
   float lv[2][16];
 #pragma unroll
   for (int t = 0; t < 16; ++t) lv[0][t] = lv_at(lds, code_addr<MODE>(R1, 0, t));
-  uint32_t kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    stage<CD, MODE, DQ>(acc, lds, 0, R1, R0, lv, p, L, ra, wave, kt + 1, true, a_row, b_row, xr, h, tid);
-    fetch_w<MODE, DQ>(R1, p, L, rc, rq, rs, kt + 3, KT);
+  uint32_t kt = 0;  // relative to k0
+  for (; kt + 2 <= nst; kt += 2) {
+    stage<CD, MODE, DQ>(acc, lds, 0, R1, R0, lv, p, L, ra, wave, k0 + kt + 1, true, a_row, b_row, xr, h, tid);
+    fetch_w<MODE, DQ>(R1, p, L, rc, rq, rs, k0 + kt + 3, k1);
     wait_vmcnt<NW>();  // this wave's copy of stage kt + 1 has landed (the code loads may still fly)
     wait_lgkm0();      // and its decode writes are in LDS
     barrier_only();
-    const bool more = kt + 2 < KT;
-    stage<CD, MODE, DQ>(acc, lds, 1, R0, R1, lv, p, L, ra, wave, kt + 2, more, a_row, b_row, xr, h, tid);
-    fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, kt + 4, KT);
+    const bool more = kt + 2 < nst;
+    stage<CD, MODE, DQ>(acc, lds, 1, R0, R1, lv, p, L, ra, wave, k0 + kt + 2, more, a_row, b_row, xr, h, tid);
+    fetch_w<MODE, DQ>(R0, p, L, rc, rq, rs, k0 + kt + 4, k1);
     if (more) wait_vmcnt<NW>(); else __builtin_amdgcn_s_waitcnt(0);
     wait_lgkm0();
     barrier_only();
   }
-  if (kt < KT) {
-    stage<CD, MODE, DQ>(acc, lds, 0, R1, R0, lv, p, L, ra, wave, kt + 1, false, a_row, b_row, xr, h, tid);
+  if (kt < nst) {
+    stage<CD, MODE, DQ>(acc, lds, 0, R1, R0, lv, p, L, ra, wave, k0 + kt + 1, false, a_row, b_row, xr, h, tid);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  lora_segment<CD, MODE, true>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
-  epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
+  // the low-rank tail joins the last slice (or the whole tile)
+  if (rt < 0 || slice == p.split - 1)
+    lora_segment<CD, MODE, true>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+  if (rt < 0) epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
+  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
 }
 
 
@@ -895,15 +911,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
   else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
 }
 
+template <int CD, int S>
+int launch_split_sum(const Big& b, hipStream_t s);
+
+// The fused GEMM, and for a cut last round the sum of its slices (one profiling
+// scope: together they are the GEMM).
 template <int CD, int MODE>
 int run(const Big& b, hipStream_t s, int kind) {
-  const int64_t tiles = (int64_t)b.tiles_m * b.tiles_n;
+  const int64_t items = (int64_t)b.full + (int64_t)b.rem * b.split;
   ProfScope prof(kind, s);
   if (b.w.dq)
-    k_fused256<CD, MODE, 1><<<dim3((unsigned)tiles), dim3(kThreads), 0, s>>>(b, host_tables());
+    k_fused256<CD, MODE, 1><<<dim3((unsigned)items), dim3(kThreads), 0, s>>>(b, host_tables());
   else
-    k_fused256<CD, MODE, 0><<<dim3((unsigned)tiles), dim3(kThreads), 0, s>>>(b, host_tables());
-  return check_launch(MODE == MODE_FWD ? "k_fused256<fwd>" : "k_fused256<dx>");
+    k_fused256<CD, MODE, 0><<<dim3((unsigned)items), dim3(kThreads), 0, s>>>(b, host_tables());
+  int rc = check_launch(MODE == MODE_FWD ? "k_fused256<fwd>" : "k_fused256<dx>");
+  if (rc || !b.rem) return rc;
+  return b.split == 2 ? launch_split_sum<CD, 2>(b, s) : launch_split_sum<CD, 4>(b, s);
 }
 
 // The dense GEMM, and for a cut last round the sum of its slices (both inside one
@@ -915,9 +938,13 @@ int run_dense(const Big& b, const void* bd, hipStream_t s, int kind) {
   k_dense256<CD, MODE><<<dim3((unsigned)items), dim3(kThreads), 0, s>>>(b, bd);
   int rc = check_launch(MODE == MODE_FWD ? "k_dense256<fwd>" : "k_dense256<dx>");
   if (rc || !b.rem) return rc;
+  return b.split == 2 ? launch_split_sum<CD, 2>(b, s) : launch_split_sum<CD, 4>(b, s);
+}
+
+template <int CD, int S>
+int launch_split_sum(const Big& b, hipStream_t s) {
   const dim3 g(kTileAcc / (4 * kThreads), (unsigned)b.rem);
-  if (b.split == 2) k_split_sum<CD, 2><<<g, dim3(kThreads), 0, s>>>(b);
-  else k_split_sum<CD, 4><<<g, dim3(kThreads), 0, s>>>(b);
+  k_split_sum<CD, S><<<g, dim3(kThreads), 0, s>>>(b);
   return check_launch("k_split_sum");
 }
 
@@ -945,8 +972,10 @@ bool fused256_ok(const LayerCall& c, bool dx) {
   return fits_buffers(c, c.m * c.w.cols * 2);
 }
 
-// y = [x | T][W~ | B]^T + bias.  t_cd: [m, r_pad] compute-dtype s x A^T.
-int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* y) {
+// y = [x | T][W~ | B]^T + bias.  t_cd: [m, r_pad] compute-dtype s x A^T; sp and
+// split_ws as for the dense kernel (dense_split(m, rows, cols)).
+int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* y, const DenseSplit& sp,
+                     void* split_ws) {
   Big b = {};
   b.a1 = c.x;
   b.ld_a1 = c.w.cols;
@@ -962,12 +991,15 @@ int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* 
   b.tiles_n = (int32_t)ceil_div(c.w.rows, TILE);
   b.out = y;
   b.bias = c.bias;
+  set_split(b, sp, split_ws);
   if (c.cd == CD_BF16) return run<CD_BF16, MODE_FWD>(b, c.stream, QLORA_K_FWD_GEMM);
   return run<CD_F16, MODE_FWD>(b, c.stream, QLORA_K_FWD_GEMM);
 }
 
-// dX = [dY | dT][W~ ; A].  dt_cd: [m, r_pad] compute-dtype s dY B.
-int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r_pad, void* dx) {
+// dX = [dY | dT][W~ ; A].  dt_cd: [m, r_pad] compute-dtype s dY B; sp and split_ws
+// as for the dense kernel (dense_split(m, cols, rows)).
+int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r_pad, void* dx, const DenseSplit& sp,
+                void* split_ws) {
   Big b = {};
   b.a1 = dy;
   b.ld_a1 = c.w.rows;
@@ -983,6 +1015,7 @@ int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r
   b.tiles_n = (int32_t)ceil_div(c.w.cols, TILE);
   b.out = dx;
   b.bias = nullptr;
+  set_split(b, sp, split_ws);
   if (c.cd == CD_BF16) return run<CD_BF16, MODE_DX>(b, c.stream, QLORA_K_BWD_DX);
   return run<CD_F16, MODE_DX>(b, c.stream, QLORA_K_BWD_DX);
 }

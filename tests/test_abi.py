@@ -158,8 +158,9 @@ def test_workspace_query(lib):
     fused = lib.qlora_workspace_bytes(0 | (2 << 8), 2048, 4096, 4096, 64, 1)
     dense = lib.qlora_workspace_bytes(0 | (4 << 8), 2048, 4096, 4096, 64, 1)
     assert dense - fused >= 4096 * 4096 * 2
-    assert lib.qlora_workspace_bytes(0, 2048, 4096, 4096, 64, 1) == dense      # default at 2048 tokens
-    assert lib.qlora_workspace_bytes(0, 512, 4096, 4096, 64, 1) == lib.qlora_workspace_bytes(2 << 8, 512, 4096, 4096, 64, 1)
+    assert lib.qlora_workspace_bytes(0, 2048, 4096, 4096, 64, 1) == dense      # the default path
+    assert lib.qlora_workspace_bytes(0, 32, 4096, 4096, 64, 1) == lib.qlora_workspace_bytes(4 << 8, 32, 4096, 4096, 64, 1)
+    assert lib.qlora_workspace_bytes(2 << 8, 32, 4096, 4096, 64, 1) < lib.qlora_workspace_bytes(0, 32, 4096, 4096, 64, 1)
     assert lib.qlora_workspace_bytes(1 | (4 << 8), 512, 4096, 4096, 64, 1) >= 4096 * 4096 * 2
     assert lib.qlora_workspace_bytes(0 | (16 << 8), 512, 4096, 4096, 64, 1) == 0  # unknown flag
     # LoRA dropout stages x M (and, in the backward, a zero dT operand) in the workspace

@@ -1,6 +1,7 @@
-"""GPU parity of the dense 256 x 256 GEMM when the tiles of an incomplete last
-round are cut into contraction slices (two or four per tile, summed in slice
-order by the slice that finishes last), against the fp64 oracle through the C ABI.
+"""GPU parity of the 256 x 256 GEMMs (dequantize-then-GEMM and fused NF4 decode)
+when the tiles of an incomplete last round are cut into contraction slices (two or
+four per tile, whose fp32 partial sums a second launch adds in slice order),
+against the fp64 oracle through the C ABI.
 
 One round is one tile per compute unit.  A GEMM with T tiles on C units takes
 floor(T / C) whole rounds; the R = T mod C tiles left over are cut into the
@@ -8,8 +9,8 @@ largest S in {2, 4} with R * S <= C and at least 4 contraction stages of 64 per
 slice.  Small cases compare every element (ragged M and N, a bias, the low-rank
 tail on the last slice); the full projection sizes whose tile counts leave an
 incomplete round (gate / up forward, down dX: 16 x 56 tiles) compare sampled
-entries.  Repeats on a workspace holding stale arrival counters and outputs
-filled with NaN must give the same bits."""
+entries.  Repeats on a workspace full of stale bytes and outputs filled with NaN
+must give the same bits."""
 import numpy as np
 import pytest
 import torch
@@ -24,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 
 def expected_split(M, NB, K1):
-    """(whole-tile workgroups, cut tiles, slices) the dense GEMM uses on this GPU."""
+    """(whole-tile workgroups, cut tiles, slices) the 256 x 256 GEMMs use on this GPU."""
     C = torch.cuda.get_device_properties(0).multi_processor_count
     T = -(-M // 256) * -(-NB // 256)
     F, R = divmod(T, C)
@@ -39,35 +40,37 @@ def gpu_q(L, g):
     return qn.quantize(g["W"], L.block_size, L.double_quant, L.dq_group)
 
 
+@pytest.mark.parametrize("path", ["dequant", "fused"])
 @pytest.mark.parametrize("cd", ["bf16", "f16"])
 @pytest.mark.parametrize("M,N,K,r,bias,S", [
     (300, 260, 1024, 16, True, 4),   # 2 x 2 tiles, both ragged, 16 stages -> 4 slices of 4
     (520, 200, 512, 24, False, 2),   # 3 x 1 tiles, 8 stages -> 2 slices
     (257, 64, 1280, 5, True, 4),     # a one-row ragged tile row, odd rank, 20 stages -> 5 per slice
 ])
-def test_split_forward_every_element(cd, M, N, K, r, bias, S):
+def test_split_forward_every_element(path, cd, M, N, K, r, bias, S):
     assert expected_split(M, N, K)[2] == S
     L = inputs.random_layer(M, N, K, r, seed=M + N + K + r, cd=cd, with_bias=bias, with_dy=False)
-    say("split fwd", cd, M, N, K, r, "S", S)
+    say("split fwd", path, cd, M, N, K, r, "S", S)
     g = to_gpu(L)
-    y = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], path="dequant")
+    y = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], path=path)
     torch.cuda.synchronize()
     o = oracle_layer(L)
     ref = oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"])
     assert_close(to_np(y), ref, cd, "split fwd %s %dx%dx%d" % (cd, M, N, K))
 
 
+@pytest.mark.parametrize("path", ["dequant", "fused"])
 @pytest.mark.parametrize("cd", ["bf16", "f16"])
 @pytest.mark.parametrize("M,N,K,r,S", [
     (300, 1024, 320, 16, 4),  # dX [300, 320]: 2 x 2 tiles, contraction 1024 -> 4 slices
     (200, 512, 256, 8, 2),    # dX one tile, contraction 512 -> 2 slices
 ])
-def test_split_backward_dx_every_element(cd, M, N, K, r, S):
+def test_split_backward_dx_every_element(path, cd, M, N, K, r, S):
     assert expected_split(M, K, N)[2] == S
     L = inputs.random_layer(M, N, K, r, seed=3 * M + N + r, cd=cd)
-    say("split bwd", cd, M, N, K, r, "S", S)
+    say("split bwd", path, cd, M, N, K, r, "S", S)
     g = to_gpu(L)
-    dx, da, db = qn.linear_bwd(gpu_q(L, g), g["x"], g["dY"], g["A"], g["B"], L.alpha, path="dequant")
+    dx, da, db = qn.linear_bwd(gpu_q(L, g), g["x"], g["dY"], g["A"], g["B"], L.alpha, path=path)
     torch.cuda.synchronize()
     o = oracle_layer(L)
     rdx, rda, rdb = oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"])
@@ -76,17 +79,19 @@ def test_split_backward_dx_every_element(cd, M, N, K, r, S):
     assert_close(to_np(db), rdb, cd, "split dB")
 
 
-def test_split_repeats_bit_identical_on_stale_workspace():
-    """The dequantize pass clears the arrival counters: a workspace left full of
-    0xff bytes, or holding the counters of the previous call, gives the same bits,
-    and every output element is written (outputs start as NaN)."""
-    M, N, K, r = 300, 260, 1024, 16
+@pytest.mark.parametrize("path", ["dequant", "fused"])
+def test_split_repeats_bit_identical_on_stale_workspace(path):
+    """A workspace left full of 0xff bytes, or holding the partial sums of the
+    previous call, gives the same bits, and every output element is written
+    (outputs start as NaN)."""
+    M, N, K, r = 300, 512, 1024, 16  # forward 2 x 2 tiles in 4 slices, dX 2 x 4 tiles in 2
+    assert expected_split(M, N, K)[2] == 4 and expected_split(M, K, N)[2] == 2
     L = inputs.random_layer(M, N, K, r, seed=41, with_bias=True)
-    say("split stale workspace")
+    say("split stale workspace", path)
     g = to_gpu(L)
     q = gpu_q(L, g)
     dt = TORCH_DT[L.cd]
-    flags = _lib.QLORA_FLAG_DEQUANT_GEMM
+    flags = _lib.QLORA_FLAG_DEQUANT_GEMM if path == "dequant" else _lib.QLORA_FLAG_FUSED
     wsf = torch.full((qn.workspace_bytes(_lib.QLORA_OP_FWD, M, N, K, r, dt, flags),), 255, dtype=torch.uint8,
                      device="cuda")
     wsb = torch.full((qn.workspace_bytes(_lib.QLORA_OP_BWD, M, N, K, r, dt, flags),), 255, dtype=torch.uint8,
@@ -94,9 +99,9 @@ def test_split_repeats_bit_identical_on_stale_workspace():
     ys, dxs = [], []
     for _ in range(3):
         y = torch.full((M, N), float("nan"), dtype=dt, device="cuda")
-        qn.linear_fwd(q, g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], path="dequant", workspace=wsf, out=y)
+        qn.linear_fwd(q, g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], path=path, workspace=wsf, out=y)
         dx = torch.full((M, K), float("nan"), dtype=dt, device="cuda")
-        qn.linear_bwd(q, g["x"], g["dY"], g["A"], g["B"], L.alpha, path="dequant", workspace=wsb, dx_out=dx)
+        qn.linear_bwd(q, g["x"], g["dY"], g["A"], g["B"], L.alpha, path=path, workspace=wsb, dx_out=dx)
         torch.cuda.synchronize()
         ys.append(y.clone())
         dxs.append(dx.clone())
@@ -107,13 +112,14 @@ def test_split_repeats_bit_identical_on_stale_workspace():
     assert_close(to_np(dxs[0]), oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"])[0], L.cd, "dX")
 
 
-def test_split_forward_full_size_sampled():
+@pytest.mark.parametrize("path", ["dequant", "fused"])
+def test_split_forward_full_size_sampled(path):
     """gate_proj at 4096 tokens: 16 x 56 tiles, three whole rounds and 128 tiles in
     two slices each on a 256-CU GPU."""
     (L,) = inputs.prefill(projections=["gate_proj"])
-    say("split fwd full", L.M, L.N, L.K, expected_split(L.M, L.N, L.K))
+    say("split fwd full", path, L.M, L.N, L.K, expected_split(L.M, L.N, L.K))
     g = to_gpu(L)
-    y = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, path="dequant")
+    y = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, path=path)
     torch.cuda.synchronize()
     o = oracle_layer(L)
     rng = np.random.default_rng(17)
@@ -122,7 +128,7 @@ def test_split_forward_full_size_sampled():
     jj[:4] = [0, 0, L.N - 1, L.N - 1]
     ref = oracle.forward_at(o["x"], o["W"], o["A"], o["B"], o["s"], ii, jj)
     assert_close(to_np(y)[ii, jj], ref, "bf16", "gate_proj fwd sampled")
-    y2 = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, path="dequant")
+    y2 = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, path=path)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
 
