@@ -336,19 +336,23 @@ __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-struct Frags {
-  u32x4_t a[4], b[4];
+// A fragments of the wave's four 32-row blocks, B fragments of its JB 32-column blocks.
+template <int JB>
+struct FragsT {
+  u32x4_t a[4], b[JB];
 };
+using Frags = FragsT<4>;
 
 // Fragments of 16-element step ks: lane (row l % 32, half l / 32) reads logical
 // chunk 2 ks + half of rows wm + 32 i + l % 32 (A) and wn + 32 j + l % 32 (B).
-__device__ __forceinline__ void read_frags(Frags& F, const char* As, const char* Bs, int a_row, int b_row,
+template <int JB>
+__device__ __forceinline__ void read_frags(FragsT<JB>& F, const char* As, const char* Bs, int a_row, int b_row,
                                            int xr, int h, int ks) {
   const int cphys = ((2 * ks + h) ^ xr) << 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) F.a[i] = *(const u32x4_t*)(As + (a_row + 32 * i) * ROWB + cphys);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) F.b[j] = *(const u32x4_t*)(Bs + (b_row + 32 * j) * ROWB + cphys);
+  for (int j = 0; j < JB; ++j) F.b[j] = *(const u32x4_t*)(Bs + (b_row + 32 * j) * ROWB + cphys);
 }
 
 // SWAP: the W-side fragment goes in as the MFMA's row operand, so block (i, j) is
@@ -533,13 +537,14 @@ __device__ __forceinline__ f32x4_t acc4(const f32x16_t& a, int q) {
 // (transposed) block (i, j) gives row wm + 32 i + lane % 32 the four columns
 // wn + 32 j + 8 q + 4 (lane / 32) .. + 3 from elements 4 q .. 4 q + 3 (one 16-byte
 // store; lanes l and l + 32 fill 32 contiguous bytes of a row).
-__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[4][4], float* dst, int wm, int wn, int lane) {
+template <int JB>
+__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[4][JB], float* dst, int wm, int wn, int lane) {
   const rsrc_t r = make_rsrc(dst, kTileAcc * 4);
   const uint32_t base = (uint32_t)(((wm + (lane & 31)) * TILE + wn + 4 * (lane >> 5)) * 4);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc4(acc[i][j], q)), r, (int)base,
@@ -581,26 +586,29 @@ __global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
 
 // Epilogue of the 256-tile kernels, whose blocks are accumulated transposed: lane
 // (r = lane % 32, h = lane / 32) of block (i, j) holds output row 32 i + r, columns
-// 32 j + 8 q + 4 h + e in element 4 q + e.  Each wave rounds its 128 x 128 block
-// (+ bias) to the compute dtype in its own 32 KiB of LDS (rows of 256 bytes; 16-byte
-// chunk c of row m at chunk c ^ (m % 16), so neither the 8-byte writes nor the
-// 16-byte row reads collide on banks), then writes whole rows: 16 lanes per row, 4
-// rows of 256 contiguous bytes per store instruction.  Entered with the LDS free.
-template <int CD>
-__device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][4], const Big& p, char* lds, int64_t m0,
+// 32 j + 8 q + 4 h + e in element 4 q + e.  Each wave rounds its 128 x 32 JB block
+// (+ bias) to the compute dtype in its own 8 JB KiB of LDS (rows of 64 JB bytes;
+// 16-byte chunk c of row m at chunk c ^ (m % 4 JB), so neither the 8-byte writes nor
+// the 16-byte row reads collide on banks), then writes whole rows: 4 JB lanes per
+// row, 64 / (4 JB) rows of 64 JB contiguous bytes per store instruction.  Entered
+// with the LDS free.
+template <int CD, int JB>
+__device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][JB], const Big& p, char* lds, int64_t m0,
                                              int64_t n0, int wave, int wm, int wn, int lane, int h) {
-  char* W = lds + wave * 32768;
+  constexpr int RB = 64 * JB;  // bytes per staged row
+  constexpr int NC = 4 * JB;   // 16-byte chunks per row
+  char* W = lds + wave * (128 * RB);
   const int r = lane & 31;
-  float bv[4][4][4];  // bias of the lane's columns (j, q, e)
+  float bv[JB][4][4];  // bias of the lane's columns (j, q, e)
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < JB; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e) bv[j][q][e] = 0.f;
   if (p.bias) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -613,23 +621,23 @@ __device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][4], const 
   for (int i = 0; i < 4; ++i) {
     const int m = 32 * i + r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t w2[2];
         w2[0] = pack2<CD>(acc[i][j][4 * q] + bv[j][q][0], acc[i][j][4 * q + 1] + bv[j][q][1]);
         w2[1] = pack2<CD>(acc[i][j][4 * q + 2] + bv[j][q][2], acc[i][j][4 * q + 3] + bv[j][q][3]);
-        *(uint2*)(W + m * 256 + (((4 * j + q) ^ (m & 15)) << 4) + 8 * h) = make_uint2(w2[0], w2[1]);
+        *(uint2*)(W + m * RB + (((4 * j + q) ^ (m & (NC - 1))) << 4) + 8 * h) = make_uint2(w2[0], w2[1]);
       }
   }
   wait_lgkm0();  // the wave reads back only what it wrote
-  const int c = lane & 15;
+  const int c = lane & (NC - 1);
   const int64_t col = n0 + wn + 8 * c;
   const bool vec = (p.NB & 7) == 0;
 #pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int m = 4 * it + (lane >> 4);
-    const u32x4_t v = *(const u32x4_t*)(W + m * 256 + ((c ^ (m & 15)) << 4));
+  for (int it = 0; it < 2 * NC; ++it) {
+    const int m = (64 / NC) * it + lane / NC;
+    const u32x4_t v = *(const u32x4_t*)(W + m * RB + ((c ^ (m & (NC - 1))) << 4));
     const int64_t row = m0 + wm + m;
     if (row >= p.M) continue;
     uint16_t* dst = (uint16_t*)p.out + row * p.NB + col;
@@ -774,6 +782,7 @@ struct Copy {
   uint32_t a_off, b_off, a_step, b_step, soff;
 };
 
+// Waves 0..3 copy (one per SIMD); with eight waves, waves 4..7 only compute.
 __device__ __forceinline__ void copy_one(const Copy& cp, char* dst_a, char* dst_b, int wave, int d, bool b_side) {
   if (!b_side)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.ra, (lds_void*)(dst_a + (4 * d + wave) * 1024), 16,
@@ -783,38 +792,52 @@ __device__ __forceinline__ void copy_one(const Copy& cp, char* dst_a, char* dst_
                                              (int)(cp.b_off + d * cp.b_step), (int)cp.soff, 0, 0);
 }
 
-template <int CD, int DO_COPY>
-__device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][4], char* lds, int cur, const Copy& cp, int wave,
+// One stage of a wave's 128 x 32 JB block (NW = 16 / JB waves): 4 sub-steps of 4 JB
+// MFMAs; the 4 + JB fragment reads of the next sub-step are spread over the MFMAs
+// of the first three, and (DO_COPY, waves 0..3) the wave's 8 copies of each operand
+// for the next stage go between the MFMAs of sub-steps 0 (activations) and 1 (W side).
+template <int CD, int DO_COPY, int JB>
+__device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][JB], char* lds, int cur, const Copy& cp, int wave,
                                             int a_row, int b_row, int xr, int h) {
+  constexpr int NW = 16 / JB, NMF = 4 * JB, NRD = 4 + JB;
   char* As = lds + cur * TILE_BYTES;
   char* Bs = lds + (2 + cur) * TILE_BYTES;
   char* An = lds + (cur ^ 1) * TILE_BYTES;
   char* Bn = lds + (2 + (cur ^ 1)) * TILE_BYTES;
-  Frags F[2];
+  FragsT<JB> F[2];
   read_frags(F[0], As, Bs, a_row, b_row, xr, h, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    Frags& C = F[ks & 1];
-    Frags& N = F[(ks + 1) & 1];
+    FragsT<JB>& C = F[ks & 1];
+    FragsT<JB>& N = F[(ks + 1) & 1];
     const int cphys = ((2 * (ks + 1) + h) ^ xr) << 4;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int i = t >> 2, j = t & 3;
+    for (int t = 0; t < NMF; ++t) {
+      const int i = t / JB, j = t % JB;
       acc[i][j] = mfma<CD>(C.b[j], C.a[i], acc[i][j]);  // block (i, j) transposed
-      if (ks < 3 && (t & 1) == 0) {
-        const int r = t >> 1;
-        if (r < 4) N.a[r] = *(const u32x4_t*)(As + (a_row + 32 * r) * ROWB + cphys);
-        else N.b[r - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (r - 4)) * ROWB + cphys);
+      if (ks < 3) {
+#pragma unroll
+        for (int r = 0; r < NRD; ++r)
+          if (r * NMF / NRD == t) {
+            if (r < 4) N.a[r] = *(const u32x4_t*)(As + (a_row + 32 * r) * ROWB + cphys);
+            else N.b[r - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (r - 4)) * ROWB + cphys);
+          }
       }
-      if (DO_COPY && ks < 2 && (t & 1) == 1) copy_one(cp, An, Bn, wave, t >> 1, ks == 1);
+      if constexpr (DO_COPY) {
+        if (NW == 4 && ks < 2 && (t & 1) == 1) copy_one(cp, An, Bn, wave, t >> 1, ks == 1);
+        if (NW == 8 && ks < 2 && wave < 4) copy_one(cp, An, Bn, wave, t, ks == 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-template <int CD, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd) {
+template <int CD, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_dense256(Big p, const void* bd) {
+  // NW waves of 128 x 32 JB output blocks: 4 waves of 128 x 128 (one per SIMD) or 8 of
+  // 128 x 64 (two per SIMD, so one wave's MFMAs can run while the other waits)
+  constexpr int JB = 16 / NW, WNC = 8 / JB;  // WNC: waves along the tile's columns
   // [A0 | A1 | B0 | B1]
   __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -827,13 +850,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
   slice = __builtin_amdgcn_readfirstlane(slice);
   rt = __builtin_amdgcn_readfirstlane(rt);
   const int64_t m0 = (int64_t)tm * TILE, n0 = (int64_t)tn * TILE;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int wm = (wave / WNC) * 128, wn = (wave % WNC) * (32 * JB);
   const int h = lane >> 5;
   const int a_row = wm + (lane & 31), b_row = wn + (lane & 31);
   const int xr = swz(lane & 31);
-  // rows 8 (4 d + wave) + lane / 8 (d = 0..7) of each tile; rows past M or NB read
-  // past their buffer (the row is in the lane offset) and land as zeros
-  const int row = 8 * wave + (lane >> 3);
+  // copies by waves 0..3: rows 8 (4 d + wave) + lane / 8 (d = 0..7) of each tile;
+  // rows past M or NB read past their buffer (the row is in the lane offset) and land
+  // as zeros
+  const int row = 8 * (wave & 3) + (lane >> 3);
   const int c = (lane & 7) ^ swz(row);  // the logical chunk this lane's copies fetch
   Copy main_cp;
   main_cp.ra = make_rsrc(p.a1, p.M * p.ld_a1 * 2);
@@ -843,11 +867,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
   main_cp.a_step = (uint32_t)(32 * p.ld_a1 * 2);
   main_cp.b_step = (uint32_t)(32 * p.K1 * 2);
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][JB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -884,7 +908,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
     cp.soff = 0;
     return cp;
   };
-  {
+  if (wave < 4) {
     const Copy cp = copy_of(0);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
@@ -904,9 +928,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_dense256(Big p, const void* bd)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // a tail whose W-side operand cannot be copied row by row (fwd with r % 8 != 0)
-  if (has_tail && !dma_tail)
-    lora_segment<CD, MODE, true>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+  // a tail whose W-side operand cannot be copied row by row (fwd with r % 8 != 0):
+  // the host takes the four-wave form for it
+  if constexpr (NW == 4) {
+    if (has_tail && !dma_tail)
+      lora_segment<CD, MODE, true>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+  }
   if (rt < 0) epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
   else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
 }
@@ -935,7 +962,11 @@ template <int CD, int MODE>
 int run_dense(const Big& b, const void* bd, hipStream_t s, int kind) {
   const int64_t items = (int64_t)b.full + (int64_t)b.rem * b.split;
   ProfScope prof(kind, s);
-  k_dense256<CD, MODE><<<dim3((unsigned)items), dim3(kThreads), 0, s>>>(b, bd);
+  // eight waves (two per SIMD) unless the low-rank tail cannot be copied row by row
+  if (b.b2_rows)
+    k_dense256<CD, MODE, 8><<<dim3((unsigned)items), dim3(8 * 64), 0, s>>>(b, bd);
+  else
+    k_dense256<CD, MODE, 4><<<dim3((unsigned)items), dim3(4 * 64), 0, s>>>(b, bd);
   int rc = check_launch(MODE == MODE_FWD ? "k_dense256<fwd>" : "k_dense256<dx>");
   if (rc || !b.rem) return rc;
   return b.split == 2 ? launch_split_sum<CD, 2>(b, s) : launch_split_sum<CD, 4>(b, s);
