@@ -237,7 +237,9 @@ def bench_path_sweep(qn, torch, lib, inputs, copies=8, replays=5):
     copies of the two quantized weights (about 300 MB of codes and scales, more than
     the 256 MB last-level cache), so each call reads its weight from HBM as a block
     of a real model would.  Reports time per q + gate pair, TFLOP/s and the
-    workspace each path needs (the memory side of the trade-off)."""
+    workspace each path needs (the memory side of the trade-off).  A third column,
+    "cached", runs qlora_linear_fwd_cached on W~ dequantized once per weight copy
+    beforehand (held resident: 2 bytes per weight instead of about 0.53)."""
     ms = (32, 64, 128, 256, 512, 1024, 2048, 4096)
     Ls = inputs.prefill(seed=0, cd="bf16", m=max(ms), projections=["q_proj", "gate_proj"])
     x = Ls[0].x.to("cuda")
@@ -250,22 +252,35 @@ def bench_path_sweep(qn, torch, lib, inputs, copies=8, replays=5):
         del W
         qs = [qn.NF4Weight(q0.rows, q0.cols, q0.block_size, True, q0.dq_group, q0.codes.clone(), None,
                            q0.absmax_q.clone(), q0.absmax_scale2.clone()) for _ in range(copies)]
+        wcs = [qn.dequantize(q, x.dtype) for q in qs]
         projs.append((L, qs, [q.descriptor() for q in qs], L.A.to("cuda"), L.B.to("cuda"),
-                      torch.empty(max(ms), L.N, dtype=x.dtype, device="cuda")))
+                      torch.empty(max(ms), L.N, dtype=x.dtype, device="cuda"), wcs))
         del q0
-    paths = (("fused", qn._lib.QLORA_FLAG_FUSED), ("dequant", qn._lib.QLORA_FLAG_DEQUANT_GEMM))
-    wsb = max(qn.workspace_bytes(0, m, L.N, L.K, L.r, x.dtype, f) for m in ms for L in Ls for _, f in paths)
+    paths = (("fused", qn._lib.QLORA_FLAG_FUSED), ("dequant", qn._lib.QLORA_FLAG_DEQUANT_GEMM), ("cached", None))
+
+    def ws_need(m, L, flag):
+        if flag is None:
+            return qn.workspace_bytes(qn._lib.QLORA_OP_FWD_CACHED, m, L.N, L.K, L.r, x.dtype)
+        return qn.workspace_bytes(0, m, L.N, L.K, L.r, x.dtype, flag)
+
+    wsb = max(ws_need(m, L, fl) for m in ms for L in Ls for _, fl in paths)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    f = lib.qlora_linear_fwd
     st = torch.cuda.Stream()
     out = {"weights_cycled": copies, "timing": "HIP graph of the 2 x copies calls, replayed %d times" % replays}
     for m in ms:
         flops = sum(fwd_flops(m, L.N, L.K, L.r) for L in Ls)
         res = {}
         for path, flag in paths:
-            calls = [(ctypes.byref(d), x.data_ptr(), m, A.data_ptr(), B.data_ptr(), L.r, float(L.alpha), flag, None,
-                      cd, y.data_ptr(), None, ws.data_ptr(), ws.numel(), st.cuda_stream)
-                     for c in range(copies) for (L, qs, ds, A, B, y) in projs for d in (ds[c],)]
+            if flag is None:
+                f = lib.qlora_linear_fwd_cached
+                calls = [(wc[c].data_ptr(), L.N, L.K, x.data_ptr(), m, A.data_ptr(), B.data_ptr(), L.r,
+                          float(L.alpha), 0, None, cd, y.data_ptr(), None, ws.data_ptr(), ws.numel(), st.cuda_stream)
+                         for c in range(copies) for (L, qs, ds, A, B, y, wc) in projs]
+            else:
+                f = lib.qlora_linear_fwd
+                calls = [(ctypes.byref(d), x.data_ptr(), m, A.data_ptr(), B.data_ptr(), L.r, float(L.alpha), flag,
+                          None, cd, y.data_ptr(), None, ws.data_ptr(), ws.numel(), st.cuda_stream)
+                         for c in range(copies) for (L, qs, ds, A, B, y, wc) in projs for d in (ds[c],)]
 
             def fwd():
                 for a in calls:
@@ -299,9 +314,11 @@ def bench_path_sweep(qn, torch, lib, inputs, copies=8, replays=5):
             same = same and all(torch.equal(e, p[5][:m]) for e, p in zip(eager, projs))
             sec = e0.elapsed_time(e1) / 1e3 / (replays * copies)
             del g
-            need = max(qn.workspace_bytes(0, m, L.N, L.K, L.r, x.dtype, flag) for L in Ls)
+            need = max(ws_need(m, L, flag) for L in Ls)
             res[path] = {"ms": round(sec * 1e3, 4), "tflops": round(flops / sec / 1e12, 1),
                          "workspace_mb": round(need / 2 ** 20, 1), "replay_matches_eager": same}
+            if flag is None:
+                res[path]["resident_w_mb"] = round(sum(L.N * L.K * 2 for L in Ls) / 2 ** 20, 1)
         res["faster"] = min(("fused", "dequant"), key=lambda k: res[k]["ms"])
         out["m%d" % m] = res
     del projs, ws, x

@@ -9,6 +9,7 @@ hand-written HIP kernels; there is no CPU or PyTorch fallback.
 Public API (names follow the pages' problem statement):
     quantize(w, block_size=64, double_quant=False, dq_group=256 | "global") -> NF4Weight
     dequantize(q, dtype=torch.bfloat16) -> Tensor [rows, cols]
+    linear_fwd_cached(w_cd, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False)
     linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False, path="auto",
                dropout_mask=None, dropout_p=0.0)
     linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False, path="auto",
@@ -237,6 +238,40 @@ def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t:
             _ptr(bias), dtype_code(dt), _ptr(mk), p, _ptr(y), _ptr(t0), _ptr(ws), ws.numel() * ws.element_size(),
             _stream_ptr(x.device)))
     y = y.reshape(*lead, q.rows)
+    return (y, t0) if (save_t or t_out is not None) else y
+
+
+def linear_fwd_cached(w_cd, x, lora_a, lora_b, alpha: float, bias=None, save_t: bool = False,
+                      rslora: bool = False, workspace=None, out=None, t_out=None):
+    """Cached-dequant forward: ``w_cd`` is W~ [rows, cols] in x's dtype (bf16 / f16),
+    dequantized once by ``dequantize(q, dtype)`` and kept by the caller; returns
+    x . w_cd^T + s (x . A^T) . B^T (+ bias), or (y, T0) when save_t."""
+    torch = _torch()
+    dt = x.dtype
+    rows, cols = w_cd.shape
+    _need_cuda("w_cd", w_cd, dt)
+    x2, lead = _flatten(x, cols)
+    x2 = x2.contiguous()
+    for name, t in (("x", x2), ("lora_a", lora_a), ("lora_b", lora_b), ("bias", bias)):
+        _need_cuda(name, t, dt)
+    r = lora_a.shape[0]
+    m = x2.shape[0]
+    y = out if out is not None else torch.empty(m, rows, dtype=dt, device=x.device)
+    _need_cuda("out", y, dt)
+    if y.numel() != m * rows:
+        raise ValueError("out must hold %d x %d elements" % (m, rows))
+    t0 = t_out if t_out is not None else (
+        torch.empty(m, r, dtype=torch.float32, device=x.device) if save_t else None)
+    _need_cuda("t_out", t0, torch.float32)
+    if t0 is not None and t0.numel() != m * r:
+        raise ValueError("t_out must hold %d x %d fp32 elements" % (m, r))
+    flags = _lib.QLORA_FLAG_RSLORA if rslora else 0
+    ws = _workspace(workspace_bytes(_lib.QLORA_OP_FWD_CACHED, m, rows, cols, r, dt, flags), x.device, workspace)
+    _lib.check(_lib.lib().qlora_linear_fwd_cached(
+        _ptr(w_cd.contiguous()), rows, cols, _ptr(x2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), flags,
+        _ptr(bias), dtype_code(dt), _ptr(y), _ptr(t0), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream_ptr(x.device)))
+    y = y.reshape(*lead, rows)
     return (y, t0) if (save_t or t_out is not None) else y
 
 

@@ -19,7 +19,7 @@ STATUS_NAMES = {
 }
 QLORA_F32, QLORA_BF16, QLORA_F16 = 0, 1, 2
 QLORA_FLAG_RSLORA, QLORA_FLAG_FUSED, QLORA_FLAG_DEQUANT_GEMM, QLORA_FLAG_DROPOUT = 1, 2, 4, 8
-QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_FLAGS_SHIFT = 0, 1, 8
+QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_FWD_CACHED, QLORA_OP_FLAGS_SHIFT = 0, 1, 2, 8
 
 # Every function the header declares, for the export check.
 EXPORTED = (
@@ -27,7 +27,7 @@ EXPORTED = (
     "qlora_workspace_bytes", "qlora_last_error", "qlora_nf4_levels", "qlora_abi_version",
     "qlora_profile_enable", "qlora_profile_read", "qlora_kernel_name", "qlora_merge",
     "qlora_mse_loss_grad", "qlora_adamw_step", "qlora_stack_train_step", "qlora_stack_workspace_bytes",
-    "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
+    "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_linear_fwd_cached",
 )
 QLORA_MSE_WORKSPACE_BYTES = 4096
 KERNEL_KINDS = ("quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
@@ -91,6 +91,7 @@ def _declare(lib):
     lib.qlora_linear_fwd_dropout.argtypes = [P, vp, i64, vp, vp, i32, f32, i32, vp, i32, vp, f32, vp, vp, vp, sz, vp]
     lib.qlora_linear_bwd_dropout.argtypes = [P, vp, vp, i64, vp, vp, i32, f32, i32, i32, vp, f32, vp, vp, vp, vp, vp,
                                              sz, vp]
+    lib.qlora_linear_fwd_cached.argtypes = [vp, i64, i64, vp, i64, vp, vp, i32, f32, i32, vp, i32, vp, vp, vp, sz, vp]
     lib.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.qlora_workspace_bytes.restype = sz
     lib.qlora_last_error.argtypes = []

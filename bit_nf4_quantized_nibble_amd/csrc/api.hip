@@ -339,6 +339,10 @@ size_t qlora_workspace_bytes(int32_t op, int64_t m, int64_t rows, int64_t cols, 
   op &= (1 << QLORA_OP_FLAGS_SHIFT) - 1;
   if (flags & ~(QLORA_FLAG_RSLORA | QLORA_FLAG_FUSED | QLORA_FLAG_DEQUANT_GEMM | QLORA_FLAG_DROPOUT)) return 0;
   if (op == QLORA_OP_FWD) return fwd_workspace_bytes(m, rows, cols, r, cd, flags);
+  if (op == QLORA_OP_FWD_CACHED) {
+    if (flags & ~QLORA_FLAG_RSLORA || (cd != CD_BF16 && cd != CD_F16)) return 0;
+    return cached_fwd_workspace_bytes(m, rows, cols, r, cd);
+  }
   if (op == QLORA_OP_BWD) return bwd_workspace_bytes(m, rows, cols, r, cd, flags);
   return 0;
 }
@@ -416,6 +420,47 @@ int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void*
     return set_error(QLORA_ERR_INVALID_ARG, "linear_fwd: QLORA_FLAG_DROPOUT belongs to qlora_linear_fwd_dropout");
   return fwd_impl(w, x, m, lora_a, lora_b, r, alpha, flags, bias, cd, nullptr, 0.f, y, t_save, ws, ws_bytes, stream,
                   "linear_fwd");
+}
+
+int qlora_linear_fwd_cached(const void* w_cd, int64_t rows, int64_t cols, const void* x, int64_t m,
+                            const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,
+                            const void* bias, int32_t cd, void* y, float* t_save, void* ws, size_t ws_bytes,
+                            void* stream) {
+  g_err[0] = 0;
+  const char* who = "linear_fwd_cached";
+  if (cd != CD_BF16 && cd != CD_F16) return set_error(QLORA_ERR_DTYPE, "%s: compute dtype must be bf16 or f16", who);
+  if (m < 0 || rows < 1 || cols < 1) return set_error(QLORA_ERR_SHAPE, "%s: bad shape", who);
+  if (r < 1) return set_error(QLORA_ERR_INVALID_ARG, "%s: rank r must be >= 1 (got %d)", who, r);
+  if (!isfinite(alpha)) return set_error(QLORA_ERR_INVALID_ARG, "%s: alpha must be finite", who);
+  if (flags & ~QLORA_FLAG_RSLORA) return set_error(QLORA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", who, flags);
+  if (!w_cd || !x || !lora_a || !lora_b || !y)
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: null w_cd / x / lora_a / lora_b / y", who);
+  if (cols % 64 != 0)
+    return set_error(QLORA_ERR_UNSUPPORTED, "%s: cols (%lld) must be a multiple of 64", who, (long long)cols);
+  const int64_t lim = 0x7fff0000LL;
+  if (rows * cols * 2 >= lim || m * cols * 2 >= lim)
+    return set_error(QLORA_ERR_UNSUPPORTED, "%s: w_cd or x spans 2 GiB or more", who);
+  if (m == 0) return QLORA_OK;
+  int rc = check_ws(ws, ws_bytes, cached_fwd_workspace_bytes(m, rows, cols, r, cd), who);
+  if (rc) return rc;
+  LayerCall c;
+  c.w = Nf4W{};
+  c.w.rows = rows;
+  c.w.cols = cols;
+  c.cd = cd;
+  c.m = m;
+  c.r = r;
+  c.scale = lora_scale(alpha, r, flags);
+  c.flags = flags;
+  c.x = x;
+  c.drop_mask = nullptr;
+  c.lora_a = lora_a;
+  c.lora_b = lora_b;
+  c.bias = bias;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_forward_cached(c, w_cd, y, t_save);
 }
 
 int qlora_linear_fwd_dropout(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,

@@ -272,6 +272,8 @@ size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int
 // dequantize ones), or null.
 int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s, const SkRed* red = nullptr);
 int launch_forward(const LayerCall& c, void* y, float* t_save);
+size_t cached_fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
+int launch_forward_cached(const LayerCall& c, const void* wd, void* y, float* t_save);
 int launch_backward(const LayerCall& c, const void* dy, const float* t_saved, void* dx,
                     float* d_a, float* d_b);
 int launch_merge(const Nf4W& w, const void* a, const void* b, int32_t r, float s, int cd, void* out,

@@ -434,6 +434,10 @@ bool dense_path(int64_t m, int64_t rows, int64_t cols, int cd, int32_t flags, bo
   return true;
 }
 
+// Internal plan flag: W~ comes from the caller (cached-dequant forward), so the
+// workspace holds no copy of it.
+constexpr int32_t kFlagCachedW = 1 << 20;
+
 // Whether the 256 x 256 GEMMs (dense or fused) may take a call of this dtype: their
 // cut last round needs its slices' partial sums in the workspace.
 inline bool big_tiles(int cd) { return cd == CD_BF16 || cd == CD_F16; }
@@ -457,7 +461,7 @@ FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   if (skinny_ok(cd, r)) part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(m, cols));
   P.off_wd = P.off_part + al(part);
   P.dense = dense_path(m, rows, cols, cd, flags, false);
-  P.off_xm = P.off_wd + (P.dense ? al(rows * cols * es) : 0);  // x M with LoRA dropout
+  P.off_xm = P.off_wd + (P.dense && !(flags & kFlagCachedW) ? al(rows * cols * es) : 0);  // x M with LoRA dropout
   P.off_split = P.off_xm + ((flags & QLORA_FLAG_DROPOUT) ? al(m * cols * es) : 0);
   P.dsp = dense_split(m, rows, cols);
   P.total = P.off_split + (big_tiles(cd) ? al(dense_split_bytes(P.dsp)) : 0);
@@ -839,7 +843,47 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   return QLORA_OK;
 }
 
+// Forward with W~ [rows][cols] in cd that the caller dequantized once and keeps
+// (cached-dequant mode): T = s x A^T by the rank-product kernels, then the dense
+// 256 x 256 GEMM reads W~ where it lies.
+template <int CD>
+int forward_cached_t(const LayerCall& c, const void* wd, void* y, float* t_save) {
+  const int64_t M = c.m, N = c.w.rows, K = c.w.cols;
+  const FwdPlan P = plan_fwd(M, N, K, c.r, CD, c.flags | kFlagCachedW);
+  char* ws = (char*)c.ws;
+  void* tcd = ws + P.off_tcd;
+  float* part = (float*)(ws + P.off_part);
+  int rc;
+  if (skinny_ok(CD, c.r)) {
+    int S;
+    if ((rc = skinny(CD, false, c.x, K, M, c.lora_a, K, M, c.r, K, part, &S, c.stream, QLORA_K_LORA_DOWN))) return rc;
+    SkRed red;
+    red.part = part;
+    red.S = S;
+    red.P = M;
+    red.R = c.r;
+    red.out32 = t_save;
+    red.sccd = c.scale;
+    red.outcd = tcd;
+    red.ldcd = P.r_pad;
+    if ((rc = skinny_reduce_jobs(CD, red, nullptr, c.stream))) return rc;
+  } else if ((rc = lora_down<CD>(c, c.x, P.st, part, t_save, 1.0f, tcd, c.scale, P.r_pad))) {
+    return rc;
+  }
+  return dense256_forward(c, wd, tcd, P.r_pad, y, P.dsp, ws + P.off_split);
+}
+
 }  // namespace
+
+size_t cached_fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
+  return (size_t)plan_fwd(m, rows, cols, r, cd, QLORA_FLAG_DEQUANT_GEMM | kFlagCachedW).total;
+}
+
+int launch_forward_cached(const LayerCall& c, const void* wd, void* y, float* t_save) {
+  if (c.cd == CD_BF16) return forward_cached_t<CD_BF16>(c, wd, y, t_save);
+  if (c.cd == CD_F16) return forward_cached_t<CD_F16>(c, wd, y, t_save);
+  return set_error(QLORA_ERR_DTYPE, "linear_fwd_cached: compute dtype must be bf16 or f16");
+}
 
 int gemv_forward(const LayerCall& c, void* y, float* t_save);  // gemv.hip
 size_t gemv_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);

@@ -69,9 +69,9 @@ enum {
   QLORA_FLAG_DROPOUT = 8       /* workspace queries only: size for the *_dropout calls */
 };
 
-/* Workspace queries: op is QLORA_OP_FWD or QLORA_OP_BWD, OR'ed with the call's
+/* Workspace queries: op is QLORA_OP_FWD, QLORA_OP_BWD or QLORA_OP_FWD_CACHED, OR'ed with the call's
  * flags shifted left by QLORA_OP_FLAGS_SHIFT (the path decides the size). */
-enum { QLORA_OP_FWD = 0, QLORA_OP_BWD = 1, QLORA_OP_FLAGS_SHIFT = 8 };
+enum { QLORA_OP_FWD = 0, QLORA_OP_BWD = 1, QLORA_OP_FWD_CACHED = 2, QLORA_OP_FLAGS_SHIFT = 8 };
 
 /*
  * An NF4-quantized frozen weight W [rows, cols].  Descriptor memory is the
@@ -287,6 +287,26 @@ int qlora_linear_bwd_dropout(const qlora_nf4_t* w, const void* x, const void* dy
                              const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,
                              int32_t cd, const uint8_t* mask, float p, const float* t_saved, void* dx,
                              float* d_a, float* d_b, void* ws, size_t ws_bytes, void* stream);
+
+/* Cached-dequant forward (qlora-rs CONFIG "cache_dequantized"; the memory-for-speed
+ * trade-off of BOOK "Tooling" and the README's on-the-fly versus cached dequant):
+ * the caller dequantizes the frozen weight once with qlora_nf4_dequantize(w, cd,
+ * w_cd) and keeps w_cd; each call then computes
+ *   y = x w_cd^T + s (x A^T) B^T (+ bias)
+ * with the dense GEMM reading w_cd in place (no NF4 decode, no copy of W~ in the
+ * workspace; the resident copy costs rows x cols x 2 bytes instead of the packed
+ * 0.5 + scales).  Given w_cd from qlora_nf4_dequantize, y equals qlora_linear_fwd
+ * with QLORA_FLAG_DEQUANT_GEMM bit for bit for m > 16.
+ * w_cd: device [rows, cols] in cd (bf16 or f16), row-major.  Other arguments as for
+ * qlora_linear_fwd; flags: 0 or QLORA_FLAG_RSLORA.  ws: at least
+ * qlora_workspace_bytes(QLORA_OP_FWD_CACHED, m, rows, cols, r, cd) bytes.
+ * Errors: QLORA_ERR_DTYPE unless cd is bf16 / f16; QLORA_ERR_UNSUPPORTED if cols is
+ * not a multiple of 64 or w_cd (or x) spans 2 GiB or more; QLORA_ERR_INVALID_ARG for
+ * null pointers, r < 1, non-finite alpha or other flags; QLORA_ERR_WORKSPACE. */
+int qlora_linear_fwd_cached(const void* w_cd, int64_t rows, int64_t cols, const void* x, int64_t m,
+                            const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,
+                            const void* bias, int32_t cd, void* y, float* t_save, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* Workspace size in bytes for op (QLORA_OP_FWD / QLORA_OP_BWD, optionally OR'ed
  * with flags << QLORA_OP_FLAGS_SHIFT) on this layer shape; 0 for an invalid query.

@@ -131,6 +131,38 @@ def test_forward_shape_refusals(lib):
     assert fwd(lib, desc(), m=0) == OK                          # no tokens: nothing to do
 
 
+def fwd_cached(lib, w=FAKE, rows=256, cols=512, x=FAKE, m=128, a=FAKE, b=FAKE, r=8, alpha=16.0, flags=0, cd=1,
+               y=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.qlora_linear_fwd_cached(w, rows, cols, x, m, a, b, r, alpha, flags, None, cd, y, None, ws, ws_bytes,
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), INVALID),
+    (dict(x=None), INVALID),
+    (dict(y=None), INVALID),
+    (dict(r=0), INVALID),
+    (dict(alpha=float("nan")), INVALID),
+    (dict(flags=2), INVALID),        # path flags do not apply: W~ is given
+    (dict(cd=0), DTYPE),             # f32 has no dense 256 x 256 GEMM
+    (dict(cols=96), UNSUP),
+    (dict(rows=0), SHAPE),
+    (dict(ws_bytes=16), WS),
+    (dict(m=0), OK),
+])
+def test_forward_cached_refusals(lib, kw, status):
+    assert fwd_cached(lib, **kw) == status
+
+
+def test_forward_cached_workspace(lib):
+    cached = lib.qlora_workspace_bytes(2, 2048, 4096, 4096, 64, 1)
+    dense = lib.qlora_workspace_bytes(0 | (4 << 8), 2048, 4096, 4096, 64, 1)
+    assert 0 < cached and dense - cached >= 4096 * 4096 * 2      # no copy of W~ in the workspace
+    assert lib.qlora_workspace_bytes(2 | (1 << 8), 2048, 4096, 4096, 64, 1) == cached  # rsLoRA
+    assert lib.qlora_workspace_bytes(2 | (2 << 8), 2048, 4096, 4096, 64, 1) == 0       # path flag
+    assert lib.qlora_workspace_bytes(2, 2048, 4096, 4096, 64, 0) == 0                  # f32
+
+
 def test_backward_refusals(lib):
     d = desc()
 

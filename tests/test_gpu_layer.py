@@ -99,6 +99,26 @@ def test_forward_decode_epilogue_paths(m, N, K, r, bias):
     assert oracle.rel_l2(got, ref_t0) <= 1e-5, "decode T0"
 
 
+@pytest.mark.parametrize("m,N,K,r,dq,bias", [
+    (5, 72, 8192, 16, True, True),     # 16 contraction slices of 512
+    (16, 130, 1536, 12, False, False),  # 3 slices: the VALU GEMV; fp32 block scales, ragged N
+    (1, 16, 512, 1, True, True),        # one slice, one row block, rank 1
+])
+def test_forward_decode_more_shapes(m, N, K, r, dq, bias):
+    """Decode (m <= 16) with the saved T0 on the slice counts and scale forms the
+    full-size cases do not reach."""
+    L = inputs.random_layer(m, N, K, r, seed=7 * m + N + r, cd="bf16", double_quant=dq, with_bias=bias,
+                            with_dy=False)
+    say("fwd decode shapes", m, N, K, r, dq, bias)
+    g = to_gpu(L)
+    y, t0 = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], save_t=True)
+    torch.cuda.synchronize()
+    o = oracle_layer(L)
+    assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"]), "bf16", "decode y")
+    ref_t0 = np.asarray(o["x"], np.float64) @ np.asarray(o["A"], np.float64).T
+    assert oracle.rel_l2(to_np(t0).astype(np.float64), ref_t0) <= 1e-5, "decode T0"
+
+
 def test_forward_save_t_and_leading_dims():
     L = inputs.random_layer(60, 128, 256, 8, seed=3, with_dy=False)
     say("fwd save_t")
