@@ -32,9 +32,15 @@
 //   dX:      the contraction runs over W's rows, so a lane decodes an 8 x 8 block
 //            (8 rows x one 32-bit word of codes) and packs pairs from adjacent
 //            rows, writing 16-byte runs of the transposed tile [k][n].
-// The workgroup -> tile map keeps the tiles that run concurrently on one XCD
-// (workgroups b, b + 8, ... share an XCD) in the same row block, so their common
-// activation tile stays in that XCD's L2.
+// The workgroup -> tile map gives each XCD (workgroups b, b + 8, ... share one) a
+// compact block of tiles, so their common operand tiles stay in that XCD's L2.
+//
+// The dense kernel (dequantize-then-GEMM: W~ already in the compute dtype) copies
+// both operands by DMA and runs 8 waves of 128 x 64 (two per SIMD, 185 registers
+// each) with waves 0..3 issuing the copies; a forward whose rank is not a multiple
+// of 8 takes the 4-wave form, whose low-rank tail is the fused kernel's code.  An
+// incomplete last round of tiles is cut into contraction slices whose fp32 partial
+// sums k_split_sum adds (both kernels).
 #include <algorithm>
 
 #include "common.h"
