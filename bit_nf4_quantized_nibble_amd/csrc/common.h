@@ -46,6 +46,17 @@ struct Nf4W {
                              // every block (fewer than 2^31), else -1
 };
 
+// Byte e of x in one instruction (left to itself the compiler shifts and masks:
+// two instructions for bytes 1 and 2).
+__device__ __forceinline__ uint32_t byte_of(uint32_t x, int e) {
+  if (e == 0) return x & 0xffu;
+  if (e == 3) return x >> 24;
+  uint32_t r;
+  if (e == 1) asm("v_bfe_u32 %0, %1, 8, 8" : "=v"(r) : "v"(x));
+  else asm("v_bfe_u32 %0, %1, 16, 8" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // Block of flat element e, and second-level group of block b.  Shifts when the
 // sizes are powers of two (a 64-bit division costs dozens of instructions).
 __device__ __forceinline__ int64_t block_of(const Nf4W& w, int64_t e) {

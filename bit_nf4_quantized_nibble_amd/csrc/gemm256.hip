@@ -239,17 +239,6 @@ __device__ __forceinline__ void fetch_w(CodeRegs& R, const Big& p, const Lane& L
 }
 
 // Level lookup: a = 4 * code (byte address into the 16-word table).
-// Byte e of x in one instruction (left to itself the compiler shifts and masks:
-// two instructions for bytes 1 and 2).
-__device__ __forceinline__ uint32_t byte_of(uint32_t x, int e) {
-  if (e == 0) return x & 0xffu;
-  if (e == 3) return x >> 24;
-  uint32_t r;
-  if (e == 1) asm("v_bfe_u32 %0, %1, 8, 8" : "=v"(r) : "v"(x));
-  else asm("v_bfe_u32 %0, %1, 16, 8" : "=v"(r) : "v"(x));
-  return r;
-}
-
 __device__ __forceinline__ float lv_at(const char* lds, uint32_t a) {
   return *(const float*)(lds + LV_OFF + a);
 }

@@ -102,17 +102,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
 }
 __device__ __forceinline__ uint32_t oob_unless(bool ok, uint32_t off) { return off | ((uint32_t)(!ok) << 31); }
 
-// Byte e of x in one instruction (left to itself the compiler shifts and masks:
-// two instructions for bytes 1 and 2).
-__device__ __forceinline__ uint32_t byte_of(uint32_t x, int e) {
-  if (e == 0) return x & 0xffu;
-  if (e == 3) return x >> 24;
-  uint32_t r;
-  if (e == 1) asm("v_bfe_u32 %0, %1, 8, 8" : "=v"(r) : "v"(x));
-  else asm("v_bfe_u32 %0, %1, 16, 8" : "=v"(r) : "v"(x));
-  return r;
-}
-
 template <int CD>
 __device__ __forceinline__ f32x4v_t mfma16(u32x4_t a, u32x4_t b, f32x4v_t c) {
   if constexpr (CD == CD_BF16)
