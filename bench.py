@@ -686,8 +686,8 @@ def main():
                     help="run one part (for profiling); the JSON line needs the full run")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU; --gpus %d is not supported "
-              "(the layer would shard data-parallel over tokens, see the design notes)" % args.gpus,
+        print("bench.py: the benchmark measures one GPU; --gpus %d is not supported "
+              "(the layer would shard data-parallel over tokens)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
