@@ -125,7 +125,9 @@ constexpr int kGemvThreads = 512;  // 8 waves: row group w % 4 (16 rows), slice 
 
 template <int CD, int DQ>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvP p, Nf4Tables tab) {
-  __shared__ float s_lv[16];
+  // the level pair of every code byte (element 2b in the high nibble, 2b + 1 in the low
+  // one): one 8-byte LDS read per two codes
+  __shared__ __attribute__((aligned(16))) float2 s_pair[256];
   __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxM][kSlice + 8];  // +16 B per row: no bank conflicts
   // the codes of the slice, [64 rows][256 bytes]; 16-byte chunk c of row r sits at
   // chunk c ^ (r % 16), so the 16 rows a read instruction touches hit 16 bank groups
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvP p, Nf4Tables t
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave & 3, half = wave >> 2;
-  if (tid < 16) s_lv[tid] = tab.lv[tid];
+  if (tid < 256) s_pair[tid] = make_float2(tab.lv[tid >> 4], tab.lv[tid & 15]);
   const Nf4W& w = p.w;
   const int64_t K = w.cols, N = w.rows;
   const int64_t n0 = (int64_t)blockIdx.x * kRowBlock;
@@ -221,12 +223,12 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvP p, Nf4Tables t
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint32_t word = cw[u];
-        const uint32_t hi4 = (word >> 2) & 0x3c3c3c3cu, lo4 = (word << 2) & 0x3c3c3c3cu;
         u32x4_t a;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)  // byte b: element 2b in the high nibble, 2b + 1 in the low one
-          a[b] = pack2<CD>(fl32_mul(*(const float*)((const char*)s_lv + byte_of(hi4, b)), s),
-                           fl32_mul(*(const float*)((const char*)s_lv + byte_of(lo4, b)), s));
+        for (int b = 0; b < 4; ++b) {  // byte b: element 2b in the high nibble, 2b + 1 in the low one
+          const float2 lv2 = *(const float2*)((const char*)s_pair + (byte_of(word, b) << 3));
+          a[b] = pack2<CD>(fl32_mul(lv2.x, s), fl32_mul(lv2.y, s));
+        }
         acc[u] = mfma16<CD>(a, *(const u32x4_t*)&xs[rl][128 * j + 32 * q + 8 * u], acc[u]);
       }
     }
