@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -130,11 +131,15 @@ int validate_layer(const qlora_nf4_t* w, const void* x, int64_t m, const void* l
     return set_error(QLORA_ERR_INVALID_ARG, "%s: QLORA_FLAG_FUSED and QLORA_FLAG_DEQUANT_GEMM exclude each other", who);
   if (w->rows < 1 || w->cols < 1) return set_error(QLORA_ERR_SHAPE, "%s: empty weight", who);
   if (!x || !lora_a || !lora_b) return set_error(QLORA_ERR_INVALID_ARG, "%s: null x / lora_a / lora_b", who);
-  if (w->cols % 64 != 0)
-    return set_error(QLORA_ERR_UNSUPPORTED, "%s: cols (%lld) must be a multiple of 64", who, (long long)w->cols);
-  if (w->block_size % 32 != 0 || w->cols % w->block_size != 0)
-    return set_error(QLORA_ERR_UNSUPPORTED, "%s: block_size %d must be a multiple of 32 dividing cols", who,
-                     w->block_size);
+  if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b))
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: x, lora_a and lora_b must be 16-byte aligned", who);
+  return QLORA_OK;
+}
+
+// Optional device arrays of a layer call: null, or 16-byte aligned.
+int check_aligned(const char* who, const char* names, std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return set_error(QLORA_ERR_INVALID_ARG, "%s: %s must be 16-byte aligned", who, names);
   return QLORA_OK;
 }
 
@@ -311,9 +316,6 @@ int qlora_nf4_quantize(const float* w, qlora_nf4_t* q, void* stream) {
   if (n == 0) return QLORA_OK;
   if (!w) return set_error(QLORA_ERR_INVALID_ARG, "quantize: null weight");
   if (!aligned16(w)) return set_error(QLORA_ERR_INVALID_ARG, "quantize: weight must be 16-byte aligned");
-  const int32_t bs = q->block_size;
-  if (bs < 8 || bs > 512 || (bs & (bs - 1)))
-    return set_error(QLORA_ERR_UNSUPPORTED, "quantize: block_size %d (need a power of two in 8..512)", bs);
   if ((rc = check_tables("quantize"))) return rc;
   return launch_quantize(w, q, (hipStream_t)stream);
 }
@@ -327,8 +329,6 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, int32_t out_dtype, void* out, voi
   if (n == 0) return QLORA_OK;
   if (!out) return set_error(QLORA_ERR_INVALID_ARG, "dequantize: null output");
   if (!aligned16(out)) return set_error(QLORA_ERR_INVALID_ARG, "dequantize: output must be 16-byte aligned");
-  if (q->block_size % 8 != 0)
-    return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: block_size %d must be a multiple of 8", q->block_size);
   if ((rc = check_tables("dequantize"))) return rc;
   return launch_dequantize(q, out_dtype, out, (hipStream_t)stream);
 }
@@ -354,6 +354,7 @@ int fwd_impl(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
   int rc = validate_layer(w, x, m, lora_a, lora_b, r, alpha, flags, cd, who);
   if (rc) return rc;
   if (!y) return set_error(QLORA_ERR_INVALID_ARG, "%s: null y", who);
+  if ((rc = check_aligned(who, "y, bias, t_save and the dropout mask", {y, bias, t_save, mask}))) return rc;
   if (m == 0) return QLORA_OK;
   if (mask) flags |= QLORA_FLAG_DROPOUT;
   if ((rc = check_ws(ws, ws_bytes, fwd_workspace_bytes(m, w->rows, w->cols, r, cd, flags), who))) return rc;
@@ -383,6 +384,8 @@ int bwd_impl(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m, con
   int rc = validate_layer(w, x, m, lora_a, lora_b, r, alpha, flags, cd, who);
   if (rc) return rc;
   if (!dy || !d_a || !d_b) return set_error(QLORA_ERR_INVALID_ARG, "%s: null dy / d_a / d_b", who);
+  if ((rc = check_aligned(who, "dy, dx, d_a, d_b, t_saved and the dropout mask", {dy, dx, d_a, d_b, t_saved, mask})))
+    return rc;
   if (m == 0) return set_error(QLORA_ERR_SHAPE, "%s: m must be >= 1 (dA, dB would be all zero)", who);
   if (mask) flags |= QLORA_FLAG_DROPOUT;
   if ((rc = check_ws(ws, ws_bytes, bwd_workspace_bytes(m, w->rows, w->cols, r, cd, flags), who))) return rc;
@@ -435,14 +438,15 @@ int qlora_linear_fwd_cached(const void* w_cd, int64_t rows, int64_t cols, const 
   if (flags & ~QLORA_FLAG_RSLORA) return set_error(QLORA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", who, flags);
   if (!w_cd || !x || !lora_a || !lora_b || !y)
     return set_error(QLORA_ERR_INVALID_ARG, "%s: null w_cd / x / lora_a / lora_b / y", who);
+  int rc = check_aligned(who, "w_cd, x, lora_a, lora_b, y, bias and t_save", {w_cd, x, lora_a, lora_b, y, bias, t_save});
+  if (rc) return rc;
   if (cols % 64 != 0)
     return set_error(QLORA_ERR_UNSUPPORTED, "%s: cols (%lld) must be a multiple of 64", who, (long long)cols);
   const int64_t lim = 0x7fff0000LL;
   if (rows * cols * 2 >= lim || m * cols * 2 >= lim)
     return set_error(QLORA_ERR_UNSUPPORTED, "%s: w_cd or x spans 2 GiB or more", who);
   if (m == 0) return QLORA_OK;
-  int rc = check_ws(ws, ws_bytes, cached_fwd_workspace_bytes(m, rows, cols, r, cd), who);
-  if (rc) return rc;
+  if ((rc = check_ws(ws, ws_bytes, cached_fwd_workspace_bytes(m, rows, cols, r, cd), who))) return rc;
   LayerCall c;
   c.w = Nf4W{};
   c.w.rows = rows;

@@ -129,6 +129,28 @@ __device__ __forceinline__ void decode32(const Nf4W& w, int64_t e, const float* 
   }
 }
 
+// Decode the (up to) 32 weights of W row `row` at columns k0 .. k0+31 for any even
+// block size and any cols: one code byte and one block scale per element, zero past
+// the row's end (blocks may cross rows: the block is that of the flat index).
+__device__ __forceinline__ void decode32_any(const Nf4W& w, int64_t row, int64_t k0, const float* s_lv,
+                                             float (&f)[32]) {
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    f[e] = 0.f;
+    const int64_t k = k0 + e;
+    if (k < w.cols) {
+      const int64_t flat = row * w.cols + k;
+      const uint32_t byte = w.codes[flat >> 1];
+      const uint32_t c = (flat & 1) ? (byte & 15u) : (byte >> 4);  // element 2j in the high nibble
+      f[e] = fl32_mul(s_lv[c], block_scale(w, block_of(w, flat)));
+    }
+  }
+}
+
+// decode32 needs each 32-element chunk inside one block with 16-byte aligned codes:
+// a block size and a row length that are multiples of 32.
+__device__ __forceinline__ bool chunks32(const Nf4W& w) { return (w.bs & 31) == 0 && (w.cols & 31) == 0; }
+
 template <int CD, int LK, int BR>
 __device__ __forceinline__ void load_tile(char* lds, const Opnd& o, const Nf4W& w, const float* s_lv,
                                           int64_t i0, int64_t k0, int tid) {
@@ -194,7 +216,8 @@ __device__ __forceinline__ void load_tile(char* lds, const Opnd& o, const Nf4W& 
       char* dst = lds + row * ROWB + c * 32 * ES;
       if (gi < w.rows && gk < w.cols) {
         float f[32];
-        decode32<CD>(w, gi * w.cols + gk, s_lv, f);
+        if (chunks32(w)) decode32<CD>(w, gi * w.cols + gk, s_lv, f);
+        else decode32_any(w, gi, gk, s_lv, f);
         if constexpr (CD == CD_F32) {
 #pragma unroll
           for (int d = 0; d < 8; ++d)
@@ -221,7 +244,8 @@ __device__ __forceinline__ void load_tile(char* lds, const Opnd& o, const Nf4W& 
       const int64_t gn = k0 + nr, gk = i0 + 32 * c;
       float f[32];
       if (gn < w.rows && gk < w.cols) {
-        decode32<CD>(w, gn * w.cols + gk, s_lv, f);
+        if (chunks32(w)) decode32<CD>(w, gn * w.cols + gk, s_lv, f);
+        else decode32_any(w, gn, gk, s_lv, f);
       } else {
 #pragma unroll
         for (int e = 0; e < 32; ++e) f[e] = 0.f;
@@ -442,6 +466,14 @@ constexpr int32_t kFlagCachedW = 1 << 20;
 // cut last round needs its slices' partial sums in the workspace.
 inline bool big_tiles(int cd) { return cd == CD_BF16 || cd == CD_F16; }
 
+// Layers whose block size is a multiple of 32 dividing cols, with cols a multiple
+// of 64, take the tiled kernels (decode GEMV, rank-product kernels, 256 x 256
+// GEMMs).  Every other layer the quantize call accepts (any even block size, any
+// cols, blocks that run across rows) takes the generic tile engine for all of its
+// products, decoding W per element.  The workspace queries do not know the block
+// size; they always cover the generic engine's needs.
+inline bool fast_layout(const Nf4W& w) { return w.bs % 32 == 0 && w.cols % 64 == 0 && w.cols % w.bs == 0; }
+
 // Workspace plan shared by the size query and the launchers.
 struct FwdPlan {
   int64_t r_pad;
@@ -581,6 +613,7 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
   void* tcd = ws + P.off_tcd;
   float* part = (float*)(ws + P.off_part);
   int rc;
+  const bool fast = fast_layout(c.w);
   // input of the low-rank branch: x, or x M with LoRA dropout
   const void* lx = c.x;
   if (c.drop_mask) {
@@ -590,10 +623,10 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
   // T0 = x A^T (fp32, saved on request) and T = s T0 in cd for the GEMM's tail.  On
   // the dequantize-then-GEMM path the reduction of the skinny kernel's slices rides
   // on the dequantize launch.
-  const bool dense = P.dense && dense256_ok(c, false);
+  const bool dense = fast && P.dense && dense256_ok(c, false);
   SkRed red;
   bool red_pending = false;
-  if (skinny_ok(CD, c.r)) {
+  if (fast && skinny_ok(CD, c.r)) {
     int S;
     if ((rc = skinny(CD, false, lx, K, M, c.lora_a, K, M, c.r, K, part, &S, c.stream, QLORA_K_LORA_DOWN))) return rc;
     red.part = part;
@@ -614,7 +647,7 @@ int forward_gemm(const LayerCall& c, void* y, float* t_save) {
     if ((rc = dequant_into(c.w, CD, wd, false, c.stream, red_pending ? &red : nullptr))) return rc;
     return dense256_forward(c, wd, tcd, P.r_pad, y, P.dsp, ws + P.off_split);
   }
-  if (fused256_ok(c, false)) return fused256_forward(c, tcd, P.r_pad, y, P.dsp, ws + P.off_split);
+  if (fast && fused256_ok(c, false)) return fused256_forward(c, tcd, P.r_pad, y, P.dsp, ws + P.off_split);
 
   GemmParams p = base_params(c);
   p.a1 = opnd<CD>(c.x, K, M, K);
@@ -637,6 +670,8 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
                   float* d_b) {
   const int64_t M = c.m, N = c.w.rows, K = c.w.cols, r = c.r;
   BwdPlan P = plan_bwd(M, N, K, c.r, CD, c.flags);
+  const bool fast = fast_layout(c.w);
+  if (!fast) P.sk = P.sk_n = P.dense = false;  // the generic engine for every product (see fast_layout)
   char* ws = (char*)c.ws;
   float* t0 = (float*)(ws + P.off_t0);
   float* dt = (float*)(ws + P.off_dt);
@@ -738,7 +773,7 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
     void* wdt = ws + P.off_wdt;
     if ((rc = dequant_into(c.w, CD, wdt, true, c.stream, red_dt_pending ? &red_dt : nullptr))) return rc;
     if ((rc = dense256_dx(c, dy, wdt, dt_gemm, P.r_pad, dx, P.dsp, ws + P.off_split, at))) return rc;
-  } else if (dx && fused256_ok(c, true)) {
+  } else if (dx && fast && fused256_ok(c, true)) {
     rc = fused256_dx(c, dy, dt_gemm, P.r_pad, dx, P.dsp, ws + P.off_split);
     if (rc) return rc;
   } else if (dx) {
@@ -890,7 +925,11 @@ size_t gemv_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, in
 constexpr int64_t kGemvMaxM = 16;
 
 size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
-  if (m <= kGemvMaxM && !(flags & QLORA_FLAG_DROPOUT)) return gemv_workspace_bytes(m, rows, cols, r, cd);
+  // m <= 16 takes the decode GEMV, or the generic engine for a layout the GEMV does
+  // not take (the query does not see the block size): T and the rank-product
+  // partial sums, which come first in the GEMM path's plan.
+  if (m <= kGemvMaxM && !(flags & QLORA_FLAG_DROPOUT))
+    return std::max(gemv_workspace_bytes(m, rows, cols, r, cd), (size_t)plan_fwd(m, rows, cols, r, cd, flags).off_wd);
   return (size_t)plan_fwd(m, rows, cols, r, cd, flags).total;
 }
 
@@ -899,7 +938,7 @@ size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int
 }
 
 int launch_forward(const LayerCall& c, void* y, float* t_save) {
-  if (c.m <= kGemvMaxM && !c.drop_mask) return gemv_forward(c, y, t_save);
+  if (c.m <= kGemvMaxM && !c.drop_mask && fast_layout(c.w)) return gemv_forward(c, y, t_save);
   switch (c.cd) {
     case CD_BF16: return forward_gemm<CD_BF16>(c, y, t_save);
     case CD_F16: return forward_gemm<CD_F16>(c, y, t_save);

@@ -33,6 +33,29 @@ __device__ __forceinline__ uint32_t nearest_code(float x, const int* __restrict_
   return (uint32_t)(base[b] + (x >= thr[b] ? 1 : 0));
 }
 
+// x = fl32(w / a) by Markstein's correction: r = RN(1/a) once per block, then
+// y = RN(w r) is within an ulp of w / a and RN(y + RN(w - a y) r) = RN(w / a).
+// Blocks of very small or very large magnitude are rescaled by an exact power of
+// two first so that 1/a stays a normal number.  The caller passes the block's
+// sc, as = a sc and rcp = RN(1 / as) (see block_recip); a == 0 gives x = 0.
+struct BlockRecip {
+  float sc, as, rcp;
+};
+__device__ __forceinline__ BlockRecip block_recip(float a) {
+  BlockRecip r;
+  r.sc = (a < 0x1p-64f) ? 0x1p64f : ((a > 0x1p64f) ? 0x1p-64f : 1.0f);
+  r.as = a * r.sc;
+  r.rcp = 1.0f / r.as;
+  return r;
+}
+__device__ __forceinline__ float normalize(float w, float a, const BlockRecip& r) {
+  const float ws = w * r.sc;
+  const float y = ws * r.rcp;
+  const float rem = fmaf(-r.as, y, ws);
+  const float x = fmaf(rem, r.rcp, y);
+  return a == 0.0f ? 0.0f : x;
+}
+
 template <int BS>
 __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__ w, int64_t n,
                                                        uint8_t* __restrict__ codes,
@@ -87,22 +110,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
         absmax[blk0 + blk_local] = a;
     }
 
-    // x = fl32(w / a) by Markstein's correction: r = RN(1/a) once per block, then
-    // y = RN(w r) is within an ulp of w / a and RN(y + RN(w - a y) r) = RN(w / a).
-    // Blocks of very small or very large magnitude are rescaled by an exact power
-    // of two first so that 1/a stays a normal number.
-    const float sc = (a < 0x1p-64f) ? 0x1p64f : ((a > 0x1p64f) ? 0x1p-64f : 1.0f);
-    const float as = a * sc;
-    const float rcp = 1.0f / as;
+    const BlockRecip br = block_recip(a);
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float ws = v[i] * sc;
-      float y = ws * rcp;
-      float rem = fmaf(-as, y, ws);
-      float x = fmaf(rem, rcp, y);
-      if (a == 0.0f) x = 0.0f;
-      uint32_t c = nearest_code(x, s_base, s_thr);
+      const uint32_t c = nearest_code(normalize(v[i], a, br), s_base, s_thr);
       // element 2k -> high nibble of byte k
       word |= c << ((i >> 1) * 8 + ((i & 1) ? 0 : 4));
     }
@@ -233,6 +245,94 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(Nf4W q, int64_t n, void
       *(u32x4_t*)((uint16_t*)out + e) = o;
     }
   }
+}
+
+// Any even block size (the kernels above take powers of two from 8 to 512): one
+// wavefront per block.  Lane l reads the weight pairs (2j, 2j + 1) with j = l + 64 i
+// of its block, the block absmax is combined across the wavefront, and lane l
+// writes the code bytes j it read.  Without double quantization lane 0 stores the
+// absmax; with it, lane 0 folds the block absmax into scale2[group] as a maximum
+// (atomic max on the bits of non-negative floats, from zero) and k_dq_any_q
+// encodes the u8 scales in a second pass.  Same values as the one-pass kernels.
+constexpr int kAnyBlocksPerWg = kThreads / 64;
+
+__device__ __forceinline__ float block_absmax_wave(const float* __restrict__ wb, int64_t bs, int lane) {
+  float a = 0.0f;
+  for (int64_t j = lane; 2 * j < bs; j += 64) {
+    const float2 v = *(const float2*)(wb + 2 * j);
+    a = fmaxf(a, fmaxf(fabsf(v.x), fabsf(v.y)));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+  return a;
+}
+
+__global__ __launch_bounds__(kThreads) void k_quantize_any(const float* __restrict__ w, int64_t nb, int64_t bs,
+                                                           uint8_t* __restrict__ codes, float* __restrict__ absmax,
+                                                           float* __restrict__ gmax, int64_t dq_group,
+                                                           Nf4Tables tab) {
+  __shared__ int s_base[32];
+  __shared__ float s_thr[32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 32) {
+    s_base[tid] = tab.bucket_base[tid];
+    s_thr[tid] = tab.bucket_thr[tid];
+  }
+  __syncthreads();
+  const int64_t b = (int64_t)blockIdx.x * kAnyBlocksPerWg + (tid >> 6);
+  if (b >= nb) return;
+  const float* wb = w + b * bs;
+  const float a = block_absmax_wave(wb, bs, lane);
+  if (lane == 0) {
+    if (gmax) atomicMax((uint32_t*)gmax + b / dq_group, __float_as_uint(a));
+    else absmax[b] = a;
+  }
+  const BlockRecip br = block_recip(a);
+  uint8_t* cb = codes + b * (bs / 2);
+  for (int64_t j = lane; 2 * j < bs; j += 64) {
+    const float2 v = *(const float2*)(wb + 2 * j);
+    const uint32_t hi = nearest_code(normalize(v.x, a, br), s_base, s_thr);
+    const uint32_t lo = nearest_code(normalize(v.y, a, br), s_base, s_thr);
+    cb[j] = (uint8_t)((hi << 4) | lo);  // element 2j in the high nibble
+  }
+}
+
+// Second pass of double quantization for any block size: q_b = round-half-even(a_b / S)
+// with S = fl32(max / 255) of the block's group (gmax still holds the maximum).
+__global__ __launch_bounds__(kThreads) void k_dq_any_q(const float* __restrict__ w, int64_t nb, int64_t bs,
+                                                       uint8_t* __restrict__ absmax_q,
+                                                       const float* __restrict__ gmax, int64_t dq_group) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t b = (int64_t)blockIdx.x * kAnyBlocksPerWg + (tid >> 6);
+  if (b >= nb) return;
+  const float a = block_absmax_wave(w + b * bs, bs, lane);
+  if (lane == 0) {
+    const float S = gmax[b / dq_group] / 255.0f;
+    double q = 0.0;
+    if (S > 0.0f) {
+      q = __builtin_rint((double)a / (double)S);
+      q = q < 0.0 ? 0.0 : (q > 255.0 ? 255.0 : q);
+    }
+    absmax_q[b] = (uint8_t)q;
+  }
+}
+
+// Dequantize for any even block size and any n: thread i decodes code byte i
+// (elements 2i and 2i + 1, which share a block because blocks start at even
+// offsets) and stores the pair.
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void k_dequantize_any(Nf4W q, int64_t n, void* __restrict__ out,
+                                                             Nf4Tables tab) {
+  __shared__ float s_lv[16];
+  if (threadIdx.x < 16) s_lv[threadIdx.x] = tab.lv[threadIdx.x];
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (2 * i >= n) return;
+  const uint32_t byte = q.codes[i];
+  const float s = block_scale(q, block_of(q, 2 * i));
+  const float f0 = fl32_mul(s_lv[byte >> 4], s), f1 = fl32_mul(s_lv[byte & 15u], s);
+  if constexpr (OUT == CD_F32) *(float2*)((float*)out + 2 * i) = make_float2(f0, f1);
+  else *(uint32_t*)((uint16_t*)out + 2 * i) = pack2<OUT>(f0, f1);
 }
 
 }  // namespace
@@ -401,9 +501,32 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restr
   }
 }
 
+// Any even block size outside the power-of-two kernels (see k_quantize_any).
+int launch_quantize_any(const float* w, const qlora_nf4_t* q, hipStream_t s) {
+  const int64_t n = q->rows * q->cols;
+  const int64_t bs = q->block_size, nb = n / bs;
+  const int64_t grid = ceil_div(nb, kAnyBlocksPerWg);
+  if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "quantize: tensor too large");
+  const Nf4Tables& t = host_tables();
+  ProfScope prof(QLORA_K_QUANTIZE, s);
+  if (q->double_quant) {
+    const int64_t ng = ceil_div(nb, q->dq_group);
+    k_fill_zero<<<dim3((unsigned)ceil_div(ng, kThreads)), dim3(kThreads), 0, s>>>(q->absmax_scale2, ng);
+    k_quantize_any<<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, nb, bs, q->codes, nullptr, q->absmax_scale2,
+                                                                   q->dq_group, t);
+    k_dq_any_q<<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, nb, bs, q->absmax_q, q->absmax_scale2,
+                                                               q->dq_group);
+    k_dq_large_finish<<<dim3((unsigned)ceil_div(ng, kThreads)), dim3(kThreads), 0, s>>>(q->absmax_scale2, ng);
+  } else {
+    k_quantize_any<<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, nb, bs, q->codes, q->absmax, nullptr, 1, t);
+  }
+  return check_launch("k_quantize_any");
+}
+
 int launch_quantize(const float* w, const qlora_nf4_t* q, hipStream_t s) {
   const int64_t n = q->rows * q->cols;
   const int bs = q->block_size;
+  if (bs < 8 || bs > 512 || (bs & (bs - 1))) return launch_quantize_any(w, q, s);
   const int64_t nb = n / bs;
   // dq: 0 none, 1 groups of up to 4096 blocks (one workgroup each, one pass),
   // 2 larger groups (spans of 16384 elements, a second pass for the u8 scales).
@@ -488,13 +611,22 @@ int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s, const SkRed* r
     return check_launch("k_dequant_chunks");
   }
   if (red && (rc = skinny_reduce_jobs(cd, *red, nullptr, s))) return rc;
-  const int64_t grid = ceil_div(ceil_div(n, 32), kThreads);
+  if (w.bs % 8 == 0 && n % 32 == 0) {
+    const int64_t grid = ceil_div(n / 32, kThreads);
+    if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
+    if (cd == CD_BF16) k_dequantize<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+    else if (cd == CD_F16) k_dequantize<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+    else if (cd == CD_F32) k_dequantize<CD_F32><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+    else return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
+    return check_launch("k_dequantize");
+  }
+  const int64_t grid = ceil_div(n / 2, kThreads);
   if (grid > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
-  if (cd == CD_BF16) k_dequantize<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
-  else if (cd == CD_F16) k_dequantize<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
-  else if (cd == CD_F32) k_dequantize<CD_F32><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+  if (cd == CD_BF16) k_dequantize_any<CD_BF16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+  else if (cd == CD_F16) k_dequantize_any<CD_F16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
+  else if (cd == CD_F32) k_dequantize_any<CD_F32><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, n, out, t);
   else return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
-  return check_launch("k_dequantize");
+  return check_launch("k_dequantize_any");
 }
 
 template <int OUT, int DQ>

@@ -21,6 +21,12 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates or frees device memory.  Matrices are row-major and dense.
+ *     The fp32 weight and the codes of quantize / dequantize, the dequantized
+ *     output, and every array of a layer call (x, dy, adapters, bias, outputs,
+ *     masks, saved T0, gradients) start on a 16-byte boundary: the kernels move
+ *     16-byte vectors, and an unaligned pointer is refused with
+ *     QLORA_ERR_INVALID_ARG.  Workspaces are 256-byte aligned.  The merge, MSE
+ *     and AdamW calls take any element-aligned arrays.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = null stream).
  *   - Arguments are validated on the host before anything is launched: on any
  *     error nothing is written and no work is queued.  Errors: a negative
@@ -85,7 +91,7 @@ enum { QLORA_OP_FWD = 0, QLORA_OP_BWD = 1, QLORA_OP_FWD_CACHED = 2, QLORA_OP_FLA
 typedef struct {
   int64_t rows;
   int64_t cols;
-  int32_t block_size;   /* even; the quantize kernel takes 8..512 with block_size/8 a power of two */
+  int32_t block_size;   /* any even size; powers of two from 8 to 512 take the vectorized kernels */
   int32_t double_quant; /* 0 or 1 */
   int32_t dq_group;     /* blocks per second-level scale when double_quant (>= 1; a value
                            >= rows*cols/block_size gives one scale for the whole tensor) */
@@ -102,13 +108,15 @@ typedef struct {
  * packing and, if q->double_quant, the u8 + fp32 encoding of the block scales.
  * Pages: qlora-rs README "Honest capability matrix" (NF4 pack/unpack, block absmax,
  * double quant that drops the resident fp32 scales) and "NF4 Quantization".
- * Writes q->codes and either q->absmax or q->absmax_q + q->absmax_scale2.  Groups of
- * up to 4096 blocks are encoded in one pass over W; larger ones (one group for the
- * whole tensor included: the "global" scale-of-scales) take a second pass.
+ * Writes q->codes and either q->absmax or q->absmax_q + q->absmax_scale2.  Block
+ * sizes that are powers of two from 8 to 512 run on a vectorized kernel (groups of
+ * up to 4096 blocks are encoded in one pass over W; larger ones, one group for the
+ * whole tensor included: the "global" scale-of-scales, take a second pass); every
+ * other even block size on a one-wavefront-per-block kernel (with double
+ * quantization in two passes).  The results are the same bits either way.
  * An empty tensor (rows * cols == 0) is a no-op that returns QLORA_OK.
  * Errors: QLORA_ERR_SHAPE (n % block_size, odd block_size, negative dims),
- * QLORA_ERR_UNSUPPORTED (block_size outside 8..512 or block_size/8 not a power of
- * two), QLORA_ERR_INVALID_ARG (null pointers, reserved != 0).
+ * QLORA_ERR_INVALID_ARG (null or unaligned pointers, reserved != 0).
  * NaN / Inf in W are outside the contract (codes are then unspecified, no fault).
  */
 int qlora_nf4_quantize(const float* w, qlora_nf4_t* q, void* stream);
@@ -122,21 +130,27 @@ int qlora_nf4_quantize(const float* w, qlora_nf4_t* q, void* stream);
 int qlora_nf4_dequantize(const qlora_nf4_t* q, int32_t out_dtype, void* out, void* stream);
 
 /*
- * Forward of the QLoRA linear layer, fused dequantize + GEMM:
+ * Forward of the QLoRA linear layer:
  *   y [m, rows] = x [m, cols] . W~^T + s (x . A^T) . B^T (+ bias [rows])
  * x, lora_a [r, cols], lora_b [rows, r], bias, y are in dtype cd; accumulation is
  * fp32.  t_save (nullable) receives T0 = x A^T in fp32 [m, r] for the backward.
  * Pages: qlora-rs README "Quick Start" (QuantizedLinear::forward) and "Honest
  * capability matrix"; rust_ai_core QLoraConfig scale() = alpha / r; "LoRA and QLoRA,
  * mathematically" eq. (6.3.6) and "Tooling" (dequant fused with the matmul).
+ * How W~ meets x (see the path flags): m <= 16 runs the decode GEMV (split
+ * contraction, W~ decoded in registers); above that, by default, W~ is dequantized
+ * once into the workspace and a dense 256 x 256 MFMA GEMM reads it
+ * (dequantize-then-GEMM); QLORA_FLAG_FUSED decodes W~ tile by tile inside the GEMM
+ * instead.  These kernels take bf16 / f16 layers whose block size is a multiple of
+ * 32 dividing cols, with cols a multiple of 64.  Every other layer (f32, any even
+ * block size, any cols, blocks that run across rows) runs on a generic MFMA tile
+ * engine that decodes W~ per element: the same W~ bits, the sums in another order.
  * ws: device workspace of at least qlora_workspace_bytes(QLORA_OP_FWD, ...) bytes,
  * 256-byte aligned.  m == 0 is a no-op.  Errors: QLORA_ERR_INVALID_ARG (null
- * x/lora_a/lora_b/y, r < 1, non-finite alpha, unknown flags), QLORA_ERR_SHAPE
- * (m < 0, empty weight), QLORA_ERR_DTYPE, QLORA_ERR_UNSUPPORTED (cols % 64 != 0 or
- * block_size not a multiple of 32 dividing cols), QLORA_ERR_WORKSPACE.  With both
- * path flags set: QLORA_ERR_INVALID_ARG.  Shapes the fast paths do not take (f32,
- * block sizes that are not powers of two, W rows % 64 != 0 for dX) run on a
- * generic tile kernel with the same results.
+ * x/lora_a/lora_b/y, unaligned pointers, r < 1, non-finite alpha, unknown flags,
+ * both path flags), QLORA_ERR_SHAPE (m < 0, empty weight), QLORA_ERR_DTYPE,
+ * QLORA_ERR_WORKSPACE, QLORA_ERR_UNSUPPORTED (a buffer beyond the kernels' 32-bit
+ * offsets, where no generic form exists).
  */
 int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
                      const void* lora_b, int32_t r, float alpha, int32_t flags,
@@ -339,10 +353,10 @@ enum {
   QLORA_K_DEQUANTIZE,
   QLORA_K_LORA_DOWN,  /* T = s x A^T (prologue of the forward; T0 in the backward) */
   QLORA_K_REDUCE,     /* fixed-order sum of split-contraction partials */
-  QLORA_K_FWD_GEMM,   /* fused dequant-GEMM forward, m > 16 */
+  QLORA_K_FWD_GEMM,   /* forward GEMM y = [x | T][W~ | B]^T, m > 16 (dense or fused) */
   QLORA_K_GEMV,       /* decode forward, m <= 16 (its LoRA prologue counts as LORA_DOWN) */
   QLORA_K_BWD_DT,     /* dT = s dY B */
-  QLORA_K_BWD_DX,     /* fused dequant-GEMM dX = dY W~ + dT A */
+  QLORA_K_BWD_DX,     /* backward GEMM dX = dY W~ + dT A (dense or fused) */
   QLORA_K_BWD_DA,     /* dA = dT^T x */
   QLORA_K_BWD_DB,     /* dB = s dY^T T0 */
   QLORA_K_MERGE,      /* adapter merge into the dense weight */

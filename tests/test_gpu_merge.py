@@ -134,16 +134,20 @@ def test_merged_weight_reproduces_the_layer_forward():
 @pytest.mark.parametrize("name", [p[0] for p in inputs.PREFILL_PROJECTIONS])
 def test_merge_full_size_sampled_rows(name):
     """The seven projections of the Llama-3-8B-shaped block at r = 64, in the launch
-    configuration the benchmark times; 64 sampled rows (first and last included)
-    compared element by element."""
+    configuration the benchmark times; one random row in every 64-row tile of the
+    kernel (first and last rows included) compared element by element, and the whole
+    output (NaN before the call) finite."""
     (L,) = inputs.prefill(m=1, projections=[name])
     say("merge full", name)
     q = qn.quantize(L.W.cuda(), L.block_size, L.double_quant, L.dq_group)
-    out = qn.merge(q, L.A.cuda(), L.B.cuda(), L.alpha)
+    out = torch.full((L.N, L.K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    qn.merge(q, L.A.cuda(), L.B.cuda(), L.alpha, out=out)
     torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "unwritten merge outputs"
     what = oracle.dequantize(oracle.quantize(L.W.numpy(), L.block_size, L.double_quant, L.dq_group))
     rng = np.random.default_rng(9)
-    rows = np.unique(np.concatenate([[0, L.N - 1], rng.integers(0, L.N, 62)]))
+    bands = np.arange(0, L.N, 64)
+    rows = np.unique(np.concatenate([[0, L.N - 1], np.minimum(bands + rng.integers(0, 64, bands.size), L.N - 1)]))
     A = oracle.operand(L.A, "bf16")
     B = np.ascontiguousarray(oracle.operand(L.B, "bf16")[rows])
     s = L.alpha / L.r

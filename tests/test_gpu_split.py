@@ -8,8 +8,8 @@ floor(T / C) whole rounds; the R = T mod C tiles left over are cut into the
 largest S in {2, 4} with R * S <= C and at least 4 contraction stages of 64 per
 slice.  Small cases compare every element (ragged M and N, a bias, the low-rank
 tail on the last slice); the full projection sizes whose tile counts leave an
-incomplete round (gate / up forward, down dX: 16 x 56 tiles) compare sampled
-entries.  Repeats on a workspace full of stale bytes and outputs filled with NaN
+incomplete round (gate / up forward, down dX: 16 x 56 tiles) are covered tile by
+tile in test_gpu_fullsize.py.  Repeats on a workspace full of stale bytes and outputs filled with NaN
 must give the same bits."""
 import numpy as np
 import pytest
@@ -110,40 +110,3 @@ def test_split_repeats_bit_identical_on_stale_workspace(path):
     o = oracle_layer(L)
     assert_close(to_np(ys[0]), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"]), L.cd, "fwd")
     assert_close(to_np(dxs[0]), oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"])[0], L.cd, "dX")
-
-
-@pytest.mark.parametrize("path", ["dequant", "fused"])
-def test_split_forward_full_size_sampled(path):
-    """gate_proj at 4096 tokens: 16 x 56 tiles, three whole rounds and 128 tiles in
-    two slices each on a 256-CU GPU."""
-    (L,) = inputs.prefill(projections=["gate_proj"])
-    say("split fwd full", path, L.M, L.N, L.K, expected_split(L.M, L.N, L.K))
-    g = to_gpu(L)
-    y = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, path=path)
-    torch.cuda.synchronize()
-    o = oracle_layer(L)
-    rng = np.random.default_rng(17)
-    ii, jj = rng.integers(0, L.M, 384), rng.integers(0, L.N, 384)
-    ii[:4] = [0, L.M - 1, 0, L.M - 1]
-    jj[:4] = [0, 0, L.N - 1, L.N - 1]
-    ref = oracle.forward_at(o["x"], o["W"], o["A"], o["B"], o["s"], ii, jj)
-    assert_close(to_np(y)[ii, jj], ref, "bf16", "gate_proj fwd sampled")
-    y2 = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, path=path)
-    torch.cuda.synchronize()
-    assert torch.equal(y, y2)
-
-
-def test_split_dx_full_size_sampled():
-    """down_proj at 4096 tokens: dX [4096, 14336] is 16 x 56 tiles, contraction 4096."""
-    (L,) = inputs.prefill(with_dy=True, projections=["down_proj"])
-    say("split dX full", L.M, L.N, L.K, expected_split(L.M, L.K, L.N))
-    g = to_gpu(L)
-    dx, _, _ = qn.linear_bwd(gpu_q(L, g), g["x"], g["dY"], g["A"], g["B"], L.alpha, path="dequant")
-    torch.cuda.synchronize()
-    o = oracle_layer(L)
-    rng = np.random.default_rng(18)
-    ii, kk = rng.integers(0, L.M, 256), rng.integers(0, L.K, 256)
-    ii[:2] = [0, L.M - 1]
-    kk[:2] = [L.K - 1, 0]
-    ref = oracle.backward_dx_at(o["dY"], o["W"], o["A"], o["B"], o["s"], ii, kk)
-    assert_close(to_np(dx)[ii, kk], ref, "bf16", "down_proj dX sampled")
