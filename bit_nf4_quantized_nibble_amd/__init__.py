@@ -10,6 +10,7 @@ Public API (names follow the pages' problem statement):
     quantize(w, block_size=64, double_quant=False, dq_group=256 | "global") -> NF4Weight
     dequantize(q, dtype=torch.bfloat16) -> Tensor [rows, cols]
     linear_fwd_cached(w_cd, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False)
+    linear_fwd_noalloc(q, x, lora_a, lora_b, alpha, bias=None, out=None, t_out=None, rslora=False, path="auto")
     linear_fwd(q, x, lora_a, lora_b, alpha, bias=None, save_t=False, rslora=False, path="auto",
                dropout_mask=None, dropout_p=0.0)
     linear_bwd(q, x, dy, lora_a, lora_b, alpha, t_saved=None, need_dx=True, rslora=False, path="auto",
@@ -34,6 +35,7 @@ from . import _lib
 from ._lib import QloraError, QloraNf4  # noqa: F401
 
 __all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "merge", "workspace_bytes",
+           "linear_fwd_noalloc", "linear_fwd_cached",
            "levels", "QloraError", "dtype_code", "profile_enable", "profile_read", "mse_loss_grad",
            "adamw_step", "StackLayer", "stack_train_step", "stack_workspace_bytes"]
 
@@ -239,6 +241,33 @@ def linear_fwd(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, save_t:
             _stream_ptr(x.device)))
     y = y.reshape(*lead, q.rows)
     return (y, t0) if (save_t or t_out is not None) else y
+
+
+def linear_fwd_noalloc(q: NF4Weight, x, lora_a, lora_b, alpha: float, bias=None, out=None, t_out=None,
+                       rslora: bool = False, path: str = "auto"):
+    """The forward through qlora_linear_fwd_noalloc: no workspace, the library's own
+    scratch array instead (for graph capture and serving loops that cannot
+    allocate).  ``out`` (and ``t_out`` for T0) may be preallocated; returns y, or
+    (y, T0) when ``t_out`` is given."""
+    torch = _torch()
+    dt = x.dtype
+    x2, lead = _flatten(x, q.cols)
+    x2 = x2.contiguous()
+    for name, t in (("x", x2), ("lora_a", lora_a), ("lora_b", lora_b), ("bias", bias)):
+        _need_cuda(name, t, dt)
+    r = lora_a.shape[0]
+    m = x2.shape[0]
+    y = out if out is not None else torch.empty(m, q.rows, dtype=dt, device=x.device)
+    _need_cuda("out", y, dt)
+    _need_cuda("t_out", t_out, torch.float32)
+    if y.numel() != m * q.rows or (t_out is not None and t_out.numel() != m * r):
+        raise ValueError("out / t_out have the wrong size")
+    d = q.descriptor()
+    _lib.check(_lib.lib().qlora_linear_fwd_noalloc(
+        ctypes.byref(d), _ptr(x2), m, _ptr(lora_a), _ptr(lora_b), r, float(alpha), _flags(rslora, path),
+        _ptr(bias), dtype_code(dt), _ptr(y), _ptr(t_out), _stream_ptr(x.device)))
+    y = y.reshape(*lead, q.rows)
+    return (y, t_out) if t_out is not None else y
 
 
 def linear_fwd_cached(w_cd, x, lora_a, lora_b, alpha: float, bias=None, save_t: bool = False,

@@ -28,6 +28,7 @@ EXPORTED = (
     "qlora_profile_enable", "qlora_profile_read", "qlora_kernel_name", "qlora_merge",
     "qlora_mse_loss_grad", "qlora_adamw_step", "qlora_stack_train_step", "qlora_stack_workspace_bytes",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_linear_fwd_cached",
+    "qlora_linear_fwd_noalloc", "qlora_noalloc_scratch_bytes",
 )
 QLORA_MSE_WORKSPACE_BYTES = 4096
 KERNEL_KINDS = ("quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
@@ -92,6 +93,10 @@ def _declare(lib):
     lib.qlora_linear_bwd_dropout.argtypes = [P, vp, vp, i64, vp, vp, i32, f32, i32, i32, vp, f32, vp, vp, vp, vp, vp,
                                              sz, vp]
     lib.qlora_linear_fwd_cached.argtypes = [vp, i64, i64, vp, i64, vp, vp, i32, f32, i32, vp, i32, vp, vp, vp, sz, vp]
+    lib.qlora_linear_fwd_noalloc.argtypes = [P, vp, i64, vp, vp, i32, f32, i32, vp, i32, vp, vp, vp]
+    lib.qlora_linear_fwd_noalloc.restype = ctypes.c_int
+    lib.qlora_noalloc_scratch_bytes.argtypes = []
+    lib.qlora_noalloc_scratch_bytes.restype = sz
     lib.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.qlora_workspace_bytes.restype = sz
     lib.qlora_last_error.argtypes = []

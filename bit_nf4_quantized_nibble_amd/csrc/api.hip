@@ -162,6 +162,37 @@ int check_ws(void* ws, size_t ws_bytes, size_t need, const char* who) {
   return QLORA_OK;
 }
 
+// ---------------------------------------------------------------- scratch memory
+// The workspace of qlora_linear_fwd_noalloc: a device array in the library's own
+// code object, so the call allocates nothing.  Every GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: the device address of each GPU's copy comes from
+// hipGetSymbolAddress with that GPU current, once per device, and only that
+// address is ever handed to kernels.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on first use).
+int scratch_address(void** out, const char* who) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(QLORA_ERR_HIP, "%s: no current device (or device index %d beyond %d)", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(QLORA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed: %s", who, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
+
 }  // namespace
 
 const Nf4Tables& host_tables() {
@@ -424,6 +455,29 @@ int qlora_linear_fwd(const qlora_nf4_t* w, const void* x, int64_t m, const void*
   return fwd_impl(w, x, m, lora_a, lora_b, r, alpha, flags, bias, cd, nullptr, 0.f, y, t_save, ws, ws_bytes, stream,
                   "linear_fwd");
 }
+
+int qlora_linear_fwd_noalloc(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
+                             const void* lora_b, int32_t r, float alpha, int32_t flags, const void* bias,
+                             int32_t cd, void* y, float* t_save, void* stream) {
+  g_err[0] = 0;
+  const char* who = "linear_fwd_noalloc";
+  if (flags & QLORA_FLAG_DROPOUT)
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: QLORA_FLAG_DROPOUT belongs to qlora_linear_fwd_dropout", who);
+  // Above 16 tokens the fused kernels, unless the caller asks for the copy of W~.
+  if (!(flags & QLORA_FLAG_DEQUANT_GEMM)) flags |= QLORA_FLAG_FUSED;
+  int rc = validate_layer(w, x, m, lora_a, lora_b, r, alpha, flags, cd, who);
+  if (rc) return rc;
+  const size_t need = fwd_workspace_bytes(m, w->rows, w->cols, r, cd, flags);
+  if (need > kScratchBytes)
+    return set_error(QLORA_ERR_WORKSPACE, "%s: this call needs %zu bytes of scratch memory, the library holds %zu",
+                     who, need, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws, who))) return rc;
+  return fwd_impl(w, x, m, lora_a, lora_b, r, alpha, flags, bias, cd, nullptr, 0.f, y, t_save, ws, kScratchBytes,
+                  stream, who);
+}
+
+size_t qlora_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int qlora_linear_fwd_cached(const void* w_cd, int64_t rows, int64_t cols, const void* x, int64_t m,
                             const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,

@@ -322,6 +322,30 @@ int qlora_linear_fwd_cached(const void* w_cd, int64_t rows, int64_t cols, const 
                             const void* bias, int32_t cd, void* y, float* t_save, void* ws, size_t ws_bytes,
                             void* stream);
 
+/*
+ * The forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and errors as qlora_linear_fwd without the workspace: the call uses a
+ * scratch array of qlora_noalloc_scratch_bytes() bytes (16 MiB) that the library
+ * holds in each GPU's memory for the life of the process, and calls no allocating
+ * routine.  Above 16 tokens it takes the fused kernels (no copy of W~) unless
+ * flags has QLORA_FLAG_DEQUANT_GEMM.  A call whose workspace
+ * (qlora_workspace_bytes of the same path) exceeds the scratch array is refused
+ * with QLORA_ERR_WORKSPACE before anything runs (the decode calls of the
+ * Llama-3-8B-shaped projections need at most a few MiB; fused forwards fit while
+ * their rank products and cut last round stay under the limit).  The scratch array is looked
+ * up on the current device (the one the stream and arrays belong to) on its first
+ * use there.  Calls on one GPU share its array: two calls that overlap on one GPU
+ * (concurrent streams, or threads) race and give undefined results; calls on one
+ * stream are ordered and safe.  Nothing in the array needs to start at zero.
+ */
+int qlora_linear_fwd_noalloc(const qlora_nf4_t* w, const void* x, int64_t m, const void* lora_a,
+                             const void* lora_b, int32_t r, float alpha, int32_t flags, const void* bias,
+                             int32_t cd, void* y, float* t_save, void* stream);
+
+/* Bytes of the scratch array qlora_linear_fwd_noalloc uses on each GPU.  Pure host. */
+size_t qlora_noalloc_scratch_bytes(void);
+
 /* Workspace size in bytes for op (QLORA_OP_FWD / QLORA_OP_BWD, optionally OR'ed
  * with flags << QLORA_OP_FLAGS_SHIFT) on this layer shape; 0 for an invalid query.
  * Pure host function. */
