@@ -7,11 +7,10 @@
 // does at most 32 flops per weight, so it is bound by HBM.
 //
 // Two launches (bf16 / f16):
-//   k_gemv_mfma  split-K over the contraction.  Workgroup (row block of 64, K
-//                slice) issues every code load of its slice at once, stages the m
-//                token rows of x for the slice in LDS, decodes W~ exactly in
-//                registers and lets MFMA 16x16x32 do the token sums (W~ rows as
-//                the A operand, x^T as B; tokens past m are zeros).  The LoRA
+//   k_gemv_k     split-K over the contraction.  Workgroup (row block of 32, slice
+//                of 1024) issues every load of its tile at once, decodes W~ exactly
+//                and lets MFMA 16x16x32 do the token sums (W~ rows as the A
+//                operand, x^T as B; tokens past m are zeros).  The LoRA
 //                down-projection rides along: the rows of lora_a are r extra
 //                (dense) rows of the same product.  Partial sums of every slice go
 //                to the workspace with plain stores.
@@ -76,7 +75,6 @@ __global__ __launch_bounds__(kThreads) void k_lora_t(const void* __restrict__ x,
 // ---------------------------------------------------------------------------
 // MFMA split-K decode GEMV (bf16 / f16).
 // ---------------------------------------------------------------------------
-constexpr int kRowBlock = 64;   // W rows per workgroup (16 per wave)
 
 struct GemvP {
   Nf4W w;
@@ -112,136 +110,224 @@ __device__ __forceinline__ f32x4v_t mfma16(u32x4_t a, u32x4_t b, f32x4v_t c) {
                                                   0, 0, 0);
 }
 
-// Lane l of wave w: W row n0 + 16 w + l % 16; in step j of the slice it holds the
-// 32 codes at k = kb + 128 j + 32 (l / 16) .. +32, one 16-byte load.  MFMA u of the
-// step takes codes 8u .. 8u+8 of them against x at the same k (the 4 x 16-lane
-// groups together cover the step's 128 k, in a permuted but consistent order).
-// Every load is a buffer load: rows past N (or past r, or tokens past m) read past
-// their buffer and return zeros, so the kernel has no per-lane branches.
-constexpr int kSlice = 512;               // K elements per slice: 4 steps of 128
+// Split-K decode GEMV.  Workgroup = 4 waves on a tile of 32 W rows x 1024
+// contraction elements (slice sl); wave w takes the sub-slice [kb + 256 w,
+// kb + 256 (w + 1)) of the 32 rows (two row groups of 16), so the x fragments a lane
+// loads are its own and serve both row groups.  MFMA 16x16x32: W~ [16 rows x 32 k]
+// as A, x^T [32 k x 16 tokens] as B (tokens past m read as zeros).  Lane l
+// (q = l / 16, rl = l % 16) in sub-step s of row group g holds row 16 g + rl and the
+// 32 codes of chunk q + 4 s (of the sub-slice's eight 32-code chunks); MFMA u takes
+// codes 8 u .. 8 u + 8 of them, and x is loaded in the same permuted k order.
+// Memory: each wave loads its codes as 8 rows x 128 contiguous bytes per
+// instruction (two per row group) and transposes them to the MFMA layout through
+// its own LDS region, so no wave waits for another until the final sum.  Every load
+// is issued before the first wait, in the order the decode needs them (row group
+// 0's codes, the block scales, x, row group 1's codes), since a wave sees its loads
+// complete in issue order.  Each weight decodes exactly to W~ = cd(fl32(L[c] s_b))
+// (one 8-byte LDS read of a level pair per code byte); the four waves' partial sums
+// are added in wave order through LDS.  Rows past N (and lora_a rows past r) read
+// past their buffers: zeros, no branch.
+constexpr int kRows = 32;      // W rows per workgroup
+constexpr int kSliceK = 1024;  // contraction elements per slice
+constexpr int kWaveK = 256;    // contraction elements per wave
+constexpr int kGemvThreads = 256;
 
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kGemvThreads = 512;  // 8 waves: row group w % 4 (16 rows), slice half w / 4 (2 steps)
+// Chunk (16 bytes = 32 codes) c of tile row r in a wave's [32 rows][128 bytes] LDS
+// tile: rows r and r + 2 share banks, so the chunk index is XORed with (r / 2) % 8.
+__device__ __forceinline__ int tile_off(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
 
-template <int CD, int DQ>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvP p, Nf4Tables tab) {
-  // the level pair of every code byte (element 2b in the high nibble, 2b + 1 in the low
-  // one): one 8-byte LDS read per two codes
+template <int CD, int DQ, int NBK>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab) {
   __shared__ __attribute__((aligned(16))) float2 s_pair[256];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxM][kSlice + 8];  // +16 B per row: no bank conflicts
-  // the codes of the slice, [64 rows][256 bytes]; 16-byte chunk c of row r sits at
-  // chunk c ^ (r % 16), so the 16 rows a read instruction touches hit 16 bank groups
-  __shared__ __attribute__((aligned(1024))) uint8_t cs[kRowBlock * kSlice / 2];
-  __shared__ f32x4v_t red[4][64];  // second-half sums, per row group and lane
+  __shared__ float s_sc[4][kRows][8];  // per wave: block scales [row][block within the sub-slice]
+  __shared__ __attribute__((aligned(16))) unsigned char s_codes[4][kRows * 128];  // per wave, swizzled
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave & 3, half = wave >> 2;
-  if (tid < 256) s_pair[tid] = make_float2(tab.lv[tid >> 4], tab.lv[tid & 15]);
+  const int q = lane >> 4, rl = lane & 15;
   const Nf4W& w = p.w;
   const int64_t K = w.cols, N = w.rows;
-  const int64_t n0 = (int64_t)blockIdx.x * kRowBlock;
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
   const bool lora = n0 >= p.n_pad;  // a block of lora_a rows (uniform per workgroup)
   const int sl = blockIdx.y;
-  const int64_t kb = (int64_t)sl * kSlice;
-  const int q = lane >> 4, rl = lane & 15;
-  const int64_t row = n0 + 16 * grp + rl;  // column of the partial sums
-
-  // x for the slice first (thread: token tid / 32, 16-byte chunks tid % 32 + 32 j)
-  const int xm = tid >> 5, xc = tid & 31;
+  const int64_t kw = (int64_t)sl * kSliceK + kWaveK * wave;  // the wave's sub-slice
   const rsrc_t rx = make_rsrc(p.x, p.M * K * 2);
-  u32x4_t xv[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    xv[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rx, (int)((xm * K + kb + 8 * (xc + 32 * j)) * 2), 0, 0));
+  u32x4_t xv[2][4];  // x of token rl: sub-step s, MFMA u -> k = kw + 32 (q + 4 s) + 8 u
+  f32x4v_t acc[2] = {};
 
-  // four accumulators (one per MFMA of a step) keep the MFMAs independent
-  f32x4v_t acc[4] = {};
   if (lora) {
-    // dense rows t = row - n_pad of lora_a, in the same k order as the codes
-    const int64_t t = row - p.n_pad;
+    // dense rows t = row - n_pad of lora_a in the same k order; only the row groups
+    // that hold rows below r
+    const int groups = (int)min<int64_t>(2, (p.r - (n0 - p.n_pad) + 15) / 16);
     const rsrc_t ra = make_rsrc(p.A, (int64_t)p.r * K * 2);
-    u32x4_t av[2][4];
+    u32x4_t av[2][2][4];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t t = n0 + 16 * g + rl - p.n_pad;
+          av[g][st][u] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                           ra, (int)oob_unless(t < p.r && g < groups, (uint32_t)((t * K + kw + 32 * (q + 4 * st) + 8 * u) * 2)),
+                           0, 0));
+        }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        av[jj][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                        ra, (int)oob_unless(t < p.r, (uint32_t)((t * K + kb + 128 * (2 * half + jj) + 32 * q + 8 * u) * 2)),
-                        0, 0));
+        xv[st][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rx, (int)((rl * K + kw + 32 * (q + 4 * st) + 8 * u) * 2), 0, 0));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) *(u32x4_t*)&xs[xm][8 * (xc + 32 * j)] = xv[j];
-    __syncthreads();
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc[u] = mfma16<CD>(av[jj][u], *(const u32x4_t*)&xs[rl][128 * (2 * half + jj) + 32 * q + 8 * u], acc[u]);
+        for (int u = 0; u < 4; ++u) acc[g] = mfma16<CD>(av[g][st][u], xv[st][u], acc[g]);
   } else {
-    const bool rok = row < N;
     const rsrc_t rc = make_rsrc(w.codes, N * K / 2);
+    // codes: instruction i loads tile rows 8 i + lane / 8, 16-byte chunk lane % 8
+    u32x4_t cw[4];
+    auto load_codes = [&](int i) {
+      const int64_t grow = n0 + 8 * i + (lane >> 3);
+      cw[i] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                       rc, (int)oob_unless(grow < N, (uint32_t)((grow * K + kw) / 2 + 16 * (lane & 7))), 0, 0));
+    };
+    load_codes(0);
+    load_codes(1);
+    // block scales of the wave's tile: lane l < 32 takes row l, blocks b0 .. b0 + nbk
+    // of the sub-slice (bs >= 32: nbk <= 8, a power of two dividing b0), as one
+    // naturally aligned load of the nbk u8 (or fp32) scales and one fp32 load per
+    // second-level group they touch
     const int64_t nb = N * K / w.bs;
     const rsrc_t rq = DQ ? make_rsrc(w.absmax_q, nb) : make_rsrc(w.absmax, nb * 4);
-    const rsrc_t rs = make_rsrc(DQ ? (const void*)w.scale2 : (const void*)w.absmax,
-                                DQ ? (((nb - 1) >> w.g_shift) + 1) * 4 : nb * 4);
-    // codes: DMA instruction i of wave w fills rows 4 (8 i + w) .. +4, 256 bytes each:
-    // lane l lands in physical chunk l % 16 of row l / 16 and fetches the logical
-    // chunk that maps there (rows past N read past the buffer: zeros)
+    const int64_t srow = n0 + (lane & 31);
+    const uint32_t b0 = (uint32_t)((srow * K + kw) >> w.bs_shift);  // a multiple of NBK
+    const bool sok = lane < kRows && srow < N;
+    uint32_t sraw[NBK];  // DQ: the u8 scales packed little-endian; else the fp32 scales
+    uint32_t sf[NBK];    // DQ: second-level scale of each group touched (ngr <= NBK)
+    const int ngr = (w.g_shift >= 31 || NBK <= (1 << w.g_shift)) ? 1 : NBK >> w.g_shift;
+    if constexpr (DQ) {
+      const uint32_t off = oob_unless(sok, b0);
+      if constexpr (NBK == 1) sraw[0] = __builtin_amdgcn_raw_buffer_load_b8(rq, (int)off, 0, 0);
+      else if constexpr (NBK == 2) sraw[0] = __builtin_amdgcn_raw_buffer_load_b16(rq, (int)off, 0, 0);
+      else if constexpr (NBK == 4) sraw[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)off, 0, 0);
+      else {
+        const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, (int)off, 0, 0));
+        sraw[0] = v[0];
+        sraw[1] = v[1];
+      }
+      const rsrc_t rs = make_rsrc(w.scale2, (((nb - 1) >> w.g_shift) + 1) * 4);
+      sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)oob_unless(sok, (b0 >> w.g_shift) * 4), 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 4 * (8 * i + wave) + (lane >> 4);
-      const int c = (lane & 15) ^ (r & 15);
-      const int64_t grow = n0 + r;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rc, (lds_void*)(cs + (8 * i + wave) * 1024), 16,
-          (int)oob_unless(grow < N, (uint32_t)((grow * K + kb) / 2 + 16 * c)), 0, 0, 0);
-    }
-    uint32_t sq[2];
-    float sf[2];
+      for (int j = 1; j < NBK; ++j) sf[j] = 0u;
+      if (ngr > 1) {  // groups smaller than the sub-slice (uniform; rare)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int64_t e = row * K + kb + 128 * (2 * half + jj) + 32 * q;  // 32 codes in one block (bs >= 32)
-      const uint32_t b = (uint32_t)(e >> w.bs_shift);
-      if constexpr (DQ) {
-        sq[jj] = __builtin_amdgcn_raw_buffer_load_b8(rq, (int)oob_unless(rok, b), 0, 0);
-        sf[jj] = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(rs, (int)oob_unless(rok, (b >> w.g_shift) * 4), 0, 0));
+        for (int j = 1; j < NBK; ++j)
+          sf[j] = __builtin_amdgcn_raw_buffer_load_b32(
+              rs, (int)oob_unless(sok && j < ngr, ((b0 >> w.g_shift) + j) * 4), 0, 0);
+      }
+    } else {
+      const uint32_t off = oob_unless(sok, b0 * 4);
+      if constexpr (NBK == 1) sraw[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)off, 0, 0);
+      else if constexpr (NBK == 2) {
+        const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, (int)off, 0, 0));
+        sraw[0] = v[0];
+        sraw[1] = v[1];
       } else {
-        sf[jj] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rq, (int)oob_unless(rok, b * 4), 0, 0));
+#pragma unroll
+        for (int h = 0; h < NBK / 4; ++h) {
+          const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            rq, (int)oob_unless(sok, b0 * 4 + 16 * h), 0, 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sraw[4 * h + e] = v[e];
+        }
       }
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) *(u32x4_t*)&xs[xm][8 * (xc + 32 * j)] = xv[j];
-    __builtin_amdgcn_s_waitcnt(((DQ ? 4 : 2) & 15) | (7 << 4) | (15 << 8));  // the DMA (the scales may fly)
-    __syncthreads();
-    const int crow = (16 * grp + rl) * (kSlice / 2);
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * half + jj;
-      const u32x4_t cw = *(const u32x4_t*)(cs + crow + 16 * ((4 * j + q) ^ rl));
-      const float s = DQ ? (float)sq[jj] * sf[jj] : sf[jj];
+      for (int u = 0; u < 4; ++u)
+        xv[st][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rx, (int)((rl * K + kw + 32 * (q + 4 * st) + 8 * u) * 2), 0, 0));
+    load_codes(2);
+    load_codes(3);
+    __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first wait
+    // level pair of code byte tid (element 2b in the high nibble), from the kernel
+    // arguments
+    {
+      float lhi = tab.lv[0], llo = tab.lv[0];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t word = cw[u];
-        u32x4_t a;
+      for (int i = 1; i < 16; ++i) {
+        lhi = (tid >> 4) == i ? tab.lv[i] : lhi;
+        llo = (tid & 15) == i ? tab.lv[i] : llo;
+      }
+      s_pair[tid] = make_float2(lhi, llo);
+    }
+    __syncthreads();  // the level pairs (everything after is the wave's own)
+    unsigned char* tile = s_codes[wave];
+    if (lane < kRows) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {  // byte b: element 2b in the high nibble, 2b + 1 in the low one
-          const float2 lv2 = *(const float2*)((const char*)s_pair + (byte_of(word, b) << 3));
-          a[b] = pack2<CD>(fl32_mul(lv2.x, s), fl32_mul(lv2.y, s));
+      for (int j = 0; j < NBK; ++j) {
+        if constexpr (DQ) {
+          const uint32_t qb = byte_of(sraw[j >> 2], j & 3);
+          const int gi = ngr == 1 ? 0 : (j >> w.g_shift);
+          float s2 = __uint_as_float(sf[0]);
+#pragma unroll
+          for (int k = 1; k < NBK; ++k) s2 = k == gi ? __uint_as_float(sf[k]) : s2;
+          s_sc[wave][lane][j] = fl32_mul((float)qb, s2);
+        } else {
+          s_sc[wave][lane][j] = __uint_as_float(sraw[j]);
         }
-        acc[u] = mfma16<CD>(a, *(const u32x4_t*)&xs[rl][128 * j + 32 * q + 8 * u], acc[u]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      // rows 16 g .. 16 g + 15 arrived with instructions 2 g and 2 g + 1
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *(u32x4_t*)(tile + tile_off(16 * g + 8 * h + (lane >> 3), lane & 7)) = cw[2 * g + h];
+      __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
+      u32x4_t cv[2];
+      float sc[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int c = q + 4 * st;
+        cv[st] = *(const u32x4_t*)(tile + tile_off(16 * g + rl, c));
+        sc[st] = s_sc[wave][16 * g + rl][NBK == 1 ? 0 : (32 * c) >> w.bs_shift];
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float2 lv2[4][4];  // the 16 level pairs of the chunk, requested before the first use
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) lv2[u][b] = *(const float2*)((const char*)s_pair + (byte_of(cv[st][u], b) << 3));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          u32x4_t a;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) a[b] = pack2<CD>(fl32_mul(lv2[u][b].x, sc[st]), fl32_mul(lv2[u][b].y, sc[st]));
+          acc[g] = mfma16<CD>(a, xv[st][u], acc[g]);
+        }
       }
     }
   }
 
-  // sum of the four accumulators and the two halves; then the partial sums
-  // D[row 16 g + 4 q + v][token rl] of this slice
-  f32x4v_t v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  if (half) red[grp][lane] = v;
+  // acc[g] = D[rows 16 g + 4 q .. +3][token rl] of this wave's sub-slice; waves 0 and
+  // 1 add the four waves' sums of row groups 0 and 1, in wave order
+  f32x4v_t* red = (f32x4v_t*)&s_codes[0][0];  // [wave][group][lane]
   __syncthreads();
-  if (half) return;
-  v += red[grp][lane];
-  if (rl < p.M) *(f32x4v_t*)(p.part + ((int64_t)sl * kMaxM + rl) * p.ld + n0 + 16 * grp + 4 * q) = v;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) red[(wave * 2 + g) * 64 + lane] = acc[g];
+  __syncthreads();
+  if (wave < 2) {
+    const int g = wave;
+    const f32x4v_t v = (red[g * 64 + lane] + red[(2 + g) * 64 + lane]) + (red[(4 + g) * 64 + lane] + red[(6 + g) * 64 + lane]);
+    if (rl < p.M) *(f32x4v_t*)(p.part + ((int64_t)sl * kMaxM + rl) * p.ld + n0 + 16 * g + 4 * q) = v;
+  }
 }
 
 // y[m, n] = sum over slices of the partials + T[m, :] . B[n, :] + bias[n], with
@@ -393,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(Nf4W w, const void* __restric
   }
 }
 
-// Split of the contraction into S slices of 512 elements (S in {1, 2, 4, 8, 16}).
+// Split of the contraction into S slices of 1024 elements (S in {1, 2, 4, 8, 16}).
 struct GemvPlan {
   bool mfma;
   int32_t S;
@@ -401,11 +487,11 @@ struct GemvPlan {
 };
 GemvPlan plan_gemv(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
   GemvPlan P = {};
-  P.S = (int32_t)(cols / kSlice);
-  P.mfma = (cd == CD_BF16 || cd == CD_F16) && rows > 0 && cols % kSlice == 0 &&
+  P.S = (int32_t)(cols / kSliceK);
+  P.mfma = (cd == CD_BF16 || cd == CD_F16) && rows > 0 && cols % kSliceK == 0 &&
            (P.S == 1 || P.S == 2 || P.S == 4 || P.S == 8 || P.S == 16);
-  P.n_pad = round_up(rows, kRowBlock);
-  P.r_pad = round_up(r, kRowBlock);
+  P.n_pad = round_up(rows, kRows);
+  P.r_pad = round_up(r, kRows);
   P.ld = P.n_pad + P.r_pad;
   P.off_part = round_up(m * r * 4, 256);  // T for the VALU path
   P.total = P.off_part + (P.mfma ? round_up((int64_t)P.S * kMaxM * P.ld * 4, 256) : 0);
@@ -437,10 +523,19 @@ int gemv_forward_t(const LayerCall& c, void* y, float* t_save) {
       p.S = P.S;
       {
         ProfScope prof(QLORA_K_GEMV, c.stream);
-        const dim3 grid((unsigned)(P.ld / kRowBlock), (unsigned)P.S);
-        if (c.w.dq) k_gemv_mfma<CD, 1><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables());
-        else k_gemv_mfma<CD, 0><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables());
-        int rc = check_launch("k_gemv_mfma");
+        const dim3 grid((unsigned)(P.ld / kRows), (unsigned)P.S);
+        const int nbk = c.w.bs_shift >= 8 ? 1 : 1 << (8 - c.w.bs_shift);  // blocks per 256-element sub-slice
+        switch (nbk * 2 + (c.w.dq ? 1 : 0)) {
+          case 2: k_gemv_k<CD, 0, 1><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
+          case 3: k_gemv_k<CD, 1, 1><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
+          case 4: k_gemv_k<CD, 0, 2><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
+          case 5: k_gemv_k<CD, 1, 2><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
+          case 8: k_gemv_k<CD, 0, 4><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
+          case 9: k_gemv_k<CD, 1, 4><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
+          case 16: k_gemv_k<CD, 0, 8><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
+          default: k_gemv_k<CD, 1, 8><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
+        }
+        int rc = check_launch("k_gemv_k");
         if (rc) return rc;
       }
       ProfScope prof(QLORA_K_REDUCE, c.stream);
