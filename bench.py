@@ -14,7 +14,7 @@ Also reported on the same line, each against its own MI355X roofline:
   gemv      decode forward at m = 1, 4, 16 (4096x4096, r = 16), GB/s over cold weights
   quantize  NF4 quantize of a 4096x4096 fp32 weight without / with double quant, GB/s
   dequantize  the double-quantized weight back to bf16 / fp32, GB/s
-  dtype_sweep  the prefill forward in f16 and f32 compute
+  dtype_sweep  the prefill forward in bf16, f16 and f32 compute (10 warm-up, 100 timed passes)
   merge     the adapter merge of the block's seven projections, GB/s
   stack_train_step  forward + MSE + backward + AdamW of a 3-layer stack of projection shapes
   cpu_baseline  the oracle (plain C, fp64) on a bounded sample of the step's work
@@ -210,9 +210,13 @@ def bench_step(args, qn, torch, lib, inputs, flags=0, hashes=None):
     return result
 
 
-def bench_dtype_sweep(qn, torch, lib, inputs, steps=3):
+def bench_dtype_sweep(qn, torch, lib, inputs, warmup=10, steps=100):
+    """The block's prefill forward (seven projections, 4096 tokens) in bf16, f16 and
+    f32 compute, timed like the headline: `warmup` untimed passes, then `steps`
+    passes with the device time of each from event pairs between them (median,
+    p10, p90) and the mean over the whole loop."""
     out = {}
-    for cd in ("f16", "f32"):
+    for cd in ("bf16", "f16", "f32"):
         layers, keep = build_block(cd, False, qn, torch, lib, inputs)
         flops = sum(fwd_flops(l.M, l.N, l.K, l.r) for l in layers)
 
@@ -220,11 +224,15 @@ def bench_dtype_sweep(qn, torch, lib, inputs, steps=3):
             for l in layers:
                 l.fwd()
 
-        fwd()
-        sec = time_loop(fwd, steps, torch)
-        tf = flops / sec / 1e12
-        peak = PEAK_BF16_TFLOPS if cd == "f16" else PEAK_F32_TFLOPS
-        out[cd] = {"ms": round(sec * 1e3, 3), "tflops": round(tf, 2), "peak": peak, "frac": round(tf / peak, 4)}
+        for _ in range(warmup):
+            fwd()
+        per = []
+        sec = time_loop(fwd, steps, torch, per_step=per)
+        pc = percentiles(per)
+        tf = flops / (pc["median"] / 1e3) / 1e12
+        peak = PEAK_BF16_TFLOPS if cd != "f32" else PEAK_F32_TFLOPS
+        out[cd] = {"ms_median": pc["median"], "ms_p10": pc["p10"], "ms_p90": pc["p90"], "ms_mean": round(sec * 1e3, 4),
+                   "passes": steps, "warmup": warmup, "tflops": round(tf, 2), "peak": peak, "frac": round(tf / peak, 4)}
         del layers, keep
         torch.cuda.empty_cache()
     return out
