@@ -244,11 +244,12 @@ def bench_path_sweep(qn, torch, lib, inputs, copies=8, replays=5):
     written once into the call's workspace).  The calls cycle through `copies`
     copies of the two quantized weights (about 300 MB of codes and scales, more than
     the 256 MB last-level cache), so each call reads its weight from HBM as a block
-    of a real model would.  Reports time per q + gate pair, TFLOP/s and the
+    of a real model would.  "auto" is the call without a path flag (up to 64 tokens
+    the split-K decode kernel, above that dequantize-then-GEMM).  Reports time per q + gate pair, TFLOP/s and the
     workspace each path needs (the memory side of the trade-off).  A third column,
     "cached", runs qlora_linear_fwd_cached on W~ dequantized once per weight copy
     beforehand (held resident: 2 bytes per weight instead of about 0.53)."""
-    ms = (32, 64, 128, 256, 512, 1024, 2048, 4096)
+    ms = (16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
     Ls = inputs.prefill(seed=0, cd="bf16", m=max(ms), projections=["q_proj", "gate_proj"])
     x = Ls[0].x.to("cuda")
     cd = qn.dtype_code(x.dtype)
@@ -264,7 +265,8 @@ def bench_path_sweep(qn, torch, lib, inputs, copies=8, replays=5):
         projs.append((L, qs, [q.descriptor() for q in qs], L.A.to("cuda"), L.B.to("cuda"),
                       torch.empty(max(ms), L.N, dtype=x.dtype, device="cuda"), wcs))
         del q0
-    paths = (("fused", qn._lib.QLORA_FLAG_FUSED), ("dequant", qn._lib.QLORA_FLAG_DEQUANT_GEMM), ("cached", None))
+    paths = (("auto", 0), ("fused", qn._lib.QLORA_FLAG_FUSED), ("dequant", qn._lib.QLORA_FLAG_DEQUANT_GEMM),
+             ("cached", None))
 
     def ws_need(m, L, flag):
         if flag is None:
@@ -327,7 +329,7 @@ def bench_path_sweep(qn, torch, lib, inputs, copies=8, replays=5):
                          "workspace_mb": round(need / 2 ** 20, 1), "replay_matches_eager": same}
             if flag is None:
                 res[path]["resident_w_mb"] = round(sum(L.N * L.K * 2 for L in Ls) / 2 ** 20, 1)
-        res["faster"] = min(("fused", "dequant"), key=lambda k: res[k]["ms"])
+        res["faster"] = min(("auto", "fused", "dequant"), key=lambda k: res[k]["ms"])
         out["m%d" % m] = res
     del projs, ws, x
     torch.cuda.empty_cache()

@@ -922,15 +922,24 @@ int launch_forward_cached(const LayerCall& c, const void* wd, void* y, float* t_
 
 int gemv_forward(const LayerCall& c, void* y, float* t_save);  // gemv.hip
 size_t gemv_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
-constexpr int64_t kGemvMaxM = 16;
+bool gemv_mfma_ok(const LayerCall& c);
+// The decode GEMV takes every call of at most 16 tokens (on the VALU where its MFMA
+// form does not apply), and calls of 17 to 64 tokens that carry no path flag when
+// its MFMA form applies (one decode of W~ serves up to four 16-token column groups).
+constexpr int64_t kGemvMaxM = 16, kGemvMfmaMaxM = 64;
+inline bool gemv_candidate(int64_t m, int32_t flags) {
+  if (flags & QLORA_FLAG_DROPOUT) return false;
+  return m <= kGemvMaxM || (m <= kGemvMfmaMaxM && !(flags & (QLORA_FLAG_FUSED | QLORA_FLAG_DEQUANT_GEMM)));
+}
 
 size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
-  // m <= 16 takes the decode GEMV, or the generic engine for a layout the GEMV does
-  // not take (the query does not see the block size): T and the rank-product
-  // partial sums, which come first in the GEMM path's plan.
-  if (m <= kGemvMaxM && !(flags & QLORA_FLAG_DROPOUT))
-    return std::max(gemv_workspace_bytes(m, rows, cols, r, cd), (size_t)plan_fwd(m, rows, cols, r, cd, flags).off_wd);
-  return (size_t)plan_fwd(m, rows, cols, r, cd, flags).total;
+  // A GEMV candidate may still run on the GEMM path (a layout the GEMV does not take:
+  // the query does not see the block size): room for both.  At most 16 tokens the
+  // GEMM path is the generic engine, which needs only T and the rank-product partial
+  // sums (the start of its plan).
+  const FwdPlan P = plan_fwd(m, rows, cols, r, cd, flags);
+  if (!gemv_candidate(m, flags)) return (size_t)P.total;
+  return std::max(gemv_workspace_bytes(m, rows, cols, r, cd), (size_t)(m <= kGemvMaxM ? P.off_wd : P.total));
 }
 
 size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags) {
@@ -938,7 +947,8 @@ size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int
 }
 
 int launch_forward(const LayerCall& c, void* y, float* t_save) {
-  if (c.m <= kGemvMaxM && !c.drop_mask && fast_layout(c.w)) return gemv_forward(c, y, t_save);
+  if (!c.drop_mask && fast_layout(c.w) && gemv_candidate(c.m, c.flags) && (c.m <= kGemvMaxM || gemv_mfma_ok(c)))
+    return gemv_forward(c, y, t_save);
   switch (c.cd) {
     case CD_BF16: return forward_gemm<CD_BF16>(c, y, t_save);
     case CD_F16: return forward_gemm<CD_F16>(c, y, t_save);

@@ -1,16 +1,17 @@
-// gemv.hip -- decode-shaped forward (m <= 16 tokens) of the QLoRA layer on gfx950.
+// gemv.hip -- decode-shaped forward (up to 64 tokens) of the QLoRA layer on gfx950.
 //
 // y[m, n] = sum_k x[m, k] W~[n, k] + sum_t T[m, t] B[n, t] (+ bias[n]),
 // T = s x A^T, W~ = cd(fl32(L[c] s_b)) (qlora-rs README "Honest capability
 // matrix": dequant honours the compute dtype; rust_ai_core QLoraConfig
-// scale() = alpha / r).  At m <= 16 the layer moves the packed weight once and
-// does at most 32 flops per weight, so it is bound by HBM.
+// scale() = alpha / r).  At a few tokens the layer moves the packed weight once and
+// does at most 2 m flops per weight, so it is bound by HBM and by the decode.
 //
-// Two launches (bf16 / f16):
+// Two launches (bf16 / f16, cols a multiple of 1024):
 //   k_gemv_k     split-K over the contraction.  Workgroup (row block of 32, slice
 //                of 1024) issues every load of its tile at once, decodes W~ exactly
 //                and lets MFMA 16x16x32 do the token sums (W~ rows as the A
-//                operand, x^T as B; tokens past m are zeros).  The LoRA
+//                operand, x^T as B; tokens past m are zeros), each decoded
+//                fragment feeding up to four 16-token column groups.  The LoRA
 //                down-projection rides along: the rows of lora_a are r extra
 //                (dense) rows of the same product.  Partial sums of every slice go
 //                to the workspace with plain stores.
@@ -18,8 +19,8 @@
 //                scheduling), forms T = s x A^T from the extra rows, and writes
 //                y = x W~^T + T B^T + bias; the kernel boundary orders it after
 //                the partial sums, so no workgroup ever waits on another.
-// f32, and shapes the MFMA kernel does not take, run k_lora_t (T = s x A^T) and
-// k_gemv (one wavefront per output row on the VALU).
+// f32, and shapes the MFMA kernel does not take (at most 16 tokens), run k_lora_t
+// (T = s x A^T) and k_gemv (one wavefront per output row on the VALU).
 #include <algorithm>
 
 #include "common.h"
@@ -87,8 +88,8 @@ struct GemvP {
   const void* bias;   // [N] cd or null
   void* y;            // [M, N] cd
   float* t0;          // [M, r] fp32 x A^T, or null
-  float* part;        // [S][16][ld] fp32 partial sums, ld = n_pad + r_pad
-  int64_t n_pad, ld;
+  float* part;        // [S][mp][ld] fp32 partial sums, ld = n_pad + r_pad, mp = m rounded up to 16
+  int64_t n_pad, ld, mp;
   int32_t S;          // slices of 512 elements
 };
 
@@ -114,19 +115,32 @@ __device__ __forceinline__ f32x4v_t mfma16(u32x4_t a, u32x4_t b, f32x4v_t c) {
 // contraction elements (slice sl); wave w takes the sub-slice [kb + 256 w,
 // kb + 256 (w + 1)) of the 32 rows (two row groups of 16), so the x fragments a lane
 // loads are its own and serve both row groups.  MFMA 16x16x32: W~ [16 rows x 32 k]
-// as A, x^T [32 k x 16 tokens] as B (tokens past m read as zeros).  Lane l
-// (q = l / 16, rl = l % 16) in sub-step s of row group g holds row 16 g + rl and the
-// 32 codes of chunk q + 4 s (of the sub-slice's eight 32-code chunks); MFMA u takes
-// codes 8 u .. 8 u + 8 of them, and x is loaded in the same permuted k order.
-// Memory: each wave loads its codes as 8 rows x 128 contiguous bytes per
-// instruction (two per row group) and transposes them to the MFMA layout through
-// its own LDS region, so no wave waits for another until the final sum.  Every load
+// as A, x^T [32 k x 16 tokens] as B (tokens past m read as zeros).  The k order is
+// permuted (the sum does not depend on it): MFMA u of sub-step s takes the
+// sub-slice's 32-code chunk 4 s + u, lane l (q = l / 16, rl = l % 16) its codes
+// 8 q .. 8 q + 8 for row 16 g + rl, so one x load instruction reads 64 contiguous
+// bytes of each token.  Memory: each wave loads its codes as 8 rows x 128
+// contiguous bytes per instruction (two per row group) and transposes them to the
+// MFMA layout through its own LDS region (a 4 x 4 word transpose within each
+// group of four chunks), so no wave waits for another until the final sum.  Every load
 // is issued before the first wait, in the order the decode needs them (row group
 // 0's codes, the block scales, x, row group 1's codes), since a wave sees its loads
 // complete in issue order.  Each weight decodes exactly to W~ = cd(fl32(L[c] s_b))
 // (one 8-byte LDS read of a level pair per code byte); the four waves' partial sums
 // are added in wave order through LDS.  Rows past N (and lora_a rows past r) read
 // past their buffers: zeros, no branch.
+// 8 * byte b of x (b a compile-time constant): one SDWA shift that reads the byte
+__device__ __forceinline__ uint32_t byte_x8(uint32_t x, int b) {
+  uint32_t r;
+  switch (b) {
+    case 0: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(x)); break;
+    case 1: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(x)); break;
+    case 2: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(x)); break;
+    default: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(x)); break;
+  }
+  return r;
+}
+
 constexpr int kRows = 32;      // W rows per workgroup
 constexpr int kSliceK = 1024;  // contraction elements per slice
 constexpr int kWaveK = 256;    // contraction elements per wave
@@ -136,11 +150,14 @@ constexpr int kGemvThreads = 256;
 // tile: rows r and r + 2 share banks, so the chunk index is XORed with (r / 2) % 8.
 __device__ __forceinline__ int tile_off(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
 
-template <int CD, int DQ, int NBK>
+template <int CD, int DQ, int NBK, int MT>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab) {
   __shared__ __attribute__((aligned(16))) float2 s_pair[256];
-  __shared__ float s_sc[4][kRows][8];  // per wave: block scales [row][block within the sub-slice]
-  __shared__ __attribute__((aligned(16))) unsigned char s_codes[4][kRows * 128];  // per wave, swizzled
+  __shared__ __attribute__((aligned(16))) float s_sc[4][kRows][8];  // per wave: block scales [row][block within the sub-slice]
+  // per wave, swizzled code tiles; then the waves' partial sums [wave][group][token group][lane]
+  __shared__ __attribute__((aligned(16))) unsigned char s_codes[4 * 2 * MT * 64 * 16 > 4 * kRows * 128
+                                                                     ? 4 * 2 * MT * 64 * 16
+                                                                     : 4 * kRows * 128];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, rl = lane & 15;
@@ -151,8 +168,20 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab)
   const int sl = blockIdx.y;
   const int64_t kw = (int64_t)sl * kSliceK + kWaveK * wave;  // the wave's sub-slice
   const rsrc_t rx = make_rsrc(p.x, p.M * K * 2);
-  u32x4_t xv[2][4];  // x of token rl: sub-step s, MFMA u -> k = kw + 32 (q + 4 s) + 8 u
-  f32x4v_t acc[2] = {};
+  // x of token 16 tg + rl: sub-step s, MFMA u -> k = kw + 32 (u + 4 s) + 8 q
+  u32x4_t xv[MT][2][4];
+  auto load_x = [&]() {
+#pragma unroll
+    for (int tg = 0; tg < MT; ++tg)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          xv[tg][st][u] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                           rx, (int)(((16 * tg + rl) * K + kw + 32 * (u + 4 * st) + 8 * q) * 2), 0, 0));
+  };
+  f32x4v_t acc[2][MT] = {};
 
   if (lora) {
     // dense rows t = row - n_pad of lora_a in the same k order; only the row groups
@@ -169,22 +198,19 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab)
           const int64_t t = n0 + 16 * g + rl - p.n_pad;
           av[g][st][u] = __builtin_bit_cast(
               u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                           ra, (int)oob_unless(t < p.r && g < groups, (uint32_t)((t * K + kw + 32 * (q + 4 * st) + 8 * u) * 2)),
+                           ra, (int)oob_unless(t < p.r && g < groups, (uint32_t)((t * K + kw + 32 * (u + 4 * st) + 8 * q) * 2)),
                            0, 0));
         }
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        xv[st][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rx, (int)((rl * K + kw + 32 * (q + 4 * st) + 8 * u) * 2), 0, 0));
+    load_x();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[g] = mfma16<CD>(av[g][st][u], xv[st][u], acc[g]);
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int tg = 0; tg < MT; ++tg) acc[g][tg] = mfma16<CD>(av[g][st][u], xv[tg][st][u], acc[g][tg]);
   } else {
     const rsrc_t rc = make_rsrc(w.codes, N * K / 2);
     // codes: instruction i loads tile rows 8 i + lane / 8, 16-byte chunk lane % 8
@@ -246,28 +272,22 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab)
         }
       }
     }
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        xv[st][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rx, (int)((rl * K + kw + 32 * (q + 4 * st) + 8 * u) * 2), 0, 0));
+    load_x();
     load_codes(2);
     load_codes(3);
     __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first wait
-    // level pair of code byte tid (element 2b in the high nibble), from the kernel
-    // arguments
+    // level pair of code byte tid (element 2b in the high nibble): lane i < 16 of
+    // every wave holds level i, and each lane fetches its two by lane permute
     {
-      float lhi = tab.lv[0], llo = tab.lv[0];
+      int lvl = 0;
 #pragma unroll
-      for (int i = 1; i < 16; ++i) {
-        lhi = (tid >> 4) == i ? tab.lv[i] : lhi;
-        llo = (tid & 15) == i ? tab.lv[i] : llo;
-      }
+      for (int i = 0; i < 16; ++i) asm("v_writelane_b32 %0, %1, %2" : "+v"(lvl) : "s"(tab.lv[i]), "n"(i));
+      const float lhi = __int_as_float(__builtin_amdgcn_ds_bpermute((tid >> 4) << 2, lvl));
+      const float llo = __int_as_float(__builtin_amdgcn_ds_bpermute((tid & 15) << 2, lvl));
       s_pair[tid] = make_float2(lhi, llo);
     }
     __syncthreads();  // the level pairs (everything after is the wave's own)
-    unsigned char* tile = s_codes[wave];
+    unsigned char* tile = s_codes + wave * (kRows * 128);
     if (lane < kRows) {
 #pragma unroll
       for (int j = 0; j < NBK; ++j) {
@@ -286,136 +306,192 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab)
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       // rows 16 g .. 16 g + 15 arrived with instructions 2 g and 2 g + 1
+      // word e of chunk c goes to word c % 4 of slot 4 (c / 4) + e: slot 4 s + q then
+      // holds codes 8 q .. 8 q + 8 of chunks 4 s .. 4 s + 3
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *(u32x4_t*)(tile + tile_off(16 * g + 8 * h + (lane >> 3), lane & 7)) = cw[2 * g + h];
+      for (int h = 0; h < 2; ++h) {
+        const int row = 16 * g + 8 * h + (lane >> 3), c = lane & 7;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *(uint32_t*)(tile + tile_off(row, 4 * (c >> 2) + e) + 4 * (c & 3)) = cw[2 * g + h][e];
+      }
       __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
       u32x4_t cv[2];
-      float sc[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int c = q + 4 * st;
-        cv[st] = *(const u32x4_t*)(tile + tile_off(16 * g + rl, c));
-        sc[st] = s_sc[wave][16 * g + rl][NBK == 1 ? 0 : (32 * c) >> w.bs_shift];
+      for (int st = 0; st < 2; ++st) cv[st] = *(const u32x4_t*)(tile + tile_off(16 * g + rl, q + 4 * st));
+      // the row's block scales; chunk c lies in block c NBK / 8 of the sub-slice
+      float scv[NBK];
+      {
+        const float* src = &s_sc[wave][16 * g + rl][0];
+        if constexpr (NBK >= 4) {
+#pragma unroll
+          for (int h = 0; h < NBK / 4; ++h) {
+            const float4 v = *(const float4*)(src + 4 * h);
+            scv[4 * h] = v.x, scv[4 * h + 1] = v.y, scv[4 * h + 2] = v.z, scv[4 * h + 3] = v.w;
+          }
+        } else if constexpr (NBK == 2) {
+          const float2 v = *(const float2*)src;
+          scv[0] = v.x, scv[1] = v.y;
+        } else {
+          scv[0] = src[0];
+        }
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        float2 lv2[4][4];  // the 16 level pairs of the chunk, requested before the first use
+        float2 lv2[4][4];  // the 16 level pairs of the sub-step, requested before the first use
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) lv2[u][b] = *(const float2*)((const char*)s_pair + (byte_of(cv[st][u], b) << 3));
+          for (int b = 0; b < 4; ++b) lv2[u][b] = *(const float2*)((const char*)s_pair + byte_x8(cv[st][u], b));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+          const float sc = scv[((4 * st + u) * NBK) >> 3];
           u32x4_t a;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) a[b] = pack2<CD>(fl32_mul(lv2[u][b].x, sc[st]), fl32_mul(lv2[u][b].y, sc[st]));
-          acc[g] = mfma16<CD>(a, xv[st][u], acc[g]);
+          for (int b = 0; b < 4; ++b) a[b] = pack2<CD>(fl32_mul(lv2[u][b].x, sc), fl32_mul(lv2[u][b].y, sc));
+#pragma unroll
+          for (int tg = 0; tg < MT; ++tg) acc[g][tg] = mfma16<CD>(a, xv[tg][st][u], acc[g][tg]);
         }
       }
     }
   }
 
-  // acc[g] = D[rows 16 g + 4 q .. +3][token rl] of this wave's sub-slice; waves 0 and
-  // 1 add the four waves' sums of row groups 0 and 1, in wave order
-  f32x4v_t* red = (f32x4v_t*)&s_codes[0][0];  // [wave][group][lane]
+  // acc[g][tg] = D[rows 16 g + 4 q .. +3][token 16 tg + rl] of this wave's sub-slice;
+  // waves 0 and 1 add the four waves' sums of row groups 0 and 1, in wave order
+  f32x4v_t* red = (f32x4v_t*)&s_codes[0];  // [wave][group][token group][lane]
   __syncthreads();
 #pragma unroll
-  for (int g = 0; g < 2; ++g) red[(wave * 2 + g) * 64 + lane] = acc[g];
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int tg = 0; tg < MT; ++tg) red[((wave * 2 + g) * MT + tg) * 64 + lane] = acc[g][tg];
   __syncthreads();
   if (wave < 2) {
     const int g = wave;
-    const f32x4v_t v = (red[g * 64 + lane] + red[(2 + g) * 64 + lane]) + (red[(4 + g) * 64 + lane] + red[(6 + g) * 64 + lane]);
-    if (rl < p.M) *(f32x4v_t*)(p.part + ((int64_t)sl * kMaxM + rl) * p.ld + n0 + 16 * g + 4 * q) = v;
+#pragma unroll
+    for (int tg = 0; tg < MT; ++tg) {
+      auto at = [&](int ww) { return red[((ww * 2 + g) * MT + tg) * 64 + lane]; };
+      const f32x4v_t v = (at(0) + at(1)) + (at(2) + at(3));
+      const int tok = 16 * tg + rl;
+      if (tok < p.M) *(f32x4v_t*)(p.part + ((int64_t)sl * p.mp + tok) * p.ld + n0 + 16 * g + 4 * q) = v;
+    }
   }
 }
 
 // y[m, n] = sum over slices of the partials + T[m, :] . B[n, :] + bias[n], with
-// T = s (sum over slices of the lora_a rows).  Workgroup (256 columns, token m)
-// forms T[m, :] in LDS; the workgroups of column block 0 also write t0 = x A^T
-// when asked.  For r <= 64, r % 8 == 0 every global load of a thread (its
-// column's S partial sums, bias, lora_b row, and its share of the r x S partial
-// sums of T) is issued before the first is used, so the kernel waits on memory
-// once; T's slices are then added in slice order through LDS.  Other ranks take
-// the same sums in two dependent rounds.
-template <int CD, int S>
+// T = s (sum over slices of the lora_a rows).  Workgroup (256 columns, TB tokens):
+// the thread of column n loads its lora_b row once and serves the TB tokens with
+// it; thread (j, t) forms T[m0 + j, t] into LDS (the workgroups of column block 0
+// also write t0 = x A^T when asked).  With r <= 64, r % 8 == 0 and S <= SM, every
+// global load of a thread (its T partial sums, lora_b row, bias, and the TB x S
+// partial sums of its column) is issued before the first is used, so the kernel
+// waits on memory once.  Every sum over slices runs in slice order, so the result
+// does not depend on scheduling.
+template <int CD, int TB, int SM>
 __global__ __launch_bounds__(kThreads) void k_gemv_epi(GemvP p) {
-  extern __shared__ float s_t[];  // [r] sums, then (fast path) [S][64] staged partial sums
+  extern __shared__ __attribute__((aligned(16))) float s_t[];  // [TB][r]
   const int tid = threadIdx.x;
-  const int m = blockIdx.y;
+  const int64_t m0 = (int64_t)blockIdx.y * TB;
+  const int nt = (int)min<int64_t>(TB, p.M - m0);
   const int64_t N = p.w.rows;
-  const float* pm = p.part + (int64_t)m * p.ld;
-  const int64_t ss = (int64_t)kMaxM * p.ld;
+  const int S = p.S;
+  const int64_t ss = p.mp * p.ld;
   const int64_t n = (int64_t)blockIdx.x * kThreads + tid;
   const int64_t nc = n < N ? n : N - 1;  // clamped: every lane loads, out-of-range lanes store nothing
-  float v = 0.f, lora = 0.f;
-  if (p.r <= 64 && (p.r & 7) == 0) {
-    float pv[S];
-#pragma unroll
-    for (int i = 0; i < S; ++i) pv[i] = pm[i * ss + nc];
-    // bias through a buffer of zero size when absent: the load returns 0, no branch
-    const rsrc_t rb = make_rsrc(p.bias, p.bias ? N * 2 : 0);
-    const uint32_t braw = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(nc * 2), 0, 0);
+  const float* pm0 = p.part + m0 * p.ld;
+  constexpr int kTE = TB * 64 > kThreads ? TB * 64 / kThreads : 1;  // elements of T per thread (r <= 64)
+  const bool fast = p.r <= 64 && (p.r & 7) == 0 && S <= SM;  // uniform
+  if (fast) {
     const rsrc_t rB = make_rsrc(p.B, N * p.r * 2);
     u32x4_t bv[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       bv[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                               rB, (int)(uint32_t)(q * 8 < p.r ? (nc * p.r + 8 * q) * 2 : 0), 0, 0));
-    // T's partial sums: slice i = tid / 64 + 4 k, rank column t = tid % 64
-    const int t = tid & 63;
-    float tp[(S + 3) / 4];
+    // bias through a buffer of zero size when absent: the load returns 0, no branch
+    const rsrc_t rb = make_rsrc(p.bias, p.bias ? N * 2 : 0);
+    const uint32_t braw = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(nc * 2), 0, 0);
+    // partial sums through a buffer: slices past S and tokens past m read as 0 with
+    // no branch, so every load is in flight before the first wait
+    const rsrc_t rp = make_rsrc(p.part, (int64_t)S * ss * 4);
+    const uint32_t base = (uint32_t)(m0 * p.ld);
+    uint32_t tp[kTE][SM], pv[TB][SM];
+    int jt[kTE], tt[kTE];
+    bool has_t[kTE];
 #pragma unroll
-    for (int k = 0; k < (S + 3) / 4; ++k) {
-      const int i = (tid >> 6) + 4 * k;
-      tp[k] = pm[(i < S ? i : 0) * ss + p.n_pad + (t < p.r ? t : 0)];
+    for (int h = 0; h < kTE; ++h) {  // element tid + 256 h of T's TB x r block
+      const int e = tid + kThreads * h;
+      jt[h] = e / p.r, tt[h] = e - jt[h] * p.r;
+      has_t[h] = e < TB * p.r && jt[h] < nt;
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
+        tp[h][i] = __builtin_amdgcn_raw_buffer_load_b32(
+            rp, (int)oob_unless(has_t[h] && i < S, (uint32_t)((i * ss + base + jt[h] * p.ld + p.n_pad + tt[h]) * 4)),
+            0, 0);
     }
 #pragma unroll
-    for (int k = 0; k < (S + 3) / 4; ++k) {
-      const int i = (tid >> 6) + 4 * k;
-      if (i < S) s_t[64 + i * 64 + t] = tp[k];
-    }
-    __syncthreads();
-    if (tid < p.r) {
-      float sum = 0.f;
+    for (int j = 0; j < TB; ++j)
 #pragma unroll
-      for (int i = 0; i < S; ++i) sum += s_t[64 + i * 64 + tid];
-      s_t[tid] = sum * p.scale;
-      if (p.t0 && blockIdx.x == 0) p.t0[(int64_t)m * p.r + tid] = sum;
-    }
-    __syncthreads();
+      for (int i = 0; i < SM; ++i)
+        pv[j][i] = __builtin_amdgcn_raw_buffer_load_b32(
+            rp, (int)oob_unless(j < nt && i < S, (uint32_t)((i * ss + base + j * p.ld + nc) * 4)), 0, 0);
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q * 8 < p.r) {
+    for (int h = 0; h < kTE; ++h)
+      if (has_t[h]) {
+        float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          lora = fmaf(s_t[8 * q + e], from_cd16<CD>((uint16_t)(bv[q][e >> 1] >> (16 * (e & 1)))), lora);
+        for (int i = 0; i < SM; ++i) sum += __uint_as_float(tp[h][i]);
+        s_t[jt[h] * p.r + tt[h]] = sum * p.scale;
+        if (p.t0 && blockIdx.x == 0) p.t0[(m0 + jt[h]) * p.r + tt[h]] = sum;
       }
-#pragma unroll
-    for (int i = 0; i < S; ++i) v += pv[i];
-    v += lora + (p.bias ? from_cd16<CD>((uint16_t)braw) : 0.f);
-  } else {
-    for (int t = tid; t < p.r; t += kThreads) {
-      float tv[S];
-#pragma unroll
-      for (int i = 0; i < S; ++i) tv[i] = pm[i * ss + p.n_pad + t];
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < S; ++i) sum += tv[i];
-      s_t[t] = sum * p.scale;
-      if (p.t0 && blockIdx.x == 0) p.t0[(int64_t)m * p.r + t] = sum;
-    }
     __syncthreads();
-    float pv[S];
+    float bf[64];
 #pragma unroll
-    for (int i = 0; i < S; ++i) pv[i] = pm[i * ss + nc];
-    const float bias = p.bias ? load_cd<CD>(p.bias, nc) : 0.f;
-    for (int t = 0; t < p.r; ++t) lora = fmaf(s_t[t], load_cd<CD>(p.B, nc * p.r + t), lora);
+    for (int e = 0; e < 64; ++e) bf[e] = from_cd16<CD>((uint16_t)(bv[e >> 3][(e & 7) >> 1] >> (16 * (e & 1))));
+    const float bias = p.bias ? from_cd16<CD>((uint16_t)braw) : 0.f;
 #pragma unroll
-    for (int i = 0; i < S; ++i) v += pv[i];
-    v += lora + bias;
+    for (int j = 0; j < TB; ++j) {
+      if (j < nt) {
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < SM; ++i) v += __uint_as_float(pv[j][i]);
+        float lora = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (q * 8 < p.r) {
+            // r % 8 == 0: two aligned 16-byte reads of T's row
+            const float4 t0v = *(const float4*)&s_t[j * p.r + 8 * q];
+            const float4 t1v = *(const float4*)&s_t[j * p.r + 8 * q + 4];
+            const float tv[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lora = fmaf(tv[e], bf[8 * q + e], lora);
+          }
+        if (n < N) store_cd<CD>(p.y, (m0 + j) * N + n, v + lora + bias);
+      }
+    }
+    return;
   }
-  if (n < N) store_cd<CD>(p.y, m * N + n, v);
+  // any rank and slice count: the same sums in dependent rounds
+  auto slice_sum = [&](const float* base) {
+    float v = 0.f;
+    for (int i = 0; i < S; ++i) v += base[(int64_t)i * ss];
+    return v;
+  };
+  for (int e = tid; e < TB * p.r; e += kThreads) {
+    const int j = e / p.r, t = e - j * p.r;
+    if (j < nt) {
+      const float sum = slice_sum(pm0 + (int64_t)j * p.ld + p.n_pad + t);
+      s_t[j * p.r + t] = sum * p.scale;
+      if (p.t0 && blockIdx.x == 0) p.t0[(m0 + j) * p.r + t] = sum;
+    }
+  }
+  __syncthreads();
+  const float bias = p.bias ? load_cd<CD>(p.bias, nc) : 0.f;
+  for (int j = 0; j < nt; ++j) {
+    const float v = slice_sum(pm0 + (int64_t)j * p.ld + nc);
+    float lora = 0.f;
+    for (int t = 0; t < p.r; ++t) lora = fmaf(s_t[j * p.r + t], load_cd<CD>(p.B, nc * p.r + t), lora);
+    if (n < N) store_cd<CD>(p.y, (m0 + j) * N + n, v + lora + bias);
+  }
 }
 
 // VALU decode GEMV: one wavefront per output row (f32, and other shapes).
@@ -479,30 +555,55 @@ __global__ __launch_bounds__(kThreads) void k_gemv(Nf4W w, const void* __restric
   }
 }
 
-// Split of the contraction into S slices of 1024 elements (S in {1, 2, 4, 8, 16}).
+// Split of the contraction into S = cols / 1024 slices of 1024 elements.
 struct GemvPlan {
   bool mfma;
   int32_t S;
-  int64_t n_pad, r_pad, ld, off_part, total;
+  int64_t n_pad, r_pad, ld, mp, off_part, total;
 };
 GemvPlan plan_gemv(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
   GemvPlan P = {};
   P.S = (int32_t)(cols / kSliceK);
-  P.mfma = (cd == CD_BF16 || cd == CD_F16) && rows > 0 && cols % kSliceK == 0 &&
-           (P.S == 1 || P.S == 2 || P.S == 4 || P.S == 8 || P.S == 16);
+  P.mfma = (cd == CD_BF16 || cd == CD_F16) && rows > 0 && cols % kSliceK == 0 && P.S >= 1;
   P.n_pad = round_up(rows, kRows);
   P.r_pad = round_up(r, kRows);
   P.ld = P.n_pad + P.r_pad;
+  P.mp = round_up(m, 16);
   P.off_part = round_up(m * r * 4, 256);  // T for the VALU path
-  P.total = P.off_part + (P.mfma ? round_up((int64_t)P.S * kMaxM * P.ld * 4, 256) : 0);
+  P.total = P.off_part + (P.mfma ? round_up((int64_t)P.S * P.mp * P.ld * 4, 256) : 0);
   return P;
+}
+
+template <int CD, int DQ, int NBK>
+void launch_gemv_mt(const GemvP& p, dim3 grid, int mt, hipStream_t st) {
+  const dim3 blk(kGemvThreads);
+  if (mt == 1) k_gemv_k<CD, DQ, NBK, 1><<<grid, blk, 0, st>>>(p, host_tables());
+  else if (mt == 2) k_gemv_k<CD, DQ, NBK, 2><<<grid, blk, 0, st>>>(p, host_tables());
+  else k_gemv_k<CD, DQ, NBK, 4><<<grid, blk, 0, st>>>(p, host_tables());
+}
+template <int CD, int DQ>
+void launch_gemv_k(const GemvP& p, dim3 grid, int nbk, int mt, hipStream_t st) {
+  if (nbk == 1) launch_gemv_mt<CD, DQ, 1>(p, grid, mt, st);
+  else if (nbk == 2) launch_gemv_mt<CD, DQ, 2>(p, grid, mt, st);
+  else if (nbk == 4) launch_gemv_mt<CD, DQ, 4>(p, grid, mt, st);
+  else launch_gemv_mt<CD, DQ, 8>(p, grid, mt, st);
+}
+
+// Whether the split-K MFMA form takes the call (bf16 / f16, cols a multiple of
+// 1024, a power-of-two block of at least 32, a power-of-two
+// or single second-level group, codes under 2 GiB, at most 64 tokens).
+bool mfma_form_ok(const LayerCall& c) {
+  const GemvPlan P = plan_gemv(c.m, c.w.rows, c.w.cols, c.r, c.cd);
+  return P.mfma && c.m <= 64 && c.w.bs_shift >= 5 && (!c.w.dq || c.w.g_shift >= 0) &&
+         c.w.rows * c.w.cols / 2 < 0x7fff0000LL && c.m * c.w.cols * 2 < 0x7fff0000LL &&
+         (int64_t)P.S * P.mp * P.ld * 4 < 0x7fff0000LL;
 }
 
 template <int CD>
 int gemv_forward_t(const LayerCall& c, void* y, float* t_save) {
   const GemvPlan P = plan_gemv(c.m, c.w.rows, c.w.cols, c.r, c.cd);
-  const bool mfma = P.mfma && c.w.bs_shift >= 5 && (!c.w.dq || c.w.g_shift >= 0) &&
-                    c.w.rows * c.w.cols / 2 < 0x7fff0000LL;
+  const bool mfma = mfma_form_ok(c);
+  if (!mfma && c.m > kMaxM) return set_error(QLORA_ERR_UNSUPPORTED, "decode: %lld tokens need the MFMA form", (long long)c.m);
   char* ws = (char*)c.ws;
   if constexpr (CD != CD_F32) {
     if (mfma) {
@@ -520,35 +621,34 @@ int gemv_forward_t(const LayerCall& c, void* y, float* t_save) {
       p.part = (float*)(ws + P.off_part);
       p.n_pad = P.n_pad;
       p.ld = P.ld;
+      p.mp = P.mp;
       p.S = P.S;
       {
         ProfScope prof(QLORA_K_GEMV, c.stream);
         const dim3 grid((unsigned)(P.ld / kRows), (unsigned)P.S);
         const int nbk = c.w.bs_shift >= 8 ? 1 : 1 << (8 - c.w.bs_shift);  // blocks per 256-element sub-slice
-        switch (nbk * 2 + (c.w.dq ? 1 : 0)) {
-          case 2: k_gemv_k<CD, 0, 1><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
-          case 3: k_gemv_k<CD, 1, 1><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
-          case 4: k_gemv_k<CD, 0, 2><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
-          case 5: k_gemv_k<CD, 1, 2><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
-          case 8: k_gemv_k<CD, 0, 4><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
-          case 9: k_gemv_k<CD, 1, 4><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
-          case 16: k_gemv_k<CD, 0, 8><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
-          default: k_gemv_k<CD, 1, 8><<<grid, dim3(kGemvThreads), 0, c.stream>>>(p, host_tables()); break;
-        }
+        const int mt = (int)(P.mp / 16);  // token groups of 16 (1, 2 or 4)
+        if (c.w.dq) launch_gemv_k<CD, 1>(p, grid, nbk, mt, c.stream);
+        else launch_gemv_k<CD, 0>(p, grid, nbk, mt, c.stream);
         int rc = check_launch("k_gemv_k");
         if (rc) return rc;
       }
       ProfScope prof(QLORA_K_REDUCE, c.stream);
-      const size_t lds = (size_t)(c.r <= 64 && c.r % 8 == 0 ? 64 * (1 + P.S) : c.r) * sizeof(float);
+      // tokens per epilogue workgroup (T's rows for them sit in LDS): one up to 16
+      // tokens (the most workgroups; re-reading lora_b is cheap), above that 8 when
+      // the slices are few enough to hold 8 x S partial sums in registers, else 4
+      int tb = c.m <= 16 ? 1 : P.S <= 8 ? 8 : 4;
+      if ((size_t)tb * c.r * sizeof(float) > 65536) tb = 1;
+      const size_t lds = (size_t)tb * c.r * sizeof(float);
       if (lds > 65536) return set_error(QLORA_ERR_UNSUPPORTED, "decode: rank %d too large", c.r);
-      const dim3 eg((unsigned)ceil_div(c.w.rows, kThreads), (unsigned)c.m);
-      switch (P.S) {
-        case 1: k_gemv_epi<CD, 1><<<eg, dim3(kThreads), lds, c.stream>>>(p); break;
-        case 2: k_gemv_epi<CD, 2><<<eg, dim3(kThreads), lds, c.stream>>>(p); break;
-        case 4: k_gemv_epi<CD, 4><<<eg, dim3(kThreads), lds, c.stream>>>(p); break;
-        case 8: k_gemv_epi<CD, 8><<<eg, dim3(kThreads), lds, c.stream>>>(p); break;
-        default: k_gemv_epi<CD, 16><<<eg, dim3(kThreads), lds, c.stream>>>(p); break;
-      }
+      const dim3 eg((unsigned)ceil_div(c.w.rows, kThreads), (unsigned)ceil_div(c.m, tb));
+      const dim3 eb(kThreads);
+      if (tb == 1 && P.S <= 4) k_gemv_epi<CD, 1, 4><<<eg, eb, lds, c.stream>>>(p);
+      else if (tb == 1) k_gemv_epi<CD, 1, 16><<<eg, eb, lds, c.stream>>>(p);
+      else if (tb == 8 && P.S <= 4) k_gemv_epi<CD, 8, 4><<<eg, eb, lds, c.stream>>>(p);
+      else if (tb == 8) k_gemv_epi<CD, 8, 8><<<eg, eb, lds, c.stream>>>(p);
+      else if (P.S <= 4) k_gemv_epi<CD, 4, 4><<<eg, eb, lds, c.stream>>>(p);
+      else k_gemv_epi<CD, 4, 16><<<eg, eb, lds, c.stream>>>(p);  // S > 16: the general rounds
       return check_launch("k_gemv_epi");
     }
   }
@@ -567,6 +667,8 @@ int gemv_forward_t(const LayerCall& c, void* y, float* t_save) {
 }
 
 }  // namespace
+
+bool gemv_mfma_ok(const LayerCall& c) { return mfma_form_ok(c); }
 
 size_t gemv_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
   return (size_t)plan_gemv(m, rows, cols, r, cd).total;

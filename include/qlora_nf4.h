@@ -59,7 +59,8 @@ typedef enum {
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1, QLORA_F16 = 2 } qlora_dtype_t;
 
 /* Flags for the forward / backward calls.  The two path flags (at most one) pick
- * how W~ meets the activations when m > 16 (m <= 16 always takes the decode GEMV):
+ * how W~ meets the activations when m > 16 (m <= 16 always takes the decode GEMV;
+ * without a path flag, 17 to 64 tokens take its MFMA form where it applies):
  *   default                  dequantize-then-GEMM (it was as fast or faster at
  *                            every m measured, 32 to 4096)
  *   QLORA_FLAG_FUSED         the fused kernels decode W~ on the fly, tile by tile
@@ -138,7 +139,8 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, int32_t out_dtype, void* out, voi
  * capability matrix"; rust_ai_core QLoraConfig scale() = alpha / r; "LoRA and QLoRA,
  * mathematically" eq. (6.3.6) and "Tooling" (dequant fused with the matmul).
  * How W~ meets x (see the path flags): m <= 16 runs the decode GEMV (split
- * contraction, W~ decoded in registers); above that, by default, W~ is dequantized
+ * contraction, W~ decoded in registers; 17 to 64 tokens too when no path flag is
+ * given and cols is a multiple of 1024); above that, by default, W~ is dequantized
  * once into the workspace and a dense 256 x 256 MFMA GEMM reads it
  * (dequantize-then-GEMM); QLORA_FLAG_FUSED decodes W~ tile by tile inside the GEMM
  * instead.  These kernels take bf16 / f16 layers whose block size is a multiple of

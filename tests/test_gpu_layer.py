@@ -100,9 +100,11 @@ def test_forward_decode_epilogue_paths(m, N, K, r, bias):
 
 
 @pytest.mark.parametrize("m,N,K,r,dq,bias", [
-    (5, 72, 8192, 16, True, True),     # 16 contraction slices of 512
-    (16, 130, 1536, 12, False, False),  # 3 slices: the VALU GEMV; fp32 block scales, ragged N
-    (1, 16, 512, 1, True, True),        # one slice, one row block, rank 1
+    (5, 72, 8192, 16, True, True),     # 8 contraction slices of 1024
+    (16, 130, 1536, 12, False, False),  # cols not a multiple of 1024: the VALU GEMV; fp32 block scales, ragged N
+    (1, 16, 512, 1, True, True),        # half a slice: the VALU GEMV, one row block, rank 1
+    (7, 256, 3072, 8, True, True),      # 3 slices
+    (9, 4096, 14336, 64, True, False),  # the down-projection shape: 14 slices
 ])
 def test_forward_decode_more_shapes(m, N, K, r, dq, bias):
     """Decode (m <= 16) with the saved T0 on the slice counts and scale forms the
@@ -117,6 +119,29 @@ def test_forward_decode_more_shapes(m, N, K, r, dq, bias):
     assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"]), "bf16", "decode y")
     ref_t0 = np.asarray(o["x"], np.float64) @ np.asarray(o["A"], np.float64).T
     assert oracle.rel_l2(to_np(t0).astype(np.float64), ref_t0) <= 1e-5, "decode T0"
+
+
+@pytest.mark.parametrize("m,N,K,r,bias", [
+    (17, 200, 1024, 16, True),    # one past the decode size: two token groups, ragged N
+    (32, 4096, 4096, 16, False),  # the decode weight at 32 tokens
+    (33, 96, 2048, 5, True),      # three token groups used of four, odd rank
+    (48, 320, 8192, 64, True),    # eight slices, rank 64
+    (64, 1024, 4096, 24, False),  # the largest count the split-K kernel takes
+    (40, 4096, 14336, 64, True),  # the down-projection shape: 14 slices, three token groups
+])
+def test_forward_medium_token_counts(m, N, K, r, bias):
+    """17 to 64 tokens without a path flag: the split-K MFMA kernel decodes each W~
+    fragment once for up to four 16-token column groups."""
+    L = inputs.random_layer(m, N, K, r, seed=3 * m + N + r, cd="bf16", with_bias=bias, with_dy=False)
+    say("fwd medium m", m, N, K, r, bias)
+    g = to_gpu(L)
+    y = torch.full((m, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    _, t0 = qn.linear_fwd(gpu_q(L, g), g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], save_t=True, out=y)
+    torch.cuda.synchronize()
+    o = oracle_layer(L)
+    assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"]), "bf16", "medium y")
+    ref_t0 = np.asarray(o["x"], np.float64) @ np.asarray(o["A"], np.float64).T
+    assert oracle.rel_l2(to_np(t0).astype(np.float64), ref_t0) <= 1e-5, "medium T0"
 
 
 def test_forward_save_t_and_leading_dims():
