@@ -691,7 +691,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "gemv", "quant", "sweep", "merge", "stack", "copyprobe", "paths"],
+    ap.add_argument("--only", choices=["step", "fusedstep", "gemv", "quant", "sweep", "merge", "stack", "copyprobe",
+                                       "paths"],
                     default=None,
                     help="run one part (for profiling); the JSON line needs the full run")
     args = ap.parse_args()
@@ -730,6 +731,10 @@ def main():
         print(json.dumps(bench_stack(qn, torch, inputs)))
         return
 
+    if args.only == "fusedstep":
+        st = bench_step(args, qn, torch, lib, inputs, flags=qn._lib.QLORA_FLAG_FUSED)
+        print(json.dumps({"ms_per_step": st["sec"] * 1e3, "kernels": st["kernels"], "roofline": st["roofline"]}))
+        return
     hashes = {} if args.only is None else None
     st = bench_step(args, qn, torch, lib, inputs, hashes=hashes)
     log("step %.3f ms" % (st["sec"] * 1e3))

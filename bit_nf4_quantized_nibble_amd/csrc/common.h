@@ -57,6 +57,30 @@ __device__ __forceinline__ uint32_t byte_of(uint32_t x, int e) {
   return r;
 }
 
+// 8 * byte b of x (b a compile-time constant): one SDWA shift that reads the byte
+__device__ __forceinline__ uint32_t byte_x8(uint32_t x, int b) {
+  uint32_t r;
+  switch (b) {
+    case 0: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(x)); break;
+    case 1: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(x)); break;
+    case 2: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(x)); break;
+    default: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(x)); break;
+  }
+  return r;
+}
+
+// Level pair of code byte e in [0, 256): (L[e >> 4], L[e & 15]), the element in the
+// high nibble first.  Lanes 0..15 of the wave take the 16 levels from the kernel
+// arguments and every lane fetches its two by lane permute (the whole wave must be
+// active).
+__device__ __forceinline__ float2 level_pair(const Nf4Tables& tab, int e) {
+  int lvl = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm("v_writelane_b32 %0, %1, %2" : "+v"(lvl) : "s"(tab.lv[i]), "n"(i));
+  return make_float2(__int_as_float(__builtin_amdgcn_ds_bpermute((e >> 4) << 2, lvl)),
+                     __int_as_float(__builtin_amdgcn_ds_bpermute((e & 15) << 2, lvl)));
+}
+
 // Block of flat element e, and second-level group of block b.  Shifts when the
 // sizes are powers of two (a 64-bit division costs dozens of instructions).
 __device__ __forceinline__ int64_t block_of(const Nf4W& w, int64_t e) {

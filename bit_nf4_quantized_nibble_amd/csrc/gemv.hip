@@ -129,18 +129,6 @@ __device__ __forceinline__ f32x4v_t mfma16(u32x4_t a, u32x4_t b, f32x4v_t c) {
 // (one 8-byte LDS read of a level pair per code byte); the four waves' partial sums
 // are added in wave order through LDS.  Rows past N (and lora_a rows past r) read
 // past their buffers: zeros, no branch.
-// 8 * byte b of x (b a compile-time constant): one SDWA shift that reads the byte
-__device__ __forceinline__ uint32_t byte_x8(uint32_t x, int b) {
-  uint32_t r;
-  switch (b) {
-    case 0: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(x)); break;
-    case 1: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(x)); break;
-    case 2: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(x)); break;
-    default: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(x)); break;
-  }
-  return r;
-}
-
 constexpr int kRows = 32;      // W rows per workgroup
 constexpr int kSliceK = 1024;  // contraction elements per slice
 constexpr int kWaveK = 256;    // contraction elements per wave
@@ -276,16 +264,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab)
     load_codes(2);
     load_codes(3);
     __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first wait
-    // level pair of code byte tid (element 2b in the high nibble): lane i < 16 of
-    // every wave holds level i, and each lane fetches its two by lane permute
-    {
-      int lvl = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) asm("v_writelane_b32 %0, %1, %2" : "+v"(lvl) : "s"(tab.lv[i]), "n"(i));
-      const float lhi = __int_as_float(__builtin_amdgcn_ds_bpermute((tid >> 4) << 2, lvl));
-      const float llo = __int_as_float(__builtin_amdgcn_ds_bpermute((tid & 15) << 2, lvl));
-      s_pair[tid] = make_float2(lhi, llo);
-    }
+    s_pair[tid] = level_pair(tab, tid);  // level pair of code byte tid
     __syncthreads();  // the level pairs (everything after is the wave's own)
     unsigned char* tile = s_codes + wave * (kRows * 128);
     if (lane < kRows) {

@@ -341,6 +341,8 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* ptr, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0, (int)bytes, 0x00020000);
 }
+// Out-of-range offset: the top bit puts it past every buffer (all are < 2 GiB).
+__device__ __forceinline__ uint32_t oob_unless(bool ok, uint32_t off) { return off | ((uint32_t)(!ok) << 31); }
 
 // Raw words of the block scale of element e (converted at use, so that every load of
 // a thread leaves before any is waited on; a read past a buffer returns 0).
@@ -501,6 +503,86 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restr
   }
 }
 
+// Four-tile form of the transposed dequantize (64 x 256 slab, block size a power of
+// two >= 32): lane (nr = tid / 4, ca = tid % 4) loads the codes of row n0 + nr at
+// contraction kb + 128 h + 32 ca .. + 32 (h = 0, 1) with one 16-byte load each, so
+// one load instruction reads 64 contiguous bytes of 16 rows; each 32-code run lies
+// in one block (one scale).  A code byte decodes to its two elements through the
+// level-pair table (one LDS read, two fl32 products, one packed rounding) and the
+// two 16-bit halves go to rows k and k + 1 of tile 2 h + ca / 2 ([k][n], the same
+// swizzle as k_dequantize_t).  Tiles are TS4 bytes apart (8 KiB + 128), so the
+// four column groups of a store instruction land on distinct banks.  Same values
+// as k_dequantize.
+constexpr int TS4 = 64 * 64 * 2 + 128;
+template <int OUT, int DQ>
+__global__ __launch_bounds__(kThreads) void k_dequantize_t4(Nf4W q, void* __restrict__ out, Nf4Tables tab,
+                                                            RedJobs red, uint32_t gx, uint32_t nmain) {
+  if (blockIdx.x >= nmain) {
+    skreduce_block<OUT>(red, blockIdx.x - nmain);
+    return;
+  }
+  __shared__ __attribute__((aligned(16))) float2 s_pair[256];
+  __shared__ __attribute__((aligned(16))) unsigned char tile[4 * TS4];
+  const int tid = threadIdx.x;
+  const int64_t n = q.rows * q.cols;
+  const rsrc_t rc = make_rsrc(q.codes, n / 2);
+  const ScaleRsrc rs = make_scale_rsrc<DQ>(q, n >> q.bs_shift);
+  const int64_t n0 = (int64_t)(blockIdx.x / gx) * 64, kb = (int64_t)(blockIdx.x % gx) * 256;
+  const int nr = tid >> 2, ca = tid & 3;
+  u32x4_t cw[2];
+  uint32_t qa[2], s2[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t k = kb + 128 * h + 32 * ca;
+    const bool ok = k < q.cols;  // cols % 64 == 0: a 32-code run is all inside or all outside
+    const int64_t e0 = (n0 + nr) * q.cols + k;
+    cw[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rc, (int)oob_unless(ok, (uint32_t)(e0 / 2)), 0, 0));
+    load_scale<DQ>(rs, q, ok ? (uint32_t)(e0 >> q.bs_shift) : 0u, qa[h], s2[h]);
+  }
+  s_pair[tid] = level_pair(tab, tid);
+  __syncthreads();
+  // byte address of element (k, n0 + nr) in a tile, less k * 128, for (k >> 4) & 3 = 2 (ca & 1) + v
+  const int odd = ca & 1;
+  int base[2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v)
+    base[v] = 4096 * odd + 16 * ((nr >> 3) ^ (2 * ((2 * odd + v) & 3))) + 2 * (nr & 7);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float sc = scale_of<DQ>(qa[h], s2[h]);
+    unsigned char* tb = tile + (2 * h + (ca >> 1)) * TS4;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float2 lv[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) lv[b] = *(const float2*)((const char*)s_pair + byte_x8(cw[h][w], b));
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        // byte 4 w + b: elements k = 32 (ca & 1) + 8 w + 2 b (high nibble) and k + 1
+        const uint32_t pk = pack2<OUT>(fl32_mul(lv[b].x, sc), fl32_mul(lv[b].y, sc));
+        unsigned char* at = tb + base[w >> 1] + (8 * w + 2 * b) * 128;
+        *(uint16_t*)at = (uint16_t)pk;
+        *(uint16_t*)(at + 128) = (uint16_t)(pk >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  // lanes 4 kr .. 4 kr + 3 write output row kr of each tile: chunks 0..3 (64
+  // contiguous bytes) with one instruction, chunks 4..7 with the next
+  const int kr = tid >> 2, sw = 2 * ((kr >> 4) & 3);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (kb + 64 * u >= q.cols) break;
+    const unsigned char* row = tile + u * TS4 + kr * 128;
+    const u32x4_t v0 = *(const u32x4_t*)(row + 16 * (ca ^ sw));
+    const u32x4_t v1 = *(const u32x4_t*)(row + 16 * ((ca + 4) ^ sw));
+    uint16_t* o = (uint16_t*)out + (kb + 64 * u + kr) * q.rows + n0 + 8 * ca;
+    *(u32x4_t*)o = v0;
+    *(u32x4_t*)(o + 32) = v1;
+  }
+}
+
 // Any even block size outside the power-of-two kernels (see k_quantize_any).
 int launch_quantize_any(const float* w, const qlora_nf4_t* q, hipStream_t s) {
   const int64_t n = q->rows * q->cols;
@@ -633,7 +715,8 @@ template <int OUT, int DQ>
 void run_dqt(bool four, uint32_t gx, uint32_t nmain, int64_t nred, const Nf4W& w, void* out, const Nf4Tables& t,
              const RedJobs& js, hipStream_t s) {
   const dim3 grid((unsigned)(nmain + nred));
-  if (four) k_dequantize_t<OUT, DQ, 4><<<grid, dim3(kThreads), 0, s>>>(w, out, t, js, gx, nmain);
+  if (four && w.bs_shift >= 5) k_dequantize_t4<OUT, DQ><<<grid, dim3(kThreads), 0, s>>>(w, out, t, js, gx, nmain);
+  else if (four) k_dequantize_t<OUT, DQ, 4><<<grid, dim3(kThreads), 0, s>>>(w, out, t, js, gx, nmain);
   else k_dequantize_t<OUT, DQ, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, t, js, gx, nmain);
 }
 
