@@ -11,7 +11,10 @@
 //                of 1024) issues every load of its tile at once, decodes W~ exactly
 //                and lets MFMA 16x16x32 do the token sums (W~ rows as the A
 //                operand, x^T as B; tokens past m are zeros), each decoded
-//                fragment feeding up to four 16-token column groups.  The LoRA
+//                fragment feeding up to four 16-token column groups.  With two or
+//                more token groups and many row tiles a workgroup loops over row
+//                tiles, keeping its x fragments in registers and requesting each
+//                tile's codes before it decodes the previous one.  The LoRA
 //                down-projection rides along: the rows of lora_a are r extra
 //                (dense) rows of the same product.  Partial sums of every slice go
 //                to the workspace with plain stores.
@@ -90,7 +93,8 @@ struct GemvP {
   float* t0;          // [M, r] fp32 x A^T, or null
   float* part;        // [S][mp][ld] fp32 partial sums, ld = n_pad + r_pad, mp = m rounded up to 16
   int64_t n_pad, ld, mp;
-  int32_t S;          // slices of 512 elements
+  int32_t S;          // slices of 1024 elements
+  int32_t G;          // workgroups (per slice) on W tiles; the ones after take lora_a row blocks
 };
 
 typedef float f32x4v_t __attribute__((__vector_size__(16)));
@@ -138,44 +142,240 @@ constexpr int kGemvThreads = 256;
 // tile: rows r and r + 2 share banks, so the chunk index is XORed with (r / 2) % 8.
 __device__ __forceinline__ int tile_off(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
 
+// The loads of one W tile (32 rows x the wave's 256-element sub-slice) a lane issues.
+template <int NBK>
+struct TileRegs {
+  u32x4_t cw[4];       // codes: instruction i holds tile row 8 i + lane / 8, 16-byte chunk lane % 8
+  uint32_t sraw[NBK];  // DQ: the u8 block scales packed little-endian; else the fp32 scales
+  uint32_t sf[NBK];    // DQ: the second-level scale of each group the row's blocks touch
+};
+
+// Per-lane constants of a wave's view of its sub-slice.
+struct WaveView {
+  int lane, wave, q, rl;
+  int64_t K, N, kw;  // kw: first contraction element of the wave's sub-slice
+  int ngr;           // second-level groups a row's blocks touch in the sub-slice (1 unless groups are small)
+};
+
+template <int NBK>
+__device__ __forceinline__ void issue_codes(const GemvP& p, const WaveView& v, int64_t n0, int i, TileRegs<NBK>& t) {
+  const rsrc_t rc = make_rsrc(p.w.codes, v.N * v.K / 2);
+  const int64_t grow = n0 + 8 * i + (v.lane >> 3);
+  t.cw[i] = __builtin_bit_cast(
+      u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                   rc, (int)oob_unless(grow < v.N, (uint32_t)((grow * v.K + v.kw) / 2 + 16 * (v.lane & 7))), 0, 0));
+}
+
+// Block scales of the wave's tile: lane l < 32 takes row l, blocks b0 .. b0 + NBK of
+// the sub-slice (bs >= 32: NBK <= 8, a power of two dividing b0), as one naturally
+// aligned load of the NBK u8 (or fp32) scales and one fp32 load per second-level
+// group they touch.
+template <int DQ, int NBK>
+__device__ __forceinline__ void issue_scales(const GemvP& p, const WaveView& v, int64_t n0, TileRegs<NBK>& t) {
+  const Nf4W& w = p.w;
+  const int64_t nb = v.N * v.K / w.bs;
+  const rsrc_t rq = DQ ? make_rsrc(w.absmax_q, nb) : make_rsrc(w.absmax, nb * 4);
+  const int64_t srow = n0 + (v.lane & 31);
+  const uint32_t b0 = (uint32_t)((srow * v.K + v.kw) >> w.bs_shift);  // a multiple of NBK
+  const bool sok = v.lane < kRows && srow < v.N;
+  if constexpr (DQ) {
+    const uint32_t off = oob_unless(sok, b0);
+    if constexpr (NBK == 1) t.sraw[0] = __builtin_amdgcn_raw_buffer_load_b8(rq, (int)off, 0, 0);
+    else if constexpr (NBK == 2) t.sraw[0] = __builtin_amdgcn_raw_buffer_load_b16(rq, (int)off, 0, 0);
+    else if constexpr (NBK == 4) t.sraw[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)off, 0, 0);
+    else {
+      const u32x2_t u = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, (int)off, 0, 0));
+      t.sraw[0] = u[0];
+      t.sraw[1] = u[1];
+    }
+    const rsrc_t rs = make_rsrc(w.scale2, (((nb - 1) >> w.g_shift) + 1) * 4);
+    t.sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)oob_unless(sok, (b0 >> w.g_shift) * 4), 0, 0);
+#pragma unroll
+    for (int j = 1; j < NBK; ++j) t.sf[j] = 0u;
+    if (v.ngr > 1) {  // groups smaller than the sub-slice (uniform; rare)
+#pragma unroll
+      for (int j = 1; j < NBK; ++j)
+        t.sf[j] = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, (int)oob_unless(sok && j < v.ngr, ((b0 >> w.g_shift) + j) * 4), 0, 0);
+    }
+  } else {
+    const uint32_t off = oob_unless(sok, b0 * 4);
+    if constexpr (NBK == 1) t.sraw[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)off, 0, 0);
+    else if constexpr (NBK == 2) {
+      const u32x2_t u = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, (int)off, 0, 0));
+      t.sraw[0] = u[0];
+      t.sraw[1] = u[1];
+    } else {
+#pragma unroll
+      for (int h = 0; h < NBK / 4; ++h) {
+        const u32x4_t u = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rq, (int)oob_unless(sok, b0 * 4 + 16 * h), 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t.sraw[4 * h + e] = u[e];
+      }
+    }
+  }
+}
+
+template <int DQ, int NBK>
+__device__ __forceinline__ void issue_tile(const GemvP& p, const WaveView& v, int64_t n0, TileRegs<NBK>& t) {
+  issue_codes(p, v, n0, 0, t);
+  issue_codes(p, v, n0, 1, t);
+  issue_scales<DQ>(p, v, n0, t);
+  issue_codes(p, v, n0, 2, t);
+  issue_codes(p, v, n0, 3, t);
+}
+
+// x of token 16 tg + rl for the wave's sub-slice: sub-step s, MFMA u -> k = kw +
+// 32 (u + 4 s) + 8 q (tokens past m read as zeros).
+template <int MT>
+__device__ __forceinline__ void load_x(const GemvP& p, const WaveView& v, u32x4_t (&xv)[MT][2][4]) {
+  const rsrc_t rx = make_rsrc(p.x, p.M * v.K * 2);
+#pragma unroll
+  for (int tg = 0; tg < MT; ++tg)
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        xv[tg][st][u] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         rx, (int)(((16 * tg + v.rl) * v.K + v.kw + 32 * (u + 4 * st) + 8 * v.q) * 2), 0, 0));
+}
+
+// acc[g][tg] += W~[rows 16 g .. +16 of the tile, the wave's sub-slice] x^T for the
+// tile whose loads t holds.  sc_w: the wave's [32][8] block-scale region, tile: its
+// [32][128-byte] code tile (both the wave's own).
 template <int CD, int DQ, int NBK, int MT>
+__device__ __forceinline__ void decode_mfma(const GemvP& p, const WaveView& v, const TileRegs<NBK>& t,
+                                            float (*sc_w)[8], unsigned char* tile, const float2* s_pair,
+                                            const u32x4_t (&xv)[MT][2][4], f32x4v_t (&acc)[2][MT]) {
+  const int lane = v.lane, q = v.q, rl = v.rl;
+  if (lane < kRows) {
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) {
+      if constexpr (DQ) {
+        const uint32_t qb = byte_of(t.sraw[j >> 2], j & 3);
+        const int gi = v.ngr == 1 ? 0 : (j >> p.w.g_shift);
+        float s2 = __uint_as_float(t.sf[0]);
+#pragma unroll
+        for (int k = 1; k < NBK; ++k) s2 = k == gi ? __uint_as_float(t.sf[k]) : s2;
+        sc_w[lane][j] = fl32_mul((float)qb, s2);
+      } else {
+        sc_w[lane][j] = __uint_as_float(t.sraw[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    // rows 16 g .. 16 g + 15 arrived with instructions 2 g and 2 g + 1; word e of
+    // chunk c goes to word c % 4 of slot 4 (c / 4) + e: slot 4 s + q then holds codes
+    // 8 q .. 8 q + 8 of chunks 4 s .. 4 s + 3
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 16 * g + 8 * h + (lane >> 3), c = lane & 7;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *(uint32_t*)(tile + tile_off(row, 4 * (c >> 2) + e) + 4 * (c & 3)) = t.cw[2 * g + h][e];
+    }
+    __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
+    u32x4_t cv[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) cv[st] = *(const u32x4_t*)(tile + tile_off(16 * g + rl, q + 4 * st));
+    // the row's block scales; chunk c lies in block c NBK / 8 of the sub-slice
+    float scv[NBK];
+    {
+      const float* src = &sc_w[16 * g + rl][0];
+      if constexpr (NBK >= 4) {
+#pragma unroll
+        for (int h = 0; h < NBK / 4; ++h) {
+          const float4 f = *(const float4*)(src + 4 * h);
+          scv[4 * h] = f.x, scv[4 * h + 1] = f.y, scv[4 * h + 2] = f.z, scv[4 * h + 3] = f.w;
+        }
+      } else if constexpr (NBK == 2) {
+        const float2 f = *(const float2*)src;
+        scv[0] = f.x, scv[1] = f.y;
+      } else {
+        scv[0] = src[0];
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float2 lv2[4][4];  // the 16 level pairs of the sub-step, requested before the first use
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) lv2[u][b] = *(const float2*)((const char*)s_pair + byte_x8(cv[st][u], b));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float sc = scv[((4 * st + u) * NBK) >> 3];
+        u32x4_t a;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) a[b] = pack2<CD>(fl32_mul(lv2[u][b].x, sc), fl32_mul(lv2[u][b].y, sc));
+#pragma unroll
+        for (int tg = 0; tg < MT; ++tg) acc[g][tg] = mfma16<CD>(a, xv[tg][st][u], acc[g][tg]);
+      }
+    }
+  }
+}
+
+// acc[g][tg] = D[rows 16 g + 4 q .. +3][token 16 tg + rl] of this wave's sub-slice;
+// waves 0 and 1 add the four waves' sums of row groups 0 and 1 in wave order and
+// store them as slice sl's partial sums of rows n0 .. n0 + 31.  red: [wave][group]
+// [token group][lane], a buffer of its own (the next tile's code writes may start
+// while waves 0 and 1 still read it).
+template <int MT>
+__device__ __forceinline__ void reduce_store(const GemvP& p, const WaveView& v, f32x4v_t (&acc)[2][MT],
+                                             f32x4v_t* red, int sl, int64_t n0) {
+  __syncthreads();  // the previous tile's readers are done with red
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int tg = 0; tg < MT; ++tg) red[((v.wave * 2 + g) * MT + tg) * 64 + v.lane] = acc[g][tg];
+  __syncthreads();
+  if (v.wave < 2) {
+    const int g = v.wave;
+#pragma unroll
+    for (int tg = 0; tg < MT; ++tg) {
+      auto at = [&](int ww) { return red[((ww * 2 + g) * MT + tg) * 64 + v.lane]; };
+      const f32x4v_t s = (at(0) + at(1)) + (at(2) + at(3));
+      const int tok = 16 * tg + v.rl;
+      if (tok < p.M) *(f32x4v_t*)(p.part + ((int64_t)sl * p.mp + tok) * p.ld + n0 + 16 * g + 4 * v.q) = s;
+    }
+  }
+}
+
+// Split-K GEMV kernel.  Workgroups x < p.G take W tiles: tile blockIdx.x alone
+// (LOOP = 0), or tiles blockIdx.x, blockIdx.x + G, ... (LOOP = 1: the wave's x
+// fragments stay in registers for every tile, and each tile's codes and scales are
+// requested before the previous tile is decoded); workgroups from G on take one
+// 32-row block of lora_a each.
+template <int CD, int DQ, int NBK, int MT, int LOOP>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab) {
   __shared__ __attribute__((aligned(16))) float2 s_pair[256];
-  __shared__ __attribute__((aligned(16))) float s_sc[4][kRows][8];  // per wave: block scales [row][block within the sub-slice]
-  // per wave, swizzled code tiles; then the waves' partial sums [wave][group][token group][lane]
-  __shared__ __attribute__((aligned(16))) unsigned char s_codes[4 * 2 * MT * 64 * 16 > 4 * kRows * 128
-                                                                     ? 4 * 2 * MT * 64 * 16
-                                                                     : 4 * kRows * 128];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q = lane >> 4, rl = lane & 15;
-  const Nf4W& w = p.w;
-  const int64_t K = w.cols, N = w.rows;
-  const int64_t n0 = (int64_t)blockIdx.x * kRows;
-  const bool lora = n0 >= p.n_pad;  // a block of lora_a rows (uniform per workgroup)
+  __shared__ __attribute__((aligned(16))) float s_sc[4][kRows][8];  // per wave: block scales [row][block of the sub-slice]
+  __shared__ __attribute__((aligned(16))) unsigned char s_tile[4 * kRows * 128];  // per wave: swizzled code tile
+  __shared__ f32x4v_t s_red[4 * 2 * MT * 64];
+  WaveView v;
+  const int tid = threadIdx.x;
+  v.lane = tid & 63;
+  v.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  v.q = v.lane >> 4;
+  v.rl = v.lane & 15;
+  v.K = p.w.cols;
+  v.N = p.w.rows;
   const int sl = blockIdx.y;
-  const int64_t kw = (int64_t)sl * kSliceK + kWaveK * wave;  // the wave's sub-slice
-  const rsrc_t rx = make_rsrc(p.x, p.M * K * 2);
-  // x of token 16 tg + rl: sub-step s, MFMA u -> k = kw + 32 (u + 4 s) + 8 q
+  v.kw = (int64_t)sl * kSliceK + kWaveK * v.wave;
+  v.ngr = (p.w.g_shift >= 31 || NBK <= (1 << p.w.g_shift)) ? 1 : NBK >> p.w.g_shift;
+  const int G = (int)p.G;
   u32x4_t xv[MT][2][4];
-  auto load_x = [&]() {
-#pragma unroll
-    for (int tg = 0; tg < MT; ++tg)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          xv[tg][st][u] = __builtin_bit_cast(
-              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                           rx, (int)(((16 * tg + rl) * K + kw + 32 * (u + 4 * st) + 8 * q) * 2), 0, 0));
-  };
-  f32x4v_t acc[2][MT] = {};
+  f32x4v_t acc[2][MT];
 
-  if (lora) {
+  if ((int)blockIdx.x >= G) {
     // dense rows t = row - n_pad of lora_a in the same k order; only the row groups
     // that hold rows below r
+    const int64_t n0 = p.n_pad + (int64_t)(blockIdx.x - G) * kRows;
     const int groups = (int)min<int64_t>(2, (p.r - (n0 - p.n_pad) + 15) / 16);
-    const rsrc_t ra = make_rsrc(p.A, (int64_t)p.r * K * 2);
+    const rsrc_t ra = make_rsrc(p.A, (int64_t)p.r * v.K * 2);
     u32x4_t av[2][2][4];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -183,14 +383,19 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab)
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int64_t t = n0 + 16 * g + rl - p.n_pad;
+          const int64_t t = n0 + 16 * g + v.rl - p.n_pad;
           av[g][st][u] = __builtin_bit_cast(
               u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                           ra, (int)oob_unless(t < p.r && g < groups, (uint32_t)((t * K + kw + 32 * (u + 4 * st) + 8 * q) * 2)),
+                           ra, (int)oob_unless(t < p.r && g < groups,
+                                               (uint32_t)((t * v.K + v.kw + 32 * (u + 4 * st) + 8 * v.q) * 2)),
                            0, 0));
         }
-    load_x();
+    load_x<MT>(p, v, xv);
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int tg = 0; tg < MT; ++tg) acc[g][tg] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -199,159 +404,54 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_k(GemvP p, Nf4Tables tab)
         for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int tg = 0; tg < MT; ++tg) acc[g][tg] = mfma16<CD>(av[g][st][u], xv[tg][st][u], acc[g][tg]);
-  } else {
-    const rsrc_t rc = make_rsrc(w.codes, N * K / 2);
-    // codes: instruction i loads tile rows 8 i + lane / 8, 16-byte chunk lane % 8
-    u32x4_t cw[4];
-    auto load_codes = [&](int i) {
-      const int64_t grow = n0 + 8 * i + (lane >> 3);
-      cw[i] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                       rc, (int)oob_unless(grow < N, (uint32_t)((grow * K + kw) / 2 + 16 * (lane & 7))), 0, 0));
-    };
-    load_codes(0);
-    load_codes(1);
-    // block scales of the wave's tile: lane l < 32 takes row l, blocks b0 .. b0 + nbk
-    // of the sub-slice (bs >= 32: nbk <= 8, a power of two dividing b0), as one
-    // naturally aligned load of the nbk u8 (or fp32) scales and one fp32 load per
-    // second-level group they touch
-    const int64_t nb = N * K / w.bs;
-    const rsrc_t rq = DQ ? make_rsrc(w.absmax_q, nb) : make_rsrc(w.absmax, nb * 4);
-    const int64_t srow = n0 + (lane & 31);
-    const uint32_t b0 = (uint32_t)((srow * K + kw) >> w.bs_shift);  // a multiple of NBK
-    const bool sok = lane < kRows && srow < N;
-    uint32_t sraw[NBK];  // DQ: the u8 scales packed little-endian; else the fp32 scales
-    uint32_t sf[NBK];    // DQ: second-level scale of each group touched (ngr <= NBK)
-    const int ngr = (w.g_shift >= 31 || NBK <= (1 << w.g_shift)) ? 1 : NBK >> w.g_shift;
-    if constexpr (DQ) {
-      const uint32_t off = oob_unless(sok, b0);
-      if constexpr (NBK == 1) sraw[0] = __builtin_amdgcn_raw_buffer_load_b8(rq, (int)off, 0, 0);
-      else if constexpr (NBK == 2) sraw[0] = __builtin_amdgcn_raw_buffer_load_b16(rq, (int)off, 0, 0);
-      else if constexpr (NBK == 4) sraw[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)off, 0, 0);
-      else {
-        const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, (int)off, 0, 0));
-        sraw[0] = v[0];
-        sraw[1] = v[1];
-      }
-      const rsrc_t rs = make_rsrc(w.scale2, (((nb - 1) >> w.g_shift) + 1) * 4);
-      sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)oob_unless(sok, (b0 >> w.g_shift) * 4), 0, 0);
-#pragma unroll
-      for (int j = 1; j < NBK; ++j) sf[j] = 0u;
-      if (ngr > 1) {  // groups smaller than the sub-slice (uniform; rare)
-#pragma unroll
-        for (int j = 1; j < NBK; ++j)
-          sf[j] = __builtin_amdgcn_raw_buffer_load_b32(
-              rs, (int)oob_unless(sok && j < ngr, ((b0 >> w.g_shift) + j) * 4), 0, 0);
-      }
-    } else {
-      const uint32_t off = oob_unless(sok, b0 * 4);
-      if constexpr (NBK == 1) sraw[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)off, 0, 0);
-      else if constexpr (NBK == 2) {
-        const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, (int)off, 0, 0));
-        sraw[0] = v[0];
-        sraw[1] = v[1];
-      } else {
-#pragma unroll
-        for (int h = 0; h < NBK / 4; ++h) {
-          const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                            rq, (int)oob_unless(sok, b0 * 4 + 16 * h), 0, 0));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sraw[4 * h + e] = v[e];
-        }
-      }
-    }
-    load_x();
-    load_codes(2);
-    load_codes(3);
-    __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first wait
-    s_pair[tid] = level_pair(tab, tid);  // level pair of code byte tid
-    __syncthreads();  // the level pairs (everything after is the wave's own)
-    unsigned char* tile = s_codes + wave * (kRows * 128);
-    if (lane < kRows) {
-#pragma unroll
-      for (int j = 0; j < NBK; ++j) {
-        if constexpr (DQ) {
-          const uint32_t qb = byte_of(sraw[j >> 2], j & 3);
-          const int gi = ngr == 1 ? 0 : (j >> w.g_shift);
-          float s2 = __uint_as_float(sf[0]);
-#pragma unroll
-          for (int k = 1; k < NBK; ++k) s2 = k == gi ? __uint_as_float(sf[k]) : s2;
-          s_sc[wave][lane][j] = fl32_mul((float)qb, s2);
-        } else {
-          s_sc[wave][lane][j] = __uint_as_float(sraw[j]);
-        }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      // rows 16 g .. 16 g + 15 arrived with instructions 2 g and 2 g + 1
-      // word e of chunk c goes to word c % 4 of slot 4 (c / 4) + e: slot 4 s + q then
-      // holds codes 8 q .. 8 q + 8 of chunks 4 s .. 4 s + 3
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 16 * g + 8 * h + (lane >> 3), c = lane & 7;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *(uint32_t*)(tile + tile_off(row, 4 * (c >> 2) + e) + 4 * (c & 3)) = cw[2 * g + h][e];
-      }
-      __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
-      u32x4_t cv[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) cv[st] = *(const u32x4_t*)(tile + tile_off(16 * g + rl, q + 4 * st));
-      // the row's block scales; chunk c lies in block c NBK / 8 of the sub-slice
-      float scv[NBK];
-      {
-        const float* src = &s_sc[wave][16 * g + rl][0];
-        if constexpr (NBK >= 4) {
-#pragma unroll
-          for (int h = 0; h < NBK / 4; ++h) {
-            const float4 v = *(const float4*)(src + 4 * h);
-            scv[4 * h] = v.x, scv[4 * h + 1] = v.y, scv[4 * h + 2] = v.z, scv[4 * h + 3] = v.w;
-          }
-        } else if constexpr (NBK == 2) {
-          const float2 v = *(const float2*)src;
-          scv[0] = v.x, scv[1] = v.y;
-        } else {
-          scv[0] = src[0];
-        }
-      }
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float2 lv2[4][4];  // the 16 level pairs of the sub-step, requested before the first use
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) lv2[u][b] = *(const float2*)((const char*)s_pair + byte_x8(cv[st][u], b));
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float sc = scv[((4 * st + u) * NBK) >> 3];
-          u32x4_t a;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) a[b] = pack2<CD>(fl32_mul(lv2[u][b].x, sc), fl32_mul(lv2[u][b].y, sc));
-#pragma unroll
-          for (int tg = 0; tg < MT; ++tg) acc[g][tg] = mfma16<CD>(a, xv[tg][st][u], acc[g][tg]);
-        }
-      }
-    }
+    reduce_store<MT>(p, v, acc, s_red, sl, n0);
+    return;
   }
 
-  // acc[g][tg] = D[rows 16 g + 4 q .. +3][token 16 tg + rl] of this wave's sub-slice;
-  // waves 0 and 1 add the four waves' sums of row groups 0 and 1, in wave order
-  f32x4v_t* red = (f32x4v_t*)&s_codes[0];  // [wave][group][token group][lane]
-  __syncthreads();
+  float (*sc_w)[8] = s_sc[v.wave];
+  unsigned char* tile = s_tile + v.wave * (kRows * 128);
+  auto run_tile = [&](const TileRegs<NBK>& t, int64_t n0) {
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int tg = 0; tg < MT; ++tg) red[((wave * 2 + g) * MT + tg) * 64 + lane] = acc[g][tg];
-  __syncthreads();
-  if (wave < 2) {
-    const int g = wave;
-#pragma unroll
-    for (int tg = 0; tg < MT; ++tg) {
-      auto at = [&](int ww) { return red[((ww * 2 + g) * MT + tg) * 64 + lane]; };
-      const f32x4v_t v = (at(0) + at(1)) + (at(2) + at(3));
-      const int tok = 16 * tg + rl;
-      if (tok < p.M) *(f32x4v_t*)(p.part + ((int64_t)sl * p.mp + tok) * p.ld + n0 + 16 * g + 4 * q) = v;
+      for (int tg = 0; tg < MT; ++tg) acc[g][tg] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+    decode_mfma<CD, DQ, NBK, MT>(p, v, t, sc_w, tile, s_pair, xv, acc);
+    reduce_store<MT>(p, v, acc, s_red, sl, n0);
+  };
+  if constexpr (!LOOP) {
+    // every load in flight before the first wait, in the order the decode needs them
+    // (row group 0's codes, the block scales, x, row group 1's codes): a wave sees its
+    // loads complete in issue order
+    const int64_t n0 = (int64_t)blockIdx.x * kRows;
+    TileRegs<NBK> t;
+    issue_codes(p, v, n0, 0, t);
+    issue_codes(p, v, n0, 1, t);
+    issue_scales<DQ>(p, v, n0, t);
+    load_x<MT>(p, v, xv);
+    issue_codes(p, v, n0, 2, t);
+    issue_codes(p, v, n0, 3, t);
+    __builtin_amdgcn_sched_barrier(0);
+    s_pair[tid] = level_pair(tab, tid);  // level pair of code byte tid
+    __syncthreads();                     // the level pairs (everything after is the wave's own)
+    run_tile(t, n0);
+  } else {
+    // tiles rt = blockIdx.x + G i of the n_tiles weight tiles, two register sets in turn
+    const int nt = (int)(p.n_pad / kRows);
+    int rt = blockIdx.x;
+    TileRegs<NBK> ta, tb;
+    load_x<MT>(p, v, xv);
+    issue_tile<DQ>(p, v, (int64_t)rt * kRows, ta);
+    s_pair[tid] = level_pair(tab, tid);
+    __syncthreads();
+    while (true) {
+      const int rb = rt + G;
+      if (rb < nt) issue_tile<DQ>(p, v, (int64_t)rb * kRows, tb);
+      run_tile(ta, (int64_t)rt * kRows);
+      if (rb >= nt) break;
+      rt = rb + G;
+      if (rt < nt) issue_tile<DQ>(p, v, (int64_t)rt * kRows, ta);
+      run_tile(tb, (int64_t)rb * kRows);
+      if (rt >= nt) break;
     }
   }
 }
@@ -553,20 +653,32 @@ GemvPlan plan_gemv(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd) {
   return P;
 }
 
-template <int CD, int DQ, int NBK>
+template <int CD, int DQ, int NBK, int LOOP>
 void launch_gemv_mt(const GemvP& p, dim3 grid, int mt, hipStream_t st) {
   const dim3 blk(kGemvThreads);
-  if (mt == 1) k_gemv_k<CD, DQ, NBK, 1><<<grid, blk, 0, st>>>(p, host_tables());
-  else if (mt == 2) k_gemv_k<CD, DQ, NBK, 2><<<grid, blk, 0, st>>>(p, host_tables());
-  else k_gemv_k<CD, DQ, NBK, 4><<<grid, blk, 0, st>>>(p, host_tables());
+  if (mt == 1) k_gemv_k<CD, DQ, NBK, 1, LOOP><<<grid, blk, 0, st>>>(p, host_tables());
+  else if (mt == 2) k_gemv_k<CD, DQ, NBK, 2, LOOP><<<grid, blk, 0, st>>>(p, host_tables());
+  else k_gemv_k<CD, DQ, NBK, 4, LOOP><<<grid, blk, 0, st>>>(p, host_tables());
 }
-template <int CD, int DQ>
-void launch_gemv_k(const GemvP& p, dim3 grid, int nbk, int mt, hipStream_t st) {
-  if (nbk == 1) launch_gemv_mt<CD, DQ, 1>(p, grid, mt, st);
-  else if (nbk == 2) launch_gemv_mt<CD, DQ, 2>(p, grid, mt, st);
-  else if (nbk == 4) launch_gemv_mt<CD, DQ, 4>(p, grid, mt, st);
-  else launch_gemv_mt<CD, DQ, 8>(p, grid, mt, st);
+template <int CD, int DQ, int LOOP>
+void launch_gemv_nbk(const GemvP& p, dim3 grid, int nbk, int mt, hipStream_t st) {
+  if (nbk == 1) launch_gemv_mt<CD, DQ, 1, LOOP>(p, grid, mt, st);
+  else if (nbk == 2) launch_gemv_mt<CD, DQ, 2, LOOP>(p, grid, mt, st);
+  else if (nbk == 4) launch_gemv_mt<CD, DQ, 4, LOOP>(p, grid, mt, st);
+  else launch_gemv_mt<CD, DQ, 8, LOOP>(p, grid, mt, st);
 }
+template <int CD>
+void launch_gemv_k(const GemvP& p, dim3 grid, bool dq, bool loop, int nbk, int mt, hipStream_t st) {
+  if (dq && loop) launch_gemv_nbk<CD, 1, 1>(p, grid, nbk, mt, st);
+  else if (dq) launch_gemv_nbk<CD, 1, 0>(p, grid, nbk, mt, st);
+  else if (loop) launch_gemv_nbk<CD, 0, 1>(p, grid, nbk, mt, st);
+  else launch_gemv_nbk<CD, 0, 0>(p, grid, nbk, mt, st);
+}
+
+// Workgroups the looping form aims at: as many as fit at once (256 CUs x the
+// looping kernel's workgroups per CU: 3, 2, 1 for 1, 2, 4 token groups by its
+// registers).
+inline int64_t gemv_loop_slots(int mt) { return 256 * (mt == 1 ? 3 : mt == 2 ? 2 : 1); }
 
 // Whether the split-K MFMA form takes the call (bf16 / f16, cols a multiple of
 // 1024, a power-of-two block of at least 32, a power-of-two
@@ -604,11 +716,17 @@ int gemv_forward_t(const LayerCall& c, void* y, float* t_save) {
       p.S = P.S;
       {
         ProfScope prof(QLORA_K_GEMV, c.stream);
-        const dim3 grid((unsigned)(P.ld / kRows), (unsigned)P.S);
         const int nbk = c.w.bs_shift >= 8 ? 1 : 1 << (8 - c.w.bs_shift);  // blocks per 256-element sub-slice
         const int mt = (int)(P.mp / 16);  // token groups of 16 (1, 2 or 4)
-        if (c.w.dq) launch_gemv_k<CD, 1>(p, grid, nbk, mt, c.stream);
-        else launch_gemv_k<CD, 0>(p, grid, nbk, mt, c.stream);
+        const int64_t nt = P.n_pad / kRows, lt = P.r_pad / kRows;  // W tiles, lora_a row blocks
+        const int64_t slots = gemv_loop_slots(mt), g_loop = std::max<int64_t>(1, slots / P.S);
+        // measured: the looping form wins with two or more token groups (x re-reads
+        // dominate), at most 8 slices and at least 3 tiles per workgroup; at one
+        // token group many independent workgroups hide latency better
+        const bool loop = mt >= 2 && P.S <= 8 && nt >= 3 * g_loop;
+        p.G = (int32_t)(loop ? g_loop : nt);
+        const dim3 grid((unsigned)(p.G + lt), (unsigned)P.S);
+        launch_gemv_k<CD>(p, grid, c.w.dq, loop, nbk, mt, c.stream);
         int rc = check_launch("k_gemv_k");
         if (rc) return rc;
       }

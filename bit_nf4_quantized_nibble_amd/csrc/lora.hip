@@ -11,7 +11,7 @@
 //
 // All four are C[p, t] = sum_k Aop[p, k] Bop[t, k] with t < r <= 64: one skinny
 // kernel, output tile 128 (p) x 64 (t), 4 waves of 32 x 64 (two MFMA 32x32x16
-// tiles each), 64-element contraction stages in three LDS buffers (the copy runs
+// tiles each), 64-element contraction stages in three LDS buffers (the copies run
 // two stages ahead), and a split of the contraction into S slices whose fp32
 // partial sums a second kernel adds in slice order.  Bop is always a small [t][k]
 // matrix with k contiguous (A, or a transposed copy of B, dT or T0 made by
@@ -38,7 +38,9 @@ constexpr int ROWB = 128;        // swizzled NT / Bop LDS row: 64 elements
 constexpr int XROW = 2 * BP;     // swizzled TN LDS row: 128 elements (256 bytes)
 constexpr int A_BYTES = 16384;   // NT: 128 rows x 128 B; TN: 64 rows x 256 B
 constexpr int B_BYTES = BR * ROWB;   // 8 KiB
-constexpr int NBUF = 3;
+constexpr int DEPTH = 2;          // stages whose copies fly ahead of the one in use (two
+                                 // workgroups per CU fit; deeper prefetch measured no faster)
+constexpr int NBUF = DEPTH + 1;
 constexpr int STAGE = A_BYTES + B_BYTES;
 constexpr int kCopies = 6;       // DMA instructions per lane per stage (4 Aop + 2 Bop)
 static_assert(BR == kRedBR && kThreads == kRedThreads, "the partial-sum layout the reduction reads");
@@ -165,15 +167,20 @@ __global__ __launch_bounds__(kThreads) void k_skinny(SkP2 ps) {
     else copy_a_nt(p, ra, dst, p0, wave, lane, k);
     copy_b(p, rb, dst + A_BYTES, wave, lane, k);
   };
-  copy(0);
-  if (nst > 1) copy(1);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nst) copy(d);
   for (int s = 0; s < nst; ++s) {
-    // stage s landed in every wave (stage s + 1 may still fly); stage s - 1's reads done
-    if (s + 1 < nst) wait_vm<kCopies>();
+    // stage s landed in every wave (the up to DEPTH - 1 later stages may still fly;
+    // a wave sees its copies complete in issue order); stage s - 1's reads done
+    const int ahead = min(DEPTH - 1, nst - 1 - s);
+    if (ahead >= 3) wait_vm<3 * kCopies>();
+    else if (ahead == 2) wait_vm<2 * kCopies>();
+    else if (ahead == 1) wait_vm<kCopies>();
     else wait_vm<0>();
     __builtin_amdgcn_s_waitcnt(0x3f | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     barrier_only();
-    if (s + 2 < nst) copy(s + 2);  // into the buffer stage s - 1 used
+    if (s + DEPTH < nst) copy(s + DEPTH);  // into the buffer stage s - 1 used
     const char* As = lds + (s % NBUF) * STAGE;
     const char* Bs = As + A_BYTES;
 #pragma unroll

@@ -128,6 +128,8 @@ def test_forward_decode_more_shapes(m, N, K, r, dq, bias):
     (48, 320, 8192, 64, True),    # eight slices, rank 64
     (64, 1024, 4096, 24, False),  # the largest count the split-K kernel takes
     (40, 4096, 14336, 64, True),  # the down-projection shape: 14 slices, three token groups
+    (24, 14336, 4096, 16, True),  # the gate shape: workgroups loop over 3 or 4 row tiles each
+    (64, 6170, 4096, 24, False),  # four token groups looping over a ragged last row tile
 ])
 def test_forward_medium_token_counts(m, N, K, r, bias):
     """17 to 64 tokens without a path flag: the split-K MFMA kernel decodes each W~
