@@ -8,7 +8,9 @@ one step = the forward of all seven projections followed by their backward (dX,
 dA, dB), each call on the library's default path (at 4096 tokens: W~ dequantized
 into the workspace, then the dense MFMA GEMM).  value = algorithmic TFLOP/s of
 that step (dequantization is not credited).  The same step forced onto the fused
-dequant-GEMM kernels (QLORA_FLAG_FUSED) is reported beside it.
+dequant-GEMM kernels (QLORA_FLAG_FUSED) is reported beside it, and the step with the
+projections that read the same x (q / k / v, gate / up) forwarded as one
+qlora_linear_fwd_group call each (grouped_forward_step).
 
 Also reported on the same line, each against its own MI355X roofline:
   gemv      decode forward at m = 1, 4, 16 (4096x4096, r = 16), GB/s over cold weights
@@ -94,6 +96,60 @@ class Layer:
             raise RuntimeError("bwd %s: %d %s" % (self.name, rc, self.lib.qlora_last_error()))
 
 
+class GroupUnit:
+    """Layers that read the same x called as one group (qlora_linear_fwd_group /
+    qlora_linear_bwd_group): the outputs side by side in one [M, sum N] buffer, dY
+    likewise, one dX (the sum of the group's input gradients); adapters, T0, dA and
+    dB in the layers' own buffers."""
+
+    def __init__(self, layers, x, torch, lib, qn, group_bwd=True):
+        self.layers, self.lib, self.name = layers, lib, "+".join(l.name for l in layers)
+        self.group_bwd = group_bwd
+        g = len(layers)
+        M, K = layers[0].M, layers[0].K
+        N = sum(l.N for l in layers)
+        vp = ctypes.c_void_p
+        self.w = (ctypes.POINTER(qn._lib.QloraNf4) * g)(*[ctypes.pointer(l.desc) for l in layers])
+        self.a = (vp * g)(*[l.A.data_ptr() for l in layers])
+        self.b = (vp * g)(*[l.B.data_ptr() for l in layers])
+        self.r = (ctypes.c_int32 * g)(*[l.r for l in layers])
+        self.alpha = (ctypes.c_float * g)(*[float(l.alpha) for l in layers])
+        self.t0 = (vp * g)(*[l.t0.data_ptr() for l in layers])
+        self.da = (vp * g)(*[l.da.data_ptr() for l in layers])
+        self.db = (vp * g)(*[l.db.data_ptr() for l in layers])
+        self.y = torch.empty(M, N, dtype=x.dtype, device="cuda")
+        self.dy = torch.cat([l.dY for l in layers], dim=1).contiguous()
+        self.dx = torch.empty(M, K, dtype=x.dtype, device="cuda")
+        cd = qn.dtype_code(x.dtype)
+        wsf = lib.qlora_group_workspace_bytes(0, g, self.w, M, self.r, cd)
+        wsb = lib.qlora_group_workspace_bytes(1, g, self.w, M, self.r, cd)
+        self.ws_f = torch.empty(max(wsf, 1), dtype=torch.uint8, device="cuda")
+        self.ws_b = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        self.fwd_args = (g, self.w, x.data_ptr(), M, self.a, self.b, self.r, self.alpha, 0, None, cd,
+                         self.y.data_ptr(), self.t0, self.ws_f.data_ptr(), self.ws_f.numel(), stream)
+        self.bwd_args = (g, self.w, x.data_ptr(), self.dy.data_ptr(), M, self.a, self.b, self.r, self.alpha, 0, cd,
+                         self.t0, self.dx.data_ptr(), self.da, self.db, self.ws_b.data_ptr(), self.ws_b.numel(),
+                         stream)
+
+    def fwd(self):
+        rc = self.lib.qlora_linear_fwd_group(*self.fwd_args)
+        if rc:
+            raise RuntimeError("fwd %s: %d %s" % (self.name, rc, self.lib.qlora_last_error()))
+
+    def bwd(self):
+        if not self.group_bwd:  # each projection's own backward on the T0 the group forward saved
+            for l in self.layers:
+                l.bwd()
+            return
+        rc = self.lib.qlora_linear_bwd_group(*self.bwd_args)
+        if rc:
+            raise RuntimeError("bwd %s: %d %s" % (self.name, rc, self.lib.qlora_last_error()))
+
+
+GROUPS = (("q_proj", "k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",))
+
+
 def tensor_sha256(t):
     import hashlib
     return hashlib.sha256(t.contiguous().view(-1).view(__import__("torch").uint8).numpy().tobytes()).hexdigest()
@@ -148,8 +204,14 @@ def percentiles(ms):
     return {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4), "n": len(v)}
 
 
-def bench_step(args, qn, torch, lib, inputs, flags=0, hashes=None):
+def bench_step(args, qn, torch, lib, inputs, flags=0, hashes=None, grouped=False):
     layers, keep = build_block("bf16", True, qn, torch, lib, inputs, flags=flags, hashes=hashes)
+    units = layers
+    if grouped:  # projections that read the same x as one call each (q / k / v, gate / up)
+        by = {l.name: l for l in layers}
+        xs = keep[0]
+        units = [GroupUnit([by[n] for n in grp], xs[by[grp[0]].K], torch, lib, qn, grouped == "both")
+                 if len(grp) > 1 else by[grp[0]] for grp in GROUPS]
     torch.cuda.synchronize()
     flops = sum(fwd_flops(l.M, l.N, l.K, l.r) + bwd_flops(l.M, l.N, l.K, l.r) for l in layers)
     ff = {k: 0.0 for k in ("fwd_gemm", "lora_down", "bwd_dx", "bwd_dt", "bwd_da", "bwd_db")}
@@ -162,10 +224,10 @@ def bench_step(args, qn, torch, lib, inputs, flags=0, hashes=None):
         ff["bwd_db"] += 2.0 * l.N * l.r * l.M
 
     def step():
-        for l in layers:
-            l.fwd()
-        for l in layers:
-            l.bwd()
+        for u in units:
+            u.fwd()
+        for u in units:
+            u.bwd()
 
     log("warmup", args.warmup)
     for _ in range(args.warmup):
@@ -200,12 +262,12 @@ def bench_step(args, qn, torch, lib, inputs, flags=0, hashes=None):
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic() if (dom == "fwd_gemm" and flags == 0) else None,
+                "traffic": measured_traffic() if (dom == "fwd_gemm" and flags == 0 and not grouped) else None,
                 "avg_launch_ms": round(dom_ms, 4), "flops_per_launch": dom_flops}
     result = dict(sec=sec, flops=flops, kernels=kernels, roofline=roofline, step_ms=percentiles(step_ms),
                   fwd_ms=sum(kernels.get(k, {}).get("ms_per_step", 0) for k in ("fwd_gemm", "lora_down")),
                   layers=[(l.name, l.N, l.K) for l in layers])
-    del layers, keep
+    del layers, keep, units
     torch.cuda.empty_cache()
     return result
 
@@ -691,8 +753,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "fusedstep", "gemv", "quant", "sweep", "merge", "stack", "copyprobe",
-                                       "paths"],
+    ap.add_argument("--only", choices=["step", "fusedstep", "groupstep", "groupfwdstep", "gemv", "quant", "sweep",
+                                       "merge", "stack", "copyprobe", "paths"],
                     default=None,
                     help="run one part (for profiling); the JSON line needs the full run")
     args = ap.parse_args()
@@ -731,8 +793,10 @@ def main():
         print(json.dumps(bench_stack(qn, torch, inputs)))
         return
 
-    if args.only == "fusedstep":
-        st = bench_step(args, qn, torch, lib, inputs, flags=qn._lib.QLORA_FLAG_FUSED)
+    if args.only in ("fusedstep", "groupstep", "groupfwdstep"):
+        grouped = {"groupstep": "both", "groupfwdstep": "fwd"}.get(args.only, False)
+        st = bench_step(args, qn, torch, lib, inputs, flags=qn._lib.QLORA_FLAG_FUSED if args.only == "fusedstep" else 0,
+                        grouped=grouped)
         print(json.dumps({"ms_per_step": st["sec"] * 1e3, "kernels": st["kernels"], "roofline": st["roofline"]}))
         return
     hashes = {} if args.only is None else None
@@ -743,6 +807,8 @@ def main():
         return
     stf = bench_step(args, qn, torch, lib, inputs, flags=qn._lib.QLORA_FLAG_FUSED)
     log("fused step %.3f ms" % (stf["sec"] * 1e3))
+    stg = bench_step(args, qn, torch, lib, inputs, grouped="fwd")
+    log("grouped-forward step %.3f ms" % (stg["sec"] * 1e3))
     gemv = bench_gemv(qn, torch, lib, inputs)
     log("gemv done")
     quant = bench_quant(qn, torch, inputs)
@@ -790,6 +856,11 @@ def main():
                             "tflops": round(stf["flops"] / stf["sec"] / 1e12, 2),
                             "frac_bf16_peak": round(stf["flops"] / stf["sec"] / 1e12 / PEAK_BF16_TFLOPS, 4),
                             "roofline": stf["roofline"], "kernels": stf["kernels"]},
+        "grouped_forward_step": {"ms_per_step": round(stg["sec"] * 1e3, 4),
+                                 "tflops": round(stg["flops"] / stg["sec"] / 1e12, 2),
+                                 "frac_bf16_peak": round(stg["flops"] / stg["sec"] / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                 "forward": "q/k/v and gate/up each one qlora_linear_fwd_group call",
+                                 "backward": "per projection", "kernels": stg["kernels"]},
         "gemv": gemv,
         "quantize": quant,
         "dtype_sweep_forward": sweep,

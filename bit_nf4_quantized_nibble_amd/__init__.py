@@ -37,7 +37,8 @@ from ._lib import QloraError, QloraNf4  # noqa: F401
 __all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "merge", "workspace_bytes",
            "linear_fwd_noalloc", "linear_fwd_cached",
            "levels", "QloraError", "dtype_code", "profile_enable", "profile_read", "mse_loss_grad",
-           "adamw_step", "StackLayer", "stack_train_step", "stack_workspace_bytes"]
+           "adamw_step", "StackLayer", "stack_train_step", "stack_workspace_bytes",
+           "linear_fwd_group", "linear_bwd_group", "group_workspace_bytes"]
 
 
 def _torch():
@@ -302,6 +303,101 @@ def linear_fwd_cached(w_cd, x, lora_a, lora_b, alpha: float, bias=None, save_t: 
         _stream_ptr(x.device)))
     y = y.reshape(*lead, rows)
     return (y, t0) if (save_t or t_out is not None) else y
+
+
+class _GroupArgs:
+    """ctypes arrays for the g projections of a group call (kept alive with it)."""
+
+    def __init__(self, qs, lora_as=None, lora_bs=None, alphas=None):
+        g = len(qs)
+        if not 1 <= g <= _lib.QLORA_GROUP_MAX:
+            raise ValueError("a group holds 1 to %d projections" % _lib.QLORA_GROUP_MAX)
+        self.g = g
+        self.descs = [q.descriptor() for q in qs]
+        self.w = (ctypes.POINTER(_lib.QloraNf4) * g)(*[ctypes.pointer(d) for d in self.descs])
+        ranks = [a.shape[0] for a in lora_as] if lora_as is not None else [0] * g
+        self.r = (ctypes.c_int32 * g)(*ranks)
+        if lora_as is not None:
+            self.a = (ctypes.c_void_p * g)(*[_ptr(a) for a in lora_as])
+            self.b = (ctypes.c_void_p * g)(*[_ptr(b) for b in lora_bs])
+            self.alpha = (ctypes.c_float * g)(*[float(a) for a in alphas])
+
+    @staticmethod
+    def ptrs(ts):
+        return None if ts is None else (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
+
+
+def group_workspace_bytes(op: int, qs, m: int, ranks, dtype) -> int:
+    """Workspace bytes of a group call (op QLORA_OP_FWD / QLORA_OP_BWD)."""
+    ga = _GroupArgs(qs)
+    ga.r = (ctypes.c_int32 * ga.g)(*[int(r) for r in ranks])
+    return int(_lib.lib().qlora_group_workspace_bytes(op, ga.g, ga.w, m, ga.r, dtype_code(dtype)))
+
+
+def linear_fwd_group(qs, x, lora_as, lora_bs, alphas, bias=None, save_t: bool = False, rslora: bool = False,
+                     workspace=None, out=None):
+    """Projections that read the same x in one call: returns y [m, sum rows_i] with
+    projection i's output in its columns (and the list of T0_i = x A_i^T in fp32 when
+    save_t).  bias, if given, is [sum rows_i]."""
+    torch = _torch()
+    dt = x.dtype
+    cols = qs[0].cols
+    x2, lead = _flatten(x, cols)
+    x2 = x2.contiguous()
+    _need_cuda("x", x2, dt)
+    for i, (a, b) in enumerate(zip(lora_as, lora_bs)):
+        _need_cuda("lora_a[%d]" % i, a, dt)
+        _need_cuda("lora_b[%d]" % i, b, dt)
+    _need_cuda("bias", bias, dt)
+    m = x2.shape[0]
+    N = sum(q.rows for q in qs)
+    y = out if out is not None else torch.empty(m, N, dtype=dt, device=x.device)
+    _need_cuda("out", y, dt)
+    if y.numel() != m * N:
+        raise ValueError("out must hold %d x %d elements" % (m, N))
+    ts = [torch.empty(m, a.shape[0], dtype=torch.float32, device=x.device) for a in lora_as] if save_t else None
+    ga = _GroupArgs(qs, lora_as, lora_bs, alphas)
+    ws = _workspace(group_workspace_bytes(_lib.QLORA_OP_FWD, qs, m, [a.shape[0] for a in lora_as], dt), x.device,
+                    workspace)
+    _lib.check(_lib.lib().qlora_linear_fwd_group(
+        ga.g, ga.w, _ptr(x2), m, ga.a, ga.b, ga.r, ga.alpha, _lib.QLORA_FLAG_RSLORA if rslora else 0, _ptr(bias),
+        dtype_code(dt), _ptr(y), _GroupArgs.ptrs(ts), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream_ptr(x.device)))
+    y = y.reshape(*lead, N)
+    return (y, ts) if save_t else y
+
+
+def linear_bwd_group(qs, x, dy, lora_as, lora_bs, alphas, t_saved=None, need_dx: bool = True,
+                     rslora: bool = False, workspace=None):
+    """Gradients of a group with the bases frozen: dy [m, sum rows_i] laid out like the
+    forward's y.  Returns (dX = sum of the projections' input gradients, or None;
+    the list of dA_i fp32; the list of dB_i fp32)."""
+    torch = _torch()
+    dt = x.dtype
+    cols = qs[0].cols
+    N = sum(q.rows for q in qs)
+    x2, lead = _flatten(x, cols)
+    dy2, _ = _flatten(dy, N)
+    x2, dy2 = x2.contiguous(), dy2.contiguous()
+    _need_cuda("x", x2, dt)
+    _need_cuda("dy", dy2, dt)
+    m = x2.shape[0]
+    dx = torch.empty(m, cols, dtype=dt, device=x.device) if need_dx else None
+    das = [torch.empty(a.shape[0], cols, dtype=torch.float32, device=x.device) for a in lora_as]
+    dbs = [torch.empty(q.rows, a.shape[0], dtype=torch.float32, device=x.device) for q, a in zip(qs, lora_as)]
+    if t_saved is not None:
+        for t in t_saved:
+            _need_cuda("t_saved", t, torch.float32)
+    ga = _GroupArgs(qs, lora_as, lora_bs, alphas)
+    ws = _workspace(group_workspace_bytes(_lib.QLORA_OP_BWD, qs, m, [a.shape[0] for a in lora_as], dt), x.device,
+                    workspace)
+    _lib.check(_lib.lib().qlora_linear_bwd_group(
+        ga.g, ga.w, _ptr(x2), _ptr(dy2), m, ga.a, ga.b, ga.r, ga.alpha, _lib.QLORA_FLAG_RSLORA if rslora else 0,
+        dtype_code(dt), _GroupArgs.ptrs(t_saved), _ptr(dx), _GroupArgs.ptrs(das), _GroupArgs.ptrs(dbs), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream_ptr(x.device)))
+    if dx is not None:
+        dx = dx.reshape(*lead, cols)
+    return dx, das, dbs
 
 
 def linear_bwd(q: NF4Weight, x, dy, lora_a, lora_b, alpha: float, t_saved=None, need_dx: bool = True,

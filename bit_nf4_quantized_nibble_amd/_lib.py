@@ -29,7 +29,9 @@ EXPORTED = (
     "qlora_mse_loss_grad", "qlora_adamw_step", "qlora_stack_train_step", "qlora_stack_workspace_bytes",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_linear_fwd_cached",
     "qlora_linear_fwd_noalloc", "qlora_noalloc_scratch_bytes",
+    "qlora_linear_fwd_group", "qlora_linear_bwd_group", "qlora_group_workspace_bytes",
 )
+QLORA_GROUP_MAX = 8
 QLORA_MSE_WORKSPACE_BYTES = 4096
 KERNEL_KINDS = ("quantize", "dequantize", "lora_down", "reduce", "fwd_gemm", "gemv",
                 "bwd_dt", "bwd_dx", "bwd_da", "bwd_db", "merge", "loss", "optim")
@@ -107,11 +109,16 @@ def _declare(lib):
     lib.qlora_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.qlora_kernel_name.argtypes = [i32]
     lib.qlora_kernel_name.restype = ctypes.c_char_p
+    # group calls: arrays of g pointers / values
+    lib.qlora_linear_fwd_group.argtypes = [i32, vp, vp, i64, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, sz, vp]
+    lib.qlora_linear_bwd_group.argtypes = [i32, vp, vp, vp, i64, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.qlora_group_workspace_bytes.argtypes = [i32, i32, vp, i64, vp, i32]
+    lib.qlora_group_workspace_bytes.restype = sz
     for name in ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
                  "qlora_linear_bwd", "qlora_nf4_levels", "qlora_abi_version",
                  "qlora_profile_enable", "qlora_profile_read", "qlora_merge", "qlora_mse_loss_grad",
                  "qlora_adamw_step", "qlora_stack_train_step", "qlora_linear_fwd_dropout",
-                 "qlora_linear_bwd_dropout"):
+                 "qlora_linear_bwd_dropout", "qlora_linear_fwd_group", "qlora_linear_bwd_group"):
         getattr(lib, name).restype = ctypes.c_int
 
 

@@ -543,6 +543,120 @@ int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_
                   stream, "linear_bwd");
 }
 
+namespace {
+// The group's projections as single-layer calls.  query: a workspace query (shapes
+// only, no pointers checked).
+int build_group(int32_t g, const qlora_nf4_t* const* w, const void* x, int64_t m, const void* const* lora_a,
+                const void* const* lora_b, const int32_t* r, const float* alpha, int32_t flags, int32_t cd,
+                void* ws, size_t ws_bytes, void* stream, bool query, const char* who, GroupCall& gc) {
+  if (g < 1 || g > QLORA_GROUP_MAX)
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: group size %d outside 1 .. %d", who, g, QLORA_GROUP_MAX);
+  if (!w || !r || (!query && (!alpha || !lora_a || !lora_b)))
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: null array argument", who);
+  if (flags & ~QLORA_FLAG_RSLORA)
+    return set_error(QLORA_ERR_INVALID_ARG, "%s: flags 0x%x (the group takes QLORA_FLAG_RSLORA only)", who, flags);
+  int64_t off = 0, toff = 0;
+  gc.g = g;
+  for (int i = 0; i < g; ++i) {
+    int rc;
+    if (query) {
+      if (!w[i]) return set_error(QLORA_ERR_INVALID_ARG, "%s: null weight %d", who, i);
+      if ((rc = validate_desc(w[i], false, who))) return rc;
+      if (!valid_cd(cd)) return set_error(QLORA_ERR_DTYPE, "%s: bad compute dtype %d", who, cd);
+      if (m < 0 || r[i] < 1 || w[i]->rows < 1) return set_error(QLORA_ERR_SHAPE, "%s: bad shape", who);
+    } else if ((rc = validate_layer(w[i], x, m, lora_a[i], lora_b[i], r[i], alpha[i], flags, cd, who))) {
+      return rc;
+    }
+    if (w[i]->cols != w[0]->cols)
+      return set_error(QLORA_ERR_SHAPE, "%s: weight %d has %lld cols, weight 0 %lld", who, i, (long long)w[i]->cols,
+                       (long long)w[0]->cols);
+    LayerCall& c = gc.c[i];
+    c.w = make_w(w[i]);
+    c.cd = cd;
+    c.m = m;
+    c.r = r[i];
+    c.scale = query ? 1.f : lora_scale(alpha[i], r[i], flags);
+    c.flags = flags;
+    c.x = x;
+    c.drop_mask = nullptr;
+    c.lora_a = query ? nullptr : lora_a[i];
+    c.lora_b = query ? nullptr : lora_b[i];
+    c.bias = nullptr;
+    c.ws = ws;
+    c.ws_bytes = ws_bytes;
+    c.stream = (hipStream_t)stream;
+    gc.off[i] = off;
+    gc.toff[i] = toff;
+    off += w[i]->rows;
+    toff += round_up(r[i], 8);
+  }
+  gc.off[g] = off;
+  gc.toff[g] = toff;
+  gc.N = off;
+  gc.R8 = toff;
+  gc.RP = round_up(toff, 64);
+  return QLORA_OK;
+}
+
+int check_group_ptrs(const char* who, int32_t g, float* const* a, const char* name) {
+  if (!a) return QLORA_OK;
+  for (int i = 0; i < g; ++i)
+    if (a[i] && !aligned16(a[i])) return set_error(QLORA_ERR_INVALID_ARG, "%s: %s[%d] must be 16-byte aligned", who, name, i);
+  return QLORA_OK;
+}
+}  // namespace
+
+int qlora_linear_fwd_group(int32_t g, const qlora_nf4_t* const* w, const void* x, int64_t m,
+                           const void* const* lora_a, const void* const* lora_b, const int32_t* r,
+                           const float* alpha, int32_t flags, const void* bias, int32_t cd, void* y,
+                           float* const* t_save, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "linear_fwd_group";
+  GroupCall gc;
+  int rc = build_group(g, w, x, m, lora_a, lora_b, r, alpha, flags, cd, ws, ws_bytes, stream, false, who, gc);
+  if (rc) return rc;
+  if (!y) return set_error(QLORA_ERR_INVALID_ARG, "%s: null y", who);
+  if ((rc = check_aligned(who, "y and bias", {y, bias}))) return rc;
+  if ((rc = check_group_ptrs(who, g, t_save, "t_save"))) return rc;
+  if (m == 0) return QLORA_OK;
+  if ((rc = check_ws(ws, ws_bytes, group_workspace_bytes(QLORA_OP_FWD, gc), who))) return rc;
+  if ((rc = check_tables(who))) return rc;
+  return launch_forward_group(gc, bias, y, t_save, ws, (hipStream_t)stream);
+}
+
+int qlora_linear_bwd_group(int32_t g, const qlora_nf4_t* const* w, const void* x, const void* dy, int64_t m,
+                           const void* const* lora_a, const void* const* lora_b, const int32_t* r,
+                           const float* alpha, int32_t flags, int32_t cd, const float* const* t_saved,
+                           void* dx, float* const* d_a, float* const* d_b, void* ws, size_t ws_bytes,
+                           void* stream) {
+  g_err[0] = 0;
+  const char* who = "linear_bwd_group";
+  GroupCall gc;
+  int rc = build_group(g, w, x, m, lora_a, lora_b, r, alpha, flags, cd, ws, ws_bytes, stream, false, who, gc);
+  if (rc) return rc;
+  if (!dy || !d_a || !d_b) return set_error(QLORA_ERR_INVALID_ARG, "%s: null dy / d_a / d_b", who);
+  for (int i = 0; i < g; ++i)
+    if (!d_a[i] || !d_b[i]) return set_error(QLORA_ERR_INVALID_ARG, "%s: null d_a[%d] / d_b[%d]", who, i, i);
+  if ((rc = check_aligned(who, "dy and dx", {dy, dx}))) return rc;
+  if ((rc = check_group_ptrs(who, g, d_a, "d_a")) || (rc = check_group_ptrs(who, g, d_b, "d_b")) ||
+      (rc = check_group_ptrs(who, g, (float* const*)t_saved, "t_saved")))
+    return rc;
+  if (m == 0) return set_error(QLORA_ERR_SHAPE, "%s: m must be >= 1 (dA, dB would be all zero)", who);
+  if ((rc = check_ws(ws, ws_bytes, group_workspace_bytes(QLORA_OP_BWD, gc), who))) return rc;
+  if ((rc = check_tables(who))) return rc;
+  return launch_backward_group(gc, dy, t_saved, dx, d_a, d_b, ws, (hipStream_t)stream);
+}
+
+size_t qlora_group_workspace_bytes(int32_t op, int32_t g, const qlora_nf4_t* const* w, int64_t m,
+                                   const int32_t* r, int32_t cd) {
+  if (op != QLORA_OP_FWD && op != QLORA_OP_BWD) return 0;
+  GroupCall gc;
+  if (build_group(g, w, nullptr, m, nullptr, nullptr, r, nullptr, 0, cd, nullptr, 0, nullptr, true, "group_workspace",
+                  gc))
+    return 0;
+  return group_workspace_bytes(op, gc);
+}
+
 int qlora_linear_bwd_dropout(const qlora_nf4_t* w, const void* x, const void* dy, int64_t m,
                              const void* lora_a, const void* lora_b, int32_t r, float alpha, int32_t flags,
                              int32_t cd, const uint8_t* mask, float p, const float* t_saved, void* dx,

@@ -248,6 +248,7 @@ struct SkRed {
   float sccd = 1.f;
   void* outcd = nullptr;
   int64_t ldcd = 0;
+  int64_t wcd = 0;  // columns of outcd written per row (zeros from R on); 0: ldcd
   void* outt = nullptr;
   int64_t ldt = 0;
   const float* side = nullptr;
@@ -294,6 +295,7 @@ struct TransposeSpec {
   float scale = 1.f;
   void* dst = nullptr;
   int64_t ld_dst = 0;
+  int64_t w_dst = 0;  // columns of dst written per row (zeros from rows on); 0: ld_dst
 };
 int transpose_jobs(int cd, const TransposeSpec& a, const TransposeSpec* b, hipStream_t s);
 
@@ -305,12 +307,56 @@ size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int
 size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags);
 // red: a reduction that rides on the same launch (its workgroups follow the
 // dequantize ones), or null.
-int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s, const SkRed* red = nullptr);
+// W~ into out: [rows, cols], or transposed [cols][ldo] (ldo = 0: rows) for the dX GEMM.
+int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s, const SkRed* red = nullptr,
+                 int64_t ldo = 0);
 int launch_forward(const LayerCall& c, void* y, float* t_save);
 size_t cached_fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
 int launch_forward_cached(const LayerCall& c, const void* wd, void* y, float* t_save);
 int launch_backward(const LayerCall& c, const void* dy, const float* t_saved, void* dx,
                     float* d_a, float* d_b);
+
+// The tiled kernels' entry points shared across files (gemm256.hip, lora.hip) and
+// the layouts they take (gemm.hip, group.hip).
+int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* y, const DenseSplit& sp,
+                     void* split_ws);
+int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r_pad, void* dx, const DenseSplit& sp,
+                void* split_ws);
+bool fused256_ok(const LayerCall& c, bool dx);
+bool dense256_ok(const LayerCall& c, bool dx);
+int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y,
+                     const DenseSplit& sp, void* split_ws);
+int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx,
+                const DenseSplit& sp, void* split_ws, const void* a_t);
+DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1);
+size_t dense_split_bytes(const DenseSplit& sp);
+// the rank-r products on the skinny MFMA kernel (lora.hip)
+bool skinny_ok(int cd, int64_t r);
+size_t skinny_part_bytes(int64_t P, int64_t Kc);
+int skinny(int cd, bool tn, const void* a, int64_t lda, int64_t arows, const void* b, int64_t ldb, int64_t P,
+           int64_t R, int64_t Kc, float* part, int* S_out, hipStream_t s, int kind);
+int skinny_reduce(int cd, const float* part, int S, int64_t P, int64_t R, float sc32, float* out32, bool trans,
+                  float sccd, void* outcd, int64_t ldcd, hipStream_t s);
+int transpose_small(int cd, const void* src, bool src_f32, int64_t ld_src, int64_t rows, int64_t cols, float scale,
+                    void* dst, int64_t ld_dst, hipStream_t s);
+// Layouts the tiled kernels take: block a multiple of 32 that divides cols, cols a
+// multiple of 64 (everything else runs on the generic tile engine).
+inline bool fast_layout(const Nf4W& w) { return w.bs % 32 == 0 && w.cols % 64 == 0 && w.cols % w.bs == 0; }
+
+// Projections that read the same input, called as one group (group.hip).
+constexpr int kGroupMax = QLORA_GROUP_MAX;
+struct GroupCall {
+  int g = 0;
+  LayerCall c[kGroupMax];       // projection i as a single-layer call (its workspace set per use)
+  int64_t off[kGroupMax + 1];   // first column of projection i in the concatenated output; off[g] = N
+  int64_t toff[kGroupMax + 1];  // first column of its slice of the concatenated rank operand
+  int64_t N = 0, R8 = 0, RP = 0;  // sum of the rows; of the ranks each rounded up to 8; R8 rounded up to 64
+};
+size_t group_workspace_bytes(int op, const GroupCall& gc);
+int launch_forward_group(const GroupCall& gc, const void* bias, void* y, float* const* t_save, void* ws,
+                         hipStream_t s);
+int launch_backward_group(const GroupCall& gc, const void* dy, const float* const* t_saved, void* dx,
+                          float* const* d_a, float* const* d_b, void* ws, hipStream_t s);
 int launch_merge(const Nf4W& w, const void* a, const void* b, int32_t r, float s, int cd, void* out,
                  hipStream_t st);
 int launch_mse(const void* y, const void* t, int64_t n, int cd, float* loss, void* dy, float* partial,

@@ -30,28 +30,6 @@
 
 namespace qnf4 {
 
-// gemm256.hip: the 256 x 256 double-buffered fused kernels (bf16 / f16).
-int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* y, const DenseSplit& sp,
-                     void* split_ws);
-int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r_pad, void* dx, const DenseSplit& sp,
-                void* split_ws);
-bool fused256_ok(const LayerCall& c, bool dx);
-bool dense256_ok(const LayerCall& c, bool dx);
-// lora.hip: the rank-r products on the skinny MFMA kernel
-bool skinny_ok(int cd, int64_t r);
-size_t skinny_part_bytes(int64_t P, int64_t Kc);
-int skinny(int cd, bool tn, const void* a, int64_t lda, int64_t arows, const void* b, int64_t ldb, int64_t P,
-           int64_t R, int64_t Kc, float* part, int* S_out, hipStream_t s, int kind);
-int skinny_reduce(int cd, const float* part, int S, int64_t P, int64_t R, float sc32, float* out32, bool trans,
-                  float sccd, void* outcd, int64_t ldcd, hipStream_t s);
-int transpose_small(int cd, const void* src, bool src_f32, int64_t ld_src, int64_t rows, int64_t cols, float scale,
-                    void* dst, int64_t ld_dst, hipStream_t s);
-int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64_t r_pad, void* y,
-                     const DenseSplit& sp, void* split_ws);
-int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx,
-                const DenseSplit& sp, void* split_ws, const void* a_t);
-DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1);
-size_t dense_split_bytes(const DenseSplit& sp);
 
 namespace {
 
@@ -467,12 +445,11 @@ constexpr int32_t kFlagCachedW = 1 << 20;
 inline bool big_tiles(int cd) { return cd == CD_BF16 || cd == CD_F16; }
 
 // Layers whose block size is a multiple of 32 dividing cols, with cols a multiple
-// of 64, take the tiled kernels (decode GEMV, rank-product kernels, 256 x 256
-// GEMMs).  Every other layer the quantize call accepts (any even block size, any
-// cols, blocks that run across rows) takes the generic tile engine for all of its
-// products, decoding W per element.  The workspace queries do not know the block
-// size; they always cover the generic engine's needs.
-inline bool fast_layout(const Nf4W& w) { return w.bs % 32 == 0 && w.cols % 64 == 0 && w.cols % w.bs == 0; }
+// of 64 (fast_layout), take the tiled kernels (decode GEMV, rank-product kernels,
+// 256 x 256 GEMMs).  Every other layer the quantize call accepts (any even block
+// size, any cols, blocks that run across rows) takes the generic tile engine for
+// all of its products, decoding W per element.  The workspace queries do not know
+// the block size; they always cover the generic engine's needs.
 
 // Workspace plan shared by the size query and the launchers.
 struct FwdPlan {

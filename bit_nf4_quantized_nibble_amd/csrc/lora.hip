@@ -222,14 +222,16 @@ __global__ __launch_bounds__(kThreads) void k_skreduce(RedJobs js) {
 }
 
 // dst [cols][ld_dst] (cd) = cd(scale * src[rows][ld_src]^T), src in cd or fp32;
-// columns rows .. ld_dst-1 of dst are zeros.  Tiles of 64 x 64 through LDS; one
+// each dst row gets wd columns (ld_dst unless a narrower slice of a wider matrix is
+// written), columns rows .. wd-1 zeros.  Tiles of 64 x 64 through LDS; one
 // launch can carry two such jobs (workgroups [0, tiles of job 0) take job 0).
 struct TrJob {
   const void* src;
   int64_t ld_src, rows, cols;
   float scale;
   void* dst;
-  int64_t ld_dst;
+  int64_t ld_dst;  // row stride of dst
+  int64_t wd;      // columns of dst written per row (zeros from rows on)
   int32_t tiles_x, tiles;
 };
 struct TrJobs {
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void k_transpose(TrJobs js) {
   for (int i = 0; i < 16; ++i) {
     const int y = ty + 4 * i;
     const int64_t c = c0 + y, r = r0 + tx;
-    if (c < j.cols && r < j.ld_dst) store_cd<CD>(j.dst, c * j.ld_dst + r, r < j.rows ? t[tx][y] : 0.f);
+    if (c < j.cols && r < j.wd) store_cd<CD>(j.dst, c * j.ld_dst + r, r < j.rows ? t[tx][y] : 0.f);
   }
 }
 
@@ -361,7 +363,8 @@ int skinny(int cd, bool tn, const void* a, int64_t lda, int64_t arows, const voi
 namespace {
 // The device form of a reduction; false if it does not fit 32-bit indexing.
 bool red_job(const SkRed& r, RedJob& j) {
-  const int64_t width = (r.outcd && r.ldcd > r.R) ? r.ldcd : r.R;
+  const int64_t wc = r.wcd ? r.wcd : r.ldcd;  // columns of the cd output written per row
+  const int64_t width = (r.outcd && wc > r.R) ? wc : r.R;
   const int64_t rows = ((r.outt || r.side_t) && r.ldt > r.P) ? r.ldt : r.P;
   const int64_t lim = 1LL << 31;
   if (rows * width >= lim || 8 * r.P * BR >= 2 * lim || r.R * r.ldt >= lim || r.P * r.ldcd >= lim || r.S > 8)
@@ -445,7 +448,8 @@ int transpose_jobs(int cd, const TransposeSpec& a, const TransposeSpec* b, hipSt
     j.scale = t->scale;
     j.dst = t->dst;
     j.ld_dst = t->ld_dst;
-    j.tiles_x = (int32_t)ceil_div(t->ld_dst, 64);
+    j.wd = t->w_dst ? t->w_dst : t->ld_dst;
+    j.tiles_x = (int32_t)ceil_div(j.wd, 64);
     j.tiles = (int32_t)(j.tiles_x * ceil_div(t->cols, 64));
     total += j.tiles;
   }

@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, 
 // Workgroup b < gx * (rows / 64) takes slab (b % gx, b / gx); the ones from there
 // on run the reduction `red` instead (see reduce_dev.h).
 template <int OUT, int DQ, int T>
-__global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restrict__ out, Nf4Tables tab,
+__global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restrict__ out, int64_t ldo, Nf4Tables tab,
                                                            RedJobs red, uint32_t gx, uint32_t nmain) {
   if (blockIdx.x >= nmain) {
     skreduce_block<OUT>(red, blockIdx.x - nmain);
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restr
     if (kb + 64 * u >= q.cols) break;
     const u32x4_t v0 = *(const u32x4_t*)&tile[u][kr * 64 + ((ca ^ sw) << 3)];
     const u32x4_t v1 = *(const u32x4_t*)&tile[u][kr * 64 + (((ca + 4) ^ sw) << 3)];
-    uint16_t* o = (uint16_t*)out + (kb + 64 * u + kr) * q.rows + n0 + 8 * ca;
+    uint16_t* o = (uint16_t*)out + (kb + 64 * u + kr) * ldo + n0 + 8 * ca;
     *(u32x4_t*)o = v0;
     *(u32x4_t*)(o + 32) = v1;
   }
@@ -515,8 +515,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restr
 // as k_dequantize.
 constexpr int TS4 = 64 * 64 * 2 + 128;
 template <int OUT, int DQ>
-__global__ __launch_bounds__(kThreads) void k_dequantize_t4(Nf4W q, void* __restrict__ out, Nf4Tables tab,
-                                                            RedJobs red, uint32_t gx, uint32_t nmain) {
+__global__ __launch_bounds__(kThreads) void k_dequantize_t4(Nf4W q, void* __restrict__ out, int64_t ldo,
+                                                            Nf4Tables tab, RedJobs red, uint32_t gx, uint32_t nmain) {
   if (blockIdx.x >= nmain) {
     skreduce_block<OUT>(red, blockIdx.x - nmain);
     return;
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_t4(Nf4W q, void* __rest
     const unsigned char* row = tile + u * TS4 + kr * 128;
     const u32x4_t v0 = *(const u32x4_t*)(row + 16 * (ca ^ sw));
     const u32x4_t v1 = *(const u32x4_t*)(row + 16 * ((ca + 4) ^ sw));
-    uint16_t* o = (uint16_t*)out + (kb + 64 * u + kr) * q.rows + n0 + 8 * ca;
+    uint16_t* o = (uint16_t*)out + (kb + 64 * u + kr) * ldo + n0 + 8 * ca;
     *(u32x4_t*)o = v0;
     *(u32x4_t*)(o + 32) = v1;
   }
@@ -712,19 +712,23 @@ int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s, const SkRed* r
 }
 
 template <int OUT, int DQ>
-void run_dqt(bool four, uint32_t gx, uint32_t nmain, int64_t nred, const Nf4W& w, void* out, const Nf4Tables& t,
-             const RedJobs& js, hipStream_t s) {
+void run_dqt(bool four, uint32_t gx, uint32_t nmain, int64_t nred, const Nf4W& w, void* out, int64_t ldo,
+             const Nf4Tables& t, const RedJobs& js, hipStream_t s) {
   const dim3 grid((unsigned)(nmain + nred));
-  if (four && w.bs_shift >= 5) k_dequantize_t4<OUT, DQ><<<grid, dim3(kThreads), 0, s>>>(w, out, t, js, gx, nmain);
-  else if (four) k_dequantize_t<OUT, DQ, 4><<<grid, dim3(kThreads), 0, s>>>(w, out, t, js, gx, nmain);
-  else k_dequantize_t<OUT, DQ, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, t, js, gx, nmain);
+  if (four && w.bs_shift >= 5) k_dequantize_t4<OUT, DQ><<<grid, dim3(kThreads), 0, s>>>(w, out, ldo, t, js, gx, nmain);
+  else if (four) k_dequantize_t<OUT, DQ, 4><<<grid, dim3(kThreads), 0, s>>>(w, out, ldo, t, js, gx, nmain);
+  else k_dequantize_t<OUT, DQ, 1><<<grid, dim3(kThreads), 0, s>>>(w, out, ldo, t, js, gx, nmain);
 }
 
 // Dequantize W into a compute-dtype buffer inside a layer call: [rows, cols]
-// (forward) or its transpose [cols, rows] (dX).  The transpose needs rows and cols
-// to be multiples of 64.
-int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s, const SkRed* red) {
+// (forward) or its transpose [cols][ldo] (dX; ldo = 0 means rows, a larger ldo
+// writes W~^T as the column slice of a wider matrix).  The transpose needs rows and
+// cols to be multiples of 64.
+int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s, const SkRed* red, int64_t ldo) {
   if (transposed) {
+    if (ldo == 0) ldo = w.rows;
+    if (ldo < w.rows || ldo % 8 || w.cols * ldo >= (1LL << 31))
+      return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: output stride %lld not supported", (long long)ldo);
     const Nf4Tables& t = host_tables();
     RedJobs js;
     int64_t nred;
@@ -739,11 +743,11 @@ int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t 
     const int64_t gx = ceil_div(w.cols, T4 ? 256 : 64), nmain = gx * (w.rows / 64);
     if (nmain + nred > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize^T: tensor too large");
     if (cd == CD_BF16) {
-      if (w.dq) run_dqt<CD_BF16, 1>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, t, js, s);
-      else run_dqt<CD_BF16, 0>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, t, js, s);
+      if (w.dq) run_dqt<CD_BF16, 1>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, ldo, t, js, s);
+      else run_dqt<CD_BF16, 0>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, ldo, t, js, s);
     } else if (cd == CD_F16) {
-      if (w.dq) run_dqt<CD_F16, 1>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, t, js, s);
-      else run_dqt<CD_F16, 0>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, t, js, s);
+      if (w.dq) run_dqt<CD_F16, 1>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, ldo, t, js, s);
+      else run_dqt<CD_F16, 0>(T4, (uint32_t)gx, (uint32_t)nmain, nred, w, out, ldo, t, js, s);
     }
     else return set_error(QLORA_ERR_DTYPE, "dequantize^T: bad dtype %d", cd);
     return check_launch("k_dequantize_t");

@@ -176,6 +176,65 @@ int qlora_linear_bwd(const qlora_nf4_t* w, const void* x, const void* dy, int64_
                      float* d_b, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * A group of g QLoRA projections that read the same input x (the q / k / v
+ * projections of an attention block, the gate / up projections of an MLP), in one
+ * call.  Projection i has weight w[i] [rows_i, cols] (cols the same for all),
+ * adapters lora_a[i] [r[i], cols], lora_b[i] [rows_i, r[i]] and scale alpha[i] / r[i]
+ * (alpha[i] / sqrt(r[i]) with QLORA_FLAG_RSLORA).  The outputs sit side by side:
+ *   y [m, N] with N = sum rows_i, columns off_i .. off_i + rows_i of projection i
+ *   (off_i = rows_0 + ... + rows_{i-1}), each exactly what qlora_linear_fwd gives for
+ *   that projection up to the order of its fp32 sums; bias (nullable) is [N].
+ * t_save (nullable array of g nullable pointers): T0_i = x A_i^T fp32 [m, r[i]].
+ * Page: "LoRA and QLoRA, mathematically", "Rank, alpha, and target modules" (the
+ * adapted modules of a block: q, k, v, o, gate, up, down); the layer itself as in
+ * qlora_linear_fwd.
+ * How: bf16 / f16, more than 64 tokens, layouts the 256 x 256 kernels take, rows_i
+ * multiples of 64 and r[i] <= 64: every W~_i is dequantized into one [N, cols] buffer of the workspace,
+ * the rank products write T_i side by side, and one dense GEMM reads
+ * [x | T] [W~ | B]^T with B block-diagonal (row n of projection i holds B_i[n] in
+ * the columns of T_i), so the short launches of small projections and the cut last
+ * rounds of large ones merge.  Otherwise each projection runs through
+ * qlora_linear_fwd into the workspace and a copy places its columns.
+ * Flags: QLORA_FLAG_RSLORA only.  ws: qlora_group_workspace_bytes(QLORA_OP_FWD, ...)
+ * bytes, 256-byte aligned.  Arrays 16-byte aligned as for qlora_linear_fwd.
+ * Errors: as qlora_linear_fwd for each projection, plus QLORA_ERR_INVALID_ARG for
+ * g < 1, g > QLORA_GROUP_MAX, null arrays or other flags, and QLORA_ERR_SHAPE for
+ * differing cols.
+ */
+#define QLORA_GROUP_MAX 8
+int qlora_linear_fwd_group(int32_t g, const qlora_nf4_t* const* w, const void* x, int64_t m,
+                           const void* const* lora_a, const void* const* lora_b, const int32_t* r,
+                           const float* alpha, int32_t flags, const void* bias, int32_t cd, void* y,
+                           float* const* t_save, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the group with the base weights frozen:
+ *   dX = sum_i (dY_i W~_i + dT_i A_i)  [m, cols] (cd; skipped when dx == NULL),
+ *   dA_i = dT_i^T x,  dB_i = s_i dY_i^T T0_i  (fp32, overwritten),  dT_i = s_i dY_i B_i,
+ * with dy [m, N] laid out like the forward's y (dY_i its columns off_i ..).  dX is the
+ * gradient of the block input the projections share.  On the tiled path one fp32
+ * accumulation runs over every projection's contraction and is rounded once;
+ * otherwise each projection's dX from qlora_linear_bwd (rounded to cd) is added in
+ * fp32 and the sum rounded.
+ * t_saved (nullable array, or array of nullable pointers): the forward's T0_i.
+ * How: as the forward (one dense dX GEMM over the concatenated contraction
+ * [dY | dT] [W~ ; A]), otherwise per projection and an fp32 sum of the dX terms.
+ * ws: qlora_group_workspace_bytes(QLORA_OP_BWD, ...) bytes.
+ * Errors: as qlora_linear_bwd for each projection, and as qlora_linear_fwd_group.
+ */
+int qlora_linear_bwd_group(int32_t g, const qlora_nf4_t* const* w, const void* x, const void* dy, int64_t m,
+                           const void* const* lora_a, const void* const* lora_b, const int32_t* r,
+                           const float* alpha, int32_t flags, int32_t cd, const float* const* t_saved,
+                           void* dx, float* const* d_a, float* const* d_b, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Workspace bytes for qlora_linear_fwd_group (op QLORA_OP_FWD) or
+ * qlora_linear_bwd_group (QLORA_OP_BWD) on these g weights; 0 for an invalid query.
+ * Pure host function. */
+size_t qlora_group_workspace_bytes(int32_t op, int32_t g, const qlora_nf4_t* const* w, int64_t m,
+                                   const int32_t* r, int32_t cd);
+
+/*
  * Fold the trained adapter into a dense weight (the step after training):
  *   out [rows, cols] = RNE_cd(w_hat + s (B . A)),  s = alpha / r (alpha / sqrt(r)
  *   with QLORA_FLAG_RSLORA),

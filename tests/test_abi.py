@@ -287,3 +287,69 @@ def test_dropout_entry_points_refuse_on_the_host(lib):
     assert b(mask=None) == INVALID
     assert b(p=1.5) == INVALID
     assert b(ws_bytes=16) == WS
+
+
+def group_args(descs, n=None):
+    n = len(descs) if n is None else n
+    W = (ctypes.POINTER(_lib.QloraNf4) * len(descs))(*[ctypes.pointer(d) for d in descs])
+    A = (ctypes.c_void_p * len(descs))(*([FAKE] * len(descs)))
+    R = (ctypes.c_int32 * len(descs))(*([8] * len(descs)))
+    AL = (ctypes.c_float * len(descs))(*([16.0] * len(descs)))
+    return W, A, R, AL
+
+
+def group_fwd(lib, descs, g=None, x=FAKE, m=128, flags=0, bias=None, cd=1, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    W, A, R, AL = group_args(descs)
+    return lib.qlora_linear_fwd_group(len(descs) if g is None else g, W, x, m, A, A, R, AL, flags, bias, cd, y,
+                                      None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=0), INVALID),
+    (dict(g=9), INVALID),
+    (dict(flags=2), INVALID),         # the group takes the rsLoRA flag only
+    (dict(y=None), INVALID),
+    (dict(y=FAKE + 8), INVALID),
+    (dict(bias=FAKE + 4), INVALID),
+    (dict(cd=5), DTYPE),
+    (dict(ws_bytes=16), WS),
+])
+def test_group_forward_refusals(lib, kw, status):
+    assert group_fwd(lib, [desc(), desc(rows=128)], **kw) == status
+    assert last_error(lib)
+
+
+def test_group_refuses_mixed_cols_and_accepts_no_tokens(lib):
+    assert group_fwd(lib, [desc(), desc(cols=128)]) == SHAPE
+    assert group_fwd(lib, [desc(), desc(rows=128)], m=0) == OK
+
+
+def test_group_backward_refusals(lib):
+    descs = [desc(), desc(rows=128)]
+    W, A, R, AL = group_args(descs)
+    G = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    Z = (ctypes.c_void_p * 2)(FAKE, None)
+
+    def bwd(dy=FAKE, dx=FAKE, da=G, db=G, m=128, ws_bytes=1 << 40):
+        return lib.qlora_linear_bwd_group(2, W, FAKE, dy, m, A, A, R, AL, 0, 1, None, dx, da, db, FAKE, ws_bytes,
+                                          None)
+    assert bwd(m=0) == SHAPE
+    assert bwd(dy=None) == INVALID
+    assert bwd(da=Z) == INVALID
+    assert bwd(dx=FAKE + 2) == INVALID
+    assert bwd(ws_bytes=8) == WS
+
+
+def test_group_workspace_query(lib):
+    """The tiled path holds the concatenated W~ (bf16 q / k / v at 4096 tokens);
+    invalid queries give 0."""
+    descs = [desc(rows=4096, cols=4096), desc(rows=1024, cols=4096), desc(rows=1024, cols=4096)]
+    W = (ctypes.POINTER(_lib.QloraNf4) * 3)(*[ctypes.pointer(d) for d in descs])
+    R = (ctypes.c_int32 * 3)(64, 64, 64)
+    fwd_b = lib.qlora_group_workspace_bytes(0, 3, W, 4096, R, 1)
+    bwd_b = lib.qlora_group_workspace_bytes(1, 3, W, 4096, R, 1)
+    assert fwd_b >= 6144 * 4096 * 2 and bwd_b >= 6144 * 4096 * 2
+    assert lib.qlora_group_workspace_bytes(0, 0, W, 4096, R, 1) == 0
+    assert lib.qlora_group_workspace_bytes(2, 3, W, 4096, R, 1) == 0
+    mixed = (ctypes.POINTER(_lib.QloraNf4) * 2)(ctypes.pointer(desc()), ctypes.pointer(desc(cols=128)))
+    assert lib.qlora_group_workspace_bytes(0, 2, mixed, 16, R, 1) == 0
