@@ -263,9 +263,12 @@ struct SkSpec {
   int64_t lda = 0, arows = 0;
   const void* b = nullptr;
   int64_t ldb = 0, P = 0, R = 0, Kc = 0;
+  bool bt = false;     // b as stored [brows][ldb] with the R columns contiguous (NT, R % 8 == 0)
+  int64_t brows = 0;
 };
+struct TransposeSpec;
 int skinny_jobs(int cd, bool tn, const SkSpec& a, float* part, int* S_out, const SkSpec* b2, float* part2,
-                int* S2, hipStream_t s, int kind);
+                int* S2, hipStream_t s, int kind, const TransposeSpec* ride = nullptr);
 // The device form of one or two reductions (workgroups of kRedThreads threads, one
 // thread per element; job 1 takes the workgroups after job 0's nblk).
 constexpr int kRedThreads = 256;

@@ -503,7 +503,7 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   P.off_dt = P.off_t0 + al(m * r * 4);
   P.off_dtcd = P.off_dt + al(m * r * 4);
   P.off_bt = P.off_dtcd + al(m * P.r_pad * es);
-  P.off_dtt = P.off_bt + (P.sk_n ? al(r * P.n_pad * es) : 0);
+  P.off_dtt = P.off_bt + (P.sk_n && r % 8 ? al(r * P.n_pad * es) : 0);  // B^T only when lora_b cannot be read as stored
   P.off_t0t = P.off_dtt + (P.sk ? al(r * P.m_pad * es) : 0);
   P.off_part = P.off_t0t + (P.sk_n ? al(r * P.m_pad * es) : 0);
   int64_t part = (int64_t)P.st.S * m * r * 4;
@@ -694,17 +694,39 @@ int backward_gemm(const LayerCall& c, const void* dy, const float* t_saved, void
   SkRed red_dt;  // the dT reduction, launched here or riding on W~^T's dequantize
   bool red_dt_pending = false;
   if (P.sk_n) {
-    void* bt = ws + P.off_bt;  // B^T [r][n_pad], zero past N
-    TransposeSpec tb;
-    tb.src = c.lora_b;
-    tb.ld_src = r;
-    tb.rows = N;
-    tb.cols = r;
-    tb.dst = bt;
-    tb.ld_dst = P.n_pad;
-    if ((rc = transpose_jobs(CD, tb, at ? &ta : nullptr, c.stream))) return rc;
+    // dY against lora_b: read as stored when r is a multiple of 8 (A^T's transpose
+    // rides on the same launch), else against a transposed copy B^T [r][n_pad], zero
+    // past N
+    SkSpec sd;
+    sd.a = dy;
+    sd.lda = N;
+    sd.arows = M;
+    sd.P = M;
+    sd.R = r;
+    sd.Kc = P.n_pad;
+    const TransposeSpec* ride = nullptr;
+    if (r % 8 == 0) {
+      sd.b = c.lora_b;
+      sd.ldb = r;
+      sd.bt = true;
+      sd.brows = N;
+      ride = at ? &ta : nullptr;
+    } else {
+      void* bt = ws + P.off_bt;
+      TransposeSpec tb;
+      tb.src = c.lora_b;
+      tb.ld_src = r;
+      tb.rows = N;
+      tb.cols = r;
+      tb.dst = bt;
+      tb.ld_dst = P.n_pad;
+      if ((rc = transpose_jobs(CD, tb, at ? &ta : nullptr, c.stream))) return rc;
+      sd.b = bt;
+      sd.ldb = P.n_pad;
+    }
     int S;
-    if ((rc = skinny(CD, false, dy, N, M, bt, P.n_pad, M, r, P.n_pad, part, &S, c.stream, QLORA_K_BWD_DT))) return rc;
+    if ((rc = skinny_jobs(CD, false, sd, part, &S, nullptr, nullptr, nullptr, c.stream, QLORA_K_BWD_DT, ride)))
+      return rc;
     red_dt.part = part;
     red_dt.S = S;
     red_dt.P = M;

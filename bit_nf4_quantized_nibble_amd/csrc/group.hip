@@ -330,14 +330,8 @@ int launch_backward_group(const GroupCall& gc, const void* dy, const float* cons
       if ((rc = skinny_reduce(c.cd, part, S, m, c.r, 1.0f, (float*)(w + P.t0), false, 0.f, nullptr, 0, s))) return rc;
       T0 = (const float*)(w + P.t0);
     }
-    // B_i^T [r_i][n64] for dT_i; A_i^T into its slice of the stacked A^T [cols][RP]
-    TransposeSpec tb, ta;
-    tb.src = c.lora_b;
-    tb.ld_src = c.r;
-    tb.rows = Ni;
-    tb.cols = c.r;
-    tb.dst = w + P.bt;
-    tb.ld_dst = n64;
+    // A_i^T into its slice of the stacked A^T [cols][RP]
+    TransposeSpec ta;
     ta.src = c.lora_a;
     ta.ld_src = K;
     ta.rows = c.r;
@@ -345,11 +339,38 @@ int launch_backward_group(const GroupCall& gc, const void* dy, const float* cons
     ta.dst = w + P.at + gc.toff[i] * es;
     ta.ld_dst = gc.RP;
     ta.w_dst = slice_width(gc, i);
-    if ((rc = transpose_jobs(c.cd, tb, &ta, s))) return rc;
     // dT_i = s_i dY_i B_i: its slice of dT (cd) for the dX GEMM's tail, dT_i^T and T0_i^T
-    // for dA_i and dB_i; the reduction rides on W_i's transposed dequantize
+    // for dA_i and dB_i; the reduction rides on W_i's transposed dequantize.  lora_b_i
+    // is read as stored when r_i is a multiple of 8 (A_i^T's transpose then rides on
+    // the same launch), else through B_i^T [r_i][n64]
+    SkSpec sd;
+    sd.a = dyi;
+    sd.lda = gc.N;
+    sd.arows = m;
+    sd.P = m;
+    sd.R = c.r;
+    sd.Kc = n64;
+    const TransposeSpec* ride = nullptr;
+    if (c.r % 8 == 0) {
+      sd.b = c.lora_b;
+      sd.ldb = c.r;
+      sd.bt = true;
+      sd.brows = Ni;
+      ride = &ta;
+    } else {
+      TransposeSpec tb;
+      tb.src = c.lora_b;
+      tb.ld_src = c.r;
+      tb.rows = Ni;
+      tb.cols = c.r;
+      tb.dst = w + P.bt;
+      tb.ld_dst = n64;
+      if ((rc = transpose_jobs(c.cd, tb, &ta, s))) return rc;
+      sd.b = w + P.bt;
+      sd.ldb = n64;
+    }
     int S;
-    if ((rc = skinny(c.cd, false, dyi, gc.N, m, w + P.bt, n64, m, c.r, n64, part, &S, s, QLORA_K_BWD_DT))) return rc;
+    if ((rc = skinny_jobs(c.cd, false, sd, part, &S, nullptr, nullptr, nullptr, s, QLORA_K_BWD_DT, ride))) return rc;
     SkRed red;
     red.part = part;
     red.S = S;

@@ -13,9 +13,11 @@
 // kernel, output tile 128 (p) x 64 (t), 4 waves of 32 x 64 (two MFMA 32x32x16
 // tiles each), 64-element contraction stages in three LDS buffers (the copies run
 // two stages ahead), and a split of the contraction into S slices whose fp32
-// partial sums a second kernel adds in slice order.  Bop is always a small [t][k]
-// matrix with k contiguous (A, or a transposed copy of B, dT or T0 made by
-// k_transpose).  Every tile is copied global -> LDS by DMA.  Aop is either
+// partial sums a second kernel adds in slice order.  Bop is a small [t][k] matrix
+// with k contiguous (A, or a transposed copy of dT or T0), or, for dT, lora_b as
+// it is stored, [k][t] with t contiguous (BT: 128-byte rows of t, chunk c of row k
+// at chunk c ^ 4 ((k / 8) % 2); a fragment is gathered with 16-bit reads like a TN
+// one).  Every tile is copied global -> LDS by DMA.  Aop is either
 //   NT: a matrix [p][k] with k contiguous (x, dY): 128-byte rows of k, 16-byte
 //       chunk c of row r at chunk c ^ swz(r), or
 //   TN: a matrix X [k][p] with p contiguous (x or dY read along the tokens):
@@ -68,8 +70,9 @@ struct SkP {
   const void* a;    // NT: [P][lda], k contiguous; TN: [arows][lda], p contiguous
   int64_t lda;
   int64_t arows;    // rows of a (TN: the true token count; rows up to Kc past it read as zeros)
-  const void* b;    // [R][ldb], k contiguous (rows >= R read as zeros)
-  int64_t ldb;
+  const void* b;    // [R][ldb], k contiguous (rows >= R read as zeros); BT: [brows][ldb],
+                    // t contiguous (rows >= brows and columns >= R read as zeros)
+  int64_t ldb, brows;
   int64_t P, R, Kc;
   int64_t kslice;   // contraction per slice (multiple of 64)
   float* part;      // [S][P][64] fp32
@@ -85,6 +88,20 @@ __device__ __forceinline__ void copy_b(const SkP& p, rsrc_t rb, char* dst, int w
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + (4 * d + wave) * 1024), 16,
                                              (int)oob_unless(row < p.R, (uint32_t)((row * p.ldb + k + 8 * c) * 2)),
                                              0, 0, 0);
+  }
+}
+
+// BT Bop tile (rows k .. k+63 of lora_b as stored, R <= 64 columns of t): rows as in
+// copy_b, logical chunk c of row `row` at physical chunk c ^ 4 ((row / 8) % 2), so the
+// two row groups of a gather instruction (rows e and 8 + e) sit on distinct banks.
+__device__ __forceinline__ void copy_b_t(const SkP& p, rsrc_t rb, char* dst, int wave, int lane, int64_t k) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const int row = 8 * (4 * d + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ (4 * ((row >> 3) & 1));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (lds_void*)(dst + (4 * d + wave) * 1024), 16,
+        (int)oob_unless(8 * c < p.R, (uint32_t)(((k + row) * p.ldb + 8 * c) * 2)), 0, 0, 0);
   }
 }
 
@@ -124,19 +141,85 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
+// dst [cols][ld_dst] (cd) = cd(scale * src[rows][ld_src]^T), src in cd or fp32;
+// each dst row gets wd columns (ld_dst unless a narrower slice of a wider matrix is
+// written), columns rows .. wd-1 zeros.  Tiles of 64 x 64 through LDS; one
+// launch can carry two such jobs (workgroups [0, tiles of job 0) take job 0), and
+// a job can ride on a rank-product launch (k_skinny).
+struct TrJob {
+  const void* src;
+  int64_t ld_src, rows, cols;
+  float scale;
+  void* dst;
+  int64_t ld_dst;  // row stride of dst
+  int64_t wd;      // columns of dst written per row (zeros from rows on)
+  int32_t tiles_x, tiles;
+};
+struct TrJobs {
+  TrJob j[2];
+};
+
+// Tile b of job j through the LDS tile t (256 threads).
+template <int CD, int SRC32>
+__device__ __forceinline__ void transpose_tile(const TrJob& j, int b, float (*t)[65]) {
+  const int64_t r0 = (int64_t)(b % j.tiles_x) * 64, c0 = (int64_t)(b / j.tiles_x) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  // all 16 loads of a thread leave before the first is used: out-of-range elements
+  // read element 0 and are replaced by zero afterwards
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
+    const int64_t at = (r < j.rows && c < j.cols) ? r * j.ld_src + c : 0;
+    v[i] = SRC32 ? ((const float*)j.src)[at] : load_cd<CD>(j.src, at);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
+    t[ty + 4 * i][tx] = (r < j.rows && c < j.cols) ? v[i] * j.scale : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int y = ty + 4 * i;
+    const int64_t c = c0 + y, r = r0 + tx;
+    if (c < j.cols && r < j.wd) store_cd<CD>(j.dst, c * j.ld_dst + r, r < j.rows ? t[tx][y] : 0.f);
+  }
+}
+
+template <int CD, int SRC32>
+__global__ __launch_bounds__(kThreads) void k_transpose(TrJobs js) {
+  __shared__ float t[64][65];
+  const int w = (int)blockIdx.x >= js.j[0].tiles ? 1 : 0;
+  transpose_tile<CD, SRC32>(js.j[w], blockIdx.x - (w ? js.j[0].tiles : 0), t);
+}
+
 // One launch carries one or two products (blockIdx.z picks the job; workgroups
-// outside a job's own grid leave at once).
+// outside a job's own grid leave at once) and optionally a transpose (plane z = nj
+// of the grid, its workgroups taking the tiles in turn).
 struct SkP2 {
   SkP j[2];
   uint32_t nx[2], ny[2];
+  uint32_t nj;  // products
+  TrJob tr;     // tr.tiles == 0: none
 };
 
-template <int CD, int TN>
+// MODE: 0 NT, 1 TN (Aop forms), 2 NT with the BT Bop.
+template <int CD, int MODE>
 __global__ __launch_bounds__(kThreads) void k_skinny(SkP2 ps) {
+  constexpr bool TN = MODE == 1, BT = MODE == 2;
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * STAGE];  // stage b: [A | B]
   const int jb = blockIdx.z;
+  if (jb == (int)ps.nj) {
+    const int nb = (int)(gridDim.x * gridDim.y);
+    for (int b = (int)(blockIdx.y * gridDim.x + blockIdx.x); b < ps.tr.tiles; b += nb) {
+      if (b != (int)(blockIdx.y * gridDim.x + blockIdx.x)) __syncthreads();  // the tile before is stored
+      transpose_tile<CD, 0>(ps.tr, b, (float (*)[65])lds);
+    }
+    return;
+  }
   if (blockIdx.x >= ps.nx[jb] || blockIdx.y >= ps.ny[jb]) return;
   const SkP& p = ps.j[jb];
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF * STAGE];  // stage b: [A | B]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 31, h = lane >> 5;
@@ -145,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny(SkP2 ps) {
   const int64_t k1 = k0 + p.kslice < p.Kc ? k0 + p.kslice : p.Kc;
   const int nst = (int)((k1 - k0) / BK);
   const rsrc_t ra = make_rsrc(p.a, p.arows * p.lda * 2);
-  const rsrc_t rb = make_rsrc(p.b, p.R * p.ldb * 2);
+  const rsrc_t rb = make_rsrc(p.b, (BT ? p.brows : p.R) * p.ldb * 2);
   const int xr = swz(i);  // swizzle of the 128-byte rows this lane reads (they differ by 32)
   // TN: column 32 wave + i is chunk pc, element pe of it; rows 8 h + j (j < 8) of
   // a 16-row step sit at chunk pc ^ ((8 h + j) % 16)
@@ -153,6 +236,13 @@ __global__ __launch_bounds__(kThreads) void k_skinny(SkP2 ps) {
   int tn_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) tn_off[j] = (8 * h + j) * XROW + 16 * (pc ^ ((8 * h + j) & 15)) + pe;
+  // BT: rank column 32 j + i of rows 8 h + e (e < 8) of a 16-row step: logical chunk
+  // 4 j + i / 8, physical chunk (4 j + i / 8) ^ 4 h; block j = 1 sits 64 bytes after
+  // block 0 for h = 0 and 64 before it for h = 1
+  int bt_off[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bt_off[e] = (8 * h + e) * ROWB + 16 * ((i >> 3) ^ (4 * h)) + 2 * (i & 7);
+  const int bt_j1 = h ? -64 : 64;
 
   f32x16_t acc[2];
 #pragma unroll
@@ -165,7 +255,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny(SkP2 ps) {
     const int64_t k = k0 + (int64_t)st * BK;
     if (TN) copy_a_tn(p, ra, dst, p0, wave, lane, k);
     else copy_a_nt(p, ra, dst, p0, wave, lane, k);
-    copy_b(p, rb, dst + A_BYTES, wave, lane, k);
+    if (BT) copy_b_t(p, rb, dst + A_BYTES, wave, lane, k);
+    else copy_b(p, rb, dst + A_BYTES, wave, lane, k);
   };
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
@@ -199,7 +290,17 @@ __global__ __launch_bounds__(kThreads) void k_skinny(SkP2 ps) {
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const u32x4_t b = *(const u32x4_t*)(Bs + (32 * j + i) * ROWB + cphys);
+        u32x4_t b;
+        if (BT) {
+          // 8 consecutive k (rows 16 ks + 8 h ..) of rank column 32 j + i
+          const char* src = Bs + 16 * ks * ROWB + j * bt_j1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            b[e] = (uint32_t)*(const uint16_t*)(src + bt_off[2 * e]) |
+                   ((uint32_t)*(const uint16_t*)(src + bt_off[2 * e + 1]) << 16);
+        } else {
+          b = *(const u32x4_t*)(Bs + (32 * j + i) * ROWB + cphys);
+        }
         acc[j] = mfma<CD>(a, b, acc[j]);
       }
     }
@@ -219,54 +320,6 @@ __global__ __launch_bounds__(kThreads) void k_skinny(SkP2 ps) {
 template <int CD>
 __global__ __launch_bounds__(kThreads) void k_skreduce(RedJobs js) {
   skreduce_block<CD>(js, blockIdx.x);
-}
-
-// dst [cols][ld_dst] (cd) = cd(scale * src[rows][ld_src]^T), src in cd or fp32;
-// each dst row gets wd columns (ld_dst unless a narrower slice of a wider matrix is
-// written), columns rows .. wd-1 zeros.  Tiles of 64 x 64 through LDS; one
-// launch can carry two such jobs (workgroups [0, tiles of job 0) take job 0).
-struct TrJob {
-  const void* src;
-  int64_t ld_src, rows, cols;
-  float scale;
-  void* dst;
-  int64_t ld_dst;  // row stride of dst
-  int64_t wd;      // columns of dst written per row (zeros from rows on)
-  int32_t tiles_x, tiles;
-};
-struct TrJobs {
-  TrJob j[2];
-};
-
-template <int CD, int SRC32>
-__global__ __launch_bounds__(kThreads) void k_transpose(TrJobs js) {
-  __shared__ float t[64][65];
-  const int w = (int)blockIdx.x >= js.j[0].tiles ? 1 : 0;
-  const TrJob& j = js.j[w];
-  const int b = blockIdx.x - (w ? js.j[0].tiles : 0);
-  const int64_t r0 = (int64_t)(b % j.tiles_x) * 64, c0 = (int64_t)(b / j.tiles_x) * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  // all 16 loads of a thread leave before the first is used: out-of-range elements
-  // read element 0 and are replaced by zero afterwards
-  float v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
-    const int64_t at = (r < j.rows && c < j.cols) ? r * j.ld_src + c : 0;
-    v[i] = SRC32 ? ((const float*)j.src)[at] : load_cd<CD>(j.src, at);
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
-    t[ty + 4 * i][tx] = (r < j.rows && c < j.cols) ? v[i] * j.scale : 0.f;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int y = ty + 4 * i;
-    const int64_t c = c0 + y, r = r0 + tx;
-    if (c < j.cols && r < j.wd) store_cd<CD>(j.dst, c * j.ld_dst + r, r < j.rows ? t[tx][y] : 0.f);
-  }
 }
 
 }  // namespace
@@ -301,7 +354,9 @@ size_t skinny_part_bytes(int64_t P, int64_t Kc) {
 // between its true width and Kc.
 namespace {
 int skinny_params(bool tn, const SkSpec& sp, float* part, SkP& p, int* S_out) {
-  if (sp.Kc % BK || sp.lda % 8 || sp.ldb % 8 || sp.ldb < sp.Kc || (tn && sp.P % 8))
+  const bool bad_b = sp.bt ? (tn || sp.R % 8 || sp.ldb < sp.R || sp.brows * sp.ldb * 2 >= (1LL << 31))
+                           : sp.ldb < sp.Kc;
+  if (sp.Kc % BK || sp.lda % 8 || sp.ldb % 8 || bad_b || (tn && sp.P % 8))
     return set_error(QLORA_ERR_UNSUPPORTED, "rank product: shape not supported by the skinny kernel");
   p = SkP{};
   p.a = sp.a;
@@ -309,6 +364,7 @@ int skinny_params(bool tn, const SkSpec& sp, float* part, SkP& p, int* S_out) {
   p.arows = sp.arows;
   p.b = sp.b;
   p.ldb = sp.ldb;
+  p.brows = sp.brows;
   p.P = sp.P;
   p.R = sp.R;
   p.Kc = sp.Kc;
@@ -316,31 +372,57 @@ int skinny_params(bool tn, const SkSpec& sp, float* part, SkP& p, int* S_out) {
   skinny_split(sp.P, sp.Kc, S_out, &p.kslice);
   return QLORA_OK;
 }
+
+// The device form of a transpose job; false when it has nothing to write.
+bool tr_job(const TransposeSpec& t, TrJob& j) {
+  if (t.ld_dst == 0 || t.cols == 0) return false;
+  j.src = t.src;
+  j.ld_src = t.ld_src;
+  j.rows = t.rows;
+  j.cols = t.cols;
+  j.scale = t.scale;
+  j.dst = t.dst;
+  j.ld_dst = t.ld_dst;
+  j.wd = t.w_dst ? t.w_dst : t.ld_dst;
+  j.tiles_x = (int32_t)ceil_div(j.wd, 64);
+  j.tiles = (int32_t)(j.tiles_x * ceil_div(t.cols, 64));
+  return j.tiles > 0;
+}
 }  // namespace
 
 // part = per-slice sums of Aop . Bop^T over the contraction 0 .. Kc (a multiple of
 // 64); Aop NT [P][lda] or TN [arows][lda]; Bop [R][ldb] with ldb >= Kc, zero
-// between its true width and Kc.  With b2 a second product of the same kind
-// shares the launch (its slice count in *S2).
+// between its true width and Kc, or (a.bt, NT only) [brows][ldb] as stored, rows
+// from brows on read as zeros.  With b2 a second product of the same kind shares
+// the launch (its slice count in *S2); with ride a transpose (compute-dtype source)
+// takes one more plane of the grid.
 int skinny_jobs(int cd, bool tn, const SkSpec& a, float* part, int* S_out, const SkSpec* b2, float* part2,
-                int* S2, hipStream_t s, int kind) {
+                int* S2, hipStream_t s, int kind, const TransposeSpec* ride) {
   SkP2 ps = {};
   int rc = skinny_params(tn, a, part, ps.j[0], S_out);
   if (rc) return rc;
   ps.nx[0] = (uint32_t)ceil_div(a.P, BP);
   ps.ny[0] = (uint32_t)*S_out;
+  ps.nj = 1;
   if (b2) {
+    if (b2->bt != a.bt) return set_error(QLORA_ERR_UNSUPPORTED, "rank product: jobs of one launch differ in form");
     if ((rc = skinny_params(tn, *b2, part2, ps.j[1], S2))) return rc;
     ps.nx[1] = (uint32_t)ceil_div(b2->P, BP);
     ps.ny[1] = (uint32_t)*S2;
+    ps.nj = 2;
   }
-  const dim3 grid(std::max(ps.nx[0], ps.nx[1]), std::max(ps.ny[0], ps.ny[1]), b2 ? 2 : 1);
+  if (ride && ride->src_f32) return set_error(QLORA_ERR_UNSUPPORTED, "rank product: a riding transpose reads cd");
+  const bool has_tr = ride && tr_job(*ride, ps.tr);
+  const dim3 grid(std::max(ps.nx[0], ps.nx[1]), std::max(ps.ny[0], ps.ny[1]), ps.nj + (has_tr ? 1 : 0));
   ProfScope prof(kind, s);
+  const int mode = tn ? 1 : a.bt ? 2 : 0;
   if (cd == CD_BF16) {
-    if (tn) k_skinny<CD_BF16, 1><<<grid, dim3(kThreads), 0, s>>>(ps);
+    if (mode == 1) k_skinny<CD_BF16, 1><<<grid, dim3(kThreads), 0, s>>>(ps);
+    else if (mode == 2) k_skinny<CD_BF16, 2><<<grid, dim3(kThreads), 0, s>>>(ps);
     else k_skinny<CD_BF16, 0><<<grid, dim3(kThreads), 0, s>>>(ps);
   } else {
-    if (tn) k_skinny<CD_F16, 1><<<grid, dim3(kThreads), 0, s>>>(ps);
+    if (mode == 1) k_skinny<CD_F16, 1><<<grid, dim3(kThreads), 0, s>>>(ps);
+    else if (mode == 2) k_skinny<CD_F16, 2><<<grid, dim3(kThreads), 0, s>>>(ps);
     else k_skinny<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(ps);
   }
   return check_launch("k_skinny");
@@ -437,22 +519,8 @@ int transpose_jobs(int cd, const TransposeSpec& a, const TransposeSpec* b, hipSt
   TrJobs js = {};
   const TransposeSpec* specs[2] = {&a, b};
   int64_t total = 0;
-  for (int k = 0; k < 2; ++k) {
-    const TransposeSpec* t = specs[k];
-    if (!t || t->ld_dst == 0 || t->cols == 0) continue;
-    TrJob& j = js.j[k];
-    j.src = t->src;
-    j.ld_src = t->ld_src;
-    j.rows = t->rows;
-    j.cols = t->cols;
-    j.scale = t->scale;
-    j.dst = t->dst;
-    j.ld_dst = t->ld_dst;
-    j.wd = t->w_dst ? t->w_dst : t->ld_dst;
-    j.tiles_x = (int32_t)ceil_div(j.wd, 64);
-    j.tiles = (int32_t)(j.tiles_x * ceil_div(t->cols, 64));
-    total += j.tiles;
-  }
+  for (int k = 0; k < 2; ++k)
+    if (specs[k] && tr_job(*specs[k], js.j[k])) total += js.j[k].tiles;
   if (total == 0) return QLORA_OK;
   ProfScope prof(QLORA_K_REDUCE, s);
   const dim3 g((unsigned)total), blk(kThreads);
