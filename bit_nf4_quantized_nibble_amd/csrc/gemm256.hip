@@ -413,9 +413,23 @@ __device__ __forceinline__ void finish_part(const float (&sc)[8], const float (&
   }
 }
 
+// The r-th fragment read of a sub-step, in the order the next sub-step's MFMAs
+// (block (i, j) at slot i JB + j) first use them: 0..3 the A fragments a[i], 4.. the
+// B fragments b[j].  JB = 2: b0 a0 b1 a1 a2 a3; JB = 4: a0 b0 b1 b2 b3 a1 a2 a3.
+template <int JB>
+__device__ __forceinline__ constexpr int frag_by_first_use(int r) {
+  if constexpr (JB == 2) {
+    constexpr int o[6] = {4, 0, 5, 1, 2, 3};
+    return o[r];
+  } else {
+    constexpr int o[8] = {0, 4, 5, 6, 7, 1, 2, 3};
+    return o[r];
+  }
+}
+
 // One stage: 64 MFMAs from LDS buffer `cur`, in 4 sub-steps of 16.  The side work
 // sits at fixed MFMA slots (fences keep the compiler from regrouping it):
-//   every other slot: one fragment read for the next sub-step;
+//   every other slot: one fragment read for the next sub-step (in order of first use);
 //   every slot: one level lookup for the next decode quarter (in sub-step 3, for
 //     quarter 0 of the next stage, from Rn);
 //   slots 8..15: one pack of the current quarter (lookups issued a sub-step ago),
@@ -449,9 +463,9 @@ __device__ __forceinline__ void stage(f32x16_t (&acc)[4][4], char* lds, int cur,
       const int i = t >> 2, j = t & 3;
       acc[i][j] = mfma<CD>(C.b[j], C.a[i], acc[i][j]);  // block (i, j) transposed
       if (ks < 3 && (t & 1) == 0) {
-        const int r = t >> 1;
-        if (r < 4) N.a[r] = *(const u32x4_t*)(As + (a_row + 32 * r) * ROWB + cphys);
-        else N.b[r - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (r - 4)) * ROWB + cphys);
+        const int f = frag_by_first_use<4>(t >> 1);
+        if (f < 4) N.a[f] = *(const u32x4_t*)(As + (a_row + 32 * f) * ROWB + cphys);
+        else N.b[f - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (f - 4)) * ROWB + cphys);
       }
       if (ks < 3) ln[t] = lv_at(lds, code_addr<MODE>(R, ks + 1, t));
       else ln[t] = lv_at(lds, code_addr<MODE>(Rn, 0, t));
@@ -800,8 +814,10 @@ __device__ __forceinline__ void copy_one(const Copy& cp, char* dst_a, char* dst_
 
 // One stage of a wave's 128 x 32 JB block (NW = 16 / JB waves): 4 sub-steps of 4 JB
 // MFMAs; the 4 + JB fragment reads of the next sub-step are spread over the MFMAs
-// of the first three, and (DO_COPY, waves 0..3) the wave's 8 copies of each operand
-// for the next stage go between the MFMAs of sub-steps 0 (activations) and 1 (W side).
+// of the first three, and (DO_COPY: the copying waves, 0..3; the caller picks the
+// form per wave, so no wave branches around its copies) the wave's 8 copies of each
+// operand for the next stage go between the MFMAs of sub-steps 0 (activations) and 1
+// (W side).
 template <int CD, int DO_COPY, int JB>
 __device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][JB], char* lds, int cur, const Copy& cp, int wave,
                                             int a_row, int b_row, int xr, int h) {
@@ -826,13 +842,14 @@ __device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][JB], char* lds, i
 #pragma unroll
         for (int r = 0; r < NRD; ++r)
           if (r * NMF / NRD == t) {
-            if (r < 4) N.a[r] = *(const u32x4_t*)(As + (a_row + 32 * r) * ROWB + cphys);
-            else N.b[r - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (r - 4)) * ROWB + cphys);
+            const int f = frag_by_first_use<JB>(r);
+            if (f < 4) N.a[f] = *(const u32x4_t*)(As + (a_row + 32 * f) * ROWB + cphys);
+            else N.b[f - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (f - 4)) * ROWB + cphys);
           }
       }
       if constexpr (DO_COPY) {
         if (NW == 4 && ks < 2 && (t & 1) == 1) copy_one(cp, An, Bn, wave, t >> 1, ks == 1);
-        if (NW == 8 && ks < 2 && wave < 4) copy_one(cp, An, Bn, wave, t, ks == 1);
+        if (NW == 8 && ks < 2) copy_one(cp, An, Bn, wave, t, ks == 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -923,10 +940,18 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dense256(Big p, const void* bd) 
     }
   }
   uint32_t u = 0;
-  for (; u + 1 < n_st; ++u) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of stage u and its fragment reads
-    barrier_only();
-    dense_stage<CD, 1>(acc, lds, u & 1, copy_of(u + 1), wave, a_row, b_row, xr, h);
+  if (NW == 4 || wave < 4) {
+    for (; u + 1 < n_st; ++u) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of stage u and its fragment reads
+      barrier_only();
+      dense_stage<CD, 1>(acc, lds, u & 1, copy_of(u + 1), wave, a_row, b_row, xr, h);
+    }
+  } else {
+    for (; u + 1 < n_st; ++u) {
+      __builtin_amdgcn_s_waitcnt(0);  // its fragment reads (the other waves copy)
+      barrier_only();
+      dense_stage<CD, 0>(acc, lds, u & 1, main_cp, wave, a_row, b_row, xr, h);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   barrier_only();
