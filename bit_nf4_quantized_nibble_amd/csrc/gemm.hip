@@ -428,17 +428,24 @@ inline int64_t al(int64_t b) { return round_up(b, kAlign); }
 // the fused kernels or faster at every token count from 32 to 4096 (q_proj and
 // gate_proj shapes, r 64, bf16); the fused kernels need no rows x cols copy in the
 // workspace, which is their reason to exist.
-bool dense_path(int64_t m, int64_t rows, int64_t cols, int cd, int32_t flags, bool dx) {
-  (void)m;
-  if (cd != CD_BF16 && cd != CD_F16) return false;
-  if (cols % 64 || (dx && rows % 64)) return false;
-  if (flags & QLORA_FLAG_FUSED) return false;
-  return true;
-}
-
 // Internal plan flag: W~ comes from the caller (cached-dequant forward), so the
 // workspace holds no copy of it.
 constexpr int32_t kFlagCachedW = 1 << 20;
+
+// Forward calls of at most this many tokens with no path flag take the fused kernel
+// when its eight-wave form applies (rank a multiple of 8): there, decoding each W
+// tile once per 256 tokens costs less than writing W~ and reading it back (q + gate
+// forward at 128 / 256 / 512 tokens: 0.111 / 0.121 / 0.156 ms fused against
+// 0.125 / 0.139 / 0.163 ms; at 1024 tokens 0.211 against 0.205).
+constexpr int64_t kFusedFwdMaxM = 768;
+
+bool dense_path(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags, bool dx) {
+  if (cd != CD_BF16 && cd != CD_F16) return false;
+  if (cols % 64 || (dx && rows % 64)) return false;
+  if (flags & QLORA_FLAG_FUSED) return false;
+  if (!dx && !(flags & (QLORA_FLAG_DEQUANT_GEMM | kFlagCachedW)) && m <= kFusedFwdMaxM && r % 8 == 0) return false;
+  return true;
+}
 
 // Whether the 256 x 256 GEMMs (dense or fused) may take a call of this dtype: their
 // cut last round needs its slices' partial sums in the workspace.
@@ -469,7 +476,7 @@ FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   int64_t part = (int64_t)P.st.S * m * r * 4;
   if (skinny_ok(cd, r)) part = std::max<int64_t>(part, (int64_t)skinny_part_bytes(m, cols));
   P.off_wd = P.off_part + al(part);
-  P.dense = dense_path(m, rows, cols, cd, flags, false);
+  P.dense = dense_path(m, rows, cols, r, cd, flags, false);
   P.off_xm = P.off_wd + (P.dense && !(flags & kFlagCachedW) ? al(rows * cols * es) : 0);  // x M with LoRA dropout
   P.off_split = P.off_xm + ((flags & QLORA_FLAG_DROPOUT) ? al(m * cols * es) : 0);
   P.dsp = dense_split(m, rows, cols);
@@ -521,7 +528,7 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   // dB's partial sums live beside dA's so that one launch reduces both
   P.off_part2 = P.off_part + al(part);
   P.off_wdt = P.off_part2 + (P.sk_n ? al((int64_t)skinny_part_bytes(rows, P.m_pad)) : 0);
-  P.dense = dense_path(m, rows, cols, cd, flags, true);
+  P.dense = dense_path(m, rows, cols, r, cd, flags, true);
   // with LoRA dropout: x M, and a zero [m, r_pad] operand for the base-only dX GEMM
   P.off_xm = P.off_wdt + (P.dense ? al(rows * cols * es) : 0);
   const bool drop = (flags & QLORA_FLAG_DROPOUT) != 0;

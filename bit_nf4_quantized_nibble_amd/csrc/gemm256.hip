@@ -969,6 +969,266 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dense256(Big p, const void* bd) 
   else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
 }
 
+
+// ---------------------------------------------------------------------------
+// Fused forward in eight waves, two per SIMD: the dense kernel's stage with the W
+// tile decoded from NF4 codes instead of copied.  Waves 0..3 decode (lane t owns W
+// row t of the tile and decodes its 64 codes of the next stage between its MFMAs,
+// as k_fused256 does); waves 4..7 copy the activation tile by DMA and otherwise only
+// multiply, so on every SIMD the copying wave's MFMAs keep the matrix core busy
+// while the decoding wave works through its decode.  (Splitting the decode evenly
+// over both waves of a SIMD was slower: their decode phases then coincide.)  The
+// low-rank tail is copied by DMA (rank a multiple of 8): its activation half by
+// waves 4..7, its lora_b half by waves 0..3.
+// ---------------------------------------------------------------------------
+enum { NEXT_NONE = 0, NEXT_DECODE = 1, NEXT_COPY = 2 };
+
+// One stage of a decoding wave: the 32 MFMAs of its 128 x 64 block from buffer cur
+// with the next sub-step's fragment reads between them, and the preparation of the
+// next stage's W tile in the other buffer: NEXT_DECODE decodes the codes R (per MFMA
+// slot two level lookups of the next quarter and one pack of two weights of the
+// current quarter, whose lookups were issued a sub-step earlier; the last sub-step
+// looks up quarter 0 of Rn); NEXT_COPY copies the tail's lora_b rows (cp).
+template <int CD, int DQ, int NEXT>
+__device__ __forceinline__ void fused8_dec_stage(f32x16_t (&acc)[4][2], char* lds, int cur, const CodeRegs& R,
+                                                 const CodeRegs& Rn, float (&lv)[2][16], const Copy& cp, int wave,
+                                                 int a_row, int b_row, int xr, int h, int tid) {
+  char* As = lds + cur * TILE_BYTES;
+  char* Bs = lds + (2 + cur) * TILE_BYTES;
+  char* An = lds + (cur ^ 1) * TILE_BYTES;
+  char* Bn = lds + (2 + (cur ^ 1)) * TILE_BYTES;
+  FragsT<2> F[2];
+  float sc[8];
+  if constexpr (NEXT == NEXT_DECODE) stage_scales<MODE_FWD, DQ>(R, sc);
+  read_frags(F[0], As, Bs, a_row, b_row, xr, h, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    FragsT<2>& C = F[ks & 1];
+    FragsT<2>& N = F[(ks + 1) & 1];
+    float (&lc)[16] = lv[ks & 1];
+    float (&ln)[16] = lv[(ks + 1) & 1];
+    const int cphys = ((2 * (ks + 1) + h) ^ xr) << 4;
+    u32x4_t o;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = t >> 1, j = t & 1;
+      acc[i][j] = mfma<CD>(C.b[j], C.a[i], acc[i][j]);  // block (i, j) transposed
+      if (ks < 3) {
+#pragma unroll
+        for (int r = 0; r < 6; ++r)
+          if (r * 8 / 6 == t) {
+            const int f = frag_by_first_use<2>(r);
+            if (f < 4) N.a[f] = *(const u32x4_t*)(As + (a_row + 32 * f) * ROWB + cphys);
+            else N.b[f - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (f - 4)) * ROWB + cphys);
+          }
+      }
+      if constexpr (NEXT == NEXT_DECODE) {
+#pragma unroll
+        for (int e = 2 * t; e < 2 * t + 2; ++e)
+          ln[e] = lv_at(lds, ks < 3 ? code_addr<MODE_FWD>(R, ks + 1, e) : code_addr<MODE_FWD>(Rn, 0, e));
+        finish_part<CD, MODE_FWD>(sc, lc, o, Bn, tid, ks, t);
+      } else if constexpr (NEXT == NEXT_COPY) {
+        if (ks == 1) copy_one(cp, An, Bn, wave, t, true);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// One stage of a copying wave: dense_stage with only the activation copies of the
+// next stage (one per MFMA slot of sub-step 0).
+template <int CD, bool COPY>
+__device__ __forceinline__ void fused8_copy_stage(f32x16_t (&acc)[4][2], char* lds, int cur, const Copy& cp, int cw,
+                                                  int a_row, int b_row, int xr, int h) {
+  char* As = lds + cur * TILE_BYTES;
+  char* Bs = lds + (2 + cur) * TILE_BYTES;
+  char* An = lds + (cur ^ 1) * TILE_BYTES;
+  FragsT<2> F[2];
+  read_frags(F[0], As, Bs, a_row, b_row, xr, h, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    FragsT<2>& C = F[ks & 1];
+    FragsT<2>& N = F[(ks + 1) & 1];
+    const int cphys = ((2 * (ks + 1) + h) ^ xr) << 4;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = t >> 1, j = t & 1;
+      acc[i][j] = mfma<CD>(C.b[j], C.a[i], acc[i][j]);
+      if (ks < 3) {
+#pragma unroll
+        for (int r = 0; r < 6; ++r)
+          if (r * 8 / 6 == t) {
+            const int f = frag_by_first_use<2>(r);
+            if (f < 4) N.a[f] = *(const u32x4_t*)(As + (a_row + 32 * f) * ROWB + cphys);
+            else N.b[f - 4] = *(const u32x4_t*)(Bs + (b_row + 32 * (f - 4)) * ROWB + cphys);
+          }
+      }
+      if (COPY && ks == 0) copy_one(cp, An, An, cw, t, false);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int CD, int DQ>
+__global__ __launch_bounds__(8 * 64, 1) void k_fused8(Big p, Nf4Tables tab) {
+  // [A0 | A1 | B0 | B1 | levels]
+  __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_BYTES + 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < 16) *(float*)(lds + LV_OFF + 4 * tid) = tab.lv[tid];
+  int tm, tn, slice, rt;
+  item_of(p, tm, tn, slice, rt);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  slice = __builtin_amdgcn_readfirstlane(slice);
+  rt = __builtin_amdgcn_readfirstlane(rt);
+  const int64_t m0 = (int64_t)tm * TILE, n0 = (int64_t)tn * TILE;
+  const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
+  const int h = lane >> 5;
+  const int a_row = wm + (lane & 31), b_row = wn + (lane & 31);
+  const int xr = swz(lane & 31);
+  const bool decoder = wave < 4;
+
+  // DMA copies (activation tile by waves 4..7; the tail's lora_b rows by waves 0..3):
+  // rows 8 (4 d + wave % 4) + lane / 8 of each tile, as in the dense kernel
+  const int row = 8 * (wave & 3) + (lane >> 3);
+  const int c = (lane & 7) ^ swz(row);
+  Copy main_cp;
+  main_cp.ra = make_rsrc(p.a1, p.M * p.ld_a1 * 2);
+  main_cp.rb = main_cp.ra;
+  main_cp.a_off = (uint32_t)(((m0 + row) * p.ld_a1 + 8 * c) * 2);
+  main_cp.b_off = 0;
+  main_cp.a_step = (uint32_t)(32 * p.ld_a1 * 2);
+  main_cp.b_step = 0;
+
+  // the codes of W row n0 + tid (decoding waves)
+  const Nf4W& w = p.w;
+  const rsrc_t rc = make_rsrc(w.codes, w.rows * w.cols / 2);
+  const int64_t nb = w.rows * w.cols / w.bs;
+  const rsrc_t rq = DQ ? make_rsrc(w.absmax_q, nb) : make_rsrc(w.absmax, nb * 4);
+  const rsrc_t rs = make_rsrc(DQ ? (const void*)w.scale2 : (const void*)w.absmax,
+                              DQ ? (((nb - 1) >> w.g_shift) + 1) * 4 : nb * 4);
+  Lane L;
+  L.row_bytes = (uint32_t)(w.cols / 2);
+  L.row_blocks = (uint32_t)(w.cols >> w.bs_shift);
+  {
+    const uint32_t wrow = (uint32_t)(n0 + (tid & 255));
+    L.ok = wrow < (uint32_t)w.rows;
+    L.c_off = wrow * L.row_bytes;
+    L.b_idx = wrow * L.row_blocks;
+  }
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const uint32_t KT = (uint32_t)(p.K1 / BK);
+  uint32_t k0 = 0, k1 = KT;
+  if (rt >= 0) {
+    k0 = (uint32_t)slice * KT / (uint32_t)p.split;
+    k1 = (uint32_t)(slice + 1) * KT / (uint32_t)p.split;
+  }
+  const bool has_tail = rt < 0 || slice == p.split - 1;
+  const uint32_t nmain = k1 - k0;
+  const uint32_t n_st = nmain + (has_tail ? (uint32_t)((p.r_pad + BK - 1) / BK) : 0u);
+  const rsrc_t ra2 = make_rsrc(p.a2, p.M * p.r_pad * 2);
+  const rsrc_t rb2 = make_rsrc(p.b2_rows, p.NB * p.ld_b2 * 2);
+  auto copy_of = [&](uint32_t u) {  // stage u's copies (u >= nmain: the tail)
+    if (u < nmain) {
+      Copy cp = main_cp;
+      cp.soff = (k0 + u) * (BK * 2);
+      return cp;
+    }
+    const uint32_t t0 = (u - nmain) * BK + 8 * c;
+    Copy cp;
+    cp.ra = ra2;
+    cp.rb = rb2;
+    cp.a_off = oob_unless(t0 < (uint32_t)p.r_pad, (uint32_t)(((m0 + row) * p.r_pad + t0) * 2));
+    cp.b_off = oob_unless(t0 < (uint32_t)p.r_b2, (uint32_t)(((n0 + row) * p.ld_b2 + t0) * 2));
+    cp.a_step = (uint32_t)(32 * p.r_pad * 2);
+    cp.b_step = (uint32_t)(32 * p.ld_b2 * 2);
+    cp.soff = 0;
+    return cp;
+  };
+
+  constexpr int NWL = fetch_w_loads<MODE_FWD, DQ>();
+  CodeRegs R0, R1;
+  float lv[2][16];
+  if (decoder) {
+    fetch_w<MODE_FWD, DQ>(R0, p, L, rc, rq, rs, k0, k1);
+    fetch_w<MODE_FWD, DQ>(R1, p, L, rc, rq, rs, k0 + 1, k1);
+  } else {
+    const Copy cp = copy_of(0);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) copy_one(cp, lds, lds, wave & 3, d, false);
+  }
+  __syncthreads();  // the level table
+  if (decoder) {
+    // stage 0's W tile (the codes of R0 landed first: R1's loads may still fly)
+    wait_vmcnt<NWL>();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) decode_quarter<CD, MODE_FWD, DQ>(R0, lds, lds + 2 * TILE_BYTES, tid, q);
+    fetch_w<MODE_FWD, DQ>(R0, p, L, rc, rq, rs, k0 + 2, k1);
+    wait_vmcnt<NWL>();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  wait_lgkm0();
+  barrier_only();
+
+  uint32_t u = 0;
+  if (decoder) {
+    // stage u decodes stage u + 1's codes: R1 for even u, R0 for odd u; the set it
+    // decoded then loads the codes of stage u + 3
+#pragma unroll
+    for (int t = 0; t < 16; ++t) lv[0][t] = lv_at(lds, code_addr<MODE_FWD>(R1, 0, t));
+    for (; u + 2 < nmain; u += 2) {
+      fused8_dec_stage<CD, DQ, NEXT_DECODE>(acc, lds, 0, R1, R0, lv, main_cp, wave, a_row, b_row, xr, h, tid);
+      fetch_w<MODE_FWD, DQ>(R1, p, L, rc, rq, rs, k0 + u + 3, k1);
+      wait_vmcnt<NWL>();  // the code loads may still fly
+      wait_lgkm0();       // the W tile writes
+      barrier_only();
+      fused8_dec_stage<CD, DQ, NEXT_DECODE>(acc, lds, 1, R0, R1, lv, main_cp, wave, a_row, b_row, xr, h, tid);
+      fetch_w<MODE_FWD, DQ>(R0, p, L, rc, rq, rs, k0 + u + 4, k1);
+      wait_vmcnt<NWL>();
+      wait_lgkm0();
+      barrier_only();
+    }
+    if (u + 1 < nmain) {  // u is even here
+      fused8_dec_stage<CD, DQ, NEXT_DECODE>(acc, lds, 0, R1, R0, lv, main_cp, wave, a_row, b_row, xr, h, tid);
+      __builtin_amdgcn_s_waitcnt(0);
+      barrier_only();
+      ++u;
+    }
+    // the tail stages (their lora_b rows copied by DMA), then the last stage
+    for (; u + 1 < n_st; ++u) {
+      fused8_dec_stage<CD, DQ, NEXT_COPY>(acc, lds, u & 1, R0, R1, lv, copy_of(u + 1), wave & 3, a_row, b_row, xr,
+                                          h, tid);
+      __builtin_amdgcn_s_waitcnt(0);
+      barrier_only();
+    }
+    fused8_dec_stage<CD, DQ, NEXT_NONE>(acc, lds, u & 1, R0, R1, lv, main_cp, wave, a_row, b_row, xr, h, tid);
+  } else {
+    for (; u + 1 < n_st; ++u) {
+      fused8_copy_stage<CD, true>(acc, lds, u & 1, copy_of(u + 1), wave & 3, a_row, b_row, xr, h);
+      __builtin_amdgcn_s_waitcnt(0);
+      barrier_only();
+    }
+    fused8_copy_stage<CD, false>(acc, lds, u & 1, main_cp, wave & 3, a_row, b_row, xr, h);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  if (rt < 0) epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
+  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
+}
+
 template <int CD, int S>
 int launch_split_sum(const Big& b, hipStream_t s);
 
@@ -978,10 +1238,16 @@ template <int CD, int MODE>
 int run(const Big& b, hipStream_t s, int kind) {
   const int64_t items = (int64_t)b.full + (int64_t)b.rem * b.split;
   ProfScope prof(kind, s);
-  if (b.w.dq)
+  if (MODE == MODE_FWD && b.b2_rows) {
+    if (b.w.dq)
+      k_fused8<CD, 1><<<dim3((unsigned)items), dim3(8 * 64), 0, s>>>(b, host_tables());
+    else
+      k_fused8<CD, 0><<<dim3((unsigned)items), dim3(8 * 64), 0, s>>>(b, host_tables());
+  } else if (b.w.dq) {
     k_fused256<CD, MODE, 1><<<dim3((unsigned)items), dim3(kThreads), 0, s>>>(b, host_tables());
-  else
+  } else {
     k_fused256<CD, MODE, 0><<<dim3((unsigned)items), dim3(kThreads), 0, s>>>(b, host_tables());
+  }
   int rc = check_launch(MODE == MODE_FWD ? "k_fused256<fwd>" : "k_fused256<dx>");
   if (rc || !b.rem) return rc;
   return b.split == 2 ? launch_split_sum<CD, 2>(b, s) : launch_split_sum<CD, 4>(b, s);
@@ -1054,6 +1320,11 @@ int fused256_forward(const LayerCall& c, const void* t_cd, int64_t r_pad, void* 
   b.out = y;
   b.bias = c.bias;
   set_split(b, sp, split_ws);
+  if (c.r % 8 == 0 && c.w.cols % BK == 0) {  // the eight-wave kernel (its tail copies lora_b rows)
+    b.b2_rows = c.lora_b;
+    b.ld_b2 = c.r;
+    b.r_b2 = c.r;
+  }
   if (c.cd == CD_BF16) return run<CD_BF16, MODE_FWD>(b, c.stream, QLORA_K_FWD_GEMM);
   return run<CD_F16, MODE_FWD>(b, c.stream, QLORA_K_FWD_GEMM);
 }

@@ -61,8 +61,10 @@ typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1, QLORA_F16 = 2 } qlora_dtype_t;
 /* Flags for the forward / backward calls.  The two path flags (at most one) pick
  * how W~ meets the activations when m > 16 (m <= 16 always takes the decode GEMV;
  * without a path flag, 17 to 64 tokens take its MFMA form where it applies):
- *   default                  dequantize-then-GEMM (it was as fast or faster at
- *                            every m measured, 32 to 4096)
+ *   default                  the forward of 65 to 768 tokens with r a multiple
+ *                            of 8 takes the fused kernels (faster there: W~ is
+ *                            not written and read back); every other call with
+ *                            m > 16 takes dequantize-then-GEMM
  *   QLORA_FLAG_FUSED         the fused kernels decode W~ on the fly, tile by tile
  *                            (no dequantized copy of W anywhere)
  *   QLORA_FLAG_DEQUANT_GEMM  W~ (forward) or W~^T (dX) is first written in cd into
@@ -140,10 +142,10 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, int32_t out_dtype, void* out, voi
  * mathematically" eq. (6.3.6) and "Tooling" (dequant fused with the matmul).
  * How W~ meets x (see the path flags): m <= 16 runs the decode GEMV (split
  * contraction, W~ decoded in registers; 17 to 64 tokens too when no path flag is
- * given and cols is a multiple of 1024); above that, by default, W~ is dequantized
- * once into the workspace and a dense 256 x 256 MFMA GEMM reads it
- * (dequantize-then-GEMM); QLORA_FLAG_FUSED decodes W~ tile by tile inside the GEMM
- * instead.  These kernels take bf16 / f16 layers whose block size is a multiple of
+ * given and cols is a multiple of 1024); from 65 to 768 tokens with r a multiple
+ * of 8, by default, the fused 256 x 256 MFMA GEMM decodes W~ tile by tile; above
+ * that W~ is dequantized once into the workspace and a dense 256 x 256 MFMA GEMM
+ * reads it (dequantize-then-GEMM).  The path flags force either.  These kernels take bf16 / f16 layers whose block size is a multiple of
  * 32 dividing cols, with cols a multiple of 64.  Every other layer (f32, any even
  * block size, any cols, blocks that run across rows) runs on a generic MFMA tile
  * engine that decodes W~ per element: the same W~ bits, the sums in another order.

@@ -199,8 +199,15 @@ def test_workspace_query(lib):
     dense = lib.qlora_workspace_bytes(0 | (4 << 8), 2048, 4096, 4096, 64, 1)
     assert dense - fused >= 4096 * 4096 * 2
     assert lib.qlora_workspace_bytes(0, 2048, 4096, 4096, 64, 1) == dense      # the default path
-    assert lib.qlora_workspace_bytes(0, 32, 4096, 4096, 64, 1) == lib.qlora_workspace_bytes(4 << 8, 32, 4096, 4096, 64, 1)
-    assert lib.qlora_workspace_bytes(2 << 8, 32, 4096, 4096, 64, 1) < lib.qlora_workspace_bytes(0, 32, 4096, 4096, 64, 1)
+    # the default forward of 65 to 768 tokens takes the fused kernel when r is a multiple
+    # of 8 (also for a decode-GEMV candidate whose layout sends it to the GEMM path)
+    for m in (32, 512, 768):
+        assert lib.qlora_workspace_bytes(0, m, 4096, 4096, 64, 1) == lib.qlora_workspace_bytes(2 << 8, m, 4096, 4096, 64, 1)
+        assert lib.qlora_workspace_bytes(0, m, 4096, 4096, 64, 1) < lib.qlora_workspace_bytes(4 << 8, m, 4096, 4096, 64, 1)
+        assert lib.qlora_workspace_bytes(0, m, 4096, 4096, 12, 1) == lib.qlora_workspace_bytes(4 << 8, m, 4096, 4096, 12, 1)
+    assert lib.qlora_workspace_bytes(0, 769, 4096, 4096, 64, 1) == lib.qlora_workspace_bytes(4 << 8, 769, 4096, 4096, 64, 1)
+    # the backward keeps dequantize-then-GEMM by default
+    assert lib.qlora_workspace_bytes(1, 512, 4096, 4096, 64, 1) == lib.qlora_workspace_bytes(1 | (4 << 8), 512, 4096, 4096, 64, 1)
     assert lib.qlora_workspace_bytes(1 | (4 << 8), 512, 4096, 4096, 64, 1) >= 4096 * 4096 * 2
     assert lib.qlora_workspace_bytes(0 | (16 << 8), 512, 4096, 4096, 64, 1) == 0  # unknown flag
     # LoRA dropout stages x M (and, in the backward, a zero dT operand) in the workspace
