@@ -138,8 +138,7 @@ __device__ __forceinline__ void tile_of(const Big& p, int& tm, int& tn) {
 // Dense kernel: workgroup -> (tile, contraction slice, index among the cut tiles
 // or -1).  The slices of the cut tiles follow the whole tiles; each XCD's chunk of
 // them is one slice of a run of consecutive tiles of the grouped order.
-__device__ __forceinline__ void item_of(const Big& p, int& tm, int& tn, int& slice, int& rt) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ void item_of(const Big& p, int b, int& tm, int& tn, int& slice, int& rt) {
   slice = 0;
   rt = -1;
   if (b < p.full) {
@@ -612,12 +611,12 @@ __global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
 // the 16-byte row reads collide on banks), then writes whole rows: 4 JB lanes per
 // row, 64 / (4 JB) rows of 64 JB contiguous bytes per store instruction.  Entered
 // with the LDS free.
-template <int CD, int JB>
-__device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][JB], const Big& p, char* lds, int64_t m0,
-                                             int64_t n0, int wave, int wm, int wn, int lane, int h) {
+template <int CD, int JB, int I0, int NI>
+__device__ __forceinline__ void epilogue_rows(const f32x16_t (&acc)[4][JB], const Big& p, char* W, int64_t m0,
+                                              int64_t n0, int wm, int wn, int lane, int h) {
+  // rows 32 I0 .. 32 (I0 + NI) of the wave's block, staged in W (row m - 32 I0)
   constexpr int RB = 64 * JB;  // bytes per staged row
   constexpr int NC = 4 * JB;   // 16-byte chunks per row
-  char* W = lds + wave * (128 * RB);
   const int r = lane & 31;
   float bv[JB][4][4];  // bias of the lane's columns (j, q, e)
 #pragma unroll
@@ -638,8 +637,8 @@ __device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][JB], const
         }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 32 * i + r;
+  for (int i = I0; i < I0 + NI; ++i) {
+    const int m = 32 * (i - I0) + r;
 #pragma unroll
     for (int j = 0; j < JB; ++j)
 #pragma unroll
@@ -655,10 +654,10 @@ __device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][JB], const
   const int64_t col = n0 + wn + 8 * c;
   const bool vec = (p.NB & 7) == 0;
 #pragma unroll 4
-  for (int it = 0; it < 2 * NC; ++it) {
+  for (int it = 0; it < NI * NC / 2; ++it) {
     const int m = (64 / NC) * it + lane / NC;
     const u32x4_t v = *(const u32x4_t*)(W + m * RB + ((c ^ (m & (NC - 1))) << 4));
-    const int64_t row = m0 + wm + m;
+    const int64_t row = m0 + wm + 32 * I0 + m;
     if (row >= p.M) continue;
     uint16_t* dst = (uint16_t*)p.out + row * p.NB + col;
     if (vec && col + 8 <= p.NB) {
@@ -671,6 +670,22 @@ __device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][JB], const
   }
 }
 
+template <int CD, int JB>
+__device__ __forceinline__ void epilogue_lds(const f32x16_t (&acc)[4][JB], const Big& p, char* lds, int64_t m0,
+                                             int64_t n0, int wave, int wm, int wn, int lane, int h) {
+  epilogue_rows<CD, JB, 0, 4>(acc, p, lds + wave * (128 * 64 * JB), m0, n0, wm, wn, lane, h);
+}
+
+// The same in two passes of 64 rows through 8 JB KiB per wave at W (the persistent
+// dense kernel stages there while the next tile's first stage lands elsewhere).
+template <int CD, int JB>
+__device__ __forceinline__ void epilogue_halves(const f32x16_t (&acc)[4][JB], const Big& p, char* W, int64_t m0,
+                                                int64_t n0, int wm, int wn, int lane, int h) {
+  epilogue_rows<CD, JB, 0, 2>(acc, p, W, m0, n0, wm, wn, lane, h);
+  wait_lgkm0();  // the first pass's reads are done before the second pass overwrites W
+  epilogue_rows<CD, JB, 2, 2>(acc, p, W, m0, n0, wm, wn, lane, h);
+}
+
 template <int CD, int MODE, int DQ>
 __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) {
   // [A0 | A1 | B0 | B1 | levels]
@@ -680,7 +695,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the DMA bases scalar
   if (tid < 16) *(float*)(lds + LV_OFF + 4 * tid) = tab.lv[tid];
   int tm, tn, slice, rt;
-  item_of(p, tm, tn, slice, rt);
+  item_of(p, blockIdx.x, tm, tn, slice, rt);
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
   slice = __builtin_amdgcn_readfirstlane(slice);
@@ -856,23 +871,84 @@ __device__ __forceinline__ void dense_stage(f32x16_t (&acc)[4][JB], char* lds, i
   }
 }
 
-template <int CD, int MODE, int NW>
+// One item of the dense kernel: a whole tile, or slice `slice` of cut tile rt.
+struct DenseItem {
+  int tm, tn, slice, rt;
+  int64_t m0, n0;
+  uint32_t k0, nmain, n_st;
+  bool has_tail, dma_tail;
+};
+
+__device__ __forceinline__ DenseItem dense_item(const Big& p, int b) {
+  DenseItem it;
+  item_of(p, b, it.tm, it.tn, it.slice, it.rt);
+  // all four are uniform: keep them (and every address derived from them) scalar
+  it.tm = __builtin_amdgcn_readfirstlane(it.tm);
+  it.tn = __builtin_amdgcn_readfirstlane(it.tn);
+  it.slice = __builtin_amdgcn_readfirstlane(it.slice);
+  it.rt = __builtin_amdgcn_readfirstlane(it.rt);
+  it.m0 = (int64_t)it.tm * TILE;
+  it.n0 = (int64_t)it.tn * TILE;
+  // Stages: [k0, k1) of the main contraction (K1 is a multiple of 64 here; all of
+  // it for a whole tile, slice `slice` of split for a cut one), then, for a whole
+  // tile or the last slice, the low-rank tail: ceil(r_pad / 64) stages of [T | B]
+  // (fwd) or [dT | A] (dX), chunks past the valid columns read as zeros.
+  const uint32_t KT = (uint32_t)(p.K1 / BK);
+  uint32_t k0 = 0, k1 = KT;
+  if (it.rt >= 0) {
+    k0 = (uint32_t)it.slice * KT / (uint32_t)p.split;
+    k1 = (uint32_t)(it.slice + 1) * KT / (uint32_t)p.split;
+  }
+  it.k0 = k0;
+  it.nmain = k1 - k0;
+  it.has_tail = it.rt < 0 || it.slice == p.split - 1;
+  it.dma_tail = it.has_tail && p.b2_rows != nullptr;
+  it.n_st = it.nmain + (it.dma_tail ? (uint32_t)((p.r_pad + BK - 1) / BK) : 0u);
+  return it;
+}
+
+// The copies of stage u of item `it` (u >= nmain: the tail) for the lane that copies
+// rows row + 32 d, logical chunk c.
+__device__ __forceinline__ Copy dense_copy(const Big& p, const void* bd, const DenseItem& it, int row, int c,
+                                           uint32_t u) {
+  Copy cp;
+  if (__builtin_expect(u < it.nmain, 1)) {
+    cp.ra = make_rsrc(p.a1, p.M * p.ld_a1 * 2);
+    cp.rb = make_rsrc(bd, p.NB * p.K1 * 2);
+    cp.a_off = (uint32_t)(((it.m0 + row) * p.ld_a1 + 8 * c) * 2);
+    cp.b_off = (uint32_t)(((it.n0 + row) * p.K1 + 8 * c) * 2);
+    cp.a_step = (uint32_t)(32 * p.ld_a1 * 2);
+    cp.b_step = (uint32_t)(32 * p.K1 * 2);
+    cp.soff = (it.k0 + u) * (BK * 2);
+    return cp;
+  }
+  const uint32_t t0 = (u - it.nmain) * BK + 8 * c;  // first tail column of this lane's chunk
+  cp.ra = make_rsrc(p.a2, p.M * p.r_pad * 2);
+  cp.rb = make_rsrc(p.b2_rows, p.NB * p.ld_b2 * 2);
+  cp.a_off = oob_unless(t0 < (uint32_t)p.r_pad, (uint32_t)(((it.m0 + row) * p.r_pad + t0) * 2));
+  cp.b_off = oob_unless(t0 < (uint32_t)p.r_b2, (uint32_t)(((it.n0 + row) * p.ld_b2 + t0) * 2));
+  cp.a_step = (uint32_t)(32 * p.r_pad * 2);
+  cp.b_step = (uint32_t)(32 * p.ld_b2 * 2);
+  cp.soff = 0;
+  return cp;
+}
+
+// PERSIST (eight waves, tail by DMA, more items than workgroups): workgroup b takes
+// items b, b + G, b + 2 G, ... (G = gridDim.x), the assignment a launch of one
+// workgroup per item would make round by round.  After an item's last stage the
+// copying waves request the next item's first stage into buffer 0 before the
+// epilogue, which then stages its rows in two passes through buffers A1 / B1, so the
+// copies land while the stores go out.
+template <int CD, int MODE, int NW, bool PERSIST>
 __global__ __launch_bounds__(64 * NW, 1) void k_dense256(Big p, const void* bd) {
   // NW waves of 128 x 32 JB output blocks: 4 waves of 128 x 128 (one per SIMD) or 8 of
   // 128 x 64 (two per SIMD, so one wave's MFMAs can run while the other waits)
   constexpr int JB = 16 / NW, WNC = 8 / JB;  // WNC: waves along the tile's columns
+  static_assert(!PERSIST || NW == 8, "the persistent form is the eight-wave one");
   // [A0 | A1 | B0 | B1]
   __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int tm, tn, slice, rt;
-  item_of(p, tm, tn, slice, rt);
-  // all four are uniform: keep them (and every address derived from them) scalar
-  tm = __builtin_amdgcn_readfirstlane(tm);
-  tn = __builtin_amdgcn_readfirstlane(tn);
-  slice = __builtin_amdgcn_readfirstlane(slice);
-  rt = __builtin_amdgcn_readfirstlane(rt);
-  const int64_t m0 = (int64_t)tm * TILE, n0 = (int64_t)tn * TILE;
   const int wm = (wave / WNC) * 128, wn = (wave % WNC) * (32 * JB);
   const int h = lane >> 5;
   const int a_row = wm + (lane & 31), b_row = wn + (lane & 31);
@@ -882,91 +958,77 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dense256(Big p, const void* bd) 
   // as zeros
   const int row = 8 * (wave & 3) + (lane >> 3);
   const int c = (lane & 7) ^ swz(row);  // the logical chunk this lane's copies fetch
-  Copy main_cp;
-  main_cp.ra = make_rsrc(p.a1, p.M * p.ld_a1 * 2);
-  main_cp.rb = make_rsrc(bd, p.NB * p.K1 * 2);
-  main_cp.a_off = (uint32_t)(((m0 + row) * p.ld_a1 + 8 * c) * 2);
-  main_cp.b_off = (uint32_t)(((n0 + row) * p.K1 + 8 * c) * 2);
-  main_cp.a_step = (uint32_t)(32 * p.ld_a1 * 2);
-  main_cp.b_step = (uint32_t)(32 * p.K1 * 2);
+  const int items = p.full + p.rem * p.split;
 
-  f32x16_t acc[4][JB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < JB; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  // Stages: [k0, k1) of the main contraction (K1 is a multiple of 64 here; all of
-  // it for a whole tile, slice `slice` of split for a cut one), then, for a whole
-  // tile or the last slice, the low-rank tail: ceil(r_pad / 64) stages of [T | B]
-  // (fwd) or [dT | A] (dX), chunks past the valid columns read as zeros.
-  const uint32_t KT = (uint32_t)(p.K1 / BK);
-  uint32_t k0 = 0, k1 = KT;
-  if (rt >= 0) {
-    k0 = (uint32_t)slice * KT / (uint32_t)p.split;
-    k1 = (uint32_t)(slice + 1) * KT / (uint32_t)p.split;
-  }
-  const bool has_tail = rt < 0 || slice == p.split - 1;
-  const bool dma_tail = has_tail && p.b2_rows != nullptr;
-  const uint32_t nmain = k1 - k0;
-  const uint32_t n_st = nmain + (dma_tail ? (uint32_t)((p.r_pad + BK - 1) / BK) : 0u);
-  const rsrc_t ra2 = make_rsrc(p.a2, p.M * p.r_pad * 2);
-  const rsrc_t rb2 = make_rsrc(p.b2_rows, p.NB * p.ld_b2 * 2);
-  auto copy_of = [&](uint32_t u) {
-    if (u < nmain) {
-      Copy cp = main_cp;
-      cp.soff = (k0 + u) * (BK * 2);
-      return cp;
-    }
-    const uint32_t t0 = (u - nmain) * BK + 8 * c;  // first tail column of this lane's chunk
-    Copy cp;
-    cp.ra = ra2;
-    cp.rb = rb2;
-    cp.a_off = oob_unless(t0 < (uint32_t)p.r_pad, (uint32_t)(((m0 + row) * p.r_pad + t0) * 2));
-    cp.b_off = oob_unless(t0 < (uint32_t)p.r_b2, (uint32_t)(((n0 + row) * p.ld_b2 + t0) * 2));
-    cp.a_step = (uint32_t)(32 * p.r_pad * 2);
-    cp.b_step = (uint32_t)(32 * p.ld_b2 * 2);
-    cp.soff = 0;
-    return cp;
-  };
+  int b = blockIdx.x;
+  DenseItem it = dense_item(p, b);
   if (wave < 4) {
-    const Copy cp = copy_of(0);
+    const Copy cp = dense_copy(p, bd, it, row, c, 0);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       copy_one(cp, lds, lds + 2 * TILE_BYTES, wave, d, false);
       copy_one(cp, lds, lds + 2 * TILE_BYTES, wave, d, true);
     }
   }
-  uint32_t u = 0;
-  if (NW == 4 || wave < 4) {
-    for (; u + 1 < n_st; ++u) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of stage u and its fragment reads
-      barrier_only();
-      dense_stage<CD, 1>(acc, lds, u & 1, copy_of(u + 1), wave, a_row, b_row, xr, h);
-    }
-  } else {
-    for (; u + 1 < n_st; ++u) {
-      __builtin_amdgcn_s_waitcnt(0);  // its fragment reads (the other waves copy)
-      barrier_only();
-      dense_stage<CD, 0>(acc, lds, u & 1, main_cp, wave, a_row, b_row, xr, h);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  barrier_only();
-  dense_stage<CD, 0>(acc, lds, u & 1, main_cp, wave, a_row, b_row, xr, h);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  for (;;) {
+    f32x16_t acc[4][JB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // a tail whose W-side operand cannot be copied row by row (fwd with r % 8 != 0):
-  // the host takes the four-wave form for it
-  if constexpr (NW == 4) {
-    if (has_tail && !dma_tail)
-      lora_segment<CD, MODE, true>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
+    uint32_t u = 0;
+    const Copy main_cp = dense_copy(p, bd, it, row, c, 0);
+    if (NW == 4 || wave < 4) {
+      for (; u + 1 < it.n_st; ++u) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of stage u and its fragment reads
+        barrier_only();
+        dense_stage<CD, 1>(acc, lds, u & 1, dense_copy(p, bd, it, row, c, u + 1), wave, a_row, b_row, xr, h);
+      }
+    } else {
+      for (; u + 1 < it.n_st; ++u) {
+        __builtin_amdgcn_s_waitcnt(0);  // its fragment reads (the other waves copy)
+        barrier_only();
+        dense_stage<CD, 0>(acc, lds, u & 1, main_cp, wave, a_row, b_row, xr, h);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier_only();
+    dense_stage<CD, 0>(acc, lds, u & 1, main_cp, wave, a_row, b_row, xr, h);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every wave is past the last stage's reads: the LDS is free
+
+    // a tail whose W-side operand cannot be copied row by row (fwd with r % 8 != 0):
+    // the host takes the four-wave form for it
+    if constexpr (NW == 4) {
+      if (it.has_tail && !it.dma_tail)
+        lora_segment<CD, MODE, true>(acc, lds, p, it.m0, it.n0, tid, wave, lane, a_row, b_row, xr, h);
+    }
+    const int nb = b + (int)gridDim.x;
+    if (PERSIST && nb < items) {
+      const DenseItem nx = dense_item(p, nb);
+      if (wave < 4) {
+        const Copy cp = dense_copy(p, bd, nx, row, c, 0);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          copy_one(cp, lds, lds + 2 * TILE_BYTES, wave, d, false);
+          copy_one(cp, lds, lds + 2 * TILE_BYTES, wave, d, true);
+        }
+      }
+      // A1 for waves 0..3, B1 for waves 4..7: 8 JB KiB each
+      char* W = lds + (wave < 4 ? TILE_BYTES : 3 * TILE_BYTES) + (wave & 3) * (64 * 64 * JB);
+      if (it.rt < 0) epilogue_halves<CD>(acc, p, W, it.m0, it.n0, wm, wn, lane, h);
+      else store_partial(acc, p.part + ((size_t)it.rt * p.split + it.slice) * kTileAcc, wm, wn, lane);
+      b = nb;
+      it = nx;
+      continue;
+    }
+    if (it.rt < 0) epilogue_lds<CD>(acc, p, lds, it.m0, it.n0, wave, wm, wn, lane, h);
+    else store_partial(acc, p.part + ((size_t)it.rt * p.split + it.slice) * kTileAcc, wm, wn, lane);
+    break;
   }
-  if (rt < 0) epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
-  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
 }
 
 
@@ -1079,7 +1141,7 @@ __global__ __launch_bounds__(8 * 64, 1) void k_fused8(Big p, Nf4Tables tab) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid < 16) *(float*)(lds + LV_OFF + 4 * tid) = tab.lv[tid];
   int tm, tn, slice, rt;
-  item_of(p, tm, tn, slice, rt);
+  item_of(p, blockIdx.x, tm, tn, slice, rt);
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
   slice = __builtin_amdgcn_readfirstlane(slice);
@@ -1259,11 +1321,15 @@ template <int CD, int MODE>
 int run_dense(const Big& b, const void* bd, hipStream_t s, int kind) {
   const int64_t items = (int64_t)b.full + (int64_t)b.rem * b.split;
   ProfScope prof(kind, s);
-  // eight waves (two per SIMD) unless the low-rank tail cannot be copied row by row
-  if (b.b2_rows)
-    k_dense256<CD, MODE, 8><<<dim3((unsigned)items), dim3(8 * 64), 0, s>>>(b, bd);
+  // eight waves (two per SIMD) unless the low-rank tail cannot be copied row by row;
+  // more items than CUs: one persistent workgroup per CU
+  const int64_t cus = cu_count();
+  if (b.b2_rows && items > cus)
+    k_dense256<CD, MODE, 8, true><<<dim3((unsigned)cus), dim3(8 * 64), 0, s>>>(b, bd);
+  else if (b.b2_rows)
+    k_dense256<CD, MODE, 8, false><<<dim3((unsigned)items), dim3(8 * 64), 0, s>>>(b, bd);
   else
-    k_dense256<CD, MODE, 4><<<dim3((unsigned)items), dim3(4 * 64), 0, s>>>(b, bd);
+    k_dense256<CD, MODE, 4, false><<<dim3((unsigned)items), dim3(4 * 64), 0, s>>>(b, bd);
   int rc = check_launch(MODE == MODE_FWD ? "k_dense256<fwd>" : "k_dense256<dx>");
   if (rc || !b.rem) return rc;
   return b.split == 2 ? launch_split_sum<CD, 2>(b, s) : launch_split_sum<CD, 4>(b, s);
