@@ -110,3 +110,43 @@ def test_split_repeats_bit_identical_on_stale_workspace(path):
     o = oracle_layer(L)
     assert_close(to_np(ys[0]), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"]), L.cd, "fwd")
     assert_close(to_np(dxs[0]), oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"])[0], L.cd, "dX")
+
+
+@pytest.mark.parametrize("path", ["dequant", "fused"])
+def test_persistent_dense_more_items_than_cus(path):
+    """More items (whole tiles + slices of the cut ones) than CUs: the dense kernel runs
+    one persistent workgroup per CU that takes items b, b + C, ... and requests the
+    next item's first stage before the current epilogue.  Ragged M (the second tile row
+    has 8 rows), a cut last round, a bias; forward (2 x 150 tiles) and dX (2 x 150 tiles
+    of [M, K]) compared element by element, outputs NaN-filled before the call."""
+    C = torch.cuda.get_device_properties(0).multi_processor_count
+    M, r = 264, 16
+    Nf, Kf = 256 * (C // 2 + 22), 512        # forward: 2 x (C/2 + 22) tiles, contraction 8 stages
+    F, R, S = expected_split(M, Nf, Kf)
+    assert F + R * S > C and R > 0, (F, R, S)
+    L = inputs.random_layer(M, Nf, Kf, r, seed=97, cd="bf16", with_bias=True, with_dy=False)
+    say("persistent fwd", path, M, Nf, Kf, "items", F + R * S)
+    g = to_gpu(L)
+    q = gpu_q(L, g)
+    y = torch.full((M, Nf), float("nan"), dtype=torch.bfloat16, device="cuda")
+    qn.linear_fwd(q, g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], path=path, out=y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()), "unwritten forward outputs"
+    o = oracle_layer(L)
+    assert_close(to_np(y), oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"]), "bf16", "persistent fwd")
+    del y, g, q
+    # dX [M, Kd]: 2 x (C / 2 + 22) tiles over a contraction of 512 W rows
+    Nd, Kd = 512, 256 * (C // 2 + 22)
+    F, R, S = expected_split(M, Kd, Nd)
+    assert F + R * S > C and R > 0, (F, R, S)
+    L = inputs.random_layer(M, Nd, Kd, r, seed=98, cd="bf16")
+    say("persistent dX", path, M, Nd, Kd, "items", F + R * S)
+    g = to_gpu(L)
+    q = gpu_q(L, g)
+    dx = torch.full((M, Kd), float("nan"), dtype=torch.bfloat16, device="cuda")
+    qn.linear_bwd(q, g["x"], g["dY"], g["A"], g["B"], L.alpha, path=path, dx_out=dx)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(dx).all()), "unwritten dX outputs"
+    o = oracle_layer(L)
+    assert_close(to_np(dx), oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"], want=("dx",))[0],
+                 "bf16", "persistent dX")
