@@ -579,9 +579,9 @@ __global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
   const int rt = blockIdx.y;
   const int idx = blockIdx.x * kThreads + threadIdx.x;
   const float* src = p.part + (size_t)rt * S * kTileAcc + 4 * idx;
-  f32x4_t v[S];
+  f32x4_t v[S];  // the partial sums are dead after this read, the output is not read again: both non-temporal
 #pragma unroll
-  for (int s = 0; s < S; ++s) v[s] = *(const f32x4_t*)(src + (size_t)s * kTileAcc);
+  for (int s = 0; s < S; ++s) v[s] = __builtin_nontemporal_load((const f32x4_t*)(src + (size_t)s * kTileAcc));
   f32x4_t t = v[0];
 #pragma unroll
   for (int s = 1; s < S; ++s) t = t + v[s];
@@ -595,7 +595,8 @@ __global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
   for (int e = 0; e < 4; ++e) o[e] = t[e] + (p.bias ? load_cd<CD>(p.bias, col + e < p.NB ? col + e : 0) : 0.f);
   uint16_t* dst = (uint16_t*)p.out + row * p.NB + col;
   if ((p.NB & 3) == 0 && col + 4 <= p.NB) {
-    *(uint2*)dst = make_uint2(pack2<CD>(o[0], o[1]), pack2<CD>(o[2], o[3]));
+    const u32x2_t w2 = {pack2<CD>(o[0], o[1]), pack2<CD>(o[2], o[3])};
+    __builtin_nontemporal_store(w2, (u32x2_t*)dst);
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
