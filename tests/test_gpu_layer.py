@@ -146,6 +146,55 @@ def test_forward_medium_token_counts(m, N, K, r, bias):
     assert oracle.rel_l2(to_np(t0).astype(np.float64), ref_t0) <= 1e-5, "medium T0"
 
 
+@pytest.mark.parametrize("m,N,K,r,bias", [
+    (65, 320, 1024, 16, True),     # one past the split-K GEMV's range: the fused kernel
+    (512, 1024, 2048, 64, False),  # 512 tokens, one GPU's share of a data-parallel x8 step
+    (768, 640, 1024, 8, True),     # the last count the fused kernel takes without a path flag
+    (769, 640, 1024, 8, True),     # the first past it: dequantize-then-GEMM
+    (700, 512, 1024, 12, False),   # rank not a multiple of 8: dequantize-then-GEMM
+])
+def test_forward_default_route_65_to_768(m, N, K, r, bias):
+    """65 to 768 tokens without a path flag: the fused forward when r is a multiple of 8,
+    dequantize-then-GEMM otherwise and above; every element against the oracle, and
+    the forced dequantize-then-GEMM path within the same tolerance."""
+    L = inputs.random_layer(m, N, K, r, seed=5 * m + N + r, cd="bf16", with_bias=bias, with_dy=False)
+    say("fwd default route m", m, N, K, r, bias)
+    g = to_gpu(L)
+    q = gpu_q(L, g)
+    y = torch.full((m, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    qn.linear_fwd(q, g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], out=y)
+    yd = qn.linear_fwd(q, g["x"], g["A"], g["B"], L.alpha, bias=g["bias"], path="dequant")
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()), "unwritten outputs"
+    o = oracle_layer(L)
+    ref = oracle.forward(o["x"], o["W"], o["A"], o["B"], o["s"], o["bias"])
+    assert_close(to_np(y), ref, "bf16", "default route y")
+    assert_close(to_np(yd), ref, "bf16", "dequant y")
+
+
+def test_forward_512_tokens_gate_shape():
+    """The gate projection's shape (14336 x 4096, r 64) at 512 tokens on the default
+    route (the fused kernel: 2 x 56 tiles cut into 2 slices): outputs NaN-filled and all
+    finite, whole rows compared for one row in every band of 32 and both edge rows of
+    each 256-row tile."""
+    m, N, K, r = 512, 14336, 4096, 64
+    L = inputs.random_layer(m, N, K, r, seed=512, cd="bf16", with_bias=False, with_dy=False)
+    say("fwd 512 tokens gate shape")
+    g = to_gpu(L)
+    q = gpu_q(L, g)
+    y = torch.full((m, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    qn.linear_fwd(q, g["x"], g["A"], g["B"], L.alpha, out=y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()), "unwritten outputs"
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([np.arange(0, m, 32) + rng.integers(0, 32, m // 32),
+                                     np.arange(0, m, 256), np.arange(255, m, 256)]))
+    o = oracle_layer(L)
+    xs = np.ascontiguousarray(np.asarray(o["x"])[rows])
+    ref = oracle.forward(xs, o["W"], o["A"], o["B"], o["s"], None)
+    assert_close(to_np(y[torch.from_numpy(rows).cuda()]), ref, "bf16", "gate shape at 512 tokens")
+
+
 def test_forward_save_t_and_leading_dims():
     L = inputs.random_layer(60, 128, 256, 8, seed=3, with_dy=False)
     say("fwd save_t")
