@@ -423,11 +423,11 @@ inline int64_t al(int64_t b) { return round_up(b, kAlign); }
 // Whether a call takes the dequantize-then-GEMM path, from its shape and flags
 // alone (the workspace query must agree with the launch).  The launch also needs
 // dense256_ok; when that fails the copy's workspace is simply unused.  Unless a
-// path flag decides, every call the GEMV does not take goes this way: with each
-// weight read from HBM, writing W~ once and running the dense GEMM was as fast as
-// the fused kernels or faster at every token count from 32 to 4096 (q_proj and
-// gate_proj shapes, r 64, bf16); the fused kernels need no rows x cols copy in the
-// workspace, which is their reason to exist.
+// path flag decides, every call above the fused forward's range (below) that the
+// GEMV does not take goes this way: with each weight read from HBM, writing W~ once
+// and running the dense GEMM is as fast as the fused kernels or faster from 1024
+// tokens up (q_proj and gate_proj shapes, r 64, bf16); the fused kernels also need
+// no rows x cols copy in the workspace.
 // Internal plan flag: W~ comes from the caller (cached-dequant forward), so the
 // workspace holds no copy of it.
 constexpr int32_t kFlagCachedW = 1 << 20;
@@ -435,8 +435,8 @@ constexpr int32_t kFlagCachedW = 1 << 20;
 // Forward calls of at most this many tokens with no path flag take the fused kernel
 // when its eight-wave form applies (rank a multiple of 8): there, decoding each W
 // tile once per 256 tokens costs less than writing W~ and reading it back (q + gate
-// forward at 128 / 256 / 512 tokens: 0.111 / 0.121 / 0.156 ms fused against
-// 0.125 / 0.139 / 0.163 ms; at 1024 tokens 0.211 against 0.205).
+// forward at 128 / 256 / 512 tokens: 0.095 / 0.109 / 0.150 ms fused against
+// 0.112 / 0.135 / 0.158 ms; at 1024 tokens 0.201 against 0.198).
 constexpr int64_t kFusedFwdMaxM = 768;
 
 bool dense_path(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags, bool dx) {

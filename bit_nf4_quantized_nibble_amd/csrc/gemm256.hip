@@ -555,19 +555,23 @@ __device__ __forceinline__ f32x4_t acc4(const f32x16_t& a, int q) {
 // Partial sums of a cut tile's slice, fp32 [256][256] row-major: the wave's
 // (transposed) block (i, j) gives row wm + 32 i + lane % 32 the four columns
 // wn + 32 j + 8 q + 4 (lane / 32) .. + 3 from elements 4 q .. 4 q + 3 (one 16-byte
-// store; lanes l and l + 32 fill 32 contiguous bytes of a row).
+// store; lanes l and l + 32 fill 32 contiguous bytes of a row).  Rows from
+// `rows` on (past the last token) are not stored: the slice sum skips them.
 template <int JB>
-__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[4][JB], float* dst, int wm, int wn, int lane) {
+__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[4][JB], float* dst, int wm, int wn, int lane,
+                                              int64_t rows) {
   const rsrc_t r = make_rsrc(dst, kTileAcc * 4);
   const uint32_t base = (uint32_t)(((wm + (lane & 31)) * TILE + wn + 4 * (lane >> 5)) * 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t off = oob_unless(wm + 32 * i + (lane & 31) < rows, base);
 #pragma unroll
     for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc4(acc[i][j], q)), r, (int)base,
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc4(acc[i][j], q)), r, (int)off,
                                                (32 * i * TILE + 32 * j + 8 * q) * 4, 0);
+  }
 }
 
 // The cut tiles' outputs: thread (b, t) of cut tile rt sums the four columns
@@ -578,6 +582,11 @@ template <int CD, int S>
 __global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
   const int rt = blockIdx.y;
   const int idx = blockIdx.x * kThreads + threadIdx.x;
+  int tm, tn;
+  grouped_tile(p, p.full + rt, tm, tn);
+  const int64_t row = (int64_t)tm * TILE + (4 * idx) / TILE;
+  const int64_t col = (int64_t)tn * TILE + (4 * idx) % TILE;
+  if (row >= p.M) return;  // a row past the last token (its partial sums were not stored)
   const float* src = p.part + (size_t)rt * S * kTileAcc + 4 * idx;
   f32x4_t v[S];  // the partial sums are dead after this read, the output is not read again: both non-temporal
 #pragma unroll
@@ -585,11 +594,6 @@ __global__ __launch_bounds__(kThreads) void k_split_sum(Big p) {
   f32x4_t t = v[0];
 #pragma unroll
   for (int s = 1; s < S; ++s) t = t + v[s];
-  int tm, tn;
-  grouped_tile(p, p.full + rt, tm, tn);
-  const int64_t row = (int64_t)tm * TILE + (4 * idx) / TILE;
-  const int64_t col = (int64_t)tn * TILE + (4 * idx) % TILE;
-  if (row >= p.M) return;
   float o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) o[e] = t[e] + (p.bias ? load_cd<CD>(p.bias, col + e < p.NB ? col + e : 0) : 0.f);
@@ -802,7 +806,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused256(Big p, Nf4Tables tab) 
   if (rt < 0 || slice == p.split - 1)
     lora_segment<CD, MODE, true>(acc, lds, p, m0, n0, tid, wave, lane, a_row, b_row, xr, h);
   if (rt < 0) epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
-  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
+  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane, p.M - m0);
 }
 
 
@@ -1024,13 +1028,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dense256(Big p, const void* bd) 
       // A1 for waves 0..3, B1 for waves 4..7: 8 JB KiB each
       char* W = lds + (wave < 4 ? TILE_BYTES : 3 * TILE_BYTES) + (wave & 3) * (64 * 64 * JB);
       if (it.rt < 0) epilogue_halves<CD>(acc, p, W, it.m0, it.n0, wm, wn, lane, h);
-      else store_partial(acc, p.part + ((size_t)it.rt * p.split + it.slice) * kTileAcc, wm, wn, lane);
+      else store_partial(acc, p.part + ((size_t)it.rt * p.split + it.slice) * kTileAcc, wm, wn, lane, p.M - it.m0);
       b = nb;
       it = nx;
       continue;
     }
     if (it.rt < 0) epilogue_lds<CD>(acc, p, lds, it.m0, it.n0, wave, wm, wn, lane, h);
-    else store_partial(acc, p.part + ((size_t)it.rt * p.split + it.slice) * kTileAcc, wm, wn, lane);
+    else store_partial(acc, p.part + ((size_t)it.rt * p.split + it.slice) * kTileAcc, wm, wn, lane, p.M - it.m0);
     break;
   }
 }
@@ -1292,11 +1296,13 @@ __global__ __launch_bounds__(8 * 64, 1) void k_fused8(Big p, Nf4Tables tab) {
   __syncthreads();
 
   if (rt < 0) epilogue_lds<CD>(acc, p, lds, m0, n0, wave, wm, wn, lane, h);
-  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane);
+  else store_partial(acc, p.part + ((size_t)rt * p.split + slice) * kTileAcc, wm, wn, lane, p.M - m0);
 }
 
 template <int CD, int S>
 int launch_split_sum(const Big& b, hipStream_t s);
+template <int CD>
+int sum_slices(const Big& b, hipStream_t s);
 
 // The fused GEMM, and for a cut last round the sum of its slices (one profiling
 // scope: together they are the GEMM).
@@ -1316,7 +1322,7 @@ int run(const Big& b, hipStream_t s, int kind) {
   }
   int rc = check_launch(MODE == MODE_FWD ? "k_fused256<fwd>" : "k_fused256<dx>");
   if (rc || !b.rem) return rc;
-  return b.split == 2 ? launch_split_sum<CD, 2>(b, s) : launch_split_sum<CD, 4>(b, s);
+  return sum_slices<CD>(b, s);
 }
 
 // The dense GEMM, and for a cut last round the sum of its slices (both inside one
@@ -1336,7 +1342,7 @@ int run_dense(const Big& b, const void* bd, hipStream_t s, int kind) {
     k_dense256<CD, MODE, 4, false><<<dim3((unsigned)items), dim3(4 * 64), 0, s>>>(b, bd);
   int rc = check_launch(MODE == MODE_FWD ? "k_dense256<fwd>" : "k_dense256<dx>");
   if (rc || !b.rem) return rc;
-  return b.split == 2 ? launch_split_sum<CD, 2>(b, s) : launch_split_sum<CD, 4>(b, s);
+  return sum_slices<CD>(b, s);
 }
 
 template <int CD, int S>
@@ -1344,6 +1350,16 @@ int launch_split_sum(const Big& b, hipStream_t s) {
   const dim3 g(kTileAcc / (4 * kThreads), (unsigned)b.rem);
   k_split_sum<CD, S><<<g, dim3(kThreads), 0, s>>>(b);
   return check_launch("k_split_sum");
+}
+
+template <int CD>
+int sum_slices(const Big& b, hipStream_t s) {
+  switch (b.split) {
+    case 2: return launch_split_sum<CD, 2>(b, s);
+    case 4: return launch_split_sum<CD, 4>(b, s);
+    case 8: return launch_split_sum<CD, 8>(b, s);
+  }
+  return set_error(QLORA_ERR_UNSUPPORTED, "split sum: %d slices", b.split);
 }
 
 void set_split(Big& b, const DenseSplit& sp, void* split_ws) {
@@ -1425,8 +1441,11 @@ int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r
 
 // One round is a tile per compute unit (the kernel needs most of a CU's LDS).  When
 // the last round is incomplete, its rem tiles are cut into split = 2 or 4
-// contraction slices (the largest that keeps rem * split within one round and at
-// least 4 stages per slice), so the round's workgroups run about 1 / split as long.
+// contraction slices, 8 when all the tokens fit one tile row (the largest that
+// keeps rem * split within one round and at least 4 stages per slice), so the
+// round's workgroups run about 1 / split as long.  (Measured on q + gate forwards:
+// 8 slices took 128 and 256 tokens from 0.111 / 0.119 to 0.096 / 0.111 ms; at 512
+// tokens the doubled partial sums cost the dequantize-then-GEMM path 6%.)
 DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1) {
   const int64_t C = cu_count();
   const int64_t tiles = ceil_div(m, TILE) * ceil_div(nb, TILE);
@@ -1434,7 +1453,9 @@ DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1) {
   const int64_t F = tiles / C, R = tiles - F * C;
   if (R == 0) return d;
   const int64_t cap = std::min<int64_t>(C / R, (k1 / BK) / 4);
-  const int32_t S = cap >= 4 ? 4 : (cap >= 2 ? 2 : 1);
+  const int32_t smax = m <= TILE ? 8 : 4;
+  int32_t S = 1;
+  while (S < smax && 2 * S <= cap) S *= 2;
   if (S == 1) return d;
   d.full = (int32_t)(F * C);
   d.rem = (int32_t)R;

@@ -32,7 +32,9 @@ def expected_split(M, NB, K1):
     if R == 0:
         return T, 0, 1
     cap = min(C // R, (K1 // 64) // 4)
-    S = 4 if cap >= 4 else (2 if cap >= 2 else 1)
+    S = 1
+    while S < (8 if M <= 256 else 4) and 2 * S <= cap:
+        S *= 2
     return (T, 0, 1) if S == 1 else (F * C, R, S)
 
 
@@ -46,6 +48,9 @@ def gpu_q(L, g):
     (300, 260, 1024, 16, True, 4),   # 2 x 2 tiles, both ragged, 16 stages -> 4 slices of 4
     (520, 200, 512, 24, False, 2),   # 3 x 1 tiles, 8 stages -> 2 slices
     (257, 64, 1280, 5, True, 4),     # a one-row ragged tile row, odd rank, 20 stages -> 5 per slice
+    (300, 1024, 2048, 8, True, 4),   # 2 x 4 tiles, 32 stages, two tile rows -> 4 slices of 8
+    (200, 1024, 2048, 8, True, 8),   # 1 x 4 tiles, 32 stages, one tile row -> 8 slices of 4
+    (256, 512, 4096, 16, False, 8),  # 1 x 2 tiles, 64 stages -> 8 slices of 8
 ])
 def test_split_forward_every_element(path, cd, M, N, K, r, bias, S):
     assert expected_split(M, N, K)[2] == S
@@ -64,6 +69,7 @@ def test_split_forward_every_element(path, cd, M, N, K, r, bias, S):
 @pytest.mark.parametrize("M,N,K,r,S", [
     (300, 1024, 320, 16, 4),  # dX [300, 320]: 2 x 2 tiles, contraction 1024 -> 4 slices
     (200, 512, 256, 8, 2),    # dX one tile, contraction 512 -> 2 slices
+    (130, 2048, 512, 16, 8),  # dX [130, 512]: 1 x 2 tiles, contraction 2048 -> 8 slices
 ])
 def test_split_backward_dx_every_element(path, cd, M, N, K, r, S):
     assert expected_split(M, K, N)[2] == S
