@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kMergeThreads) __attribute__((amdgpu_waves_per_eu(4
       o[1] = pack2<CD>(f[2], f[3]);
       o[2] = pack2<CD>(f[4], f[5]);
       o[3] = pack2<CD>(f[6], f[7]);
-      *(u32x4_t*)(orow + j * 16 * w.cols) = o;
+      __builtin_nontemporal_store(o, (u32x4_t*)(orow + j * 16 * w.cols));  // not read again here: keep A, B cached
     }
     if (next >= p.ntiles) break;
     fetch_codes<DQ>(p, R, next, tid, C);
