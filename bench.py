@@ -674,10 +674,23 @@ def measured_traffic():
 
 
 def bench_quant(qn, torch, inputs, copies=5, iters=20):
+    """Quantize and dequantize of a 4096 x 4096 weight, cycling through `copies` copies
+    (more bytes than the last-level cache).  `us`: `iters` back-to-back calls between one
+    event pair on the stream, per call; `us_event_pairs`: the same calls with the
+    library's event pair around each one (which adds the pair's own cost)."""
     W0 = inputs.roundtrip_weight(0).to("cuda")
     n = W0.numel()
     Ws = [W0.clone() for _ in range(copies)]
     out = {}
+
+    def stream_us(call):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
     for dq in (False, True):
         qs = [qn.empty_nf4(4096, 4096, 64, dq, 256) for _ in range(copies)]
         ds = [q.descriptor() for q in qs]
@@ -686,20 +699,25 @@ def bench_quant(qn, torch, inputs, copies=5, iters=20):
         for i in range(copies):
             lib.qlora_nf4_quantize(Ws[i].data_ptr(), ctypes.byref(ds[i]), stream)
         torch.cuda.synchronize()
-        qn.profile_enable(True)
-        for i in range(iters):
+
+        def quant(i):
             rc = lib.qlora_nf4_quantize(Ws[i % copies].data_ptr(), ctypes.byref(ds[i % copies]), stream)
             if rc:
                 raise RuntimeError("quantize rc %d" % rc)
+
+        us = stream_us(quant)
+        qn.profile_enable(True)
+        for i in range(iters):
+            quant(i)
         torch.cuda.synchronize()
         ms, k = qn.profile_read()["quantize"]
         qn.profile_enable(False)
         nb = n // 64
         byts = n * 4 + n // 2 + (nb + (nb + 255) // 256 * 4 if dq else nb * 4)
-        us = ms / k * 1e3
         gbs = byts / (us * 1e-6) / 1e9
         out["dq" if dq else "no_dq"] = {"us": round(us, 2), "bytes": byts, "gbs": round(gbs, 1),
-                                        "frac": round(gbs / PEAK_HBM_GBS, 4)}
+                                        "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                        "us_event_pairs": round(ms / k * 1e3, 2)}
         if dq:
             for name, dt, ob in (("bf16", torch.bfloat16, 2), ("f32", torch.float32, 4)):
                 outs = [torch.empty(4096, 4096, dtype=dt, device="cuda") for _ in range(copies)]
@@ -707,20 +725,25 @@ def bench_quant(qn, torch, inputs, copies=5, iters=20):
                 for i in range(copies):
                     lib.qlora_nf4_dequantize(ctypes.byref(ds[i]), code, outs[i].data_ptr(), stream)
                 torch.cuda.synchronize()
-                qn.profile_enable(True)
-                for i in range(iters):
+
+                def dequant(i):
                     rc = lib.qlora_nf4_dequantize(ctypes.byref(ds[i % copies]), code, outs[i % copies].data_ptr(),
                                                   stream)
                     if rc:
                         raise RuntimeError("dequantize rc %d" % rc)
+
+                us = stream_us(dequant)
+                qn.profile_enable(True)
+                for i in range(iters):
+                    dequant(i)
                 torch.cuda.synchronize()
                 ms, k = qn.profile_read()["dequantize"]
                 qn.profile_enable(False)
                 byts = n // 2 + nb + (nb + 255) // 256 * 4 + n * ob
-                us = ms / k * 1e3
                 gbs = byts / (us * 1e-6) / 1e9
                 out["dequant_dq_to_" + name] = {"us": round(us, 2), "bytes": byts, "gbs": round(gbs, 1),
-                                                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+                                                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                                "us_event_pairs": round(ms / k * 1e3, 2)}
                 del outs
         del qs
     del Ws, W0
