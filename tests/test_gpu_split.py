@@ -1,12 +1,12 @@
 """GPU parity of the 256 x 256 GEMMs (dequantize-then-GEMM and fused NF4 decode)
-when the tiles of an incomplete last round are cut into contraction slices (two or
-four per tile, whose fp32 partial sums a second launch adds in slice order),
-against the fp64 oracle through the C ABI.
+when the tiles of an incomplete last round are cut into contraction slices (two,
+four or eight per tile, whose fp32 partial sums a second launch adds in slice
+order), against the fp64 oracle through the C ABI.
 
 One round is one tile per compute unit.  A GEMM with T tiles on C units takes
 floor(T / C) whole rounds; the R = T mod C tiles left over are cut into the
-largest S in {2, 4} with R * S <= C and at least 4 contraction stages of 64 per
-slice.  Small cases compare every element (ragged M and N, a bias, the low-rank
+largest S in {2, 4} (in {2, 4, 8} when all rows fit one 256-row tile row) with
+R * S <= C and at least 4 contraction stages of 64 per slice.  Small cases compare every element (ragged M and N, a bias, the low-rank
 tail on the last slice); the full projection sizes whose tile counts leave an
 incomplete round (gate / up forward, down dX: 16 x 56 tiles) are covered tile by
 tile in test_gpu_fullsize.py.  Repeats on a workspace full of stale bytes and outputs filled with NaN
