@@ -5,12 +5,13 @@ Headline: the training step of the seven projections of one Llama-3-8B-shaped
 block (q/o 4096x4096, k/v 1024x4096, gate/up 14336x4096, down 4096x14336; NF4 block
 64 with double quantization; 4096 tokens; LoRA r = 64, alpha = 128; bf16 compute):
 one step = the forward of all seven projections followed by their backward (dX,
-dA, dB), each call on the library's default path (at 4096 tokens: W~ dequantized
-into the workspace, then the dense MFMA GEMM).  value = algorithmic TFLOP/s of
-that step (dequantization is not credited).  The same step forced onto the fused
-dequant-GEMM kernels (QLORA_FLAG_FUSED) is reported beside it, and the step with the
-projections that read the same x (q / k / v, gate / up) forwarded as one
-qlora_linear_fwd_group call each (grouped_forward_step).
+dA, dB).  The projections that read the same x (q / k / v, gate / up) are forwarded
+as one qlora_linear_fwd_group call each, as a transformer block calls them; o, down
+and every backward are per-projection calls; all on the library's default path (at
+4096 tokens: W~ dequantized into the workspace, then the dense MFMA GEMM).  value =
+algorithmic TFLOP/s of that step (dequantization is not credited).  Beside it: the
+same step with every projection a call of its own (per_projection_step), and forced
+onto the fused dequant-GEMM kernels (QLORA_FLAG_FUSED, fused_path_step).
 
 Also reported on the same line, each against its own MI355X roofline:
   gemv      decode forward at m = 1, 4, 16 (4096x4096, r = 16), GB/s over cold weights
@@ -262,7 +263,8 @@ def bench_step(args, qn, torch, lib, inputs, flags=0, hashes=None, grouped=False
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic() if (dom == "fwd_gemm" and flags == 0 and not grouped) else None,
+                "traffic": (measured_traffic(dom, "grouped" if grouped == "fwd" else "per_projection")
+                            if flags == 0 and grouped in (False, "fwd") else None),
                 "avg_launch_ms": round(dom_ms, 4), "flops_per_launch": dom_flops}
     result = dict(sec=sec, flops=flops, kernels=kernels, roofline=roofline, step_ms=percentiles(step_ms),
                   fwd_ms=sum(kernels.get(k, {}).get("ms_per_step", 0) for k in ("fwd_gemm", "lora_down")),
@@ -642,7 +644,13 @@ def copy_probe(torch, mib=512, iters=10):
             "gbs": round(2 * (mib << 20) / (us * 1e-6) / 1e9, 1)}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense256_fwd_hbm_traffic_llama3_8b_block.md")
+# Counter records of HBM traffic per launch (calibrated FETCH_SIZE + WRITE_SIZE):
+# the headline step's forward and dX GEMM launches, and the forward GEMM of the
+# per-projection step.
+TRAFFIC_FILES = {
+    "grouped": os.path.join(ROOT, "profiles", "dense256_hbm_traffic_llama3_8b_block_grouped_fwd_step.md"),
+    "per_projection": os.path.join(ROOT, "profiles", "dense256_fwd_hbm_traffic_llama3_8b_block.md"),
+}
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_nibble_amd", "csrc", f) for f in ("gemm256.hip", "common.h")]
 
 
@@ -655,20 +663,21 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter runs
-    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the kernel sources changed
+def measured_traffic(kind, step):
+    """HBM bytes per launch of kernel `kind` in `step` ("grouped" or
+    "per_projection") from the committed counter runs (calibrated FETCH_SIZE +
+    WRITE_SIZE), or None when there is no record or the kernel sources changed
     since the counters were taken."""
     try:
         vals = {}
-        with open(TRAFFIC_FILE) as fh:
+        with open(TRAFFIC_FILES[step]) as fh:
             for line in fh:
                 if line.startswith("traffic_") or line.startswith("kernel_source_hash"):
                     k, v = line.split(":", 1)
                     vals[k.strip()] = v.strip()
         if vals.get("kernel_source_hash") != kernel_source_hash():
             return None
-        return int(float(vals["traffic_bytes_per_launch"]))
+        return int(float(vals["traffic_%s_bytes_per_launch" % kind]))
     except (OSError, KeyError, ValueError):
         return None
 
@@ -788,7 +797,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "fusedstep", "groupstep", "groupfwdstep", "gemv", "quant", "sweep",
+    ap.add_argument("--only", choices=["step", "projstep", "fusedstep", "groupstep", "gemv", "quant", "sweep",
                                        "merge", "stack", "copyprobe", "paths"],
                     default=None,
                     help="run one part (for profiling); the JSON line needs the full run")
@@ -828,22 +837,22 @@ def main():
         print(json.dumps(bench_stack(qn, torch, inputs)))
         return
 
-    if args.only in ("fusedstep", "groupstep", "groupfwdstep"):
-        grouped = {"groupstep": "both", "groupfwdstep": "fwd"}.get(args.only, False)
+    if args.only in ("fusedstep", "groupstep", "projstep"):
+        grouped = "both" if args.only == "groupstep" else False
         st = bench_step(args, qn, torch, lib, inputs, flags=qn._lib.QLORA_FLAG_FUSED if args.only == "fusedstep" else 0,
                         grouped=grouped)
         print(json.dumps({"ms_per_step": st["sec"] * 1e3, "kernels": st["kernels"], "roofline": st["roofline"]}))
         return
     hashes = {} if args.only is None else None
-    st = bench_step(args, qn, torch, lib, inputs, hashes=hashes)
+    st = bench_step(args, qn, torch, lib, inputs, hashes=hashes, grouped="fwd")
     log("step %.3f ms" % (st["sec"] * 1e3))
     if args.only == "step":
         print(json.dumps({"ms_per_step": st["sec"] * 1e3, "kernels": st["kernels"], "roofline": st["roofline"]}))
         return
+    stp = bench_step(args, qn, torch, lib, inputs)
+    log("per-projection step %.3f ms" % (stp["sec"] * 1e3))
     stf = bench_step(args, qn, torch, lib, inputs, flags=qn._lib.QLORA_FLAG_FUSED)
     log("fused step %.3f ms" % (stf["sec"] * 1e3))
-    stg = bench_step(args, qn, torch, lib, inputs, grouped="fwd")
-    log("grouped-forward step %.3f ms" % (stg["sec"] * 1e3))
     gemv = bench_gemv(qn, torch, lib, inputs)
     log("gemv done")
     quant = bench_quant(qn, torch, inputs)
@@ -879,8 +888,8 @@ def main():
         "config": {"workload": "qlora_nf4_block_train_step_llama3_8b_shapes",
                    "tokens": 4096, "projections": [[n, N, K] for n, N, K in st["layers"]],
                    "r": 64, "alpha": 128, "block_size": 64, "double_quant": True, "dq_group": 256,
-                   "step": "forward of 7 projections + backward (dX, dA, dB), library default path "
-                           "(dequantize-then-GEMM at 4096 tokens)",
+                   "step": "forward of 7 projections (q/k/v and gate/up each one grouped call) + backward "
+                           "(dX, dA, dB) per projection, library default path (dequantize-then-GEMM at 4096 tokens)",
                    "flops_per_step": st["flops"], "parallelism": "single GPU"},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "step_ms_device": st["step_ms"],
@@ -891,11 +900,12 @@ def main():
                             "tflops": round(stf["flops"] / stf["sec"] / 1e12, 2),
                             "frac_bf16_peak": round(stf["flops"] / stf["sec"] / 1e12 / PEAK_BF16_TFLOPS, 4),
                             "roofline": stf["roofline"], "kernels": stf["kernels"]},
-        "grouped_forward_step": {"ms_per_step": round(stg["sec"] * 1e3, 4),
-                                 "tflops": round(stg["flops"] / stg["sec"] / 1e12, 2),
-                                 "frac_bf16_peak": round(stg["flops"] / stg["sec"] / 1e12 / PEAK_BF16_TFLOPS, 4),
-                                 "forward": "q/k/v and gate/up each one qlora_linear_fwd_group call",
-                                 "backward": "per projection", "kernels": stg["kernels"]},
+        "per_projection_step": {"ms_per_step": round(stp["sec"] * 1e3, 4),
+                                "tflops": round(stp["flops"] / stp["sec"] / 1e12, 2),
+                                "frac_bf16_peak": round(stp["flops"] / stp["sec"] / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                "forward": "each projection its own qlora_linear_fwd call",
+                                "backward": "per projection", "step_ms_device": stp["step_ms"],
+                                "roofline": stp["roofline"], "kernels": stp["kernels"]},
         "gemv": gemv,
         "quantize": quant,
         "dtype_sweep_forward": sweep,

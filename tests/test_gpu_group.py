@@ -125,3 +125,40 @@ def test_group_llama_qkv_full_size():
     # the same call again gives the same bits (the cut round's slices are summed in order)
     y2, _, dx2, _, _ = run_group(Ls, x, "bf16", False)
     assert torch.equal(y, y2) and torch.equal(dx, dx2)
+
+
+def test_group_llama_gate_up_forward_full_size():
+    """gate / up of the Llama-3-8B-shaped block at 4096 tokens, r 64, as one forward
+    call (the benchmark's MLP group): 1792 tiles of 256 x 256 over a 28672-wide
+    output, seven whole rounds on the persistent form; the output NaN-filled before
+    the call and whole rows compared in every band of 32 rows and at the edges of
+    every 256-row tile."""
+    Ls = inputs.prefill(cd="bf16", with_dy=False, projections=["gate_proj", "up_proj"])
+    say("group gate/up forward full size")
+    x = Ls[0].x
+    ops = []
+    for L in Ls:
+        qr = oracle.quantize(L.W.numpy(), L.block_size, L.double_quant, L.dq_group)
+        ops.append(dict(W=oracle.weight_operand(qr, "bf16"), A=oracle.operand(L.A, "bf16"),
+                        B=oracle.operand(L.B, "bf16"), s=L.alpha / L.r))
+    M, N = x.shape[0], sum(L.N for L in Ls)
+    rng = np.random.default_rng(11)
+    bands = np.arange(0, M, 32)
+    rows = np.unique(np.concatenate([bands + rng.integers(0, 32, bands.size),
+                                     np.arange(0, M, 256), np.arange(255, M, 256)]))
+    qs = [qn.quantize(L.W.cuda(), L.block_size, L.double_quant, L.dq_group) for L in Ls]
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    _, ts = qn.linear_fwd_group(qs, x.cuda(), [L.A.cuda() for L in Ls], [L.B.cuda() for L in Ls],
+                                [L.alpha for L in Ls], save_t=True, out=y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()), "unwritten or non-finite forward outputs"
+    xo = oracle.operand(x, "bf16")
+    xs = np.ascontiguousarray(xo[rows])
+    sel = torch.from_numpy(rows).cuda()
+    off = 0
+    for i, (L, o) in enumerate(zip(Ls, ops)):
+        got = to_np(y[sel, off:off + L.N])
+        assert_close(got, oracle.forward(xs, o["W"], o["A"], o["B"], o["s"], None), "bf16", "y[%d]" % i)
+        ref_t0 = xo.astype(np.float64) @ o["A"].astype(np.float64).T
+        assert oracle.rel_l2(to_np(ts[i]).astype(np.float64), ref_t0) <= 1e-5, "T0[%d]" % i
+        off += L.N
