@@ -383,19 +383,23 @@ __device__ __forceinline__ float scale_of(uint32_t qa, uint32_t s2) {
 // instruction covers contiguous memory across the wave.  All 8 chunks' codes and
 // scales are requested before the first is used; chunks past the end read past the
 // buffers (zeros) and store nothing.  Same values as k_dequantize.
-// Workgroups from nmain on run the reduction `red` instead (see reduce_dev.h).
+// The first gridDim.x - nmain workgroups run the reduction `red` instead (see
+// reduce_dev.h): placed ahead of the dequantize, their load latency overlaps it
+// instead of trailing the launch.
 template <int OUT, int DQ>
 __global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, void* __restrict__ out,
                                                              Nf4Tables tab, RedJobs red, uint32_t nmain) {
-  if (blockIdx.x >= nmain) {
-    skreduce_block<OUT == CD_F16 ? CD_F16 : CD_BF16>(red, blockIdx.x - nmain);
+  const uint32_t nred = gridDim.x - nmain;
+  if (blockIdx.x < nred) {
+    skreduce_block<OUT == CD_F16 ? CD_F16 : CD_BF16>(red, blockIdx.x);
     return;
   }
+  const uint32_t bx = blockIdx.x - nred;
   __shared__ float s_lv[16];
   if (threadIdx.x < 16) s_lv[threadIdx.x] = tab.lv[threadIdx.x];
   const rsrc_t rc = make_rsrc(q.codes, n / 2);
   const ScaleRsrc rs = make_scale_rsrc<DQ>(q, n >> q.bs_shift);
-  const int64_t ch0 = (int64_t)blockIdx.x * (kThreads * 8) + threadIdx.x;
+  const int64_t ch0 = (int64_t)bx * (kThreads * 8) + threadIdx.x;
   const int64_t nch = n / 8;
   uint32_t cw[8], qa[8], s2[8];
 #pragma unroll
@@ -441,15 +445,18 @@ __global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, 
 // double quantization a power-of-two group or one group), codes under 2 GiB
 // (checked by the caller).  Tiles past the last column load the first codes
 // (unused) and write nothing.
-// Workgroup b < gx * (rows / 64) takes slab (b % gx, b / gx); the ones from there
-// on run the reduction `red` instead (see reduce_dev.h).
+// The first gridDim.x - nmain workgroups run the reduction `red` (see
+// reduce_dev.h), ahead of the dequantize so that their latency overlaps it; the
+// workgroup b = blockIdx.x - (gridDim.x - nmain) after them takes slab (b % gx, b / gx).
 template <int OUT, int DQ, int T>
 __global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restrict__ out, int64_t ldo, Nf4Tables tab,
                                                            RedJobs red, uint32_t gx, uint32_t nmain) {
-  if (blockIdx.x >= nmain) {
-    skreduce_block<OUT>(red, blockIdx.x - nmain);
+  const uint32_t nred = gridDim.x - nmain;
+  if (blockIdx.x < nred) {
+    skreduce_block<OUT>(red, blockIdx.x);
     return;
   }
+  const uint32_t bx = blockIdx.x - nred;
   __shared__ float s_lv[16];
   __shared__ __attribute__((aligned(16))) uint16_t tile[T][64 * 64];  // [k][n] per tile
   const int tid = threadIdx.x;
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_t(Nf4W q, void* __restr
   const int64_t n = q.rows * q.cols;
   const rsrc_t rc = make_rsrc(q.codes, n / 2);
   const ScaleRsrc rs = make_scale_rsrc<DQ>(q, n >> q.bs_shift);
-  const int64_t n0 = (int64_t)(blockIdx.x / gx) * 64, kb = (int64_t)(blockIdx.x % gx) * (64 * T);
+  const int64_t n0 = (int64_t)(bx / gx) * 64, kb = (int64_t)(bx % gx) * (64 * T);
   const int nr = tid >> 2, kc = (tid & 3) * 16;
   uint32_t cw[T][2], qa[T][2], s2[T][2];
 #pragma unroll
@@ -517,17 +524,19 @@ constexpr int TS4 = 64 * 64 * 2 + 128;
 template <int OUT, int DQ>
 __global__ __launch_bounds__(kThreads) void k_dequantize_t4(Nf4W q, void* __restrict__ out, int64_t ldo,
                                                             Nf4Tables tab, RedJobs red, uint32_t gx, uint32_t nmain) {
-  if (blockIdx.x >= nmain) {
-    skreduce_block<OUT>(red, blockIdx.x - nmain);
+  const uint32_t nred = gridDim.x - nmain;  // the reduction's workgroups come first
+  if (blockIdx.x < nred) {
+    skreduce_block<OUT>(red, blockIdx.x);
     return;
   }
+  const uint32_t bx = blockIdx.x - nred;
   __shared__ __attribute__((aligned(16))) float2 s_pair[256];
   __shared__ __attribute__((aligned(16))) unsigned char tile[4 * TS4];
   const int tid = threadIdx.x;
   const int64_t n = q.rows * q.cols;
   const rsrc_t rc = make_rsrc(q.codes, n / 2);
   const ScaleRsrc rs = make_scale_rsrc<DQ>(q, n >> q.bs_shift);
-  const int64_t n0 = (int64_t)(blockIdx.x / gx) * 64, kb = (int64_t)(blockIdx.x % gx) * 256;
+  const int64_t n0 = (int64_t)(bx / gx) * 64, kb = (int64_t)(bx % gx) * 256;
   const int nr = tid >> 2, ca = tid & 3;
   u32x4_t cw[2];
   uint32_t qa[2], s2[2];
