@@ -269,6 +269,8 @@ struct SkSpec {
 struct TransposeSpec;
 int skinny_jobs(int cd, bool tn, const SkSpec& a, float* part, int* S_out, const SkSpec* b2, float* part2,
                 int* S2, hipStream_t s, int kind, const TransposeSpec* ride = nullptr);
+// n NT products (plain Bop form), up to four per launch; product i writes parts[i].
+int skinny_many(int cd, const SkSpec* specs, float* const* parts, int* S_out, int n, hipStream_t s, int kind);
 // The device form of one or two reductions (workgroups of kRedThreads threads, one
 // thread per element; job 1 takes the workgroups after job 0's nblk).
 constexpr int kRedThreads = 256;

@@ -119,11 +119,11 @@ bool tiled(const GroupCall& gc, bool dx) {
 }
 
 // Workspace plans.  Tiled forward: W~ [N][cols], T [m][RP], the block-diagonal B
-// [N][R8], one projection's rank-product partial sums at a time, the cut last
-// round's partial sums.
+// [N][R8], every projection's rank-product partial sums, the cut last round's
+// partial sums.
 struct GFwd {
   bool tiled;
-  int64_t wd, tcd, bd, part, split, single, tmp, total;
+  int64_t wd, tcd, bd, part, part_each, split, single, tmp, total;
   DenseSplit sp;
 };
 GFwd plan_gfwd(const GroupCall& gc) {
@@ -136,7 +136,8 @@ GFwd plan_gfwd(const GroupCall& gc) {
     P.wd = o; o += al(gc.N * K * es);
     P.tcd = o; o += al(m * gc.RP * es);
     P.bd = o; o += al(gc.N * gc.R8 * es);
-    P.part = o; o += al((int64_t)skinny_part_bytes(m, K));
+    P.part_each = al((int64_t)skinny_part_bytes(m, K));
+    P.part = o; o += gc.g * P.part_each;
     P.sp = dense_split(m, gc.N, K);
     P.split = o; o += al((int64_t)dense_split_bytes(P.sp));
   } else {
@@ -252,16 +253,30 @@ int launch_forward_group(const GroupCall& gc, const void* bias, void* y, float* 
     }
     return QLORA_OK;
   }
-  // T_i = s_i x A_i^T into its slice of T (the reduction rides on W_i's dequantize),
-  // W~_i into rows off_i .. of the concatenated W~
+  // T_i = s_i x A_i^T into its slice of T: the group's products in one launch (they
+  // read the same x), each reduction riding on W_i's dequantize, which writes W~_i
+  // into rows off_i .. of the concatenated W~
+  SkSpec specs[kGroupMax];
+  float* parts[kGroupMax];
+  int Ss[kGroupMax];
   for (int i = 0; i < gc.g; ++i) {
     const LayerCall& c = gc.c[i];
-    int S;
-    float* part = (float*)(w + P.part);
-    if ((rc = skinny(c.cd, false, c.x, K, m, c.lora_a, K, m, c.r, K, part, &S, s, QLORA_K_LORA_DOWN))) return rc;
+    specs[i].a = c.x;
+    specs[i].lda = K;
+    specs[i].arows = m;
+    specs[i].b = c.lora_a;
+    specs[i].ldb = K;
+    specs[i].P = m;
+    specs[i].R = c.r;
+    specs[i].Kc = K;
+    parts[i] = (float*)(w + P.part + i * P.part_each);
+  }
+  if ((rc = skinny_many(c0.cd, specs, parts, Ss, gc.g, s, QLORA_K_LORA_DOWN))) return rc;
+  for (int i = 0; i < gc.g; ++i) {
+    const LayerCall& c = gc.c[i];
     SkRed red;
-    red.part = part;
-    red.S = S;
+    red.part = parts[i];
+    red.S = Ss[i];
     red.P = m;
     red.R = c.r;
     red.out32 = t_save ? t_save[i] : nullptr;

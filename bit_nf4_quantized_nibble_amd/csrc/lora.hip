@@ -194,12 +194,13 @@ __global__ __launch_bounds__(kThreads) void k_transpose(TrJobs js) {
   transpose_tile<CD, SRC32>(js.j[w], blockIdx.x - (w ? js.j[0].tiles : 0), t);
 }
 
-// One launch carries one or two products (blockIdx.z picks the job; workgroups
+// One launch carries up to kSkJobs products (blockIdx.z picks the job; workgroups
 // outside a job's own grid leave at once) and optionally a transpose (plane z = nj
 // of the grid, its workgroups taking the tiles in turn).
+constexpr int kSkJobs = 4;
 struct SkP2 {
-  SkP j[2];
-  uint32_t nx[2], ny[2];
+  SkP j[kSkJobs];
+  uint32_t nx[kSkJobs], ny[kSkJobs];
   uint32_t nj;  // products
   TrJob tr;     // tr.tiles == 0: none
 };
@@ -426,6 +427,34 @@ int skinny_jobs(int cd, bool tn, const SkSpec& a, float* part, int* S_out, const
     else k_skinny<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(ps);
   }
   return check_launch("k_skinny");
+}
+
+// n NT products with the plain Bop form in as few launches as the job table allows
+// (projections of a group that read the same x: the products share their Aop tiles
+// in the caches and pay the launch once).
+int skinny_many(int cd, const SkSpec* specs, float* const* parts, int* S_out, int n, hipStream_t s, int kind) {
+  for (int first = 0; first < n; first += kSkJobs) {
+    SkP2 ps = {};
+    ps.nj = (uint32_t)std::min(kSkJobs, n - first);
+    uint32_t gx = 0, gy = 0;
+    for (uint32_t i = 0; i < ps.nj; ++i) {
+      const SkSpec& sp = specs[first + i];
+      if (sp.bt) return set_error(QLORA_ERR_UNSUPPORTED, "rank product: grouped jobs take the plain Bop form");
+      int rc = skinny_params(false, sp, parts[first + i], ps.j[i], &S_out[first + i]);
+      if (rc) return rc;
+      ps.nx[i] = (uint32_t)ceil_div(sp.P, BP);
+      ps.ny[i] = (uint32_t)S_out[first + i];
+      gx = std::max(gx, ps.nx[i]);
+      gy = std::max(gy, ps.ny[i]);
+    }
+    ProfScope prof(kind, s);
+    const dim3 grid(gx, gy, ps.nj);
+    if (cd == CD_BF16) k_skinny<CD_BF16, 0><<<grid, dim3(kThreads), 0, s>>>(ps);
+    else k_skinny<CD_F16, 0><<<grid, dim3(kThreads), 0, s>>>(ps);
+    int rc = check_launch("k_skinny");
+    if (rc) return rc;
+  }
+  return QLORA_OK;
 }
 
 int skinny(int cd, bool tn, const void* a, int64_t lda, int64_t arows, const void* b, int64_t ldb, int64_t P,
