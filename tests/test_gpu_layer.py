@@ -278,6 +278,21 @@ def test_backward_ragged(cd, path, M, N, K, r):
     assert_close(to_np(db), rdb, cd, "dB")
 
 
+@pytest.mark.parametrize("cd", ["bf16", "f16"])
+def test_backward_four_tile_transposed_dequantize_partial_slab(cd):
+    """dX on the dequantize path with W~^T from the four-tile transposed dequantize
+    (4096 x 4160: 64 row slabs x 17 column slabs of 256, the last a quarter full)."""
+    L = inputs.random_layer(130, 4096, 4160, 16, seed=41, cd=cd)
+    say("bwd multi-tile dequant^T partial slab", cd)
+    g = to_gpu(L)
+    dx, da, db = run_bwd(L, g, gpu_q(L, g), path="dequant")
+    o = oracle_layer(L)
+    rdx, rda, rdb = oracle.backward(o["x"], o["W"], o["A"], o["B"], o["dY"], o["s"])
+    assert_close(to_np(dx), rdx, cd, "dX")
+    assert_close(to_np(da), rda, cd, "dA")
+    assert_close(to_np(db), rdb, cd, "dB")
+
+
 def test_backward_saved_t_matches_recompute():
     L = inputs.random_layer(200, 192, 256, 16, seed=9)
     say("bwd saved T0")
