@@ -20,6 +20,7 @@ Also reported on the same line, each against its own MI355X roofline:
   dtype_sweep  the prefill forward in bf16, f16 and f32 compute (10 warm-up, 100 timed passes)
   merge     the adapter merge of the block's seven projections, GB/s
   stack_train_step  forward + MSE + backward + AdamW of a 3-layer stack of projection shapes
+  share_step  the headline step at 512 tokens (one GPU's share of 8-way data parallelism)
   cpu_baseline  the oracle (plain C, fp64) on a bounded sample of the step's work
   roofline  the dominant kernel of the step, timed with HIP events on its stream
 
@@ -41,6 +42,7 @@ METRIC = "fused NF4 QLoRA linear TFLOP/s (prefill/bwd) + GEMV HBM GB/s, % of roo
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+SHARE_TOKENS = 512  # one GPU's tokens when 4096 are split data-parallel over 8 GPUs
 
 
 def log(*a):
@@ -205,8 +207,8 @@ def percentiles(ms):
     return {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4), "n": len(v)}
 
 
-def bench_step(args, qn, torch, lib, inputs, flags=0, hashes=None, grouped=False):
-    layers, keep = build_block("bf16", True, qn, torch, lib, inputs, flags=flags, hashes=hashes)
+def bench_step(args, qn, torch, lib, inputs, flags=0, hashes=None, grouped=False, m=4096):
+    layers, keep = build_block("bf16", True, qn, torch, lib, inputs, m=m, flags=flags, hashes=hashes)
     units = layers
     if grouped:  # projections that read the same x as one call each (q / k / v, gate / up)
         by = {l.name: l for l in layers}
@@ -797,7 +799,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "projstep", "fusedstep", "groupstep", "gemv", "quant", "sweep",
+    ap.add_argument("--only", choices=["step", "projstep", "fusedstep", "groupstep", "sharestep", "gemv", "quant", "sweep",
                                        "merge", "stack", "copyprobe", "paths"],
                     default=None,
                     help="run one part (for profiling); the JSON line needs the full run")
@@ -837,10 +839,10 @@ def main():
         print(json.dumps(bench_stack(qn, torch, inputs)))
         return
 
-    if args.only in ("fusedstep", "groupstep", "projstep"):
-        grouped = "both" if args.only == "groupstep" else False
+    if args.only in ("fusedstep", "groupstep", "projstep", "sharestep"):
+        grouped = {"groupstep": "both", "sharestep": "fwd"}.get(args.only, False)
         st = bench_step(args, qn, torch, lib, inputs, flags=qn._lib.QLORA_FLAG_FUSED if args.only == "fusedstep" else 0,
-                        grouped=grouped)
+                        grouped=grouped, m=SHARE_TOKENS if args.only == "sharestep" else 4096)
         print(json.dumps({"ms_per_step": st["sec"] * 1e3, "kernels": st["kernels"], "roofline": st["roofline"]}))
         return
     hashes = {} if args.only is None else None
@@ -853,6 +855,8 @@ def main():
     log("per-projection step %.3f ms" % (stp["sec"] * 1e3))
     stf = bench_step(args, qn, torch, lib, inputs, flags=qn._lib.QLORA_FLAG_FUSED)
     log("fused step %.3f ms" % (stf["sec"] * 1e3))
+    sts = bench_step(args, qn, torch, lib, inputs, grouped="fwd", m=SHARE_TOKENS)
+    log("%d-token step %.3f ms" % (SHARE_TOKENS, sts["sec"] * 1e3))
     gemv = bench_gemv(qn, torch, lib, inputs)
     log("gemv done")
     quant = bench_quant(qn, torch, inputs)
@@ -906,6 +910,11 @@ def main():
                                 "forward": "each projection its own qlora_linear_fwd call",
                                 "backward": "per projection", "step_ms_device": stp["step_ms"],
                                 "roofline": stp["roofline"], "kernels": stp["kernels"]},
+        "share_step": {"tokens": SHARE_TOKENS, "ms_per_step": round(sts["sec"] * 1e3, 4),
+                       "tflops": round(sts["flops"] / sts["sec"] / 1e12, 2),
+                       "frac_bf16_peak": round(sts["flops"] / sts["sec"] / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "what": "the headline step at one GPU's share of an 8-way data-parallel 4096-token batch",
+                       "step_ms_device": sts["step_ms"], "kernels": sts["kernels"]},
         "gemv": gemv,
         "quantize": quant,
         "dtype_sweep_forward": sweep,
