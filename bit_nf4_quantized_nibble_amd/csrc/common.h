@@ -275,6 +275,7 @@ int skinny_many(int cd, const SkSpec* specs, float* const* parts, int* S_out, in
 // thread per element; job 1 takes the workgroups after job 0's nblk).
 constexpr int kRedThreads = 256;
 constexpr int kRedBR = 64;  // rank columns of the skinny kernel's partial sums
+constexpr int kRedMaxS = 32;  // contraction slices of one rank product (and its reduction)
 struct RedJob {
   const float* part;
   const float* side;

@@ -336,7 +336,7 @@ void skinny_split(int64_t P, int64_t Kc, int* S, int64_t* kslice) {
   int64_t s = ceil_div(256, tiles);
   const int64_t steps = Kc / BK;
   if (s > steps) s = steps;
-  if (s > 8) s = 8;
+  if (s > kRedMaxS) s = kRedMaxS;
   if (s < 1) s = 1;
   const int64_t ks = round_up(ceil_div(Kc, s), BK);
   *kslice = ks;
@@ -478,7 +478,8 @@ bool red_job(const SkRed& r, RedJob& j) {
   const int64_t width = (r.outcd && wc > r.R) ? wc : r.R;
   const int64_t rows = ((r.outt || r.side_t) && r.ldt > r.P) ? r.ldt : r.P;
   const int64_t lim = 1LL << 31;
-  if (rows * width >= lim || 8 * r.P * BR >= 2 * lim || r.R * r.ldt >= lim || r.P * r.ldcd >= lim || r.S > 8)
+  if (rows * width >= lim || (int64_t)r.S * r.P * BR >= 2 * lim || r.R * r.ldt >= lim || r.P * r.ldcd >= lim ||
+      r.S > kRedMaxS)
     return false;
   j.part = r.part;
   j.side = r.side;

@@ -30,15 +30,19 @@ __device__ __forceinline__ void skreduce_block(const RedJobs& js, uint32_t blk) 
     store_cd<CD>(j.outcd, (int64_t)(pr * j.ldcd + t), 0.f);
     return;
   }
-  // every load leaves before the first add (slices past S read slice 0 and are
-  // dropped; without a side input the side load reads the first partial sum)
-  float v[8];
-#pragma unroll
-  for (int z = 0; z < 8; ++z) v[z] = j.part[((uint32_t)(z < (int)j.S ? z : 0) * j.P + pr) * kRedBR + t];  // S <= 8
+  // slices in groups of 8, every load of a group issued before its first add
+  // (slices past S read slice 0 and are dropped; without a side input the side load
+  // reads the first partial sum); the sum runs in slice order
   const float sv = *(j.side ? j.side + pr * j.R + t : j.part);
   float sum = 0.f;
+  for (int z0 = 0; z0 < (int)j.S; z0 += 8) {  // S <= kRedMaxS
+    float v[8];
 #pragma unroll
-  for (int z = 0; z < 8; ++z) sum += z < (int)j.S ? v[z] : 0.f;  // slice order
+    for (int z = 0; z < 8; ++z)
+      v[z] = j.part[((uint32_t)(z0 + z < (int)j.S ? z0 + z : 0) * j.P + pr) * kRedBR + t];
+#pragma unroll
+    for (int z = 0; z < 8; ++z) sum += z0 + z < (int)j.S ? v[z] : 0.f;
+  }
   if (j.out32) j.out32[j.trans ? t * j.P + pr : pr * j.R + t] = sum * j.sc32;
   if (j.outcd) store_cd<CD>(j.outcd, (int64_t)(pr * j.ldcd + t), sum * j.sccd);
   if (j.outt) store_cd<CD>(j.outt, (int64_t)(t * j.ldt + pr), sum * j.sccd);
