@@ -169,7 +169,7 @@ int check_ws(void* ws, size_t ws_bytes, size_t need, const char* who) {
 // stand-in, not device memory: the device address of each GPU's copy comes from
 // hipGetSymbolAddress with that GPU current, once per device, and only that
 // address is ever handed to kernels.
-constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr size_t kScratchBytes = (size_t)32 << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;

@@ -334,7 +334,7 @@ int dense256_forward(const LayerCall& c, const void* wd, const void* t_cd, int64
                      const DenseSplit& sp, void* split_ws);
 int dense256_dx(const LayerCall& c, const void* dy, const void* wdt, const void* dt_cd, int64_t r_pad, void* dx,
                 const DenseSplit& sp, void* split_ws, const void* a_t);
-DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1);
+DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1, bool fused = false);
 size_t dense_split_bytes(const DenseSplit& sp);
 // the rank-r products on the skinny MFMA kernel (lora.hip)
 bool skinny_ok(int cd, int64_t r);

@@ -479,7 +479,7 @@ FwdPlan plan_fwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   P.dense = dense_path(m, rows, cols, r, cd, flags, false);
   P.off_xm = P.off_wd + (P.dense && !(flags & kFlagCachedW) ? al(rows * cols * es) : 0);  // x M with LoRA dropout
   P.off_split = P.off_xm + ((flags & QLORA_FLAG_DROPOUT) ? al(m * cols * es) : 0);
-  P.dsp = dense_split(m, rows, cols);
+  P.dsp = dense_split(m, rows, cols, !P.dense);
   P.total = P.off_split + (big_tiles(cd) ? al(dense_split_bytes(P.dsp)) : 0);
   return P;
 }
@@ -534,7 +534,7 @@ BwdPlan plan_bwd(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32
   const bool drop = (flags & QLORA_FLAG_DROPOUT) != 0;
   P.off_zero = P.off_xm + (drop ? al(m * cols * es) : 0);
   P.off_split = P.off_zero + (drop ? al(m * P.r_pad * es) : 0);
-  P.dsp = dense_split(m, cols, rows);
+  P.dsp = dense_split(m, cols, rows, !P.dense);
   // A^T [cols][r_pad] in cd: the W-side rows of the dense dX GEMM's low-rank tail
   P.off_at = P.off_split + (big_tiles(cd) ? al(dense_split_bytes(P.dsp)) : 0);
   P.total = P.off_at + (P.dense ? al(cols * P.r_pad * es) : 0);

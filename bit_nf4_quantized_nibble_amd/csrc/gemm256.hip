@@ -1441,19 +1441,21 @@ int fused256_dx(const LayerCall& c, const void* dy, const void* dt_cd, int64_t r
 
 // One round is a tile per compute unit (the kernel needs most of a CU's LDS).  When
 // the last round is incomplete, its rem tiles are cut into split = 2 or 4
-// contraction slices, 8 when all the tokens fit one tile row (the largest that
-// keeps rem * split within one round and at least 4 stages per slice), so the
-// round's workgroups run about 1 / split as long.  (Measured on q + gate forwards:
-// 8 slices took 128 and 256 tokens from 0.111 / 0.119 to 0.096 / 0.111 ms; at 512
-// tokens the doubled partial sums cost the dequantize-then-GEMM path 6%.)
-DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1) {
+// contraction slices, 8 when all the tokens fit one tile row or, for the fused
+// kernels, two (the largest that keeps rem * split within one round and at least 4
+// stages per slice), so the round's workgroups run about 1 / split as long.
+// (Measured on q + gate forwards: 8 slices took 128 and 256 tokens from 0.111 /
+// 0.119 to 0.096 / 0.111 ms; at 512 tokens the doubled partial sums cost the
+// dequantize-then-GEMM path 6%, while the decode-bound fused kernel gains: the
+// block's training step at 300 / 512 tokens 1.07 / 1.15 -> 1.03 / 1.11 ms.)
+DenseSplit dense_split(int64_t m, int64_t nb, int64_t k1, bool fused) {
   const int64_t C = cu_count();
   const int64_t tiles = ceil_div(m, TILE) * ceil_div(nb, TILE);
   DenseSplit d = {(int32_t)tiles, 0, 1};
   const int64_t F = tiles / C, R = tiles - F * C;
   if (R == 0) return d;
   const int64_t cap = std::min<int64_t>(C / R, (k1 / BK) / 4);
-  const int32_t smax = m <= TILE ? 8 : 4;
+  const int32_t smax = (m <= TILE || (fused && m <= 2 * TILE)) ? 8 : 4;
   int32_t S = 1;
   while (S < smax && 2 * S <= cap) S *= 2;
   if (S == 1) return d;

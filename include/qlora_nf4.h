@@ -389,7 +389,7 @@ int qlora_linear_fwd_cached(const void* w_cd, int64_t rows, int64_t cols, const 
  * The forward for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
  * results and errors as qlora_linear_fwd without the workspace: the call uses a
- * scratch array of qlora_noalloc_scratch_bytes() bytes (16 MiB) that the library
+ * scratch array of qlora_noalloc_scratch_bytes() bytes (32 MiB) that the library
  * holds in each GPU's memory for the life of the process, and calls no allocating
  * routine.  Above 16 tokens it takes the fused kernels (no copy of W~) unless
  * flags has QLORA_FLAG_DEQUANT_GEMM.  A call whose workspace

@@ -50,7 +50,7 @@ def test_noalloc_matches_workspace_entry_point(cases):
 def test_noalloc_refuses_calls_beyond_its_scratch():
     lib = _lib.lib()
     cap = lib.qlora_noalloc_scratch_bytes()
-    assert cap == 16 << 20
+    assert cap == 32 << 20
     # gate_proj shape at 4096 tokens on the fused path: its cut last round needs 64 MiB
     need = qn.workspace_bytes(_lib.QLORA_OP_FWD, 4096, 14336, 4096, 64, torch.bfloat16, _lib.QLORA_FLAG_FUSED)
     assert need > cap
