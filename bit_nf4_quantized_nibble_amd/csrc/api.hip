@@ -271,7 +271,14 @@ void prof_begin(int kind, hipStream_t s, void** token) {
     g_prof_free.pop_back();
   } else {
     p = new ProfRec;
-    if (hipEventCreate(&p->a) != hipSuccess || hipEventCreate(&p->b) != hipSuccess) {
+    // timing-only events: no system-scope cache writeback and invalidation when they
+    // are recorded, so the pair brackets the launch and not a flush around it
+    if (hipEventCreateWithFlags(&p->a, hipEventDisableSystemFence) != hipSuccess) {
+      delete p;
+      return;
+    }
+    if (hipEventCreateWithFlags(&p->b, hipEventDisableSystemFence) != hipSuccess) {
+      (void)hipEventDestroy(p->a);
       delete p;
       return;
     }
