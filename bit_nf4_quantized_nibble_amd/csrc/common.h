@@ -287,10 +287,13 @@ struct RedJob {
   float sc32, sccd;
   int trans;
 };
+constexpr int kRedJobs = 4;  // reductions one launch can carry
 struct RedJobs {
-  RedJob j[2];
+  RedJob j[kRedJobs];  // job w takes the workgroups after jobs 0 .. w-1 (unused jobs: nblk 0)
 };
 int make_red_jobs(const SkRed& a, const SkRed* b, RedJobs& js, int64_t& blocks);
+// Up to kRedJobs reductions (reds[0 .. n)) for one launch.
+int make_red_jobs_n(const SkRed* reds, int n, RedJobs& js, int64_t& blocks);
 
 // dst [cols][ld_dst] = cd(scale * src[rows][ld_src]^T) (src in the compute dtype or
 // fp32), columns rows .. ld_dst-1 of dst zero; one launch carries one or two.
@@ -311,11 +314,13 @@ int rank_add_masked(int cd, void* dx, const uint8_t* mask, const void* dt, int64
                     int64_t M, int64_t K, hipStream_t s);
 size_t fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags);
 size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd, int32_t flags);
-// red: a reduction that rides on the same launch (its workgroups follow the
+// red: a reduction that rides on the same launch (its workgroups come ahead of the
 // dequantize ones), or null.
 // W~ into out: [rows, cols], or transposed [cols][ldo] (ldo = 0: rows) for the dX GEMM.
 int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s, const SkRed* red = nullptr,
                  int64_t ldo = 0);
+// The group forward's weights in one launch: W~_i into outs[i], reds[i] riding on it.
+int dequant_group_into(const Nf4W* ws, int g, int cd, void* const* outs, const SkRed* reds, hipStream_t s);
 int launch_forward(const LayerCall& c, void* y, float* t_save);
 size_t cached_fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
 int launch_forward_cached(const LayerCall& c, const void* wd, void* y, float* t_save);

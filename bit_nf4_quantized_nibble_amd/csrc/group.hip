@@ -254,8 +254,8 @@ int launch_forward_group(const GroupCall& gc, const void* bias, void* y, float* 
     return QLORA_OK;
   }
   // T_i = s_i x A_i^T into its slice of T: the group's products in one launch (they
-  // read the same x), each reduction riding on W_i's dequantize, which writes W~_i
-  // into rows off_i .. of the concatenated W~
+  // read the same x), their reductions riding on one dequantize launch that writes
+  // each W~_i into rows off_i .. of the concatenated W~
   SkSpec specs[kGroupMax];
   float* parts[kGroupMax];
   int Ss[kGroupMax];
@@ -272,9 +272,12 @@ int launch_forward_group(const GroupCall& gc, const void* bias, void* y, float* 
     parts[i] = (float*)(w + P.part + i * P.part_each);
   }
   if ((rc = skinny_many(c0.cd, specs, parts, Ss, gc.g, s, QLORA_K_LORA_DOWN))) return rc;
+  Nf4W wts[kGroupMax];
+  void* outs[kGroupMax];
+  SkRed reds[kGroupMax];
   for (int i = 0; i < gc.g; ++i) {
     const LayerCall& c = gc.c[i];
-    SkRed red;
+    SkRed& red = reds[i];
     red.part = parts[i];
     red.S = Ss[i];
     red.P = m;
@@ -284,8 +287,10 @@ int launch_forward_group(const GroupCall& gc, const void* bias, void* y, float* 
     red.outcd = w + P.tcd + gc.toff[i] * es;
     red.ldcd = gc.RP;
     red.wcd = slice_width(gc, i);
-    if ((rc = dequant_into(c.w, c.cd, w + P.wd + gc.off[i] * K * es, false, s, &red))) return rc;
+    wts[i] = c.w;
+    outs[i] = w + P.wd + gc.off[i] * K * es;
   }
+  if ((rc = dequant_group_into(wts, gc.g, c0.cd, outs, reds, s))) return rc;
   DiagArgs a = {};
   a.g = gc.g;
   a.N = gc.N;

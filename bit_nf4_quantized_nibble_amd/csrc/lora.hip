@@ -502,6 +502,20 @@ bool red_job(const SkRed& r, RedJob& j) {
 }
 }  // namespace
 
+// The device form of up to kRedJobs reductions and the workgroups they take.
+int make_red_jobs_n(const SkRed* reds, int n, RedJobs& js, int64_t& blocks) {
+  js = RedJobs{};
+  blocks = 0;
+  if (n > kRedJobs) return set_error(QLORA_ERR_UNSUPPORTED, "rank product: %d reductions in one launch", n);
+  for (int i = 0; i < n; ++i) {
+    if (!red_job(reds[i], js.j[i]))
+      return set_error(QLORA_ERR_UNSUPPORTED, "rank product: %lld x %lld too large", (long long)reds[i].P,
+                       (long long)reds[i].R);
+    blocks += js.j[i].nblk;
+  }
+  return QLORA_OK;
+}
+
 // The device form of one or two reductions and the workgroups they take.
 int make_red_jobs(const SkRed& a, const SkRed* b, RedJobs& js, int64_t& blocks) {
   js = RedJobs{};

@@ -383,18 +383,35 @@ __device__ __forceinline__ float scale_of(uint32_t qa, uint32_t s2) {
 // instruction covers contiguous memory across the wave.  All 8 chunks' codes and
 // scales are requested before the first is used; chunks past the end read past the
 // buffers (zeros) and store nothing.  Same values as k_dequantize.
-// The first gridDim.x - nmain workgroups run the reduction `red` instead (see
+// The first gridDim.x - nmain workgroups run the reductions `red` instead (see
 // reduce_dev.h): placed ahead of the dequantize, their load latency overlaps it
-// instead of trailing the launch.
+// instead of trailing the launch.  One launch can dequantize up to kDqParts
+// weights (the projections of a group, each into its own output): the workgroups
+// after the reductions take part 0's chunks, then part 1's, and so on.
+constexpr int kDqParts = 4;
+struct DqParts {
+  Nf4W w[kDqParts];
+  void* out[kDqParts];
+  int64_t n[kDqParts];      // elements of part i
+  uint32_t end[kDqParts];   // workgroups of parts 0 .. i
+  int32_t np;
+};
 template <int OUT, int DQ>
-__global__ __launch_bounds__(kThreads) void k_dequant_chunks(Nf4W q, int64_t n, void* __restrict__ out,
-                                                             Nf4Tables tab, RedJobs red, uint32_t nmain) {
+__global__ __launch_bounds__(kThreads) void k_dequant_chunks(DqParts ps, Nf4Tables tab, RedJobs red, uint32_t nmain) {
   const uint32_t nred = gridDim.x - nmain;
   if (blockIdx.x < nred) {
     skreduce_block<OUT == CD_F16 ? CD_F16 : CD_BF16>(red, blockIdx.x);
     return;
   }
-  const uint32_t bx = blockIdx.x - nred;
+  uint32_t bx = blockIdx.x - nred;
+  int pi = 0;  // the part (uniform across the workgroup)
+#pragma unroll
+  for (int k = 0; k < kDqParts - 1; ++k)
+    if (pi == k && k + 1 < ps.np && bx >= ps.end[k]) pi = k + 1;
+  if (pi > 0) bx -= ps.end[pi - 1];
+  const Nf4W& q = ps.w[pi];
+  const int64_t n = ps.n[pi];
+  void* __restrict__ out = ps.out[pi];
   __shared__ float s_lv[16];
   if (threadIdx.x < 16) s_lv[threadIdx.x] = tab.lv[threadIdx.x];
   const rsrc_t rc = make_rsrc(q.codes, n / 2);
@@ -674,6 +691,39 @@ int ride_along(const SkRed* red, RedJobs& js, int64_t& blocks) {
 
 // Flat dequantize of all rows * cols elements into out (f32 / bf16 / f16); `red`
 // (bf16 / f16 only) rides on the same launch.
+// Whether k_dequant_chunks takes this weight (and, with a riding reduction, this dtype).
+bool chunks_ok(const Nf4W& w, int cd, bool red) {
+  const int64_t n = w.rows * w.cols;
+  return w.bs_shift >= 3 && n % 8 == 0 && (!w.dq || w.g_shift >= 0) && n / 2 < (1LL << 31) &&
+         !(red && cd == CD_F32);
+}
+
+// One k_dequant_chunks launch over np parts (all with or all without double
+// quantization) and the reductions riding on it.
+int launch_chunks(const DqParts& ps, int cd, bool dq, const RedJobs& js, int64_t nred, hipStream_t s) {
+  const int64_t grid = ps.end[ps.np - 1];
+  if (grid + nred > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
+  const Nf4Tables& t = host_tables();
+  const dim3 g((unsigned)(grid + nred)), blk(kThreads);
+  const uint32_t nm = (uint32_t)grid;
+  if (cd == CD_BF16) {
+    if (dq) k_dequant_chunks<CD_BF16, 1><<<g, blk, 0, s>>>(ps, t, js, nm);
+    else k_dequant_chunks<CD_BF16, 0><<<g, blk, 0, s>>>(ps, t, js, nm);
+  } else if (cd == CD_F16) {
+    if (dq) k_dequant_chunks<CD_F16, 1><<<g, blk, 0, s>>>(ps, t, js, nm);
+    else k_dequant_chunks<CD_F16, 0><<<g, blk, 0, s>>>(ps, t, js, nm);
+  } else if (cd == CD_F32) {
+    if (dq) k_dequant_chunks<CD_F32, 1><<<g, blk, 0, s>>>(ps, t, js, nm);
+    else k_dequant_chunks<CD_F32, 0><<<g, blk, 0, s>>>(ps, t, js, nm);
+  } else {
+    return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
+  }
+  return check_launch("k_dequant_chunks");
+}
+
+// The workgroups of k_dequant_chunks for n elements.
+int64_t chunk_wgs(int64_t n) { return ceil_div(n / 8, kThreads * 8); }
+
 int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s, const SkRed* red) {
   const int64_t n = w.rows * w.cols;
   const Nf4Tables& t = host_tables();
@@ -682,24 +732,14 @@ int dequant_flat(const Nf4W& w, int cd, void* out, hipStream_t s, const SkRed* r
   int rc = ride_along(red, js, nred);
   if (rc) return rc;
   ProfScope prof(QLORA_K_DEQUANTIZE, s);
-  if (w.bs_shift >= 3 && n % 8 == 0 && (!w.dq || w.g_shift >= 0) && n / 2 < (1LL << 31) &&
-      !(red && cd == CD_F32)) {
-    const int64_t grid = ceil_div(n / 8, kThreads * 8);
-    if (grid + nred > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: tensor too large");
-    const dim3 g((unsigned)(grid + nred)), blk(kThreads);
-    const uint32_t nm = (uint32_t)grid;
-    if (cd == CD_BF16) {
-      if (w.dq) k_dequant_chunks<CD_BF16, 1><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
-      else k_dequant_chunks<CD_BF16, 0><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
-    } else if (cd == CD_F16) {
-      if (w.dq) k_dequant_chunks<CD_F16, 1><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
-      else k_dequant_chunks<CD_F16, 0><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
-    } else if (cd == CD_F32) {
-      if (w.dq) k_dequant_chunks<CD_F32, 1><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
-      else k_dequant_chunks<CD_F32, 0><<<g, blk, 0, s>>>(w, n, out, t, js, nm);
-    }
-    else return set_error(QLORA_ERR_DTYPE, "dequantize: bad dtype %d", cd);
-    return check_launch("k_dequant_chunks");
+  if (chunks_ok(w, cd, red != nullptr)) {
+    DqParts ps = {};
+    ps.w[0] = w;
+    ps.out[0] = out;
+    ps.n[0] = n;
+    ps.end[0] = (uint32_t)chunk_wgs(n);  // n / 2 < 2^31
+    ps.np = 1;
+    return launch_chunks(ps, cd, w.dq != 0, js, nred, s);
   }
   if (red && (rc = skinny_reduce_jobs(cd, *red, nullptr, s))) return rc;
   if (w.bs % 8 == 0 && n % 32 == 0) {
@@ -733,6 +773,38 @@ void run_dqt(bool four, uint32_t gx, uint32_t nmain, int64_t nred, const Nf4W& w
 // (forward) or its transpose [cols][ldo] (dX; ldo = 0 means rows, a larger ldo
 // writes W~^T as the column slice of a wider matrix).  The transpose needs rows and
 // cols to be multiples of 64.
+// W~_i of g weights into outs[i] (flat, rows_i x cols_i each), reds[i] riding on the
+// same launch: one launch when every weight takes k_dequant_chunks with the same
+// double-quantization setting and g <= kDqParts, else one dequantize each.
+int dequant_group_into(const Nf4W* ws, int g, int cd, void* const* outs, const SkRed* reds, hipStream_t s) {
+  bool one = g >= 1 && g <= kDqParts && g <= kRedJobs;
+  for (int i = 0; i < g && one; ++i) one = chunks_ok(ws[i], cd, true) && ws[i].dq == ws[0].dq;
+  if (!one) {
+    for (int i = 0; i < g; ++i) {
+      const int rc = dequant_into(ws[i], cd, outs[i], false, s, &reds[i]);
+      if (rc) return rc;
+    }
+    return QLORA_OK;
+  }
+  RedJobs js;
+  int64_t nred;
+  int rc = make_red_jobs_n(reds, g, js, nred);
+  if (rc) return rc;
+  ProfScope prof(QLORA_K_DEQUANTIZE, s);
+  DqParts ps = {};
+  int64_t e = 0;
+  for (int i = 0; i < g; ++i) {
+    ps.w[i] = ws[i];
+    ps.out[i] = outs[i];
+    ps.n[i] = ws[i].rows * ws[i].cols;
+    e += chunk_wgs(ps.n[i]);
+    if (e > 0x7fffffff) return set_error(QLORA_ERR_UNSUPPORTED, "dequantize: group too large");
+    ps.end[i] = (uint32_t)e;
+  }
+  ps.np = g;
+  return launch_chunks(ps, cd, ws[0].dq != 0, js, nred, s);
+}
+
 int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t s, const SkRed* red, int64_t ldo) {
   if (transposed) {
     if (ldo == 0) ldo = w.rows;

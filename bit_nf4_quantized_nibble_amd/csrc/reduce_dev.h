@@ -10,13 +10,20 @@ namespace qnf4 {
 
 // Reductions of per-slice partial sums (see SkRed), one thread per element of a
 // rows x width grid (rows: P, or ldt with a transposed output; width: R, or ldcd
-// with a padded cd output); workgroups [0, nblk of job 0) take job 0, the rest
-// job 1.  32-bit indexing (the launcher checks the sizes).
+// with a padded cd output); workgroups [0, nblk of job 0) take job 0, the next
+// nblk of job 1 job 1, and so on.  32-bit indexing (the launcher checks the sizes).
 template <int CD>
 __device__ __forceinline__ void skreduce_block(const RedJobs& js, uint32_t blk) {
-  const int w = blk >= js.j[0].nblk ? 1 : 0;
+  int w = 0;
+  uint32_t b = blk;
+#pragma unroll
+  for (int k = 0; k < kRedJobs - 1; ++k)
+    if (w == k && b >= js.j[k].nblk) {
+      b -= js.j[k].nblk;
+      w = k + 1;
+    }
   const RedJob& j = js.j[w];
-  const uint32_t idx = (blk - (w ? js.j[0].nblk : 0u)) * kRedThreads + threadIdx.x;
+  const uint32_t idx = b * kRedThreads + threadIdx.x;
   if (idx >= j.rows * j.width) return;
   const uint32_t pr = idx / j.width, t = idx - pr * j.width;
   if (pr >= j.P) {  // zero columns P .. ldt-1 of the transposed copies
