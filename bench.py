@@ -14,7 +14,8 @@ same step with every projection a call of its own (per_projection_step), and for
 onto the fused dequant-GEMM kernels (QLORA_FLAG_FUSED, fused_path_step).
 
 Also reported on the same line, each against its own MI355X roofline:
-  gemv      decode forward at m = 1, 4, 16 (4096x4096, r = 16), GB/s over cold weights
+  gemv      decode forward at m = 1, 4, 16 (4096x4096, r = 16), GB/s over cold weights, and one
+            token through the block's seven projections (per projection and grouped)
   quantize  NF4 quantize of a 4096x4096 fp32 weight without / with double quant, GB/s
   dequantize  the double-quantized weight back to bf16 / fp32, GB/s
   dtype_sweep  the prefill forward in bf16, f16 and f32 compute (10 warm-up, 100 timed passes)
@@ -121,16 +122,19 @@ class GroupUnit:
         self.da = (vp * g)(*[l.da.data_ptr() for l in layers])
         self.db = (vp * g)(*[l.db.data_ptr() for l in layers])
         self.y = torch.empty(M, N, dtype=x.dtype, device="cuda")
-        self.dy = torch.cat([l.dY for l in layers], dim=1).contiguous()
-        self.dx = torch.empty(M, K, dtype=x.dtype, device="cuda")
         cd = qn.dtype_code(x.dtype)
         wsf = lib.qlora_group_workspace_bytes(0, g, self.w, M, self.r, cd)
-        wsb = lib.qlora_group_workspace_bytes(1, g, self.w, M, self.r, cd)
         self.ws_f = torch.empty(max(wsf, 1), dtype=torch.uint8, device="cuda")
-        self.ws_b = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
         stream = torch.cuda.current_stream().cuda_stream
         self.fwd_args = (g, self.w, x.data_ptr(), M, self.a, self.b, self.r, self.alpha, 0, None, cd,
                          self.y.data_ptr(), self.t0, self.ws_f.data_ptr(), self.ws_f.numel(), stream)
+        if layers[0].dY is None:  # forward only
+            self.bwd_args = None
+            return
+        self.dy = torch.cat([l.dY for l in layers], dim=1).contiguous()
+        self.dx = torch.empty(M, K, dtype=x.dtype, device="cuda")
+        wsb = lib.qlora_group_workspace_bytes(1, g, self.w, M, self.r, cd)
+        self.ws_b = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
         self.bwd_args = (g, self.w, x.data_ptr(), self.dy.data_ptr(), M, self.a, self.b, self.r, self.alpha, 0, cd,
                          self.t0, self.dx.data_ptr(), self.da, self.db, self.ws_b.data_ptr(), self.ws_b.numel(),
                          stream)
@@ -494,6 +498,65 @@ def gemv_stream(torch, f, sets, layer_bytes, replays=10):
             "replays_match_eager": ok}
 
 
+def bench_decode_block(qn, torch, lib, inputs, copies=3, replays=10):
+    """Decode (one token) of the block's seven projections, r 64: every projection a
+    call of its own, and q / k / v and gate / up as one group call each; `copies`
+    copies of the block's weights (more than the 256 MB last-level cache) in turn,
+    each form captured in a HIP graph and replayed (every replay's outputs must equal
+    the eager ones)."""
+    blocks = [build_block("bf16", False, qn, torch, lib, inputs, m=1) for _ in range(copies)]
+    nbytes = 0
+    for l in blocks[0][0]:
+        n, k, r = l.N, l.K, l.r
+        nbytes += n * k // 2 + n * k // 64 + n * k // 64 // 256 * 4 + 2 * k + 2 * r * k + 2 * n * r + 2 * n
+    out = {"tokens": 1, "bytes_per_block": nbytes}
+    for form in ("per_projection", "grouped"):
+        calls, outs = [], []
+        for layers, keep in blocks:
+            if form == "grouped":
+                by = {l.name: l for l in layers}
+                units = [GroupUnit([by[n] for n in grp], keep[0][by[grp[0]].K], torch, lib, qn, False)
+                         if len(grp) > 1 else by[grp[0]] for grp in GROUPS]
+            else:
+                units = layers
+            for u in units:
+                grouped = isinstance(u, GroupUnit)
+                calls.append((lib.qlora_linear_fwd_group if grouped else lib.qlora_linear_fwd, u.fwd_args))
+                outs.append(u.y)
+        for f, a in calls:
+            if f(*a):
+                raise RuntimeError("decode block: %s" % lib.qlora_last_error())
+        torch.cuda.synchronize()
+        eager = [y.clone() for y in outs]
+        st = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            h = torch.cuda.current_stream().cuda_stream
+            for f, a in calls:
+                if f(*(a[:-1] + (h,))):
+                    raise RuntimeError("decode block capture: %s" % lib.qlora_last_error())
+        for y in outs:
+            y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        ok = all(torch.equal(y, e) for y, e in zip(outs, eager))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ok = ok and all(torch.equal(y, e) for y, e in zip(outs, eager))
+        us = e0.elapsed_time(e1) / (replays * copies) * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[form] = {"us_per_block": round(us, 2), "calls_per_block": len(calls) // copies, "gbs": round(gbs, 1),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "replays_match_eager": ok}
+        del g
+    del blocks
+    torch.cuda.empty_cache()
+    return out
+
+
 def move_probe(torch, nbytes=8933376, copies=40, replays=10):
     """Empirical ceiling of one small launch that moves ~9 MB through HBM: a plain
     device copy of nbytes / 2 into another nbytes / 2 (read + write = nbytes), 40
@@ -799,7 +862,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "projstep", "fusedstep", "groupstep", "sharestep", "gemv", "quant", "sweep",
+    ap.add_argument("--only", choices=["step", "projstep", "fusedstep", "groupstep", "sharestep", "gemv", "decodeblock", "quant", "sweep",
                                        "merge", "stack", "copyprobe", "paths"],
                     default=None,
                     help="run one part (for profiling); the JSON line needs the full run")
@@ -819,6 +882,9 @@ def main():
 
     if args.only == "gemv":
         print(json.dumps(bench_gemv(qn, torch, lib, inputs)))
+        return
+    if args.only == "decodeblock":
+        print(json.dumps(bench_decode_block(qn, torch, lib, inputs)))
         return
     if args.only == "copyprobe":
         print(json.dumps(copy_probe(torch)))
@@ -859,6 +925,8 @@ def main():
     log("%d-token step %.3f ms" % (SHARE_TOKENS, sts["sec"] * 1e3))
     gemv = bench_gemv(qn, torch, lib, inputs)
     log("gemv done")
+    gemv["decode_block"] = bench_decode_block(qn, torch, lib, inputs)
+    log("decode block done")
     quant = bench_quant(qn, torch, inputs)
     log("quant done")
     sweep = bench_dtype_sweep(qn, torch, lib, inputs)

@@ -230,6 +230,7 @@ struct LayerCall {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  int64_t ldy = 0;    // row stride of y in elements (0: rows); the decode GEMV honours it
 };
 
 // One reduction of the skinny kernel's per-slice partial sums part [S][P][64] (fp32,
@@ -322,6 +323,9 @@ int dequant_into(const Nf4W& w, int cd, void* out, bool transposed, hipStream_t 
 // The group forward's weights in one launch: W~_i into outs[i], reds[i] riding on it.
 int dequant_group_into(const Nf4W* ws, int g, int cd, void* const* outs, const SkRed* reds, hipStream_t s);
 int launch_forward(const LayerCall& c, void* y, float* t_save);
+// Whether launch_forward takes the decode GEMV for this call (which writes y with
+// row stride c.ldy; the other forwards write [m, rows]).
+bool gemv_route(const LayerCall& c);
 size_t cached_fwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int cd);
 int launch_forward_cached(const LayerCall& c, const void* wd, void* y, float* t_save);
 int launch_backward(const LayerCall& c, const void* dy, const float* t_saved, void* dx,

@@ -952,9 +952,12 @@ size_t bwd_workspace_bytes(int64_t m, int64_t rows, int64_t cols, int32_t r, int
   return (size_t)plan_bwd(m, rows, cols, r, cd, flags).total;
 }
 
+bool gemv_route(const LayerCall& c) {
+  return !c.drop_mask && fast_layout(c.w) && gemv_candidate(c.m, c.flags) && (c.m <= kGemvMaxM || gemv_mfma_ok(c));
+}
+
 int launch_forward(const LayerCall& c, void* y, float* t_save) {
-  if (!c.drop_mask && fast_layout(c.w) && gemv_candidate(c.m, c.flags) && (c.m <= kGemvMaxM || gemv_mfma_ok(c)))
-    return gemv_forward(c, y, t_save);
+  if (gemv_route(c)) return gemv_forward(c, y, t_save);
   switch (c.cd) {
     case CD_BF16: return forward_gemm<CD_BF16>(c, y, t_save);
     case CD_F16: return forward_gemm<CD_F16>(c, y, t_save);

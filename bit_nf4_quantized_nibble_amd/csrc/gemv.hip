@@ -89,7 +89,8 @@ struct GemvP {
   int32_t r;
   float scale;        // s
   const void* bias;   // [N] cd or null
-  void* y;            // [M, N] cd
+  void* y;            // [M, ldy] cd
+  int64_t ldy;        // row stride of y (>= N)
   float* t0;          // [M, r] fp32 x A^T, or null
   float* part;        // [S][mp][ld] fp32 partial sums, ld = n_pad + r_pad, mp = m rounded up to 16
   int64_t n_pad, ld, mp;
@@ -544,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_epi(GemvP p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) lora = fmaf(tv[e], bf[8 * q + e], lora);
           }
-        if (n < N) store_cd<CD>(p.y, (m0 + j) * N + n, v + lora + bias);
+        if (n < N) store_cd<CD>(p.y, (m0 + j) * p.ldy + n, v + lora + bias);
       }
     }
     return;
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_epi(GemvP p) {
     const float v = slice_sum(pm0 + (int64_t)j * p.ld + nc);
     float lora = 0.f;
     for (int t = 0; t < p.r; ++t) lora = fmaf(s_t[j * p.r + t], load_cd<CD>(p.B, nc * p.r + t), lora);
-    if (n < N) store_cd<CD>(p.y, (m0 + j) * N + n, v + lora + bias);
+    if (n < N) store_cd<CD>(p.y, (m0 + j) * p.ldy + n, v + lora + bias);
   }
 }
 
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(Nf4W w, const void* __restric
                                                    const float* __restrict__ T,
                                                    const void* __restrict__ B, int32_t r,
                                                    const void* __restrict__ bias, void* __restrict__ y,
-                                                   Nf4Tables tab) {
+                                                   int64_t ldy, Nf4Tables tab) {
   __shared__ float s_lv[16];
   if (threadIdx.x < 16) s_lv[threadIdx.x] = tab.lv[threadIdx.x];
   __syncthreads();
@@ -630,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(Nf4W w, const void* __restric
     for (int t = 0; t < r; ++t) lora = fmaf(T[(int64_t)lane * r + t], load_cd<CD>(B, n * r + t), lora);
     v += lora;
     if (bias) v += load_cd<CD>(bias, n);
-    store_cd<CD>(y, (int64_t)lane * w.rows + n, v);
+    store_cd<CD>(y, (int64_t)lane * ldy + n, v);
   }
 }
 
@@ -708,6 +709,7 @@ int gemv_forward_t(const LayerCall& c, void* y, float* t_save) {
       p.scale = c.scale;
       p.bias = c.bias;
       p.y = y;
+      p.ldy = c.ldy ? c.ldy : c.w.rows;
       p.t0 = t_save;
       p.part = (float*)(ws + P.off_part);
       p.n_pad = P.n_pad;
@@ -759,7 +761,7 @@ int gemv_forward_t(const LayerCall& c, void* y, float* t_save) {
   }
   ProfScope prof(QLORA_K_GEMV, c.stream);
   k_gemv<CD><<<dim3((unsigned)ceil_div(c.w.rows, kThreads / 64)), dim3(kThreads), 0, c.stream>>>(
-      c.w, c.x, c.m, T, c.lora_b, c.r, c.bias, y, host_tables());
+      c.w, c.x, c.m, T, c.lora_b, c.r, c.bias, y, c.ldy ? c.ldy : c.w.rows, host_tables());
   return check_launch("k_gemv");
 }
 

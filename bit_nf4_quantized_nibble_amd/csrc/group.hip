@@ -244,10 +244,17 @@ int launch_forward_group(const GroupCall& gc, const void* bias, void* y, float* 
   const int64_t m = c0.m, K = c0.w.cols, es = cd_bytes(c0.cd);
   int rc;
   if (!P.tiled) {
+    // each projection by itself: the decode GEMV writes its columns of y in place (row
+    // stride N), the other forwards into the workspace and a copy places them
     for (int i = 0; i < gc.g; ++i) {
       LayerCall c = gc.c[i];
       c.bias = bias ? (const char*)bias + gc.off[i] * es : nullptr;
       c.ws = w + P.single;
+      if (gemv_route(c)) {
+        c.ldy = gc.N;
+        if ((rc = launch_forward(c, (char*)y + gc.off[i] * es, t_save ? t_save[i] : nullptr))) return rc;
+        continue;
+      }
       if ((rc = launch_forward(c, w + P.tmp, t_save ? t_save[i] : nullptr))) return rc;
       if ((rc = copy_cols(c.cd, w + P.tmp, c.w.rows, (char*)y + gc.off[i] * es, gc.N, m, c.w.rows, s))) return rc;
     }
