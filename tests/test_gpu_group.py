@@ -95,6 +95,8 @@ def test_group_tiled(M, K, shapes, cd, bias):
     (48, 1024, [(256, 16), (64, 8)], "bf16", True),    # few tokens: the split-K GEMV per projection
     (1, 1024, [(512, 16), (128, 8), (128, 8)], "bf16", True),  # decode: each GEMV writes its columns of y
     (16, 2048, [(256, 16), (256, 16)], "f16", False),
+    (1, 1024, [(512, 16), (256, 16), (256, 16)], "bf16", True),  # q / k / v-like
+    (4, 1024, [(256, 8), (512, 8), (256, 8), (256, 8)], "bf16", False),  # four projections
     (7, 512, [(96, 8), (64, 4)], "f32", True),          # the VALU GEMV, in place as well
     (100, 256, [(200, 8), (72, 4)], "bf16", True),     # rows not a multiple of 64
     (90, 128, [(64, 8), (64, 8), (32, 4)], "f32", False),
